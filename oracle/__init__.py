@@ -1,0 +1,33 @@
+"""CPU oracle for the deterministic gradient reductions — TEST INFRASTRUCTURE ONLY.
+
+This package is a plain, slow, deliberately obvious CPU statement of what the
+four reductions compute, in IEEE-754 binary32 with round-to-nearest-even, one
+rounding per ``+ - * /`` and no fused multiply-add (numpy float32 ufuncs never
+fuse). It exists so that the GPU library can be checked against something that
+shares none of its code. Only the test suite, the smoke entry point and the CPU
+baseline leg of the benchmark may import it; the product path (the C-ABI
+library and its Python binding) never does.
+
+Modules
+-------
+primitives  the three reduction primitives every case uses: the adjacent
+            pairwise tree, the sequential left fold and the accumulate-add.
+detmath     exp / log1p / softplus / sigmoid built only from correctly rounded
+            basic operations, so two independent implementations agree bitwise.
+colsum      Gated-DeltaNet gate backward: per-head column sums (Megatron-LM
+            PR #8244, ordered A_log/dt_bias reduction).
+dprob       grouped-GEMM dsReLU backward dprob with one slot per 128-wide N
+            tile (cudnn-frontend PR #521).
+index_add   stable-sort + segmented-sum index_add for the sparse-indexer dK
+            (Megatron-LM PR #7441, source 3 fix).
+wgrad       grouped weight gradient with fixed-order split-K accumulation into
+            an fp32 main_grad (FlashInfer PR #8602 and its follow-up #8924).
+fp64        the exact mathematical definitions in float64, used to pin the
+            float32 oracle.
+brute       scalar, loop-by-loop restatements for tiny inputs (pins only).
+
+Parity status: every function here is pinned by CPU tests against fp64 sums,
+closed forms, exact-integer inputs, order-revealing probes or brute force,
+except ``wgrad.mfma_chain_model``, whose matrix-core model is "parity
+unpinned" (the pages say nothing about matrix-core internals).
+"""

@@ -1,0 +1,118 @@
+"""Scalar, loop-by-loop restatements of the four cases for tiny inputs (pins only).
+
+Written separately from the vectorised oracle modules: one Python loop per
+index, ``np.float32`` scalars, the pairwise tree as recursive halving, the
+stable sort as Python's ``sorted`` (which is stable). The vectorised oracle
+must agree with these bit for bit. Test infrastructure only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import detmath
+
+F = np.float32
+NZ = np.float32(-0.0)
+
+
+def _w(bits) -> np.float32:
+    return np.array([int(bits) << 16], np.uint32).view(np.float32)[0]
+
+
+def tree(vals):
+    """Recursive halving: tree(v) = tree(left half) + tree(right half)."""
+    if len(vals) == 1:
+        return F(vals[0])
+    h = len(vals) // 2
+    return F(tree(vals[:h]) + tree(vals[h:]))
+
+
+def fold(vals):
+    acc = NZ
+    for v in vals:
+        acc = F(acc + F(v))
+    return acc
+
+
+def padded_tiles(vals, block):
+    out = []
+    for s in range(0, len(vals), block):
+        t = list(vals[s:s + block])
+        t += [NZ] * (block - len(t))
+        out.append(t)
+    return out
+
+
+def dprob(dprob0, dY, C, offs, tile_n=128):
+    M = len(dprob0)
+    out = [F(v) for v in dprob0]
+    lo = min(max(int(offs[0]), 0), M)
+    hi = min(max(int(offs[-1]), lo), M)
+    for m in range(lo, hi):
+        terms = []
+        for n in range(len(dY[m])):
+            c = _w(C[m][n])
+            sq = F(c * c) if c > 0 else F(0.0)
+            terms.append(F(_w(dY[m][n]) * sq))
+        slots = [tree(t) for t in padded_tiles(terms, tile_n)]
+        out[m] = F(out[m] + fold(slots))
+    return np.array(out, np.float32)
+
+
+def colsum(a, dg, A_log, dt_bias, dA0, ddt0, block_t):
+    T, H = len(a), len(A_log)
+    r1, r2 = [], []
+    for h in range(H):
+        nA = -detmath.exp32(np.float32(A_log[h]))[()]
+        t1, t2 = [], []
+        for t in range(T):
+            x = F(_w(a[t][h]) + F(dt_bias[h]))
+            e = detmath.exp32(F(-abs(x)))[()]
+            sp = detmath.softplus_from(np.float32(x), np.float32(e))[()]
+            sg = detmath.sigmoid_from(np.float32(x), np.float32(e))[()]
+            d = _w(dg[t][h])
+            t1.append(F(d * F(nA * sp)))
+            t2.append(F(d * F(nA * sg)))
+        r1.append(F(F(dA0[h]) + fold([tree(x) for x in padded_tiles(t1, block_t)])))
+        r2.append(F(F(ddt0[h]) + fold([tree(x) for x in padded_tiles(t2, block_t)])))
+    return np.array(r1, np.float32), np.array(r2, np.float32)
+
+
+def index_add(out0, ids, src, chunk_rows):
+    n_rows, D = len(out0), len(out0[0])
+    out = [[F(v) for v in row] for row in out0]
+    pairs = sorted([(int(i), p) for p, i in enumerate(ids) if 0 <= int(i) < n_rows], key=lambda t: t[0])
+    runs = {}
+    for i, p in pairs:
+        runs.setdefault(i, []).append(p)
+    for i, rows in runs.items():
+        for d in range(D):
+            parts = []
+            for s in range(0, len(rows), chunk_rows):
+                parts.append(fold([_w(src[p][d]) for p in rows[s:s + chunk_rows]]))
+            out[i][d] = F(out[i][d] + fold(parts))
+    return np.array(out, np.float32)
+
+
+def literal_sequential_index_add(out0, ids, src):
+    """out[id] += src[p] one row at a time in stable id order (no chunks)."""
+    n_rows = len(out0)
+    out = np.array(out0, np.float32, copy=True)
+    for i, p in sorted([(int(i), p) for p, i in enumerate(ids) if 0 <= int(i) < n_rows], key=lambda t: t[0]):
+        for d in range(out.shape[1]):
+            out[i, d] = F(out[i, d] + _w(src[p][d]))
+    return out
+
+
+def wgrad_exact_integer(main_grad0, G, X, offs):
+    """For small-integer inputs: main_grad0 + exact integer G_e^T X_e, per element."""
+    E, M, N = np.shape(main_grad0)
+    out = np.array(main_grad0, np.float32, copy=True)
+    for e in range(E):
+        for i in range(M):
+            for j in range(N):
+                s = 0
+                for r in range(int(offs[e]), int(offs[e + 1])):
+                    s += int(_w(G[r][i])) * int(_w(X[r][j]))
+                out[e, i, j] = F(out[e, i, j] + F(s))
+    return out

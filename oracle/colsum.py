@@ -1,0 +1,59 @@
+"""Gate-backward column sums, ordered (test infrastructure only).
+
+Megatron-LM PR #8244 (ordered A_log/dt_bias reduction in the fused pre-GDR
+gate backward), description: when determinism is requested each program writes
+independent FP32 partial sums and the caller reduces them on the same stream;
+the tile comes from a shape-only selector and the same tile sizes the scratch.
+The page names only the two gradients; the gate itself is the Gated-DeltaNet
+one, g = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h]), whose parameter
+gradients are
+
+    dA_log[h]   = sum_t dg[t,h] * g[t,h]
+    ddt_bias[h] = sum_t dg[t,h] * (-exp(A_log[h])) * sigmoid(a[t,h] + dt_bias[h]).
+
+Canonical order for a tile of BT rows (BT a power of two): the adjacent
+pairwise tree over the tile's rows (rows past T are -0.0), one slot per
+(tile, head); then the slots of each head are folded left to right in tile
+order and the total is added once into the output. The head-block size BH of
+the launch does not enter the arithmetic.
+
+Per-element operation order (binary32, no fused multiply-add):
+    x  = f32(a) + dt_bias[h];  nA = -exp32(A_log[h]);  e = exp32(-|x|)
+    sp = softplus32(x);        sg = sigmoid32(x)      (both from the same e)
+    t1 = f32(dg) * (nA * sp);  t2 = f32(dg) * (nA * sg)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import detmath
+from .primitives import accumulate, pairwise, sequential, tiles, widen_bf16
+
+
+def gate_terms(a_bits, dg_bits, A_log, dt_bias):
+    """Elementwise terms (t1, t2), each [T, H] float32."""
+    a = widen_bf16(a_bits)
+    dg = widen_bf16(dg_bits)
+    A_log = np.asarray(A_log, np.float32)
+    dt_bias = np.asarray(dt_bias, np.float32)
+    x = (a + dt_bias[None, :]).astype(np.float32)
+    nA = -detmath.exp32(A_log)
+    e = detmath.exp32(-np.abs(x))
+    sp = detmath.softplus_from(x, e)
+    sg = detmath.sigmoid_from(x, e)
+    g = nA[None, :] * sp
+    t1 = dg * g
+    t2 = dg * (nA[None, :] * sg)
+    return t1.astype(np.float32), t2.astype(np.float32)
+
+
+def gate_slots(a_bits, dg_bits, A_log, dt_bias, block_t: int):
+    """Per-tile partials (slot1, slot2), each [ceil(T/BT), H]."""
+    t1, t2 = gate_terms(a_bits, dg_bits, A_log, dt_bias)
+    return pairwise(tiles(t1, block_t, axis=0)), pairwise(tiles(t2, block_t, axis=0))
+
+
+def colsum(a_bits, dg_bits, A_log, dt_bias, dA_log0, ddt_bias0, block_t: int):
+    """Return (dA_log, ddt_bias) after accumulating the ordered column sums."""
+    s1, s2 = gate_slots(a_bits, dg_bits, A_log, dt_bias, block_t)
+    return accumulate(dA_log0, sequential(s1, axis=0)), accumulate(ddt_bias0, sequential(s2, axis=0))

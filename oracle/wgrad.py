@@ -1,0 +1,76 @@
+"""Grouped weight gradient with fixed-order split-K accumulation (test infrastructure only).
+
+FlashInfer PR #8602 (fuse the fp32 weight-gradient accumulate into main_grad)
+and its follow-up #8924 (deterministic weight-gradient accumulation):
+
+    main_grad[e] += G_e^T X_e,   G_e = G[o_e:o_{e+1}],  X_e = X[o_e:o_{e+1}]
+
+with expert offsets read on the device. The deterministic route's result is
+bitwise the AccumulateGrad of the deterministic dW, i.e. RN32(main_grad + dW)
+with dW computed in a fixed order (#8924 summary, item 3).
+
+Canonical order (the reading taken here):
+* The token rows of expert e are cut into K tiles of ``k_tile`` (512) rows
+  counted from the expert's first row; ``ktiles_per_split`` consecutive K tiles
+  form one split (0 means the whole expert is one split).
+* Each split s produces a float32 partial Q_s[i, j] by a chain of matrix-core
+  steps over its rows in ascending order, starting from +0.0. The steps' own
+  rounding is a property of the matrix-core instruction, which the pages do
+  not describe; ``chain`` is therefore a parameter of this oracle.
+* main_grad[e][i, j] <- RN32(main_grad[e][i, j] + fold(Q_0 .. Q_{S_e - 1}))
+  with fold the left-to-right sum starting at -0.0. An expert with no rows
+  leaves its main_grad slice bitwise unchanged.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .primitives import NEG_ZERO, accumulate, widen_bf16
+
+K_TILE = 512
+
+
+def split_ranges(offs, k_tile: int = K_TILE, ktiles_per_split: int = 0):
+    """Per expert, the list of (row_begin, row_end) of its splits."""
+    offs = np.asarray(offs, np.int64)
+    out = []
+    for e in range(len(offs) - 1):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi <= lo:
+            out.append([])
+            continue
+        step = (hi - lo) if ktiles_per_split <= 0 else k_tile * ktiles_per_split
+        out.append([(b, min(b + step, hi)) for b in range(lo, hi, step)])
+    return out
+
+
+def fold_partials(main_grad0: np.ndarray, partials) -> np.ndarray:
+    """RN32(main_grad0 + left-to-right fold of the partial list)."""
+    total = np.full(main_grad0.shape, NEG_ZERO, np.float32)
+    for q in partials:
+        total = np.add(total, np.asarray(q, np.float32), dtype=np.float32)
+    return accumulate(main_grad0, total)
+
+
+def chain_exact_rounded(g_f32: np.ndarray, x_f32: np.ndarray) -> np.ndarray:
+    """RN32 of the exact G^T X (float64 is exact for small-integer inputs).
+
+    Any summation order gives this result whenever every partial sum is an
+    exactly representable integer, so it is the chain for exact-integer pins.
+    """
+    return (g_f32.astype(np.float64).T @ x_f32.astype(np.float64)).astype(np.float32)
+
+
+def grouped_wgrad_acc(main_grad0, G_bits, X_bits, offs, k_tile: int = K_TILE, ktiles_per_split: int = 0,
+                      chain=chain_exact_rounded, experts=None) -> np.ndarray:
+    """Return the updated main_grad [E, M, N] (main_grad0 is not modified)."""
+    mg = np.array(main_grad0, np.float32, copy=True)
+    splits = split_ranges(offs, k_tile, ktiles_per_split)
+    for e, sp in enumerate(splits):
+        if experts is not None and e not in experts:
+            continue
+        if not sp:
+            continue
+        parts = [chain(widen_bf16(G_bits[b:t]), widen_bf16(X_bits[b:t])) for b, t in sp]
+        mg[e] = fold_partials(mg[e], parts)
+    return mg

@@ -1,0 +1,181 @@
+"""Seeded synthetic inputs for the four deterministic gradient reductions.
+
+This module only draws random inputs and rounds them to bfloat16 storage. It
+holds none of the reductions' arithmetic, so both the CPU oracle and the GPU
+library can be fed from it without sharing any compute code.
+
+Every tensor comes from ``numpy.random.default_rng([seed, tensor_id])`` so a
+given (seed, shape) always produces the same bits on any host. bfloat16 values
+are returned as their raw ``uint16`` bit patterns (round-to-nearest-even from
+float32), which is how they are uploaded to the device.
+
+Workload shapes follow the pages' four cases (Megatron-LM PR #8244 gate
+backward; Megatron-LM PR #7441 indexer dK; cudnn-frontend PR #521 grouped-GEMM
+dprob; FlashInfer PR #8602/#8924 grouped weight-gradient accumulate).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits", "GateInputs", "gate_inputs", "IndexAddInputs", "index_add_inputs",
+    "DprobInputs", "dprob_inputs", "WgradInputs", "wgrad_inputs",
+]
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _rng(seed: int, tensor_id: int) -> np.random.Generator:
+    return np.random.default_rng([seed, tensor_id])
+
+
+# --------------------------------------------------------------------------- gate
+@dataclass
+class GateInputs:
+    """Gated-DeltaNet gate backward inputs.
+
+    ``a`` is a contiguous [T, H] bf16 tensor. ``dg_base`` is a [T, 2H] bf16
+    tensor whose columns H..2H-1 form the strided ``dg`` view (row stride 2H,
+    element offset H), matching the non-contiguous gradient the pages test.
+    """
+    T: int
+    H: int
+    a: np.ndarray          # uint16 [T, H]
+    dg_base: np.ndarray    # uint16 [T, 2H]
+    A_log: np.ndarray      # float32 [H]
+    dt_bias: np.ndarray    # float32 [H]
+    dA_log0: np.ndarray    # float32 [H] initial accumulator
+    ddt_bias0: np.ndarray  # float32 [H]
+
+    @property
+    def dg(self) -> np.ndarray:
+        return self.dg_base[:, self.H:]
+
+
+def gate_inputs(T: int, H: int, seed: int = 1, out_init: str = "zero") -> GateInputs:
+    a = bf16_bits(_rng(seed, 0).standard_normal((T, H), dtype=np.float32))
+    dg_base = bf16_bits(_rng(seed, 1).standard_normal((T, 2 * H), dtype=np.float32))
+    A_log = _rng(seed, 2).uniform(-2.0, 1.0, H).astype(np.float32)
+    dt_bias = _rng(seed, 3).uniform(-1.0, 1.0, H).astype(np.float32)
+    if out_init == "zero":
+        o1 = np.zeros(H, np.float32); o2 = np.zeros(H, np.float32)
+    else:
+        o1 = _rng(seed, 4).standard_normal(H, dtype=np.float32)
+        o2 = _rng(seed, 5).standard_normal(H, dtype=np.float32)
+    return GateInputs(T, H, a, dg_base, A_log, dt_bias, o1, o2)
+
+
+# ---------------------------------------------------------------------- index_add
+@dataclass
+class IndexAddInputs:
+    """Sparse-indexer dK scatter: ``out[ids[p]] += src[p]`` for ids >= 0.
+
+    ``ids`` is the flattened [Q, K] top-k id matrix (int32, -1 = padding),
+    ``src`` the [Q*K, D] bf16 rows, ``out0`` the [n_rows, D] float32 start.
+    """
+    n_rows: int
+    dim: int
+    ids: np.ndarray   # int32 [P]
+    src: np.ndarray   # uint16 [P, D]
+    out0: np.ndarray  # float32 [n_rows, D]
+
+
+def zipf_ids(P: int, n_rows: int, s: float, pad_frac: float, seed: int, tensor_id: int = 0) -> np.ndarray:
+    """i.i.d. Zipf(s) ranks mapped to keys by a seeded permutation; padding -1."""
+    rng = _rng(seed, tensor_id)
+    w = np.arange(1, n_rows + 1, dtype=np.float64) ** (-s)
+    cdf = np.cumsum(w / w.sum())
+    cdf[-1] = 1.0
+    ranks = np.searchsorted(cdf, rng.random(P), side="right")
+    ranks = np.minimum(ranks, n_rows - 1)
+    perm = rng.permutation(n_rows).astype(np.int32)
+    ids = perm[ranks]
+    pad = rng.random(P) < pad_frac
+    ids[pad] = -1
+    return ids.astype(np.int32)
+
+
+def index_add_inputs(Q: int = 4096, K: int = 512, n_rows: int = 8192, dim: int = 128, seed: int = 3,
+                     zipf_s: float = 1.1, pad_frac: float = 0.05, src_std: float = 0.02,
+                     out_init: str = "zero") -> IndexAddInputs:
+    P = Q * K
+    ids = zipf_ids(P, n_rows, zipf_s, pad_frac, seed, 0)
+    src = bf16_bits(_rng(seed, 1).standard_normal((P, dim), dtype=np.float32) * np.float32(src_std))
+    if out_init == "zero":
+        out0 = np.zeros((n_rows, dim), np.float32)
+    else:
+        out0 = _rng(seed, 2).standard_normal((n_rows, dim), dtype=np.float32)
+    return IndexAddInputs(n_rows, dim, ids, src, out0)
+
+
+# -------------------------------------------------------------------------- dprob
+@dataclass
+class DprobInputs:
+    """Grouped-GEMM dsReLU backward dprob inputs (rows grouped by expert)."""
+    M: int
+    N: int
+    offs: np.ndarray   # int32 [E+1] expert row offsets
+    dY: np.ndarray     # uint16 [M, N]
+    C: np.ndarray      # uint16 [M, N]
+    dprob0: np.ndarray  # float32 [M]
+
+
+def expert_counts(total: int, E: int, min_tokens: int, seed: int, tensor_id: int = 0) -> np.ndarray:
+    rng = _rng(seed, tensor_id)
+    extra = rng.multinomial(total - E * min_tokens, [1.0 / E] * E)
+    return (min_tokens + extra).astype(np.int64)
+
+
+def dprob_inputs(M: int = 16384, N: int = 2048, E: int = 8, min_tokens: int = 256, seed: int = 4,
+                 out_init: str = "zero") -> DprobInputs:
+    counts = expert_counts(M, E, min_tokens, seed, 0) if M >= E * min_tokens else \
+        np.array([M // E + (1 if e < M % E else 0) for e in range(E)], np.int64)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    dY = bf16_bits(_rng(seed, 1).standard_normal((M, N), dtype=np.float32))
+    C = bf16_bits(_rng(seed, 2).standard_normal((M, N), dtype=np.float32))
+    if out_init == "zero":
+        d0 = np.zeros(M, np.float32)
+    else:
+        d0 = _rng(seed, 3).standard_normal(M, dtype=np.float32)
+    return DprobInputs(M, N, offs, dY, C, d0)
+
+
+# -------------------------------------------------------------------------- wgrad
+@dataclass
+class WgradInputs:
+    """Grouped weight gradient: main_grad[e] += G_e^T X_e over expert row ranges."""
+    M: int
+    N: int
+    offs: np.ndarray       # int32 [E+1]
+    G: np.ndarray          # uint16 [T_total, M]
+    X: np.ndarray          # uint16 [T_total, N]
+    main_grad0: np.ndarray  # float32 [E, M, N]
+    tokens: np.ndarray = field(default=None)
+
+
+def wgrad_inputs(E: int = 8, M: int = 1408, N: int = 2048, tokens=None, t_lo: int = 1024, t_hi: int = 8192,
+                 seed: int = 5, std: float = 0.02, out_init: str = "zero", integer: bool = False) -> WgradInputs:
+    if tokens is None:
+        tokens = _rng(seed, 0).integers(t_lo, t_hi + 1, size=E)
+    tokens = np.asarray(tokens, np.int64)
+    offs = np.concatenate([[0], np.cumsum(tokens)]).astype(np.int32)
+    T = int(offs[-1])
+    if integer:
+        G = bf16_bits(_rng(seed, 1).integers(-2, 3, size=(T, M)).astype(np.float32))
+        X = bf16_bits(_rng(seed, 2).integers(-2, 3, size=(T, N)).astype(np.float32))
+    else:
+        G = bf16_bits(_rng(seed, 1).standard_normal((T, M), dtype=np.float32) * np.float32(std))
+        X = bf16_bits(_rng(seed, 2).standard_normal((T, N), dtype=np.float32) * np.float32(std))
+    if out_init == "zero":
+        mg = np.zeros((E, M, N), np.float32)
+    elif integer:
+        mg = _rng(seed, 3).integers(-8, 9, size=(E, M, N)).astype(np.float32)
+    else:
+        mg = _rng(seed, 3).standard_normal((E, M, N), dtype=np.float32) * np.float32(1e-2)
+    return WgradInputs(M, N, offs, G, X, mg, tokens)
