@@ -1,0 +1,294 @@
+"""Python binding of libdetgrad: deterministic, atomic-free gradient reductions on MI355X.
+
+Argument marshalling only. Each function takes torch device tensors, passes
+their data pointers, strides and the current HIP stream to the C ABI of
+``libdetgrad.so`` (declared in include/detgrad.h) and raises RuntimeError with
+the library's message on a non-OK status. All arithmetic runs in the HIP
+kernels; there is no CPU or PyTorch fallback: if the library is not built,
+every call raises.
+
+Functions (same names as the C ABI):
+    det_colsum(a, dg, A_log, dt_bias, dA_log, ddt_bias, cfg=None, atomic=False)
+    det_index_add(out, ids, src, cfg=None, atomic=False)
+    det_grouped_dprob(dprob, dY, C, offs, cfg=None, atomic=False)
+    det_grouped_wgrad_acc(main_grad, G, X, offs, cfg=None, atomic=False)
+Every function accepts ``ws=`` (a Workspace or a uint8 device tensor) and
+``stream=`` (a torch.cuda.Stream); by default a cached per-stream workspace
+and torch's current stream are used.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "lib", "library_path", "DetError", "ColsumCfg", "IndexAddCfg", "DprobCfg", "WgradCfg", "Workspace",
+    "det_abi_version", "det_colsum", "det_colsum_select_cfg", "det_colsum_workspace_size", "det_index_add",
+    "det_index_add_workspace_size", "det_index_add_bad_ids", "det_grouped_dprob", "det_grouped_dprob_workspace_size",
+    "det_grouped_wgrad_acc", "det_grouped_wgrad_acc_workspace_size", "det_workspace_init", "det_detmath_eval",
+    "DET_OK", "DET_ERR_INVALID_ARG", "DET_ERR_UNSUPPORTED", "DET_ERR_WORKSPACE", "DET_ERR_OVERLAP", "DET_ERR_HIP",
+]
+
+DET_OK, DET_ERR_INVALID_ARG, DET_ERR_UNSUPPORTED, DET_ERR_WORKSPACE, DET_ERR_OVERLAP, DET_ERR_HIP = 0, -1, -2, -3, -4, -5
+DET_BF16, DET_F32 = 0, 1
+WS_HEADER_BYTES = 256
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdetgrad.so")
+
+
+class DetError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("detgrad status %d: %s" % (status, msg))
+        self.status = status
+
+
+class ColsumCfg(ctypes.Structure):
+    _fields_ = [("block_t", ctypes.c_int32), ("block_h", ctypes.c_int32)]
+
+
+class IndexAddCfg(ctypes.Structure):
+    _fields_ = [("chunk_rows", ctypes.c_int32)]
+
+
+class DprobCfg(ctypes.Structure):
+    _fields_ = [("tile_n", ctypes.c_int32), ("rows_per_wg", ctypes.c_int32)]
+
+
+class WgradCfg(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("k_tile", ctypes.c_int32),
+                ("ktiles_per_split", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_INT = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "det_abi_version": ([], _INT),
+    "det_last_error": ([], ctypes.c_char_p),
+    "det_workspace_init": ([_P, _SZ, _P], _INT),
+    "det_colsum_select_cfg": ([_I64, _I64, ctypes.POINTER(ColsumCfg)], _INT),
+    "det_colsum_workspace_size": ([_I64, _I64, ctypes.POINTER(ColsumCfg), _INT, ctypes.POINTER(_SZ)], _INT),
+    "det_colsum": ([_P, _I64, _I64, _P, _I64, _I64, _INT, _P, _P, _I64, _I64, _P, _P, ctypes.POINTER(ColsumCfg),
+                    _P, _SZ, _INT, _P], _INT),
+    "det_index_add_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(IndexAddCfg), _INT, ctypes.POINTER(_SZ)], _INT),
+    "det_index_add": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _INT, ctypes.POINTER(IndexAddCfg), _P, _SZ, _INT,
+                       _P], _INT),
+    "det_index_add_bad_ids": ([_P, _SZ, ctypes.POINTER(_I64), _P], _INT),
+    "det_grouped_dprob_workspace_size": ([_I64, _I64, ctypes.POINTER(DprobCfg), _INT, ctypes.POINTER(_SZ)], _INT),
+    "det_grouped_dprob": ([_P, _P, _I64, _P, _I64, _I64, _I64, _P, _I32, ctypes.POINTER(DprobCfg), _P, _SZ, _INT,
+                           _P], _INT),
+    "det_grouped_wgrad_acc_workspace_size": ([_I64, _I32, _I64, _I64, ctypes.POINTER(WgradCfg), _INT,
+                                              ctypes.POINTER(_SZ)], _INT),
+    "det_detmath_eval": ([_P, _P, _I64, _INT, _P], _INT),
+    "det_grouped_wgrad_acc": ([_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I32, _I64, _I64, _I64,
+                               ctypes.POINTER(WgradCfg), _P, _SZ, _INT, _P], _INT),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdetgrad.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(library_path):
+                    raise RuntimeError("libdetgrad.so is not built; run "
+                                       "`python -m deterministic_gradient_reductions_amd.build`")
+                L = ctypes.CDLL(library_path)
+                for name, (args, res) in _SIGS.items():
+                    fn = getattr(L, name)
+                    fn.argtypes = args
+                    fn.restype = res
+                _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != DET_OK:
+        raise DetError(status, lib().det_last_error().decode())
+
+
+def _atomic_flag(atomic) -> int:
+    # bools map to 0/1; any other value goes to the library, which rejects it
+    return int(atomic) if isinstance(atomic, bool) else atomic
+
+
+def _stream_handle(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def det_abi_version() -> int:
+    return lib().det_abi_version()
+
+
+# ------------------------------------------------------------------ workspace
+class Workspace:
+    """A device scratch buffer with an initialised counter header.
+
+    Owned by the caller; reused across calls on one stream. Calls that may run
+    at the same time must not share a Workspace.
+    """
+
+    def __init__(self, nbytes: int, device=None, stream=None):
+        import torch
+        self.nbytes = max(int(nbytes), WS_HEADER_BYTES)
+        # 256 extra bytes so that the start can be aligned to 256 bytes
+        self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device or "cuda")
+        base = self._buf.data_ptr()
+        self.ptr = (base + 255) // 256 * 256
+        _check(lib().det_workspace_init(ctypes.c_void_p(self.ptr), self.nbytes, _stream_handle(stream)))
+
+    def ensure(self, nbytes: int, stream=None) -> "Workspace":
+        return self if nbytes <= self.nbytes else Workspace(max(nbytes, 2 * self.nbytes), self._buf.device, stream)
+
+
+_ws_cache = {}
+
+
+def _workspace(need: int, ws, stream):
+    if need == 0 and ws is None:
+        return ctypes.c_void_p(0), 0
+    if ws is None:
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        key = (s.device.index if s.device.index is not None else torch.cuda.current_device(), s.cuda_stream)
+        cur = _ws_cache.get(key)
+        if cur is None or cur.nbytes < need:
+            cur = Workspace(max(need, 2 * (cur.nbytes if cur else 0)), device=s.device, stream=s)
+            _ws_cache[key] = cur
+        ws = cur
+    if isinstance(ws, Workspace):
+        return ctypes.c_void_p(ws.ptr), ws.nbytes
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def det_workspace_init(ws, stream=None) -> None:
+    p, n = (ctypes.c_void_p(ws.ptr), ws.nbytes) if isinstance(ws, Workspace) else (_ptr(ws), ws.numel())
+    _check(lib().det_workspace_init(p, n, _stream_handle(stream)))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DET_BF16
+    if t.dtype == torch.float32:
+        return DET_F32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+# --------------------------------------------------------------------- colsum
+def det_colsum_select_cfg(T: int, H: int) -> ColsumCfg:
+    c = ColsumCfg()
+    _check(lib().det_colsum_select_cfg(T, H, ctypes.byref(c)))
+    return c
+
+
+def det_colsum_workspace_size(T: int, H: int, cfg: ColsumCfg | None = None, atomic=False) -> int:
+    n = _SZ()
+    _check(lib().det_colsum_workspace_size(T, H, ctypes.byref(cfg) if cfg else None, _atomic_flag(atomic),
+                                           ctypes.byref(n)))
+    return n.value
+
+
+def det_colsum(a, dg, A_log, dt_bias, dA_log, ddt_bias, cfg: ColsumCfg | None = None, atomic=False, ws=None,
+               stream=None) -> None:
+    """dA_log[h] += sum_t dg*g, ddt_bias[h] += sum_t dg*(-exp(A_log))*sigmoid(a+dt_bias). a, dg: [T, H]."""
+    T, H = a.shape
+    need = det_colsum_workspace_size(T, H, cfg, atomic) if atomic in (0, 1, False, True) else 0
+    wp, wn = _workspace(need, ws, stream)
+    _check(lib().det_colsum(_ptr(a), a.stride(0), a.stride(1), _ptr(dg), dg.stride(0), dg.stride(1), _dtype_code(a),
+                            _ptr(A_log), _ptr(dt_bias), T, H, _ptr(dA_log), _ptr(ddt_bias),
+                            ctypes.byref(cfg) if cfg else None, wp, wn, _atomic_flag(atomic), _stream_handle(stream)))
+
+
+# ------------------------------------------------------------------ index_add
+def det_index_add_workspace_size(n_src: int, dim: int, n_rows: int, cfg: IndexAddCfg | None = None,
+                                 atomic=False) -> int:
+    n = _SZ()
+    _check(lib().det_index_add_workspace_size(n_src, dim, n_rows, ctypes.byref(cfg) if cfg else None,
+                                              _atomic_flag(atomic), ctypes.byref(n)))
+    return n.value
+
+
+def det_index_add(out, ids, src, cfg: IndexAddCfg | None = None, atomic=False, ws=None, stream=None) -> None:
+    """out[ids[p]] += src[p] for 0 <= ids[p] < out.shape[0]; out float32 [R, D], src bf16 [P, D]."""
+    n_rows, dim = out.shape
+    n_src = ids.numel()
+    need = det_index_add_workspace_size(n_src, dim, n_rows, cfg, atomic) if atomic in (0, 1, False, True) else 0
+    wp, wn = _workspace(need, ws, stream)
+    _check(lib().det_index_add(_ptr(out), n_rows, dim, out.stride(0), _ptr(ids), n_src, _ptr(src), src.stride(0),
+                               _dtype_code(src), ctypes.byref(cfg) if cfg else None, wp, wn, _atomic_flag(atomic),
+                               _stream_handle(stream)))
+
+
+def det_index_add_bad_ids(ws=None, stream=None) -> int:
+    wp, wn = _workspace(WS_HEADER_BYTES, ws, stream)
+    c = _I64()
+    _check(lib().det_index_add_bad_ids(wp, wn, ctypes.byref(c), _stream_handle(stream)))
+    return c.value
+
+
+# ---------------------------------------------------------------------- dprob
+def det_grouped_dprob_workspace_size(M: int, N: int, cfg: DprobCfg | None = None, atomic=False) -> int:
+    n = _SZ()
+    _check(lib().det_grouped_dprob_workspace_size(M, N, ctypes.byref(cfg) if cfg else None, _atomic_flag(atomic),
+                                                  ctypes.byref(n)))
+    return n.value
+
+
+def det_grouped_dprob(dprob, dY, C, offs, cfg: DprobCfg | None = None, atomic=False, ws=None, stream=None) -> None:
+    """dprob[m] += sum_n dY[m,n]*relu(C[m,n])^2 for offs[0] <= m < offs[E]; dY, C bf16 [M, N]."""
+    M, N = dY.shape
+    if dY.stride(1) != 1 or C.stride(1) != 1:
+        raise ValueError("dY and C must have unit column stride")
+    need = det_grouped_dprob_workspace_size(M, N, cfg, atomic) if atomic in (0, 1, False, True) else 0
+    wp, wn = _workspace(need, ws, stream)
+    _check(lib().det_grouped_dprob(_ptr(dprob), _ptr(dY), dY.stride(0), _ptr(C), C.stride(0), M, N, _ptr(offs),
+                                   offs.numel() - 1, ctypes.byref(cfg) if cfg else None, wp, wn,
+                                   _atomic_flag(atomic), _stream_handle(stream)))
+
+
+# ---------------------------------------------------------------------- wgrad
+def det_grouped_wgrad_acc_workspace_size(T_total: int, E: int, M: int, N: int, cfg: WgradCfg | None = None,
+                                         atomic=False) -> int:
+    n = _SZ()
+    _check(lib().det_grouped_wgrad_acc_workspace_size(T_total, E, M, N, ctypes.byref(cfg) if cfg else None,
+                                                      _atomic_flag(atomic), ctypes.byref(n)))
+    return n.value
+
+
+def det_grouped_wgrad_acc(main_grad, G, X, offs, cfg: WgradCfg | None = None, atomic=False, ws=None,
+                          stream=None) -> None:
+    """main_grad[e] += G[offs[e]:offs[e+1]]^T X[offs[e]:offs[e+1]]; main_grad fp32 [E, M, N]."""
+    E, M, N = main_grad.shape
+    T_total = G.shape[0]
+    if G.stride(1) != 1 or X.stride(1) != 1 or main_grad.stride(2) != 1:
+        raise ValueError("G, X and main_grad must have unit innermost stride")
+    need = det_grouped_wgrad_acc_workspace_size(T_total, E, M, N, cfg, atomic) if atomic in (0, 1, False, True) else 0
+    wp, wn = _workspace(need, ws, stream)
+    _check(lib().det_grouped_wgrad_acc(_ptr(main_grad), main_grad.stride(0), main_grad.stride(1), _ptr(G), G.stride(0),
+                                       _ptr(X), X.stride(0), _ptr(offs), E, T_total, M, N,
+                                       ctypes.byref(cfg) if cfg else None, wp, wn, _atomic_flag(atomic),
+                                       _stream_handle(stream)))
+
+
+# ---------------------------------------------------------------- diagnostics
+DETMATH_FN = {"exp32": 0, "log1p32": 1, "softplus32": 2, "sigmoid32": 3}
+
+
+def det_detmath_eval(x, y, fn: str, stream=None) -> None:
+    """y = fn(x) elementwise on the GPU with the gate's detmath sequences (tests only)."""
+    _check(lib().det_detmath_eval(_ptr(x), _ptr(y), x.numel(), DETMATH_FN[fn], _stream_handle(stream)))

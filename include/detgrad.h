@@ -1,0 +1,226 @@
+/*
+ * detgrad.h - deterministic, atomic-free gradient reductions for AMD MI355X (gfx950).
+ *
+ * Four reductions that the pages make deterministic by the same pattern: each
+ * workgroup writes its own FP32 partial sums into per-tile slots, and the slots
+ * are then reduced in a fixed canonical order on the caller's stream
+ * (Megatron-LM PR #8244, description; cudnn-frontend PR #521, first commit).
+ * Every entry point takes an `atomic` flag: 0 runs the deterministic route,
+ * 1 runs the non-deterministic comparison route that adds the same tile
+ * partials into the output with hardware float atomics.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All data pointers are device pointers (hipMalloc / torch CUDA tensors).
+ *   `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ * - A call only enqueues work on `stream`. It never allocates, never
+ *   synchronises with the host and keeps no state between calls; the caller
+ *   owns every buffer, the workspace included.
+ * - Outputs ACCUMULATE: out <- RN32(out + total), one rounding per element
+ *   (cudnn-frontend PR #521: the slot reduction "accumulates ... rather than
+ *   overwriting"; FlashInfer PR #8924: bitwise AccumulateGrad of the
+ *   deterministic dW). An empty problem leaves every output bit unchanged.
+ * - `atomic` must be exactly 0 or 1, anything else is DET_ERR_INVALID_ARG
+ *   (FlashInfer PR #8924, mode rules: only an explicit value selects a route).
+ * - With atomic = 0 the output bits are a function of the inputs and the tile
+ *   configuration only: identical from run to run, under any concurrent load.
+ *   With atomic = 1 only closeness is promised.
+ * - All arguments are checked on the host before anything is enqueued; a
+ *   non-OK status means nothing was launched. det_last_error() then returns a
+ *   thread-local description.
+ *
+ * Workspace
+ * ---------
+ * The deterministic routes need device scratch of det_*_workspace_size()
+ * bytes, 256-byte aligned. Its first 256 bytes hold small self-resetting
+ * counters: call det_workspace_init() once on a new workspace (it enqueues a
+ * tiny fill kernel on `stream`); afterwards every call leaves the counters at
+ * zero again, so the workspace never needs another fill. The slot area is
+ * never read before it is written, so it needs no initial value. One
+ * workspace must not be used by two calls that can run at the same time
+ * (for example on two streams without an event between them).
+ */
+#ifndef DETGRAD_H
+#define DETGRAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DET_ABI_VERSION 1
+#define DET_WS_HEADER_BYTES 256
+
+typedef enum {
+  DET_OK = 0,
+  DET_ERR_INVALID_ARG = -1, /* bad size, stride, pointer, flag or config    */
+  DET_ERR_UNSUPPORTED = -2, /* legal but not implemented (e.g. dtype)       */
+  DET_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned   */
+  DET_ERR_OVERLAP = -4,     /* an output overlaps an input or the workspace */
+  DET_ERR_HIP = -5          /* the HIP runtime reported an error            */
+} det_status;
+
+typedef enum { DET_BF16 = 0, DET_F32 = 1 } det_dtype;
+
+/* ABI version of the loaded library (DET_ABI_VERSION). */
+int det_abi_version(void);
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* det_last_error(void);
+
+/* Zero the counter header of a fresh workspace. Enqueued on `stream` as a
+ * small fill kernel (no memset node, so it may be graph-captured).
+ * ws: device pointer, 256-byte aligned; ws_bytes >= DET_WS_HEADER_BYTES. */
+int det_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * det_colsum: Gated-DeltaNet gate backward column sums.
+ * Megatron-LM PR #8244 (ordered A_log/dt_bias reduction of the fused pre-GDR
+ * gate backward): programs write FP32 partial sums and the caller reduces
+ * them in order; the tile is picked by a shape-only rule that also sizes the
+ * scratch and the launch, and explicit tile overrides are honoured.
+ *
+ *   x = a[t,h] + dt_bias[h],  g = -exp(A_log[h]) * softplus(x)
+ *   dA_log[h]   += sum_t dg[t,h] * g
+ *   ddt_bias[h] += sum_t dg[t,h] * (-exp(A_log[h])) * sigmoid(x)
+ *
+ * Canonical order: per tile of block_t rows and per head, the adjacent
+ * pairwise tree over the tile's rows (rows >= T count as -0.0); the tiles'
+ * slots folded left to right; one add into the output. exp, softplus and
+ * sigmoid are fixed sequences of correctly rounded float32 operations
+ * (threshold 20 for softplus), so the CPU oracle reproduces every bit.
+ * block_h only shapes the launch; it never changes a bit.
+ *
+ * a, dg: [T, H] with element strides (st, sh) >= 1, any layout (for example
+ *        a column slice of a wider tensor, or a transposed view); dtype
+ *        DET_BF16 (DET_F32 returns DET_ERR_UNSUPPORTED).
+ * A_log, dt_bias: [H] float32, contiguous. dA_log, ddt_bias: [H] float32,
+ *        accumulated, must not overlap the inputs, each other or ws.
+ * cfg:   NULL selects det_colsum_select_cfg(T, H). block_t in {64,128,256},
+ *        block_h in {8,16,32}.
+ * ws:    det_colsum_workspace_size() bytes (0 for atomic = 1; ws may be NULL). */
+typedef struct {
+  int32_t block_t;
+  int32_t block_h;
+} det_colsum_cfg;
+
+int det_colsum_select_cfg(int64_t T, int64_t H, det_colsum_cfg* out);
+int det_colsum_workspace_size(int64_t T, int64_t H, const det_colsum_cfg* cfg, int atomic, size_t* bytes);
+int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_t dg_st, int64_t dg_sh,
+               int in_dtype, const float* A_log, const float* dt_bias, int64_t T, int64_t H, float* dA_log,
+               float* ddt_bias, const det_colsum_cfg* cfg, void* ws, size_t ws_bytes, int atomic, void* stream);
+
+/* ------------------------------------------------------------------------
+ * det_index_add: out[ids[p]] += src[p] without float atomics.
+ * Megatron-LM PR #7441 (DSv4 deterministic mode), source 3: the sparse-
+ * indexer dK is accumulated by a deterministic index_add (stable sort +
+ * prefix sum) instead of atomics; padding slots are dropped.
+ *
+ * Canonical order: pairs (ids[p], p) with 0 <= ids[p] < n_rows, stably sorted
+ * by id (equal ids keep ascending p); each id's run cut into chunks of
+ * chunk_rows rows; a chunk's partial is the left-to-right fold of its rows;
+ * the chunk partials folded left to right and added once into out[id]. Ids
+ * of -1 are padding. Any other out-of-range id is dropped and counted
+ * (det_index_add_bad_ids). Ids with no rows leave out[id] untouched.
+ *
+ * out:  [n_rows, dim] float32, row stride out_ld >= dim (elements).
+ * ids:  [n_src] int32. src: [n_src, dim], row stride src_ld >= dim, DET_BF16.
+ * dim must be a multiple of 8; out_ld, src_ld multiples of 8; src and out
+ * 16-byte aligned (DET_ERR_UNSUPPORTED otherwise). n_rows <= 32768.
+ * cfg:  NULL = {chunk_rows = 256}; chunk_rows in [1, 65536].
+ * ws:   det_index_add_workspace_size() bytes (0 for atomic = 1). */
+typedef struct {
+  int32_t chunk_rows;
+} det_index_add_cfg;
+
+int det_index_add_workspace_size(int64_t n_src, int64_t dim, int64_t n_rows, const det_index_add_cfg* cfg,
+                                 int atomic, size_t* bytes);
+int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t out_ld, const int32_t* ids, int64_t n_src,
+                  const void* src, int64_t src_ld, int src_dtype, const det_index_add_cfg* cfg, void* ws,
+                  size_t ws_bytes, int atomic, void* stream);
+/* Number of ids dropped as out of range (not -1) by the last det_index_add
+ * that used this workspace. Synchronises `stream`; for tests and debugging. */
+int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* count, void* stream);
+
+/* ------------------------------------------------------------------------
+ * det_grouped_dprob: dprob of a grouped-GEMM dsReLU backward.
+ * cudnn-frontend PR #521 (deterministic dprob): one slot per N tile so every
+ * (token, tile_n) pair has exactly one writer, subtile partials parked by
+ * actual subtile, slots reduced in a fixed order, accumulating into dprob.
+ *
+ *   dprob[m] += sum_n dY[m,n] * relu(C[m,n])^2     for offs[0] <= m < offs[E]
+ *
+ * Canonical order: term = dY * (c*c if c > 0 else +0); per 128-wide N tile
+ * the adjacent pairwise tree of its terms (n >= N is -0.0); the tiles folded
+ * left to right; one add into dprob[m]. Rows outside [offs[0], offs[E])
+ * (clamped to [0, M]) are untouched. offs: [E+1] int32 device array, read
+ * only by the kernel (no host sync); rows are independent, so the grouping
+ * never changes a bit.
+ *
+ * dY, C: [M, N] bf16, row strides ldy, ldc >= N (elements).
+ * dprob: [M] float32, accumulated.
+ * cfg:   NULL = {tile_n = 128, rows_per_wg = 16}; tile_n must be 128;
+ *        rows_per_wg in [1, 1024] only shapes the launch.
+ * ws:    the deterministic route keeps every slot on chip and needs no
+ *        workspace (size 0); ws may be NULL. */
+typedef struct {
+  int32_t tile_n;
+  int32_t rows_per_wg;
+} det_dprob_cfg;
+
+int det_grouped_dprob_workspace_size(int64_t M, int64_t N, const det_dprob_cfg* cfg, int atomic, size_t* bytes);
+int det_grouped_dprob(float* dprob, const void* dY, int64_t ldy, const void* C, int64_t ldc, int64_t M, int64_t N,
+                      const int32_t* offs, int32_t E, const det_dprob_cfg* cfg, void* ws, size_t ws_bytes,
+                      int atomic, void* stream);
+
+/* ------------------------------------------------------------------------
+ * det_grouped_wgrad_acc: main_grad[e] += G_e^T X_e with fixed-order split-K.
+ * FlashInfer PR #8602 (fused fp32 weight-gradient accumulate into main_grad)
+ * and #8924 (deterministic accumulate: bitwise AccumulateGrad of the
+ * deterministic dW, identical from run to run; expert offsets on the device).
+ *
+ * Expert e owns token rows [offs[e], offs[e+1]) of G [T_total, M] and
+ * X [T_total, N] (bf16, row strides ldg >= M, ldx >= N). Its rows are cut into
+ * K tiles of k_tile (= 512) rows counted from the expert's first row, and
+ * ktiles_per_split consecutive K tiles form one split (0 = one split per
+ * expert). Each split's partial Q_s = G_s^T X_s is computed on the matrix
+ * cores in ascending row order from +0.0; then
+ *   main_grad[e] <- RN32(main_grad[e] + (((Q_0 + Q_1) + Q_2) + ...)).
+ * block_m and block_n only shape the launch.
+ *
+ * main_grad: [E, M, N] float32, element (e,i,j) at e*ld_e + i*ld_m + j;
+ *            ld_m >= N, ld_e >= M*ld_m (so an expanded tensor is rejected).
+ * offs: [E+1] int32 device array, non-decreasing, offs[E] <= T_total.
+ *       Values are read on the device only; out-of-range offsets are clamped.
+ * M, N must be multiples of 16 and ldg, ldx multiples of 8, G and X 16-byte
+ * aligned (DET_ERR_UNSUPPORTED otherwise).
+ * cfg:  NULL selects {block_m = 256, block_n = 256, k_tile = 512,
+ *       ktiles_per_split = 0}. */
+typedef struct {
+  int32_t block_m;
+  int32_t block_n;
+  int32_t k_tile;
+  int32_t ktiles_per_split;
+} det_wgrad_cfg;
+
+int det_grouped_wgrad_acc_workspace_size(int64_t T_total, int32_t E, int64_t M, int64_t N, const det_wgrad_cfg* cfg,
+                                         int atomic, size_t* bytes);
+int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_m, const void* G, int64_t ldg, const void* X,
+                          int64_t ldx, const int32_t* offs, int32_t E, int64_t T_total, int64_t M, int64_t N,
+                          const det_wgrad_cfg* cfg, void* ws, size_t ws_bytes, int atomic, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics (tests only). det_detmath_eval evaluates the device versions of
+ * the gate's exp / log1p / softplus / sigmoid sequences elementwise:
+ * fn = 0 exp32, 1 log1p32, 2 softplus32, 3 sigmoid32. x, y: [n] float32
+ * device arrays that must not overlap. Lets a test compare the GPU's bits
+ * with the CPU oracle's over any sample of inputs. */
+int det_detmath_eval(const float* x, float* y, int64_t n, int fn, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DETGRAD_H */

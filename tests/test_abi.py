@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad
+arguments on the host before any HIP call (CPU only, no kernel launches)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import deterministic_gradient_reductions_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "detgrad.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dg.library_path), reason="libdetgrad.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(det_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = ctypes.CDLL(dg.library_path)
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version():
+    assert dg.det_abi_version() == 1
+
+
+def lib():
+    return dg.lib()
+
+
+def err():
+    return lib().det_last_error().decode()
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)  # never dereferenced: every case below fails validation first
+
+
+def test_atomic_flag_must_be_0_or_1():
+    n = ctypes.c_size_t()
+    for bad in (2, -1, 7):
+        assert lib().det_grouped_dprob_workspace_size(16, 16, None, bad, ctypes.byref(n)) == dg.DET_ERR_INVALID_ARG
+        assert "atomic" in err()
+        assert lib().det_grouped_dprob(FAKE, FAKE, 16, FAKE, 16, 16, 16, FAKE, 1, None, None, 0, bad, None) == \
+            dg.DET_ERR_INVALID_ARG
+        assert lib().det_colsum(FAKE, 16, 1, FAKE, 16, 1, 0, FAKE, FAKE, 16, 16, FAKE, FAKE, None, None, 0, bad,
+                                None) == dg.DET_ERR_INVALID_ARG
+        assert lib().det_index_add_workspace_size(16, 8, 16, None, bad, ctypes.byref(n)) == dg.DET_ERR_INVALID_ARG
+        assert lib().det_grouped_wgrad_acc_workspace_size(16, 1, 16, 16, None, bad, ctypes.byref(n)) == \
+            dg.DET_ERR_INVALID_ARG
+
+
+def test_dprob_validation():
+    L = lib()
+    # negative sizes
+    assert L.det_grouped_dprob(FAKE, FAKE, 16, FAKE, 16, -1, 16, FAKE, 1, None, None, 0, 0, None) == \
+        dg.DET_ERR_INVALID_ARG
+    # ld < N
+    assert L.det_grouped_dprob(FAKE, FAKE, 8, FAKE, 16, 4, 16, FAKE, 1, None, None, 0, 0, None) == \
+        dg.DET_ERR_INVALID_ARG
+    # illegal tile
+    cfg = dg.DprobCfg(64, 16)
+    assert L.det_grouped_dprob(FAKE, FAKE, 16, FAKE, 16, 4, 16, FAKE, 1, ctypes.byref(cfg), None, 0, 0, None) == \
+        dg.DET_ERR_INVALID_ARG
+    cfg = dg.DprobCfg(128, 0)
+    assert L.det_grouped_dprob(FAKE, FAKE, 16, FAKE, 16, 4, 16, FAKE, 1, ctypes.byref(cfg), None, 0, 0, None) == \
+        dg.DET_ERR_INVALID_ARG
+    # output overlapping an input
+    base = 0x200000
+    assert L.det_grouped_dprob(P(base + 8), P(base), 16, P(base + 4096), 16, 4, 16, P(base + 8192), 1, None, None, 0,
+                               0, None) == dg.DET_ERR_OVERLAP
+    # NULL pointers
+    assert L.det_grouped_dprob(None, FAKE, 16, FAKE, 16, 4, 16, FAKE, 1, None, None, 0, 0, None) == \
+        dg.DET_ERR_INVALID_ARG
+    # empty problem: OK with nothing launched, even with NULL pointers
+    assert L.det_grouped_dprob(None, None, 0, None, 0, 0, 16, None, 1, None, None, 0, 0, None) == dg.DET_OK
+    n = ctypes.c_size_t(123)
+    assert L.det_grouped_dprob_workspace_size(16384, 2048, None, 0, ctypes.byref(n)) == dg.DET_OK and n.value == 0
+
+
+def test_colsum_validation_and_selector():
+    L = lib()
+    # shape-only rule: block_h covers H; block_t the largest of 256/128/64 that
+    # still gives >= 256 workgroups, else 64
+    c = dg.det_colsum_select_cfg(16384, 32)
+    assert (c.block_t, c.block_h) == (64, 32)
+    c = dg.det_colsum_select_cfg(4096, 16)
+    assert (c.block_t, c.block_h) == (64, 16)
+    c = dg.det_colsum_select_cfg(16384 * 4, 32)
+    assert (c.block_t, c.block_h) == (256, 32)
+    c = dg.det_colsum_select_cfg(32768, 5)
+    assert (c.block_t, c.block_h) == (128, 8)
+    c = dg.det_colsum_select_cfg(1000, 100)
+    assert (c.block_t, c.block_h) == (64, 32)
+    bad = dg.ColsumCfg(96, 16)
+    assert L.det_colsum(FAKE, 16, 1, FAKE, 16, 1, 0, FAKE, FAKE, 16, 16, FAKE, FAKE, ctypes.byref(bad), None, 0, 0,
+                        None) == dg.DET_ERR_INVALID_ARG
+    # fp32 inputs: not implemented yet
+    assert L.det_colsum(FAKE, 16, 1, FAKE, 16, 1, 1, FAKE, FAKE, 16, 16, FAKE, FAKE, None, None, 0, 0, None) == \
+        dg.DET_ERR_UNSUPPORTED
+    # workspace too small / missing / misaligned
+    n = dg.det_colsum_workspace_size(1000, 16)
+    assert n >= 256 + 2 * 16 * 4 * (1000 // 256)
+    assert L.det_colsum(FAKE, 16, 1, FAKE, 16, 1, 0, FAKE, FAKE, 1000, 16, P(0x900000), P(0x900100), None, None, 0, 0,
+                        None) == dg.DET_ERR_WORKSPACE
+    assert L.det_colsum(FAKE, 16, 1, FAKE, 16, 1, 0, FAKE, FAKE, 1000, 16, P(0x900000), P(0x900100), None,
+                        P(0xA00000), n - 4, 0, None) == dg.DET_ERR_WORKSPACE
+    assert L.det_colsum(FAKE, 16, 1, FAKE, 16, 1, 0, FAKE, FAKE, 1000, 16, P(0x900000), P(0x900100), None,
+                        P(0xA00010), n, 0, None) == dg.DET_ERR_WORKSPACE
+    # outputs overlapping each other
+    assert L.det_colsum(FAKE, 16, 1, FAKE, 16, 1, 0, FAKE, FAKE, 1000, 16, P(0x900000), P(0x900010), None,
+                        P(0xA00000), n, 0, None) == dg.DET_ERR_OVERLAP
+    # zero strides
+    assert L.det_colsum(FAKE, 0, 1, FAKE, 16, 1, 0, FAKE, FAKE, 1000, 16, P(0x900000), P(0x900100), None,
+                        P(0xA00000), n, 0, None) == dg.DET_ERR_INVALID_ARG
+
+
+def test_workspace_init_validation():
+    L = lib()
+    assert L.det_workspace_init(None, 256, None) == dg.DET_ERR_WORKSPACE
+    assert L.det_workspace_init(P(0x10010), 256, None) == dg.DET_ERR_WORKSPACE
+    assert L.det_workspace_init(P(0x10000), 64, None) == dg.DET_ERR_WORKSPACE
