@@ -6,10 +6,11 @@
 // the two gradient terms per element (detmath, so the CPU oracle can match
 // every bit) and reduces its rows with the adjacent pairwise tree in
 // registers; the remaining tree levels run over LDS. The resulting tile slot
-// (one per head and gradient) goes to the workspace; the last workgroup to
-// finish (an integer ticket in the workspace header) folds the slots of every
-// head in tile order and adds the totals into dA_log / ddt_bias. One launch,
-// no float atomics, and the ticket resets itself for the next call.
+// (one per head and gradient) goes to the workspace. A second kernel on the
+// same stream folds the slots of every head in tile order and adds the totals
+// into dA_log / ddt_bias (the page's "caller reduces them on the existing
+// stream"); the kernel boundary orders the slot writes before the fold without
+// any device-wide fence inside a kernel.
 //
 // The atomic arm computes the same tile slots and adds them into the outputs
 // with hardware float atomics, in whatever order the tiles finish.
@@ -34,7 +35,6 @@ struct ColsumArgs {
   int64_t T, H;
   float* dA_log;
   float* ddt_bias;
-  uint32_t* ticket;  // workspace header word 0
   float* slot1;      // [S][H]
   float* slot2;      // [S][H]
 };
@@ -56,7 +56,6 @@ __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
   constexpr int kNB = kWG / BH;       // row blocks per tile (threads per head)
   __shared__ float red1[kWG];
   __shared__ float red2[kWG];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int hl = tid % BH;
@@ -115,43 +114,44 @@ __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
       }
     }
   }
-  if (ATOMIC) return;
+}
 
-  // Publish the slots, then take a ticket; the last workgroup folds.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t n_wg = gridDim.x * gridDim.y;
-    const uint32_t t = atomicAdd(p.ticket, 1u);
-    s_last = (t == n_wg - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int64_t S = gridDim.x;
-  constexpr int kBatch = 16;  // slot loads in flight before the dependent adds
-  for (int64_t hh = tid; hh < p.H; hh += kWG) {
-    float tot1 = -0.0f, tot2 = -0.0f;
-    for (int64_t i0 = 0; i0 < S; i0 += kBatch) {
-      float b1[kBatch], b2[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int64_t i = i0 + j < S ? i0 + j : S - 1;
-        b1[j] = p.slot1[i * p.H + hh];
-        b2[j] = p.slot2[i * p.H + hh];
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        if (i0 + j < S) {
-          tot1 = tot1 + b1[j];
-          tot2 = tot2 + b2[j];
-        }
-      }
+// Phase 2: fold the tile slots of every head left to right and add the totals.
+// One workgroup per 32 heads. The slots are staged through LDS in pieces of
+// kPiece tiles so that all their loads are in flight together; then one thread
+// per (head, gradient) runs the strictly sequential fold over the piece.
+constexpr int kFoldHeads = 32;
+constexpr int kPiece = 128;
+
+__global__ __launch_bounds__(kWG) void colsum_fold_kernel(const float* __restrict__ slot1,
+                                                          const float* __restrict__ slot2, int64_t S, int64_t H,
+                                                          float* __restrict__ dA_log, float* __restrict__ ddt_bias) {
+  __shared__ float buf[2][kPiece][kFoldHeads];
+  const int tid = threadIdx.x;
+  const int64_t h0 = static_cast<int64_t>(blockIdx.x) * kFoldHeads;
+  const int which = tid / kFoldHeads;  // 0: dA_log, 1: ddt_bias (threads 0..63 fold)
+  const int hl = tid % kFoldHeads;
+  float tot = -0.0f;
+  for (int64_t i0 = 0; i0 < S; i0 += kPiece) {
+    const int64_t n = S - i0 < kPiece ? S - i0 : kPiece;
+    for (int j = tid; j < n * kFoldHeads; j += kWG) {
+      const int64_t i = i0 + j / kFoldHeads;
+      const int64_t h = h0 + j % kFoldHeads;
+      const bool ok = h < H;
+      buf[0][j / kFoldHeads][j % kFoldHeads] = ok ? slot1[i * H + h] : 0.0f;
+      buf[1][j / kFoldHeads][j % kFoldHeads] = ok ? slot2[i * H + h] : 0.0f;
     }
-    p.dA_log[hh] = p.dA_log[hh] + tot1;
-    p.ddt_bias[hh] = p.ddt_bias[hh] + tot2;
+    __syncthreads();
+    if (tid < 2 * kFoldHeads) {
+      for (int64_t i = 0; i < n; ++i) tot = tot + buf[which][i][hl];
+    }
+    __syncthreads();
   }
-  if (tid == 0) __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int64_t h = h0 + hl;
+  if (tid < 2 * kFoldHeads && h < H) {
+    float* o = which == 0 ? dA_log : ddt_bias;
+    o[h] = o[h] + tot;
+  }
 }
 
 bool valid_cfg(const det_colsum_cfg& c) {
@@ -169,10 +169,13 @@ size_t ws_bytes_for(int64_t T, int64_t H, const det_colsum_cfg& c) {
 template <int BT, int BH>
 void launch_one(const ColsumArgs& p, int atomic, dim3 grid, hipStream_t st) {
   constexpr int R = BT * BH / kWG;
-  if (atomic)
+  if (atomic) {
     hipLaunchKernelGGL((colsum_kernel<R, BH, true>), grid, dim3(kWG), 0, st, p);
-  else
+  } else {
     hipLaunchKernelGGL((colsum_kernel<R, BH, false>), grid, dim3(kWG), 0, st, p);
+    hipLaunchKernelGGL(colsum_fold_kernel, dim3(static_cast<uint32_t>(ceil_div(p.H, kFoldHeads))), dim3(kWG), 0, st,
+                       p.slot1, p.slot2, static_cast<int64_t>(grid.x), p.H, p.dA_log, p.ddt_bias);
+  }
 }
 
 void launch(const ColsumArgs& p, const det_colsum_cfg& c, int atomic, hipStream_t st) {
@@ -275,7 +278,6 @@ extern "C" int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void*
   p.ddt_bias = ddt_bias;
   char* w = static_cast<char*>(ws);
   const size_t slot_bytes = align_up(static_cast<size_t>(ceil_div(T, c.block_t) * H) * 4, 256);
-  p.ticket = atomic ? nullptr : reinterpret_cast<uint32_t*>(w);
   p.slot1 = atomic ? nullptr : reinterpret_cast<float*>(w + DET_WS_HEADER_BYTES);
   p.slot2 = atomic ? nullptr : reinterpret_cast<float*>(w + DET_WS_HEADER_BYTES + slot_bytes);
   launch(p, c, atomic, as_stream(stream));

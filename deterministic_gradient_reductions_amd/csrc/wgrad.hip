@@ -1,15 +1,369 @@
-// det_grouped_wgrad_acc (placeholder until the kernels land).
+// det_grouped_wgrad_acc: main_grad[e] += G_e^T X_e with a fixed-order split-K
+// (FlashInfer PR #8602: fused fp32 weight-gradient accumulate into main_grad;
+// #8924: deterministic accumulate, bitwise the AccumulateGrad of the
+// deterministic dW, with expert offsets read on the device).
+//
+// Contraction on the matrix cores. G_e [T_e x M] and X_e [T_e x N] both have
+// the token index as their row index, so the reduction runs down the rows of
+// both operands, while v_mfma_f32_32x32x16_bf16 wants each lane to hold 8
+// consecutive k values of one output row (A) or column (B). Each lane therefore
+// loads 8 token rows x 4 consecutive columns (8 bytes per row, 32 lanes cover
+// 128 contiguous columns) and transposes the 8x4 block in registers with
+// v_perm_b32. Fragment i (i = 0..3) then holds output rows m0 + 4r + i for
+// lane slot r: one MFMA computes a strided 32x32 sub-tile, and 4 x 4 MFMAs
+// cover the wave's 128 x 128 output tile. No LDS, no barriers.
+//
+// Canonical order (the oracle's): an expert's rows are cut into splits of
+// k_tile * ktiles_per_split rows counted from the expert's first row (one split
+// when ktiles_per_split = 0). A split's partial is the chain of MFMAs over its
+// rows in ascending 16-row blocks starting from +0.0 (rows past the split end
+// are zero). With one split the epilogue adds the partial into main_grad
+// directly; with several, each partial goes to scratch and a second kernel adds
+// (((Q0 + Q1) + Q2) + ...) into main_grad once.
+//
+// The atomic arm adds every split's partial into main_grad with float atomics.
 #include "common.hpp"
-using namespace detgrad;
-extern "C" int det_grouped_wgrad_acc_workspace_size(int64_t, int32_t, int64_t, int64_t, const det_wgrad_cfg*,
-                                                    int atomic, size_t* bytes) {
-  if (int s = check_atomic_flag(atomic)) return s;
-  if (bytes) *bytes = 0;
-  return set_error(DET_ERR_UNSUPPORTED, "wgrad: not implemented yet");
+
+namespace detgrad {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTileM = 128;  // workgroup tile: 128 (m) x 256 (n), 4 waves of 128 x 64
+constexpr int kTileN = 256;
+constexpr int kWaveN = 64;
+constexpr int kWave = 64;
+constexpr int kKTile = 512;
+
+struct WgradArgs {
+  float* mg;
+  int64_t ld_e, ld_m;
+  const uint16_t* G;
+  int64_t ldg;
+  const uint16_t* X;
+  int64_t ldx;
+  const int32_t* offs;
+  int E;
+  int64_t T_total;
+  int M, N;
+  int64_t split_rows;  // 0: one split per expert
+  int tiles_m, tiles_n;
+  int64_t n_units;  // tiles * max_splits
+  float* scratch;   // [max_splits][M][N]
+  int64_t max_splits;
+};
+
+// Expert row range with clamping (offsets are device data and cannot be
+// validated on the host): b_e = clamp(offs[e], b_{e-1}, T_total).
+struct Split {
+  int e;
+  int64_t g;       // global split index (scratch slot)
+  int64_t n_split;  // splits of this expert
+  int64_t r0, r1;
+};
+
+__device__ __forceinline__ bool find_split(const WgradArgs& p, int64_t g, Split& out) {
+  int64_t prev = 0, cum = 0;
+  int64_t b = p.offs[0];
+  b = b < 0 ? 0 : (b > p.T_total ? p.T_total : b);
+  prev = b;
+  for (int e = 0; e < p.E; ++e) {
+    int64_t nb = p.offs[e + 1];
+    nb = nb < prev ? prev : (nb > p.T_total ? p.T_total : nb);
+    const int64_t te = nb - prev;
+    const int64_t se = te == 0 ? 0 : (p.split_rows == 0 ? 1 : (te + p.split_rows - 1) / p.split_rows);
+    if (g < cum + se) {
+      const int64_t s = g - cum;
+      out.e = e;
+      out.g = g;
+      out.n_split = se;
+      if (p.split_rows == 0) {
+        out.r0 = prev;
+        out.r1 = nb;
+      } else {
+        out.r0 = prev + s * p.split_rows;
+        out.r1 = out.r0 + p.split_rows < nb ? out.r0 + p.split_rows : nb;
+      }
+      return true;
+    }
+    cum += se;
+    prev = nb;
+  }
+  return false;
 }
-extern "C" int det_grouped_wgrad_acc(float*, int64_t, int64_t, const void*, int64_t, const void*, int64_t,
-                                     const int32_t*, int32_t, int64_t, int64_t, int64_t, const det_wgrad_cfg*, void*,
-                                     size_t, int atomic, void*) {
+
+// Operand rows of one 16-row block for this lane: 8 token rows (k = 8*kg .. 8*kg+7
+// of the block) of 4 consecutive G columns (8 bytes) and 2 consecutive X
+// columns (4 bytes). Rows >= r1 read as zero.
+struct Rows {
+  uint2 a[8];
+  uint32_t b[8];
+};
+
+__device__ __forceinline__ void load_block(const WgradArgs& p, int64_t row, int64_t r1, int ca, int cb, Rows& v) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t r = row + e;
+    const bool ok = r < r1;
+    v.a[e] = ok ? *reinterpret_cast<const uint2*>(p.G + r * p.ldg + ca) : make_uint2(0u, 0u);
+    v.b[e] = ok ? *reinterpret_cast<const uint32_t*>(p.X + r * p.ldx + cb) : 0u;
+  }
+}
+
+// MFMA operand of column c of a lane's 8 x w block: dword q packs rows 2q
+// (low 16 bits) and 2q+1 (high 16 bits) of that column.
+__device__ __forceinline__ bf16x8_t frag_a(const uint2 (&v)[8], int c) {
+  const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+  u32x4_t d;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lo = (c >> 1) ? v[2 * q].y : v[2 * q].x;
+    const uint32_t hi = (c >> 1) ? v[2 * q + 1].y : v[2 * q + 1].x;
+    d[q] = __builtin_amdgcn_perm(hi, lo, sel);
+  }
+  return __builtin_bit_cast(bf16x8_t, d);
+}
+
+__device__ __forceinline__ bf16x8_t frag_b(const uint32_t (&v)[8], int c) {
+  const uint32_t sel = c ? 0x07060302u : 0x05040100u;
+  u32x4_t d;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = __builtin_amdgcn_perm(v[2 * q + 1], v[2 * q], sel);
+  return __builtin_bit_cast(bf16x8_t, d);
+}
+
+__device__ __forceinline__ void mma_block(const Rows& v, f32x16_t (&acc)[4][2]) {
+  const bf16x8_t fb0 = frag_b(v.b, 0), fb1 = frag_b(v.b, 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x8_t fa = frag_a(v.a, i);
+    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb0, acc[i][0], 0, 0, 0);
+    acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb1, acc[i][1], 0, 0, 0);
+  }
+}
+
+// One workgroup = 4 waves = a 128 (m) x 256 (n) output tile; wave w takes the
+// 128 x 64 columns n0 + 64w. The four waves read the same G rows (shared
+// through L1) and different X columns.
+template <bool ATOMIC>
+__global__ __launch_bounds__(4 * kWave) void wgrad_kernel(WgradArgs p) {
+  const int64_t u = blockIdx.x;
+  if (u >= p.n_units) return;
+  const int n_tiles = p.tiles_m * p.tiles_n;
+  const int64_t g = u / n_tiles;
+  const int t = static_cast<int>(u % n_tiles);
+  Split sp;
+  if (!find_split(p, g, sp)) return;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int m0 = (t / p.tiles_n) * kTileM;
+  const int n0 = (t % p.tiles_n) * kTileN + wave * kWaveN;
+  const int r = lane & 31;
+  const int kg = lane >> 5;
+  const int ca = m0 + 4 * r;
+  const int cb = n0 + 2 * r;
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  // Three register buffers: the loads of blocks k+1 and k+2 are in flight
+  // while block k runs on the matrix cores.
+  Rows v0, v1, v2;
+  const int64_t r1 = sp.r1;
+  int64_t k = sp.r0;
+  load_block(p, k + 8 * kg, r1, ca, cb, v0);
+  load_block(p, k + 16 + 8 * kg, r1, ca, cb, v1);
+  while (true) {
+    load_block(p, k + 32 + 8 * kg, r1, ca, cb, v2);
+    mma_block(v0, acc);
+    if ((k += 16) >= r1) break;
+    load_block(p, k + 32 + 8 * kg, r1, ca, cb, v0);
+    mma_block(v1, acc);
+    if ((k += 16) >= r1) break;
+    load_block(p, k + 32 + 8 * kg, r1, ca, cb, v1);
+    mma_block(v2, acc);
+    if ((k += 16) >= r1) break;
+  }
+
+  // Epilogue: lane (r, kg), MFMA (i, j), accumulator q holds output
+  // m = m0 + 4 * (8*(q/4) + 4*kg + q%4) + i,  n = n0 + 2*r + j.
+  const bool direct = sp.n_split == 1;
+  float* dst_base;
+  int64_t ld_m;
+  if (ATOMIC || direct) {
+    dst_base = p.mg + sp.e * p.ld_e;
+    ld_m = p.ld_m;
+  } else {
+    dst_base = p.scratch + sp.g * static_cast<int64_t>(p.M) * p.N;
+    ld_m = p.N;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int m = m0 + 4 * (8 * (q / 4) + 4 * kg + (q % 4)) + i;
+      float* d = dst_base + static_cast<int64_t>(m) * ld_m + cb;
+      const float v0 = acc[i][0][q], v1 = acc[i][1][q];
+      if (ATOMIC) {
+        unsafeAtomicAdd(d + 0, v0);
+        unsafeAtomicAdd(d + 1, v1);
+      } else if (direct) {
+        float2 o = *reinterpret_cast<const float2*>(d);
+        o.x = o.x + v0;
+        o.y = o.y + v1;
+        *reinterpret_cast<float2*>(d) = o;
+      } else {
+        *reinterpret_cast<float2*>(d) = make_float2(v0, v1);
+      }
+    }
+  }
+}
+
+// Fold of multi-split experts: main_grad[e] += ((Q0 + Q1) + ...) elementwise.
+__global__ __launch_bounds__(256) void wgrad_fold_kernel(WgradArgs p) {
+  const int64_t per_e = static_cast<int64_t>(p.M) * p.N / 4;  // float4 per expert
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int e = static_cast<int>(blockIdx.y);
+  if (idx >= per_e) return;
+  // locate expert e's splits (same clamping as the matrix kernel)
+  int64_t prev = p.offs[0];
+  prev = prev < 0 ? 0 : (prev > p.T_total ? p.T_total : prev);
+  int64_t g0 = 0, se = 0;
+  for (int x = 0; x <= e; ++x) {
+    int64_t nb = p.offs[x + 1];
+    nb = nb < prev ? prev : (nb > p.T_total ? p.T_total : nb);
+    const int64_t te = nb - prev;
+    const int64_t s = te == 0 ? 0 : (te + p.split_rows - 1) / p.split_rows;
+    if (x < e) g0 += s; else se = s;
+    prev = nb;
+  }
+  if (se < 2) return;
+  const int64_t m = (idx * 4) / p.N;
+  const int64_t n = (idx * 4) % p.N;
+  float4 tot = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
+  for (int64_t s = 0; s < se; ++s) {
+    const float4 q = *reinterpret_cast<const float4*>(p.scratch + (g0 + s) * static_cast<int64_t>(p.M) * p.N + m * p.N + n);
+    tot.x = tot.x + q.x; tot.y = tot.y + q.y; tot.z = tot.z + q.z; tot.w = tot.w + q.w;
+  }
+  float* d = p.mg + e * p.ld_e + m * p.ld_m + n;
+  float4 o = *reinterpret_cast<const float4*>(d);
+  o.x = o.x + tot.x; o.y = o.y + tot.y; o.z = o.z + tot.z; o.w = o.w + tot.w;
+  *reinterpret_cast<float4*>(d) = o;
+}
+
+int resolve(const det_wgrad_cfg* cfg, det_wgrad_cfg* out) {
+  det_wgrad_cfg c{kTileM, kTileN, kKTile, 0};
+  if (cfg) c = *cfg;
+  if (c.block_m != kTileM || c.block_n != kTileN)
+    return set_error(DET_ERR_UNSUPPORTED, "wgrad: block_m x block_n must be %d x %d, got %d x %d", kTileM, kTileN,
+                     c.block_m, c.block_n);
+  if (c.k_tile != kKTile) return set_error(DET_ERR_INVALID_ARG, "wgrad: k_tile must be %d, got %d", kKTile, c.k_tile);
+  if (c.ktiles_per_split < 0 || c.ktiles_per_split > (1 << 20))
+    return set_error(DET_ERR_INVALID_ARG, "wgrad: ktiles_per_split must be in [0, 2^20], got %d", c.ktiles_per_split);
+  *out = c;
+  return DET_OK;
+}
+
+int check_shape(int64_t T_total, int32_t E, int64_t M, int64_t N) {
+  if (T_total < 0 || E < 0 || M < 0 || N < 0) return set_error(DET_ERR_INVALID_ARG, "wgrad: sizes must be >= 0");
+  if (M % kTileM || N % kTileN)
+    return set_error(DET_ERR_UNSUPPORTED, "wgrad: M and N must be multiples of %d and %d, got %lld x %lld", kTileM,
+                     kTileN, static_cast<long long>(M), static_cast<long long>(N));
+  if (M > (1 << 20) || N > (1 << 20) || E > 4096) return set_error(DET_ERR_UNSUPPORTED, "wgrad: problem too large");
+  return DET_OK;
+}
+
+int64_t max_splits(int64_t T_total, int32_t E, const det_wgrad_cfg& c) {
+  if (c.ktiles_per_split == 0) return E;
+  const int64_t step = static_cast<int64_t>(c.k_tile) * c.ktiles_per_split;
+  return ceil_div(T_total, step) + E;
+}
+
+size_t scratch_bytes(int64_t T_total, int32_t E, int64_t M, int64_t N, const det_wgrad_cfg& c) {
+  if (c.ktiles_per_split == 0) return 0;  // one split per expert: partials stay in registers
+  return static_cast<size_t>(max_splits(T_total, E, c)) * static_cast<size_t>(M * N) * 4;
+}
+
+}  // namespace
+}  // namespace detgrad
+
+using namespace detgrad;
+
+extern "C" int det_grouped_wgrad_acc_workspace_size(int64_t T_total, int32_t E, int64_t M, int64_t N,
+                                                    const det_wgrad_cfg* cfg, int atomic, size_t* bytes) {
   if (int s = check_atomic_flag(atomic)) return s;
-  return set_error(DET_ERR_UNSUPPORTED, "wgrad: not implemented yet");
+  if (!bytes) return set_error(DET_ERR_INVALID_ARG, "wgrad: bytes is NULL");
+  if (int s = check_shape(T_total, E, M, N)) return s;
+  det_wgrad_cfg c;
+  if (int s = resolve(cfg, &c)) return s;
+  const size_t sb = scratch_bytes(T_total, E, M, N, c);
+  *bytes = (atomic || sb == 0) ? 0 : DET_WS_HEADER_BYTES + align_up(sb, 256);
+  return ok();
+}
+
+extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_m, const void* G, int64_t ldg,
+                                     const void* X, int64_t ldx, const int32_t* offs, int32_t E, int64_t T_total,
+                                     int64_t M, int64_t N, const det_wgrad_cfg* cfg, void* ws, size_t ws_bytes,
+                                     int atomic, void* stream) {
+  if (int s = check_atomic_flag(atomic)) return s;
+  if (int s = check_shape(T_total, E, M, N)) return s;
+  det_wgrad_cfg c;
+  if (int s = resolve(cfg, &c)) return s;
+  if (E == 0 || M == 0 || N == 0 || T_total == 0) return ok();
+  if (!main_grad || !G || !X || !offs) return set_error(DET_ERR_INVALID_ARG, "wgrad: NULL pointer");
+  if (ld_m < N || ld_e < M * ld_m)
+    return set_error(DET_ERR_INVALID_ARG, "wgrad: need ld_m >= N and ld_e >= M*ld_m (an expanded main_grad is rejected)");
+  if (ldg < M || ldx < N) return set_error(DET_ERR_INVALID_ARG, "wgrad: need ldg >= M and ldx >= N");
+  if (ldg % 4 || ldx % 2 || !aligned(G, 8) || !aligned(X, 4) || ld_m % 2 || ld_e % 2 || !aligned(main_grad, 8))
+    return set_error(DET_ERR_UNSUPPORTED, "wgrad: rows of G, X and main_grad must be 8-, 4- and 8-byte aligned");
+  const size_t sb = scratch_bytes(T_total, E, M, N, c);
+  const size_t need = (atomic || sb == 0) ? 0 : DET_WS_HEADER_BYTES + align_up(sb, 256);
+  if (int s = check_workspace(ws, ws_bytes, need)) return s;
+  const Range out = range2d(main_grad, static_cast<int64_t>(E) * M, N, ld_m, 4);
+  Range out_full;
+  out_full.lo = reinterpret_cast<uintptr_t>(main_grad);
+  out_full.hi = out_full.lo + static_cast<uintptr_t>(((E - 1) * ld_e + (M - 1) * ld_m + N) * 4);
+  (void)out;
+  if (overlaps(out_full, range2d(G, T_total, M, ldg, 2)) || overlaps(out_full, range2d(X, T_total, N, ldx, 2)) ||
+      overlaps(out_full, range1d(offs, (static_cast<size_t>(E) + 1) * 4)) || overlaps(out_full, range1d(ws, ws_bytes)))
+    return set_error(DET_ERR_OVERLAP, "wgrad: main_grad overlaps an input or the workspace");
+  WgradArgs p;
+  p.mg = main_grad;
+  p.ld_e = ld_e;
+  p.ld_m = ld_m;
+  p.G = static_cast<const uint16_t*>(G);
+  p.ldg = ldg;
+  p.X = static_cast<const uint16_t*>(X);
+  p.ldx = ldx;
+  p.offs = offs;
+  p.E = E;
+  p.T_total = T_total;
+  p.M = static_cast<int>(M);
+  p.N = static_cast<int>(N);
+  p.split_rows = c.ktiles_per_split == 0 ? 0 : static_cast<int64_t>(c.k_tile) * c.ktiles_per_split;
+  p.tiles_m = static_cast<int>(M / kTileM);
+  p.tiles_n = static_cast<int>(N / kTileN);
+  p.max_splits = max_splits(T_total, E, c);
+  p.n_units = static_cast<int64_t>(p.tiles_m) * p.tiles_n * p.max_splits;
+  p.scratch = (atomic || sb == 0) ? nullptr : reinterpret_cast<float*>(static_cast<char*>(ws) + DET_WS_HEADER_BYTES);
+  if (p.n_units > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "wgrad: too many work units");
+  const hipStream_t st = as_stream(stream);
+  if (atomic) {
+    hipLaunchKernelGGL(wgrad_kernel<true>, dim3(static_cast<uint32_t>(p.n_units)), dim3(4 * kWave), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(wgrad_kernel<false>, dim3(static_cast<uint32_t>(p.n_units)), dim3(4 * kWave), 0, st, p);
+    if (p.split_rows != 0) {
+      const int64_t per_e = M * N / 4;
+      hipLaunchKernelGGL(wgrad_fold_kernel, dim3(static_cast<uint32_t>(ceil_div(per_e, 256)), static_cast<uint32_t>(E)),
+                         dim3(256), 0, st, p);
+    }
+  }
+  return check_launch("det_grouped_wgrad_acc");
 }

@@ -128,3 +128,61 @@ def test_workspace_init_validation():
     assert L.det_workspace_init(None, 256, None) == dg.DET_ERR_WORKSPACE
     assert L.det_workspace_init(P(0x10010), 256, None) == dg.DET_ERR_WORKSPACE
     assert L.det_workspace_init(P(0x10000), 64, None) == dg.DET_ERR_WORKSPACE
+
+
+def test_index_add_validation():
+    L = lib()
+    n = ctypes.c_size_t()
+    assert L.det_index_add_workspace_size(2 ** 21, 128, 8192, None, 0, ctypes.byref(n)) == dg.DET_OK
+    assert n.value > 2 ** 21 * 4  # holds at least the permutation
+    assert L.det_index_add_workspace_size(2 ** 21, 128, 8192, None, 1, ctypes.byref(n)) == dg.DET_OK and n.value == 0
+    # dim not a multiple of 8, too many rows, bad chunk size
+    assert L.det_index_add_workspace_size(100, 12, 10, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
+    assert L.det_index_add_workspace_size(100, 16, 16385, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
+    bad = dg.IndexAddCfg(0)
+    assert L.det_index_add_workspace_size(100, 16, 10, ctypes.byref(bad), 0, ctypes.byref(n)) == dg.DET_ERR_INVALID_ARG
+    # out_ld < dim; misaligned src; overlap; fp32 src unsupported; workspace missing
+    O, I, S = P(0x100000), P(0x200000), P(0x300000)
+    assert L.det_index_add(O, 10, 16, 8, I, 100, S, 16, 0, None, None, 0, 1, None) == dg.DET_ERR_INVALID_ARG
+    assert L.det_index_add(O, 10, 16, 16, I, 100, P(0x300008), 16, 0, None, None, 0, 1, None) == dg.DET_ERR_UNSUPPORTED
+    assert L.det_index_add(O, 10, 16, 16, P(0x100010), 100, S, 16, 0, None, None, 0, 1, None) == dg.DET_ERR_OVERLAP
+    assert L.det_index_add(O, 10, 16, 16, I, 100, S, 16, 1, None, None, 0, 1, None) == dg.DET_ERR_UNSUPPORTED
+    assert L.det_index_add(O, 10, 16, 16, I, 100, S, 16, 0, None, None, 0, 0, None) == dg.DET_ERR_WORKSPACE
+    # empty problems return OK without touching anything
+    assert L.det_index_add(None, 10, 16, 16, None, 0, None, 16, 0, None, None, 0, 0, None) == dg.DET_OK
+
+
+def test_wgrad_validation():
+    L = lib()
+    n = ctypes.c_size_t()
+    # one split per expert needs no workspace; split-K needs max_splits * M * N * 4 bytes
+    assert L.det_grouped_wgrad_acc_workspace_size(36864, 8, 1408, 2048, None, 0, ctypes.byref(n)) == dg.DET_OK
+    assert n.value == 0
+    c = dg.WgradCfg(128, 256, 512, 4)
+    assert L.det_grouped_wgrad_acc_workspace_size(36864, 8, 1408, 2048, ctypes.byref(c), 0, ctypes.byref(n)) == dg.DET_OK
+    assert n.value == 256 + (36864 // 2048 + 8) * 1408 * 2048 * 4
+    assert L.det_grouped_wgrad_acc_workspace_size(36864, 8, 1408, 2048, ctypes.byref(c), 1, ctypes.byref(n)) == dg.DET_OK
+    assert n.value == 0
+    bad = dg.WgradCfg(128, 256, 256, 0)
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 256, ctypes.byref(bad), 0, ctypes.byref(n)) == \
+        dg.DET_ERR_INVALID_ARG
+    bad = dg.WgradCfg(64, 256, 512, 0)
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 256, ctypes.byref(bad), 0, ctypes.byref(n)) == \
+        dg.DET_ERR_UNSUPPORTED
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 100, 256, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
+    MG, G, X, O = P(0x1000000), P(0x9000000), P(0xA000000), P(0xB000000)
+    # an expanded main_grad (expert stride 0) is rejected
+    assert L.det_grouped_wgrad_acc(MG, 0, 256, G, 128, X, 256, O, 2, 64, 128, 256, None, None, 0, 0, None) == \
+        dg.DET_ERR_INVALID_ARG
+    # ld_m < N
+    assert L.det_grouped_wgrad_acc(MG, 128 * 256, 128, G, 128, X, 256, O, 2, 64, 128, 256, None, None, 0, 0,
+                                   None) == dg.DET_ERR_INVALID_ARG
+    # main_grad overlapping G
+    assert L.det_grouped_wgrad_acc(P(0x9000100), 128 * 256, 256, G, 128, X, 256, O, 2, 64, 128, 256, None, None, 0,
+                                   0, None) == dg.DET_ERR_OVERLAP
+    # split-K without a workspace
+    assert L.det_grouped_wgrad_acc(MG, 128 * 256, 256, G, 128, X, 256, O, 2, 64, 128, 256, ctypes.byref(c), None, 0,
+                                   0, None) == dg.DET_ERR_WORKSPACE
+    # empty problems are OK and touch nothing
+    assert L.det_grouped_wgrad_acc(None, 0, 0, None, 0, None, 0, None, 0, 0, 128, 256, None, None, 0, 0, None) == \
+        dg.DET_OK

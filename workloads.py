@@ -27,8 +27,13 @@ __all__ = [
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # finite inputs never carry out of 32 bits: the largest is 0xFF7FFFFF + 0x8000
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 def _rng(seed: int, tensor_id: int) -> np.random.Generator:
