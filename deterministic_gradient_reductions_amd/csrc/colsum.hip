@@ -134,16 +134,35 @@ __global__ __launch_bounds__(kWG) void colsum_fold_kernel(const float* __restric
   float tot = -0.0f;
   for (int64_t i0 = 0; i0 < S; i0 += kPiece) {
     const int64_t n = S - i0 < kPiece ? S - i0 : kPiece;
-    for (int j = tid; j < n * kFoldHeads; j += kWG) {
+    // every thread issues all of its loads before the first LDS store
+    constexpr int kPer = kPiece * kFoldHeads / kWG;
+    float v1[kPer], v2[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = tid + u * kWG;
       const int64_t i = i0 + j / kFoldHeads;
       const int64_t h = h0 + j % kFoldHeads;
-      const bool ok = h < H;
-      buf[0][j / kFoldHeads][j % kFoldHeads] = ok ? slot1[i * H + h] : 0.0f;
-      buf[1][j / kFoldHeads][j % kFoldHeads] = ok ? slot2[i * H + h] : 0.0f;
+      const bool ok = h < H && j < n * kFoldHeads;
+      v1[u] = ok ? slot1[i * H + h] : 0.0f;
+      v2[u] = ok ? slot2[i * H + h] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = tid + u * kWG;
+      buf[0][j / kFoldHeads][j % kFoldHeads] = v1[u];
+      buf[1][j / kFoldHeads][j % kFoldHeads] = v2[u];
     }
     __syncthreads();
     if (tid < 2 * kFoldHeads) {
-      for (int64_t i = 0; i < n; ++i) tot = tot + buf[which][i][hl];
+      int64_t i = 0;
+      for (; i + 8 <= n; i += 8) {
+        float b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) b[u] = buf[which][i + u][hl];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tot = tot + b[u];
+      }
+      for (; i < n; ++i) tot = tot + buf[which][i][hl];
     }
     __syncthreads();
   }

@@ -7,11 +7,12 @@
 // the token index as their row index, so the reduction runs down the rows of
 // both operands, while v_mfma_f32_32x32x16_bf16 wants each lane to hold 8
 // consecutive k values of one output row (A) or column (B). Each lane therefore
-// loads 8 token rows x 4 consecutive columns (8 bytes per row, 32 lanes cover
-// 128 contiguous columns) and transposes the 8x4 block in registers with
-// v_perm_b32. Fragment i (i = 0..3) then holds output rows m0 + 4r + i for
-// lane slot r: one MFMA computes a strided 32x32 sub-tile, and 4 x 4 MFMAs
-// cover the wave's 128 x 128 output tile. No LDS, no barriers.
+// reads 8 token rows x 4 consecutive columns (8 bytes per row, 32 lanes cover
+// 128 contiguous columns) from LDS and transposes the 8x4 block in registers
+// with v_perm_b32. Fragment i (i = 0..3) then holds output rows m0 + 4r + i
+// for lane slot r: one MFMA computes a strided 32x32 sub-tile, and 4 x 4 MFMAs
+// cover the wave's 128 x 128 output tile. G and X reach LDS in their memory
+// layout through coalesced 16-byte loads, double-buffered by K step.
 //
 // Canonical order (the oracle's): an expert's rows are cut into splits of
 // k_tile * ktiles_per_split rows counted from the expert's first row (one split
@@ -31,10 +32,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTileM = 128;  // workgroup tile: 128 (m) x 256 (n), 4 waves of 128 x 64
-constexpr int kTileN = 256;
-constexpr int kWaveN = 64;
-constexpr int kWave = 64;
+constexpr int kBM = 128;     // workgroup tile: 128 (m) x 512 (n), 4 waves of 128 x 128
+constexpr int kBN = 512;
+constexpr int kBK = 32;      // token rows per LDS stage
+constexpr int kWaveN = 128;
+constexpr int kThreads = 256;
+constexpr int kTileM = kBM;
+constexpr int kTileN = kBN;
 constexpr int kKTile = 512;
 
 struct WgradArgs {
@@ -94,61 +98,93 @@ __device__ __forceinline__ bool find_split(const WgradArgs& p, int64_t g, Split&
   return false;
 }
 
-// Operand rows of one 16-row block for this lane: 8 token rows (k = 8*kg .. 8*kg+7
-// of the block) of 4 consecutive G columns (8 bytes) and 2 consecutive X
-// columns (4 bytes). Rows >= r1 read as zero.
-struct Rows {
-  uint2 a[8];
-  uint32_t b[8];
-};
-
-__device__ __forceinline__ void load_block(const WgradArgs& p, int64_t row, int64_t r1, int ca, int cb, Rows& v) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int64_t r = row + e;
-    const bool ok = r < r1;
-    v.a[e] = ok ? *reinterpret_cast<const uint2*>(p.G + r * p.ldg + ca) : make_uint2(0u, 0u);
-    v.b[e] = ok ? *reinterpret_cast<const uint32_t*>(p.X + r * p.ldx + cb) : 0u;
-  }
-}
-
-// MFMA operand of column c of a lane's 8 x w block: dword q packs rows 2q
-// (low 16 bits) and 2q+1 (high 16 bits) of that column.
-__device__ __forceinline__ bf16x8_t frag_a(const uint2 (&v)[8], int c) {
-  const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+// MFMA operand of column c (0..3) of a lane's 8-row x 4-column block: dword q
+// packs rows 2q (low 16 bits) and 2q+1 (high 16 bits) of that column.
+template <int C>
+__device__ __forceinline__ bf16x8_t frag(const uint2 (&v)[8]) {
+  constexpr uint32_t sel = (C & 1) ? 0x07060302u : 0x05040100u;
   u32x4_t d;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t lo = (c >> 1) ? v[2 * q].y : v[2 * q].x;
-    const uint32_t hi = (c >> 1) ? v[2 * q + 1].y : v[2 * q + 1].x;
+    const uint32_t lo = (C >> 1) ? v[2 * q].y : v[2 * q].x;
+    const uint32_t hi = (C >> 1) ? v[2 * q + 1].y : v[2 * q + 1].x;
     d[q] = __builtin_amdgcn_perm(hi, lo, sel);
   }
   return __builtin_bit_cast(bf16x8_t, d);
 }
 
-__device__ __forceinline__ bf16x8_t frag_b(const uint32_t (&v)[8], int c) {
-  const uint32_t sel = c ? 0x07060302u : 0x05040100u;
-  u32x4_t d;
+// One K step of kBK token rows, staged in LDS as row-major [k][m] and [k][n]
+// slabs (the layout of G and X in memory). Each thread moves 16-byte chunks:
+// 2 of G (128 columns) and 8 of X (512 columns) per step. The loads are raw
+// buffer loads over the split's rows: a 32-bit per-thread offset, a scalar
+// per-chunk offset, and a record limit at the split end, so rows past it read
+// as zero without any branch.
+constexpr int kChunksA = kBM * kBK / 8 / kThreads;
+constexpr int kChunksB = kBN * kBK / 8 / kThreads;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9-family raw buffer descriptor
+
+struct Stage {
+  u32x4_t a[kChunksA];
+  u32x4_t b[kChunksB];
+};
+
+struct Src {
+  __amdgpu_buffer_rsrc_t ra, rb;  // G and X rows [r0, r1), rebased at r0
+  int32_t voff_a, voff_b;         // this thread's byte offset inside a step
+  int32_t step_a, step_b;         // bytes per kBK / kChunks rows (chunk stride)
+  int32_t krow_a, krow_b;         // bytes per token row
+};
+
+__device__ __forceinline__ void stage_load(const Src& src, int32_t krel, Stage& s) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) d[q] = __builtin_amdgcn_perm(v[2 * q + 1], v[2 * q], sel);
-  return __builtin_bit_cast(bf16x8_t, d);
+  for (int u = 0; u < kChunksA; ++u)
+    s.a[u] = __builtin_amdgcn_raw_buffer_load_b128(src.ra, src.voff_a, krel * src.krow_a + u * src.step_a, 0);
+#pragma unroll
+  for (int u = 0; u < kChunksB; ++u)
+    s.b[u] = __builtin_amdgcn_raw_buffer_load_b128(src.rb, src.voff_b, krel * src.krow_b + u * src.step_b, 0);
 }
 
-__device__ __forceinline__ void mma_block(const Rows& v, f32x16_t (&acc)[4][2]) {
-  const bf16x8_t fb0 = frag_b(v.b, 0), fb1 = frag_b(v.b, 1);
+__device__ __forceinline__ void stage_store(uint16_t (*la)[kBM], uint16_t (*lb)[kBN], const Stage& s) {
+  const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x8_t fa = frag_a(v.a, i);
-    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb0, acc[i][0], 0, 0, 0);
-    acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb1, acc[i][1], 0, 0, 0);
+  for (int u = 0; u < kChunksA; ++u) {
+    const int c = t + u * kThreads;
+    *reinterpret_cast<u32x4_t*>(&la[c / (kBM / 8)][(c % (kBM / 8)) * 8]) = s.a[u];
+  }
+#pragma unroll
+  for (int u = 0; u < kChunksB; ++u) {
+    const int c = t + u * kThreads;
+    *reinterpret_cast<u32x4_t*>(&lb[c / (kBN / 8)][(c % (kBN / 8)) * 8]) = s.b[u];
   }
 }
 
-// One workgroup = 4 waves = a 128 (m) x 256 (n) output tile; wave w takes the
-// 128 x 64 columns n0 + 64w. The four waves read the same G rows (shared
-// through L1) and different X columns.
+// One 16-row MFMA block from LDS rows [row0, row0 + 16): lane (r, kg) reads
+// rows row0 + 8*kg + e of its 4 G columns (4r..4r+3) and its 4 X columns
+// (128*wave + 4r ..), transposes, and issues 4 x 4 MFMAs.
+__device__ __forceinline__ void mma_block(const uint16_t (*la)[kBM], const uint16_t (*lb)[kBN], int row0, int r,
+                                          int kg, int wave, f32x16_t (&acc)[4][4]) {
+  uint2 ra[8], rb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ra[e] = *reinterpret_cast<const uint2*>(&la[row0 + 8 * kg + e][4 * r]);
+    rb[e] = *reinterpret_cast<const uint2*>(&lb[row0 + 8 * kg + e][kWaveN * wave + 4 * r]);
+  }
+  const bf16x8_t fa[4] = {frag<0>(ra), frag<1>(ra), frag<2>(ra), frag<3>(ra)};
+  const bf16x8_t fb[4] = {frag<0>(rb), frag<1>(rb), frag<2>(rb), frag<3>(rb)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+}
+
+// One workgroup = 4 waves = a 128 (m) x 512 (n) output tile; wave w owns the
+// 128 x 128 columns n0 + 128w. K runs in steps of kBK rows through two LDS
+// buffers: while the matrix cores work on one, the next step's global loads
+// are in flight in registers and then written to the other.
 template <bool ATOMIC>
-__global__ __launch_bounds__(4 * kWave) void wgrad_kernel(WgradArgs p) {
+__global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][kBK][kBM];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][kBK][kBN];
   const int64_t u = blockIdx.x;
   if (u >= p.n_units) return;
   const int n_tiles = p.tiles_m * p.tiles_n;
@@ -158,42 +194,62 @@ __global__ __launch_bounds__(4 * kWave) void wgrad_kernel(WgradArgs p) {
   if (!find_split(p, g, sp)) return;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int m0 = (t / p.tiles_n) * kTileM;
-  const int n0 = (t % p.tiles_n) * kTileN + wave * kWaveN;
+  const int m0 = (t / p.tiles_n) * kBM;
+  const int n0 = (t % p.tiles_n) * kBN;
   const int r = lane & 31;
   const int kg = lane >> 5;
-  const int ca = m0 + 4 * r;
-  const int cb = n0 + 2 * r;
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // Three register buffers: the loads of blocks k+1 and k+2 are in flight
-  // while block k runs on the matrix cores.
-  Rows v0, v1, v2;
-  const int64_t r1 = sp.r1;
-  int64_t k = sp.r0;
-  load_block(p, k + 8 * kg, r1, ca, cb, v0);
-  load_block(p, k + 16 + 8 * kg, r1, ca, cb, v1);
-  while (true) {
-    load_block(p, k + 32 + 8 * kg, r1, ca, cb, v2);
-    mma_block(v0, acc);
-    if ((k += 16) >= r1) break;
-    load_block(p, k + 32 + 8 * kg, r1, ca, cb, v0);
-    mma_block(v1, acc);
-    if ((k += 16) >= r1) break;
-    load_block(p, k + 32 + 8 * kg, r1, ca, cb, v1);
-    mma_block(v2, acc);
-    if ((k += 16) >= r1) break;
+  const int64_t r0 = sp.r0, r1 = sp.r1;
+  const int32_t rows = static_cast<int32_t>(r1 - r0);
+  Src src;
+  src.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.G + r0 * p.ldg), 0,
+                                             static_cast<int32_t>(rows * p.ldg * 2), kRsrcWord3);
+  src.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.X + r0 * p.ldx), 0,
+                                             static_cast<int32_t>(rows * p.ldx * 2), kRsrcWord3);
+  {
+    const int t = threadIdx.x;
+    src.krow_a = static_cast<int32_t>(p.ldg * 2);
+    src.krow_b = static_cast<int32_t>(p.ldx * 2);
+    src.voff_a = (t / (kBM / 8)) * src.krow_a + (m0 + (t % (kBM / 8)) * 8) * 2;
+    src.voff_b = (t / (kBN / 8)) * src.krow_b + (n0 + (t % (kBN / 8)) * 8) * 2;
+    src.step_a = (kThreads / (kBM / 8)) * src.krow_a;
+    src.step_b = (kThreads / (kBN / 8)) * src.krow_b;
+  }
+  Stage st;
+  stage_load(src, 0, st);
+  stage_store(lds_a[0], lds_b[0], st);
+  __syncthreads();
+  if (kBK < rows) stage_load(src, kBK, st);
+  // K loop, unrolled over the two LDS buffers so that every LDS address is a
+  // per-lane base plus a constant
+  for (int32_t k = 0; k < rows; k += 2 * kBK) {
+    mma_block(lds_a[0], lds_b[0], 0, r, kg, wave, acc);
+    if (k + 16 < rows) mma_block(lds_a[0], lds_b[0], 16, r, kg, wave, acc);
+    if (k + kBK < rows) {
+      stage_store(lds_a[1], lds_b[1], st);
+      if (k + 2 * kBK < rows) stage_load(src, k + 2 * kBK, st);
+    }
+    __syncthreads();
+    if (k + kBK >= rows) break;
+    mma_block(lds_a[1], lds_b[1], 0, r, kg, wave, acc);
+    if (k + kBK + 16 < rows) mma_block(lds_a[1], lds_b[1], 16, r, kg, wave, acc);
+    if (k + 2 * kBK < rows) {
+      stage_store(lds_a[0], lds_b[0], st);
+      if (k + 3 * kBK < rows) stage_load(src, k + 3 * kBK, st);
+    }
+    __syncthreads();
   }
 
   // Epilogue: lane (r, kg), MFMA (i, j), accumulator q holds output
-  // m = m0 + 4 * (8*(q/4) + 4*kg + q%4) + i,  n = n0 + 2*r + j.
+  // m = m0 + 4 * (8*(q/4) + 4*kg + q%4) + i,  n = n0 + 128*wave + 4*r + j.
   const bool direct = sp.n_split == 1;
   float* dst_base;
   int64_t ld_m;
@@ -204,24 +260,29 @@ __global__ __launch_bounds__(4 * kWave) void wgrad_kernel(WgradArgs p) {
     dst_base = p.scratch + sp.g * static_cast<int64_t>(p.M) * p.N;
     ld_m = p.N;
   }
+  const int nc = n0 + kWaveN * wave + 4 * r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int m = m0 + 4 * (8 * (q / 4) + 4 * kg + (q % 4)) + i;
-      float* d = dst_base + static_cast<int64_t>(m) * ld_m + cb;
-      const float v0 = acc[i][0][q], v1 = acc[i][1][q];
+      float* d = dst_base + static_cast<int64_t>(m) * ld_m + nc;
+      const float v0 = acc[i][0][q], v1 = acc[i][1][q], v2 = acc[i][2][q], v3 = acc[i][3][q];
       if (ATOMIC) {
         unsafeAtomicAdd(d + 0, v0);
         unsafeAtomicAdd(d + 1, v1);
+        unsafeAtomicAdd(d + 2, v2);
+        unsafeAtomicAdd(d + 3, v3);
       } else if (direct) {
-        float2 o = *reinterpret_cast<const float2*>(d);
-        o.x = o.x + v0;
-        o.y = o.y + v1;
-        *reinterpret_cast<float2*>(d) = o;
+        float4 o = *reinterpret_cast<const float4*>(d);
+        o.x = o.x + v0; o.y = o.y + v1; o.z = o.z + v2; o.w = o.w + v3;
+        *reinterpret_cast<float4*>(d) = o;
       } else {
-        *reinterpret_cast<float2*>(d) = make_float2(v0, v1);
+        *reinterpret_cast<float4*>(d) = make_float4(v0, v1, v2, v3);
       }
+      // keep the scheduler from hoisting every read-modify-write of the
+      // epilogue at once (that would need hundreds of registers)
+      if (q % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -277,6 +338,9 @@ int check_shape(int64_t T_total, int32_t E, int64_t M, int64_t N) {
     return set_error(DET_ERR_UNSUPPORTED, "wgrad: M and N must be multiples of %d and %d, got %lld x %lld", kTileM,
                      kTileN, static_cast<long long>(M), static_cast<long long>(N));
   if (M > (1 << 20) || N > (1 << 20) || E > 4096) return set_error(DET_ERR_UNSUPPORTED, "wgrad: problem too large");
+  // buffer loads use 32-bit byte offsets inside one split's rows
+  if (T_total * (M > N ? M : N) * 2 >= (1LL << 31))
+    return set_error(DET_ERR_UNSUPPORTED, "wgrad: T_total x max(M, N) too large for 32-bit offsets");
   return DET_OK;
 }
 
@@ -321,8 +385,8 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
   if (ld_m < N || ld_e < M * ld_m)
     return set_error(DET_ERR_INVALID_ARG, "wgrad: need ld_m >= N and ld_e >= M*ld_m (an expanded main_grad is rejected)");
   if (ldg < M || ldx < N) return set_error(DET_ERR_INVALID_ARG, "wgrad: need ldg >= M and ldx >= N");
-  if (ldg % 4 || ldx % 2 || !aligned(G, 8) || !aligned(X, 4) || ld_m % 2 || ld_e % 2 || !aligned(main_grad, 8))
-    return set_error(DET_ERR_UNSUPPORTED, "wgrad: rows of G, X and main_grad must be 8-, 4- and 8-byte aligned");
+  if (ldg % 8 || ldx % 8 || !aligned(G, 16) || !aligned(X, 16) || ld_m % 4 || ld_e % 4 || !aligned(main_grad, 16))
+    return set_error(DET_ERR_UNSUPPORTED, "wgrad: rows of G, X and main_grad must be 16-byte aligned");
   const size_t sb = scratch_bytes(T_total, E, M, N, c);
   const size_t need = (atomic || sb == 0) ? 0 : DET_WS_HEADER_BYTES + align_up(sb, 256);
   if (int s = check_workspace(ws, ws_bytes, need)) return s;
@@ -356,9 +420,9 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
   if (p.n_units > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "wgrad: too many work units");
   const hipStream_t st = as_stream(stream);
   if (atomic) {
-    hipLaunchKernelGGL(wgrad_kernel<true>, dim3(static_cast<uint32_t>(p.n_units)), dim3(4 * kWave), 0, st, p);
+    hipLaunchKernelGGL(wgrad_kernel<true>, dim3(static_cast<uint32_t>(p.n_units)), dim3(kThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL(wgrad_kernel<false>, dim3(static_cast<uint32_t>(p.n_units)), dim3(4 * kWave), 0, st, p);
+    hipLaunchKernelGGL(wgrad_kernel<false>, dim3(static_cast<uint32_t>(p.n_units)), dim3(kThreads), 0, st, p);
     if (p.split_rows != 0) {
       const int64_t per_e = M * N / 4;
       hipLaunchKernelGGL(wgrad_fold_kernel, dim3(static_cast<uint32_t>(ceil_div(per_e, 256)), static_cast<uint32_t>(E)),

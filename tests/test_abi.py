@@ -158,31 +158,34 @@ def test_wgrad_validation():
     # one split per expert needs no workspace; split-K needs max_splits * M * N * 4 bytes
     assert L.det_grouped_wgrad_acc_workspace_size(36864, 8, 1408, 2048, None, 0, ctypes.byref(n)) == dg.DET_OK
     assert n.value == 0
-    c = dg.WgradCfg(128, 256, 512, 4)
+    c = dg.WgradCfg(128, 512, 512, 4)
     assert L.det_grouped_wgrad_acc_workspace_size(36864, 8, 1408, 2048, ctypes.byref(c), 0, ctypes.byref(n)) == dg.DET_OK
     assert n.value == 256 + (36864 // 2048 + 8) * 1408 * 2048 * 4
     assert L.det_grouped_wgrad_acc_workspace_size(36864, 8, 1408, 2048, ctypes.byref(c), 1, ctypes.byref(n)) == dg.DET_OK
     assert n.value == 0
-    bad = dg.WgradCfg(128, 256, 256, 0)
-    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 256, ctypes.byref(bad), 0, ctypes.byref(n)) == \
+    bad = dg.WgradCfg(128, 512, 256, 0)
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 512, ctypes.byref(bad), 0, ctypes.byref(n)) == \
         dg.DET_ERR_INVALID_ARG
-    bad = dg.WgradCfg(64, 256, 512, 0)
-    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 256, ctypes.byref(bad), 0, ctypes.byref(n)) == \
+    bad = dg.WgradCfg(64, 512, 512, 0)
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 512, ctypes.byref(bad), 0, ctypes.byref(n)) == \
         dg.DET_ERR_UNSUPPORTED
-    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 100, 256, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 100, 512, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
     MG, G, X, O = P(0x1000000), P(0x9000000), P(0xA000000), P(0xB000000)
     # an expanded main_grad (expert stride 0) is rejected
-    assert L.det_grouped_wgrad_acc(MG, 0, 256, G, 128, X, 256, O, 2, 64, 128, 256, None, None, 0, 0, None) == \
+    assert L.det_grouped_wgrad_acc(MG, 0, 512, G, 128, X, 512, O, 2, 64, 128, 512, None, None, 0, 0, None) == \
         dg.DET_ERR_INVALID_ARG
     # ld_m < N
-    assert L.det_grouped_wgrad_acc(MG, 128 * 256, 128, G, 128, X, 256, O, 2, 64, 128, 256, None, None, 0, 0,
+    assert L.det_grouped_wgrad_acc(MG, 128 * 512, 256, G, 128, X, 512, O, 2, 64, 128, 512, None, None, 0, 0,
                                    None) == dg.DET_ERR_INVALID_ARG
     # main_grad overlapping G
-    assert L.det_grouped_wgrad_acc(P(0x9000100), 128 * 256, 256, G, 128, X, 256, O, 2, 64, 128, 256, None, None, 0,
+    assert L.det_grouped_wgrad_acc(P(0x9000100), 128 * 512, 512, G, 128, X, 512, O, 2, 64, 128, 512, None, None, 0,
                                    0, None) == dg.DET_ERR_OVERLAP
     # split-K without a workspace
-    assert L.det_grouped_wgrad_acc(MG, 128 * 256, 256, G, 128, X, 256, O, 2, 64, 128, 256, ctypes.byref(c), None, 0,
+    assert L.det_grouped_wgrad_acc(MG, 128 * 512, 512, G, 128, X, 512, O, 2, 64, 128, 512, ctypes.byref(c), None, 0,
                                    0, None) == dg.DET_ERR_WORKSPACE
+    # misaligned G rows
+    assert L.det_grouped_wgrad_acc(MG, 128 * 512, 512, G, 132, X, 512, O, 2, 64, 128, 512, None, None, 0, 0,
+                                   None) == dg.DET_ERR_UNSUPPORTED
     # empty problems are OK and touch nothing
-    assert L.det_grouped_wgrad_acc(None, 0, 0, None, 0, None, 0, None, 0, 0, 128, 256, None, None, 0, 0, None) == \
+    assert L.det_grouped_wgrad_acc(None, 0, 0, None, 0, None, 0, None, 0, 0, 128, 512, None, None, 0, 0, None) == \
         dg.DET_OK

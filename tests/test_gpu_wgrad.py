@@ -28,7 +28,7 @@ M_, N_ = 256, 512  # small shapes: 2 x 2 workgroup tiles
 
 
 def cfg(C):
-    return dg.WgradCfg(128, 256, 512, C)
+    return dg.WgradCfg(128, 512, 512, C)
 
 
 def run(inp, C=0, atomic=False, mg0=None, offs=None, G=None, X=None):
