@@ -36,17 +36,21 @@ constexpr int kBlockPos = 4096;  // source positions per count/scatter block
 constexpr int kMaxRows = 16384;  // LDS histogram capacity (64 KiB)
 constexpr int kMaxDim = 512;
 
+constexpr int kSegBlocks = 32;   // blocks per prefix segment
+
 struct Layout {
-  size_t hist, count, seg_off, chunk_off, perm, scratch, total;
-  int64_t nblk, max_chunks;
+  size_t hist, segtot, count, seg_off, chunk_off, perm, scratch, total;
+  int64_t nblk, nseg, max_chunks;
 };
 
 Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L) {
   Layout l;
   l.nblk = ceil_div(n_src, kBlockPos);
+  l.nseg = ceil_div(l.nblk, kSegBlocks);
   l.max_chunks = n_src / L + (n_rows < n_src ? n_rows : n_src) + 1;
   size_t o = DET_WS_HEADER_BYTES;
   l.hist = o;      o = align_up(o + static_cast<size_t>(l.nblk * n_rows) * 4, 256);
+  l.segtot = o;    o = align_up(o + static_cast<size_t>(l.nseg * n_rows) * 4, 256);
   l.count = o;     o = align_up(o + static_cast<size_t>(n_rows) * 4, 256);
   l.seg_off = o;   o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
   l.chunk_off = o; o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
@@ -56,22 +60,45 @@ Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L) {
   return l;
 }
 
-// ---- 1. count
+// Lanes of one wave holding the same id find each other with one ballot per
+// id bit; returns the mask of those lanes (0 for invalid lanes).
+__device__ __forceinline__ uint64_t match_peers(int32_t id, bool valid, int id_bits) {
+  uint64_t peers = __ballot(valid);
+  for (int bit = 0; bit < id_bits; ++bit) {
+    const bool set = valid && ((id >> bit) & 1);
+    const uint64_t m = __ballot(set);
+    peers &= set ? m : ~m;
+  }
+  return valid ? peers : 0ull;
+}
+
+// ---- 1. count. One LDS increment per distinct id per wave (the hot Zipf
+// key would otherwise serialise dozens of LDS atomics per instruction).
 __global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                uint32_t* __restrict__ hist, uint32_t* __restrict__ bad_accum) {
+                                                int id_bits, uint32_t* __restrict__ hist,
+                                                uint32_t* __restrict__ bad_accum) {
   extern __shared__ uint32_t lds_hist[];
   for (int k = threadIdx.x; k < n_rows; k += 256) lds_hist[k] = 0u;
   __syncthreads();
   const int64_t b = blockIdx.x;
   const int64_t p0 = b * kBlockPos;
   const int64_t p1 = p0 + kBlockPos < n_src ? p0 + kBlockPos : n_src;
+  const uint64_t lt = __lanemask_lt();
   uint32_t bad = 0;
-  for (int64_t p = p0 + threadIdx.x; p < p1; p += 256) {
-    const int32_t id = ids[p];
-    if (id >= 0 && id < n_rows)
-      atomicAdd(&lds_hist[id], 1u);
-    else if (id != -1)
-      ++bad;
+  constexpr int kPer = kBlockPos / 256;
+  int32_t idv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t p = p0 + threadIdx.x + u * 256;
+    idv[u] = p < p1 ? ids[p] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int32_t id = idv[u];
+    const bool valid = id >= 0 && id < n_rows;
+    if (!valid && id != -1) ++bad;
+    const uint64_t peers = match_peers(id, valid, id_bits);
+    if (valid && (peers & lt) == 0) atomicAdd(&lds_hist[id], static_cast<uint32_t>(__popcll(peers)));
   }
   __syncthreads();
   uint32_t* row = hist + b * n_rows;
@@ -79,23 +106,40 @@ __global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids,
   if (bad) atomicAdd(bad_accum, bad);
 }
 
-// ---- 2. per-id prefix over blocks
-__global__ __launch_bounds__(256) void ia_prefix(uint32_t* __restrict__ hist, int64_t nblk, int n_rows,
-                                                 uint32_t* __restrict__ count) {
+// ---- 2a. per id and segment of kSegBlocks blocks: exclusive prefix over the
+// segment's blocks (in place) and the segment total.
+__global__ __launch_bounds__(256) void ia_prefix_seg(uint32_t* __restrict__ hist, int64_t nblk, int n_rows,
+                                                     uint32_t* __restrict__ segtot) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  const int64_t seg = blockIdx.y;
+  if (k >= n_rows) return;
+  const int64_t b0 = seg * kSegBlocks;
+  uint32_t c[kSegBlocks];
+#pragma unroll
+  for (int j = 0; j < kSegBlocks; ++j) c[j] = (b0 + j < nblk) ? hist[(b0 + j) * n_rows + k] : 0u;
+  uint32_t run = 0;
+#pragma unroll
+  for (int j = 0; j < kSegBlocks; ++j) {
+    if (b0 + j < nblk) hist[(b0 + j) * n_rows + k] = run;
+    run += c[j];
+  }
+  segtot[seg * n_rows + k] = run;
+}
+
+// ---- 2b. per id: exclusive prefix over segments (in place) and the total.
+__global__ __launch_bounds__(256) void ia_prefix_tot(uint32_t* __restrict__ segtot, int64_t nseg, int n_rows,
+                                                     uint32_t* __restrict__ count) {
   const int k = blockIdx.x * 256 + threadIdx.x;
   if (k >= n_rows) return;
-  constexpr int kU = 8;
   uint32_t run = 0;
-  for (int64_t b0 = 0; b0 < nblk; b0 += kU) {
-    uint32_t c[kU];
+  for (int64_t s0 = 0; s0 < nseg; s0 += 16) {
+    uint32_t c[16];
 #pragma unroll
-    for (int j = 0; j < kU; ++j) c[j] = (b0 + j < nblk) ? hist[(b0 + j) * n_rows + k] : 0u;
+    for (int j = 0; j < 16; ++j) c[j] = (s0 + j < nseg) ? segtot[(s0 + j) * n_rows + k] : 0u;
 #pragma unroll
-    for (int j = 0; j < kU; ++j) {
-      if (b0 + j < nblk) {
-        hist[(b0 + j) * n_rows + k] = run;
-        run += c[j];
-      }
+    for (int j = 0; j < 16; ++j) {
+      if (s0 + j < nseg) segtot[(s0 + j) * n_rows + k] = run;
+      run += c[j];
     }
   }
   count[k] = run;
@@ -150,39 +194,67 @@ __global__ __launch_bounds__(1024) void ia_scan(const uint32_t* __restrict__ cou
   }
 }
 
-// ---- 4. stable scatter (one wave per block)
-__global__ __launch_bounds__(64) void ia_scatter(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                 int id_bits, const uint32_t* __restrict__ prefix,
-                                                 const uint32_t* __restrict__ seg_off, int32_t* __restrict__ perm) {
-  extern __shared__ uint32_t lds_cnt[];
-  const int lane = threadIdx.x;
-  for (int k = lane; k < n_rows; k += 64) lds_cnt[k] = 0u;
-  __syncthreads();
+// ---- 4. stable scatter. All 256 threads stage the block's ids and, for every
+// id, its first destination (segment offset + prefix of earlier segments +
+// prefix of earlier blocks of this segment) in LDS; then wave 0 alone walks
+// the block in order, 64 positions at a time, so the walk touches global
+// memory only to write perm. Within one wave the LDS read of an id's base
+// precedes its leader's update in program order, so no barrier is needed.
+__global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
+                                                  int id_bits, const uint32_t* __restrict__ prefix,
+                                                  const uint32_t* __restrict__ segbase,
+                                                  const uint32_t* __restrict__ seg_off, int32_t* __restrict__ perm) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* base = lds;                                     // [n_rows]
+  int32_t* lid = reinterpret_cast<int32_t*>(lds + n_rows);  // [kBlockPos]
+  const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
   const uint32_t* pre = prefix + b * n_rows;
+  const uint32_t* sb = segbase + (b / kSegBlocks) * n_rows;
+  for (int k0 = 0; k0 < n_rows; k0 += 256 * 8) {
+    uint32_t v0[8], v1[8], v2[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + tid + 256 * u;
+      v0[u] = k < n_rows ? seg_off[k] : 0u;
+      v1[u] = k < n_rows ? sb[k] : 0u;
+      v2[u] = k < n_rows ? pre[k] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + tid + 256 * u;
+      if (k < n_rows) base[k] = v0[u] + v1[u] + v2[u];
+    }
+  }
   const int64_t p0 = b * kBlockPos;
   const int64_t p1 = p0 + kBlockPos < n_src ? p0 + kBlockPos : n_src;
+  {
+    constexpr int kPer = kBlockPos / 256;
+    int32_t v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int64_t p = p0 + tid + 256 * u;
+      v[u] = p < p1 ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) lid[tid + 256 * u] = v[u];
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const int lane = tid;
   const uint64_t lt = __lanemask_lt();
-  for (int64_t base = p0; base < p1; base += 64) {
-    const int64_t p = base + lane;
-    const int32_t id = p < p1 ? ids[p] : -1;
+  for (int64_t off = 0; p0 + off < p1; off += 64) {
+    const int32_t id = lid[off + lane];
     const bool valid = id >= 0 && id < n_rows;
-    uint64_t peers = __ballot(valid);
-    for (int bit = 0; bit < id_bits; ++bit) {
-      const bool set = valid && ((id >> bit) & 1);
-      const uint64_t m = __ballot(set);
-      peers &= set ? m : ~m;
-    }
-    uint32_t old = 0;
+    const uint64_t peers = match_peers(id, valid, id_bits);
     if (valid) {
-      old = lds_cnt[id];
-      const uint32_t rank = __popcll(peers & lt);
-      const uint64_t dest = static_cast<uint64_t>(seg_off[id]) + pre[id] + old + rank;
-      if (dest < static_cast<uint64_t>(n_src)) perm[dest] = static_cast<int32_t>(p);
+      const uint32_t old = base[id];
+      const uint64_t dest = static_cast<uint64_t>(old) + static_cast<uint32_t>(__popcll(peers & lt));
+      if (dest < static_cast<uint64_t>(n_src)) perm[dest] = static_cast<int32_t>(p0 + off + lane);
+      __builtin_amdgcn_wave_barrier();
+      if ((peers & lt) == 0) base[id] = old + static_cast<uint32_t>(__popcll(peers));
     }
-    __syncthreads();  // every lane has read its id's count before any leader updates it
-    if (valid && (peers & lt) == 0) lds_cnt[id] = old + static_cast<uint32_t>(__popcll(peers));
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -212,7 +284,12 @@ __device__ __forceinline__ void store_add8(float* dst, const float (&acc)[8]) {
   *reinterpret_cast<float4*>(dst + 4) = b;
 }
 
-// ---- 5. chunk gather-sum. GS lanes per chunk, 8 dims per lane.
+// ---- 5. chunk gather-sum. GS lanes per chunk, 8 dims per lane. The chunk's
+// source positions (at most 16 per lane, GS * 16 rows) are loaded once,
+// handed out by lane shuffles; the rows are then read up to 16 at a time (all
+// their loads in flight) and folded in order.
+constexpr int kPosPerLane = 16;  // chunk capacity of ia_gather: GS * 16 rows (longer chunks: ia_gather_long)
+
 template <int GS>
 __global__ __launch_bounds__(256) void ia_gather(const uint16_t* __restrict__ src, int64_t src_ld, int dim,
                                                  const int32_t* __restrict__ perm,
@@ -220,6 +297,153 @@ __global__ __launch_bounds__(256) void ia_gather(const uint16_t* __restrict__ sr
                                                  const uint32_t* __restrict__ chunk_off, int n_rows, int L,
                                                  float* __restrict__ out, int64_t out_ld,
                                                  float* __restrict__ scratch, int64_t n_src, int64_t max_chunks) {
+  const int g = threadIdx.x / GS;
+  const int lg = threadIdx.x % GS;
+  const uint32_t c = static_cast<uint32_t>(blockIdx.x) * (256 / GS) + g;
+  const uint32_t n_chunks = chunk_off[n_rows];
+  const bool live = c < n_chunks && c < max_chunks;
+  int k = 0;
+  uint32_t r0 = 0, len = 0;
+  if (live) {
+    k = chunk_owner(chunk_off, n_rows, c);
+    const uint32_t j = c - chunk_off[k];
+    r0 = seg_off[k] + j * static_cast<uint32_t>(L);
+    const uint32_t r_end = seg_off[k + 1] < static_cast<uint64_t>(n_src) ? seg_off[k + 1] : static_cast<uint32_t>(n_src);
+    len = r0 + static_cast<uint32_t>(L) < r_end ? static_cast<uint32_t>(L) : (r_end > r0 ? r_end - r0 : 0u);
+  }
+  const bool active = live && 8 * lg < dim;
+  const int d0 = 8 * lg;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = -0.0f;
+  // positions: lane lg of the group holds rows lg, lg + GS, lg + 2 GS, ...
+  int32_t pos[kPosPerLane];
+#pragma unroll
+  for (int i = 0; i < kPosPerLane; ++i) {
+    const uint32_t t = lg + GS * i;
+    pos[i] = (live && t < len) ? perm[r0 + t] : 0;
+  }
+  constexpr int kBatch = GS < 16 ? GS : 16;  // rows whose loads are in flight together
+#pragma unroll
+  for (int i = 0; i < kPosPerLane; ++i) {
+#pragma unroll
+    for (int h = 0; h < GS; h += kBatch) {
+      if (GS * i + h >= static_cast<int>(len)) continue;  // skipped when no lane of the wave needs it
+      // rows GS*i + h .. GS*i + h + kBatch - 1 of the chunk
+      uint4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t p = __shfl(pos[i], h + u, GS);
+        const bool ok = active && GS * i + h + u < static_cast<int>(len) && p >= 0 && p < n_src;
+        v[u] = ok ? *reinterpret_cast<const uint4*>(src + p * src_ld + d0) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (active && GS * i + h + u < static_cast<int>(len)) add8_bf16(acc, v[u]);
+    }
+  }
+  if (!active) return;
+  const uint32_t nk = chunk_off[k + 1] - chunk_off[k];
+  if (nk == 1) {
+    store_add8(out + static_cast<int64_t>(k) * out_ld + d0, acc);
+  } else {
+    float* sp = scratch + static_cast<int64_t>(c) * dim + d0;
+    *reinterpret_cast<float4*>(sp) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(sp + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+// One wave per chunk (dim = 64 * DPL, DPL in {2, 4, 8}): every lane owns DPL
+// consecutive dims, so a row is one coalesced 64-lane load and a wave's time is
+// its own chunk's length (several chunks of different lengths in one wave would
+// leave lanes idle until the longest finishes). Up to 64 * 16 rows per chunk.
+template <int DPL>
+struct RowVec;
+template <>
+struct RowVec<2> { typedef uint32_t T; };
+template <>
+struct RowVec<4> { typedef uint2 T; };
+template <>
+struct RowVec<8> { typedef uint4 T; };
+
+__device__ __forceinline__ void add_bf16(float (&acc)[2], uint32_t v) {
+  acc[0] = acc[0] + bf16_lo(v); acc[1] = acc[1] + bf16_hi(v);
+}
+__device__ __forceinline__ void add_bf16(float (&acc)[4], uint2 v) {
+  acc[0] = acc[0] + bf16_lo(v.x); acc[1] = acc[1] + bf16_hi(v.x);
+  acc[2] = acc[2] + bf16_lo(v.y); acc[3] = acc[3] + bf16_hi(v.y);
+}
+__device__ __forceinline__ void add_bf16(float (&acc)[8], uint4 v) { add8_bf16(acc, v); }
+__device__ __forceinline__ uint32_t zero_vec(uint32_t) { return 0u; }
+__device__ __forceinline__ uint2 zero_vec(uint2) { return make_uint2(0u, 0u); }
+__device__ __forceinline__ uint4 zero_vec(uint4) { return make_uint4(0u, 0u, 0u, 0u); }
+
+template <int DPL>
+__global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict__ src, int64_t src_ld, int dim,
+                                                      const int32_t* __restrict__ perm,
+                                                      const uint32_t* __restrict__ seg_off,
+                                                      const uint32_t* __restrict__ chunk_off, int n_rows, int L,
+                                                      float* __restrict__ out, int64_t out_ld,
+                                                      float* __restrict__ scratch, int64_t n_src,
+                                                      int64_t max_chunks) {
+  typedef typename RowVec<DPL>::T V;
+  const int lane = threadIdx.x & 63;
+  const uint32_t c = static_cast<uint32_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const uint32_t n_chunks = chunk_off[n_rows];
+  if (c >= n_chunks || c >= max_chunks) return;  // wave-uniform
+  const int k = chunk_owner(chunk_off, n_rows, c);
+  const uint32_t j = c - chunk_off[k];
+  const uint32_t r0 = seg_off[k] + j * static_cast<uint32_t>(L);
+  uint32_t r_end = seg_off[k + 1];
+  if (r_end > static_cast<uint64_t>(n_src)) r_end = static_cast<uint32_t>(n_src);
+  const int len = static_cast<int>(r0 + static_cast<uint32_t>(L) < r_end ? static_cast<uint32_t>(L)
+                                                                          : (r_end > r0 ? r_end - r0 : 0u));
+  const int d0 = DPL * lane;
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = -0.0f;
+  int32_t pos[kPosPerLane];
+#pragma unroll
+  for (int i = 0; i < kPosPerLane; ++i) {
+    const bool ok = 64 * i + lane < len;
+    const int32_t x = perm[ok ? r0 + 64 * i + lane : r0];
+    pos[i] = ok ? x : 0;
+  }
+  // rows whose loads are in flight together: 64 / 32 / 16 for 4 / 8 / 16-byte rows
+  constexpr int kB = 128 / DPL;
+#pragma unroll
+  for (int i = 0; i < kPosPerLane; ++i) {
+#pragma unroll
+    for (int h = 0; h < 64; h += kB) {
+      if (64 * i + h >= len) continue;  // wave-uniform skip
+      V v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        int64_t p = __shfl(pos[i], h + u, 64);
+        p = (p >= 0 && p < n_src) ? p : 0;  // always a valid row; masked below
+        v[u] = *reinterpret_cast<const V*>(src + p * src_ld + d0);
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (64 * i + h + u < len) add_bf16(acc, v[u]);
+    }
+  }
+  const uint32_t nk = chunk_off[k + 1] - chunk_off[k];
+  float* dst = nk == 1 ? out + static_cast<int64_t>(k) * out_ld + d0 : scratch + static_cast<int64_t>(c) * dim + d0;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) dst[i] = (nk == 1 ? dst[i] + acc[i] : acc[i]);
+}
+
+// Chunks longer than GS * 16 rows (a large chunk_rows setting): one lane group
+// walks the rows with the permutation read as it goes.
+template <int GS>
+__global__ __launch_bounds__(256) void ia_gather_long(const uint16_t* __restrict__ src, int64_t src_ld, int dim,
+                                                      const int32_t* __restrict__ perm,
+                                                      const uint32_t* __restrict__ seg_off,
+                                                      const uint32_t* __restrict__ chunk_off, int n_rows, int L,
+                                                      float* __restrict__ out, int64_t out_ld,
+                                                      float* __restrict__ scratch, int64_t n_src,
+                                                      int64_t max_chunks) {
   const int g = threadIdx.x / GS;
   const int lg = threadIdx.x % GS;
   const uint32_t c = static_cast<uint32_t>(blockIdx.x) * (256 / GS) + g;
@@ -243,9 +467,7 @@ __global__ __launch_bounds__(256) void ia_gather(const uint16_t* __restrict__ sr
     for (int u = 0; u < kU; ++u) {
       if (active && r + u < r1) {
         const int64_t p = perm[r + u];
-        // perm holds a permutation of valid source rows; the check only keeps a
-        // corrupted workspace from turning into an out-of-bounds read
-        v[u] = (p >= 0 && p < n_src) ? *reinterpret_cast<const uint4*>(src + p * src_ld + d0) : make_uint4(0, 0, 0, 0);
+        v[u] = (p >= 0 && p < n_src) ? *reinterpret_cast<const uint4*>(src + p * src_ld + d0) : make_uint4(0u, 0u, 0u, 0u);
       }
     }
 #pragma unroll
@@ -257,47 +479,87 @@ __global__ __launch_bounds__(256) void ia_gather(const uint16_t* __restrict__ sr
   if (nk == 1) {
     store_add8(out + static_cast<int64_t>(k) * out_ld + d0, acc);
   } else {
-    float* s = scratch + static_cast<int64_t>(c) * dim + d0;
-    *reinterpret_cast<float4*>(s) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *reinterpret_cast<float4*>(s + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    float* sp = scratch + static_cast<int64_t>(c) * dim + d0;
+    *reinterpret_cast<float4*>(sp) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(sp + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
-// ---- 6. fold of multi-chunk ids
-template <int GS>
+// ---- 6. fold of multi-chunk ids: one workgroup per id. A round is a block
+// of R = floor(1024 / (dim/4)) chunk partials (at most 16 KiB); every thread
+// loads up to 4 float4 of a round, kAhead rounds are in flight in registers, each round is staged in
+// LDS, and one thread per group of 4 dims folds it left to right.
+constexpr int kAhead = 4;
+constexpr int kRoundF4 = 1024;  // float4 per round
+
 __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chunk_off, int n_rows, int dim,
                                                const float* __restrict__ scratch, float* __restrict__ out,
                                                int64_t out_ld) {
-  const int g = threadIdx.x / GS;
-  const int lg = threadIdx.x % GS;
-  const int k = blockIdx.x * (256 / GS) + g;
+  const int k = blockIdx.x;
   if (k >= n_rows) return;
   const uint32_t c0 = chunk_off[k], c1 = chunk_off[k + 1];
-  if (c1 - c0 < 2 || 8 * lg >= dim) return;
-  const int d0 = 8 * lg;
-  float acc[8];
+  if (c1 - c0 < 2) return;
+  __shared__ float4 stage[kRoundF4];
+  const int quads = dim / 4;
+  const int R = kRoundF4 / quads;  // chunks per round
+  const int tid = threadIdx.x;
+  const uint32_t n = c1 - c0;
+  const uint32_t rounds = (n + R - 1) / R;
+  const float4* base = reinterpret_cast<const float4*>(scratch + static_cast<int64_t>(c0) * dim);
+  float4 acc = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
+  // four named register buffers (rounds r, r+1, r+2, r+3 in flight)
+  float4 b0[4], b1[4], b2[4], b3[4];
+  const uint32_t round_f4 = static_cast<uint32_t>(R * quads);  // <= kRoundF4
+  const uint32_t total_f4 = n * static_cast<uint32_t>(quads);
+  // unconditional loads from a clamped (always valid) index, then a select:
+  // no branches, so the loads of several rounds stay in flight together
+  auto load = [&](uint32_t rd, float4 (&v)[4]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = -0.0f;
-  constexpr int kU = 8;
-  for (uint32_t c = c0; c < c1; c += kU) {
-    float4 a[kU], b[kU];
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t j = tid + 256 * s;      // float4 index inside the round
+      const uint32_t e = rd * round_f4 + j;  // float4 index from c0
+      const bool ok = rd < rounds && j < round_f4 && e < total_f4;
+      const float4 x = base[ok ? e : 0u];
+      v[s] = ok ? x : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  };
+  auto consume = [&](uint32_t rd, float4 (&v)[4]) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (c + u < c1) {
-        const float* s = scratch + static_cast<int64_t>(c + u) * dim + d0;
-        a[u] = *reinterpret_cast<const float4*>(s);
-        b[u] = *reinterpret_cast<const float4*>(s + 4);
+    for (int s = 0; s < 4; ++s) stage[tid + 256 * s] = v[s];
+    __syncthreads();
+    load(rd + kAhead, v);
+    if (tid < quads) {
+      const uint32_t m = n - rd * R < static_cast<uint32_t>(R) ? n - rd * R : static_cast<uint32_t>(R);
+      uint32_t i = 0;
+      for (; i + 8 <= m; i += 8) {  // 8 LDS reads in flight ahead of the dependent adds
+        float4 q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = stage[(i + u) * quads + tid];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          acc.x = acc.x + q[u].x; acc.y = acc.y + q[u].y; acc.z = acc.z + q[u].z; acc.w = acc.w + q[u].w;
+        }
+      }
+      for (; i < m; ++i) {
+        const float4 q = stage[i * quads + tid];
+        acc.x = acc.x + q.x; acc.y = acc.y + q.y; acc.z = acc.z + q.z; acc.w = acc.w + q.w;
       }
     }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (c + u < c1) {
-        acc[0] = acc[0] + a[u].x; acc[1] = acc[1] + a[u].y; acc[2] = acc[2] + a[u].z; acc[3] = acc[3] + a[u].w;
-        acc[4] = acc[4] + b[u].x; acc[5] = acc[5] + b[u].y; acc[6] = acc[6] + b[u].z; acc[7] = acc[7] + b[u].w;
-      }
-    }
+    __syncthreads();
+  };
+  load(0, b0); load(1, b1); load(2, b2); load(3, b3);
+  for (uint32_t rd = 0; rd < rounds; rd += kAhead) {
+    consume(rd, b0);
+    if (rd + 1 < rounds) consume(rd + 1, b1);
+    if (rd + 2 < rounds) consume(rd + 2, b2);
+    if (rd + 3 < rounds) consume(rd + 3, b3);
   }
-  store_add8(out + static_cast<int64_t>(k) * out_ld + d0, acc);
+  if (tid < quads) {
+    float* d = out + static_cast<int64_t>(k) * out_ld + 4 * tid;
+    float4 o = *reinterpret_cast<const float4*>(d);
+    o.x = o.x + acc.x; o.y = o.y + acc.y; o.z = o.z + acc.z; o.w = o.w + acc.w;
+    *reinterpret_cast<float4*>(d) = o;
+  }
 }
 
 // ---- atomic arm: per-element float atomics, no sort
@@ -407,22 +669,48 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   auto* scratch = reinterpret_cast<float*>(w + l.scratch);
   int id_bits = 0;
   while ((1LL << id_bits) < n_rows) ++id_bits;
-  const size_t lds = static_cast<size_t>(n_rows) * 4;
-  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds, st, ids, n_src, nr, hist, hdr);
-  hipLaunchKernelGGL(ia_prefix, dim3(ceil_div(n_rows, 256)), dim3(256), 0, st, hist, l.nblk, nr, count);
-  hipLaunchKernelGGL(ia_scan, dim3(1), dim3(1024), 0, st, count, nr, L, seg_off, chunk_off, hdr);
-  hipLaunchKernelGGL(ia_scatter, dim3(l.nblk), dim3(64), lds, st, ids, n_src, nr, id_bits, hist, seg_off, perm);
-  const int64_t grid_g = ceil_div(l.max_chunks, 256 / gs);
-  const int64_t grid_f = ceil_div(n_rows, 256 / gs);
-#define DET_IA_TAIL(G)                                                                                         \
-  if (gs == G) {                                                                                               \
-    hipLaunchKernelGGL(ia_gather<G>, dim3(grid_g), dim3(256), 0, st, s16, src_ld, (int)dim, perm, seg_off,   \
-                       chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);                                                \
-    hipLaunchKernelGGL(ia_fold<G>, dim3(grid_f), dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out,    \
-                       out_ld);                                                                                \
+  const size_t lds_count = static_cast<size_t>(n_rows) * 4;
+  const size_t lds_scatter = lds_count + kBlockPos * 4;
+  if (lds_scatter > 64 * 1024) {
+    static bool raised = false;  // allow up to the 160 KiB of a gfx950 workgroup once per process
+    if (!raised) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(ia_scatter),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      raised = true;
+    }
   }
-  DET_IA_TAIL(1) DET_IA_TAIL(2) DET_IA_TAIL(4) DET_IA_TAIL(8) DET_IA_TAIL(16) DET_IA_TAIL(32) DET_IA_TAIL(64)
+  auto* segtot = reinterpret_cast<uint32_t*>(w + l.segtot);
+  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, id_bits, hist, hdr);
+  hipLaunchKernelGGL(ia_prefix_seg, dim3(ceil_div(n_rows, 256), l.nseg), dim3(256), 0, st, hist, l.nblk, nr, segtot);
+  hipLaunchKernelGGL(ia_prefix_tot, dim3(ceil_div(n_rows, 256)), dim3(256), 0, st, segtot, l.nseg, nr, count);
+  hipLaunchKernelGGL(ia_scan, dim3(1), dim3(1024), 0, st, count, nr, L, seg_off, chunk_off, hdr);
+  hipLaunchKernelGGL(ia_scatter, dim3(l.nblk), dim3(256), lds_scatter, st, ids, n_src, nr, id_bits, hist, segtot,
+                     seg_off, perm);
+  const int64_t grid_g = ceil_div(l.max_chunks, 256 / gs);
+#define DET_IA_TAIL(G)                                                                                           \
+  if (gs == G) {                                                                                                 \
+    if (L <= G * kPosPerLane)                                                                                    \
+      hipLaunchKernelGGL(ia_gather<G>, dim3(grid_g), dim3(256), 0, st, s16, src_ld, (int)dim, perm, seg_off,   \
+                         chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);                           \
+    else                                                                                                         \
+      hipLaunchKernelGGL(ia_gather_long<G>, dim3(grid_g), dim3(256), 0, st, s16, src_ld, (int)dim, perm,       \
+                         seg_off, chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);                  \
+  }
+  const int dpl = (dim % 64 == 0) ? static_cast<int>(dim / 64) : 0;
+  if ((dpl == 2 || dpl == 4 || dpl == 8) && L <= 64 * kPosPerLane) {
+    const int64_t grid_w = ceil_div(l.max_chunks, 4);
+#define DET_IA_WAVE(D)                                                                                          \
+  if (dpl == D)                                                                                                 \
+    hipLaunchKernelGGL(ia_gather_wave<D>, dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim, perm, seg_off, \
+                       chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);
+    DET_IA_WAVE(2) DET_IA_WAVE(4) DET_IA_WAVE(8)
+#undef DET_IA_WAVE
+  } else {
+    DET_IA_TAIL(1) DET_IA_TAIL(2) DET_IA_TAIL(4) DET_IA_TAIL(8) DET_IA_TAIL(16) DET_IA_TAIL(32) DET_IA_TAIL(64)
+  }
 #undef DET_IA_TAIL
+  hipLaunchKernelGGL(ia_fold, dim3(static_cast<uint32_t>(n_rows)), dim3(256), 0, st, chunk_off, nr, (int)dim, scratch,
+                     out, out_ld);
   return check_launch("det_index_add");
 }
 

@@ -113,49 +113,78 @@ __device__ __forceinline__ bf16x8_t frag(const uint2 (&v)[8]) {
   return __builtin_bit_cast(bf16x8_t, d);
 }
 
-// One K step of kBK token rows, staged in LDS as row-major [k][m] and [k][n]
-// slabs (the layout of G and X in memory). Each thread moves 16-byte chunks:
-// 2 of G (128 columns) and 8 of X (512 columns) per step. The loads are raw
-// buffer loads over the split's rows: a 32-bit per-thread offset, a scalar
-// per-chunk offset, and a record limit at the split end, so rows past it read
-// as zero without any branch.
-constexpr int kChunksA = kBM * kBK / 8 / kThreads;
-constexpr int kChunksB = kBN * kBK / 8 / kThreads;
+// One K step of kBK token rows lands in LDS as row-major [k][m] and [k][n]
+// slabs (the layout of G and X in memory) through direct buffer-to-LDS loads:
+// each instruction moves 64 lanes x 16 bytes into 1 KiB of LDS in lane order,
+// so no registers hold the data in flight. The buffer resources cover the
+// split's rows only; rows past the split end read as zero. G: 8 instructions
+// per step (4 rows of 256 B each), X: 32 (one 1 KiB row each), 10 per wave.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9-family raw buffer descriptor
+constexpr int kDmaA = kBK * kBM * 2 / 1024;     // 1 KiB transfers of G per step
+constexpr int kDmaB = kBK * kBN * 2 / 1024;     // 1 KiB transfers of X per step
+constexpr int kDmaPerWave = (kDmaA + kDmaB) / (kThreads / 64);
 
-struct Stage {
-  u32x4_t a[kChunksA];
-  u32x4_t b[kChunksB];
-};
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
-struct Src {
-  __amdgpu_buffer_rsrc_t ra, rb;  // G and X rows [r0, r1), rebased at r0
-  int32_t voff_a, voff_b;         // this thread's byte offset inside a step
-  int32_t step_a, step_b;         // bytes per kBK / kChunks rows (chunk stride)
-  int32_t krow_a, krow_b;         // bytes per token row
-};
-
-__device__ __forceinline__ void stage_load(const Src& src, int32_t krel, Stage& s) {
-#pragma unroll
-  for (int u = 0; u < kChunksA; ++u)
-    s.a[u] = __builtin_amdgcn_raw_buffer_load_b128(src.ra, src.voff_a, krel * src.krow_a + u * src.step_a, 0);
-#pragma unroll
-  for (int u = 0; u < kChunksB; ++u)
-    s.b[u] = __builtin_amdgcn_raw_buffer_load_b128(src.rb, src.voff_b, krel * src.krow_b + u * src.step_b, 0);
+// Raw buffer descriptor: base address, stride 0, num_records bytes.
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = static_cast<int32_t>(a & 0xFFFFFFFFu);
+  r[1] = static_cast<int32_t>((a >> 32) & 0xFFFFu);
+  r[2] = static_cast<int32_t>(num_records);
+  r[3] = static_cast<int32_t>(kRsrcWord3);
+  return r;
 }
 
-__device__ __forceinline__ void stage_store(uint16_t (*la)[kBM], uint16_t (*lb)[kBN], const Stage& s) {
-  const int t = threadIdx.x;
+// LDS byte address of a __shared__ object (wave-uniform here).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const char* lds_ptr_t;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));  // generic -> LDS address space
+}
+
+// One 1 KiB transfer: every lane's 16 bytes at rsrc + voff + soff land at
+// LDS[m0 + 16 * lane]. Issued as inline assembly (as the composable-kernel
+// library does for its asynchronous copies) so that the compiler does not
+// insert conservative waits on these loads before unrelated LDS reads; the
+// kernel waits for them explicitly with s_waitcnt vmcnt.
+__device__ __forceinline__ void dma16(uint32_t lds, i32x4_t rsrc, int32_t voff, int32_t soff) {
+  asm volatile("s_mov_b32 m0, %0" : : "s"(lds) : "memory");
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+struct Src {
+  i32x4_t ra, rb;           // G and X rows [r0, r1), rebased at r0
+  int32_t voff_a, voff_b;   // this lane's byte offset inside one transfer
+  int32_t krow_a, krow_b;   // bytes per token row
+};
+
+// Issue this wave's share of the transfers of the step starting at split row krel.
+__device__ __forceinline__ void stage_issue(const Src& src, int32_t krel, uint16_t (*la)[kBM], uint16_t (*lb)[kBN],
+                                            int wave) {
 #pragma unroll
-  for (int u = 0; u < kChunksA; ++u) {
-    const int c = t + u * kThreads;
-    *reinterpret_cast<u32x4_t*>(&la[c / (kBM / 8)][(c % (kBM / 8)) * 8]) = s.a[u];
+  for (int u = 0; u < kDmaA / 4; ++u) {
+    const int i = wave * (kDmaA / 4) + u;  // transfer i covers rows 4i .. 4i+3
+    dma16(lds_addr(&la[4 * i][0]), src.ra, src.voff_a, (krel + 4 * i) * src.krow_a);
   }
 #pragma unroll
-  for (int u = 0; u < kChunksB; ++u) {
-    const int c = t + u * kThreads;
-    *reinterpret_cast<u32x4_t*>(&lb[c / (kBN / 8)][(c % (kBN / 8)) * 8]) = s.b[u];
+  for (int u = 0; u < kDmaB / 4; ++u) {
+    const int i = wave * (kDmaB / 4) + u;  // transfer i covers row i
+    dma16(lds_addr(&lb[i][0]), src.rb, src.voff_b, (krel + i) * src.krow_b);
   }
+}
+
+// Wait until this wave's transfers of the oldest in-flight step have landed
+// (the younger step's kDmaPerWave may still be pending), then meet the other
+// waves so that every wave's transfers of that step are visible.
+template <bool YOUNGER_PENDING>
+__device__ __forceinline__ void stage_wait() {
+  static_assert(kDmaPerWave == 10, "vmcnt literal below");
+  if (YOUNGER_PENDING)
+    asm volatile("s_waitcnt vmcnt(10)" : : : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  __builtin_amdgcn_s_barrier();
 }
 
 // One 16-row MFMA block from LDS rows [row0, row0 + 16): lane (r, kg) reads
@@ -177,25 +206,75 @@ __device__ __forceinline__ void mma_block(const uint16_t (*la)[kBM], const uint1
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
+// XCD-aware placement. Workgroups are dispatched to the 8 XCDs round-robin
+// (workgroup u runs on XCD u % 8), and each XCD has its own L2. XCD x takes,
+// for every split, the tiles of n-tile column x % tiles_n and of its share of
+// the m-tiles; consecutive workgroups on one XCD are tiles of the same split
+// and column, so their X rows come from that XCD's L2 after the first read.
+// Every XCD gets a share of every expert, which keeps the XCDs balanced.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bool unit_of(const WgradArgs& p, uint32_t u, int64_t& g, int& mt, int& nt) {
+  const int x = static_cast<int>(u % kXcds);
+  const int64_t slot = u / kXcds;
+  const int NT = p.tiles_n, MT = p.tiles_m;
+  if (kXcds % NT == 0) {
+    const int parts = kXcds / NT;           // m-tile parts per column
+    const int part = x / NT;
+    const int mlo = part * MT / parts, mhi = (part + 1) * MT / parts;
+    const int per = mhi - mlo;
+    if (per == 0) return false;
+    g = slot / per;
+    if (g >= p.max_splits) return false;
+    mt = mlo + static_cast<int>(slot % per);
+    nt = x % NT;
+    return true;
+  }
+  // any other column count: plain split-major order
+  const int64_t t = static_cast<int64_t>(u) % (static_cast<int64_t>(MT) * NT);
+  g = static_cast<int64_t>(u) / (static_cast<int64_t>(MT) * NT);
+  if (g >= p.max_splits) return false;
+  mt = static_cast<int>(t / NT);
+  nt = static_cast<int>(t % NT);
+  return true;
+}
+
+__host__ int64_t wgrad_grid(int tiles_m, int tiles_n, int64_t max_splits) {
+  if (kXcds % tiles_n == 0) {
+    const int parts = kXcds / tiles_n;
+    int per_max = 0;
+    for (int part = 0; part < parts; ++part) {
+      const int per = (part + 1) * tiles_m / parts - part * tiles_m / parts;
+      per_max = per > per_max ? per : per_max;
+    }
+    return static_cast<int64_t>(kXcds) * per_max * max_splits;
+  }
+  return static_cast<int64_t>(tiles_m) * tiles_n * max_splits;
+}
+
 // One workgroup = 4 waves = a 128 (m) x 512 (n) output tile; wave w owns the
 // 128 x 128 columns n0 + 128w. K runs in steps of kBK rows through two LDS
 // buffers: while the matrix cores work on one, the next step's global loads
 // are in flight in registers and then written to the other.
 template <bool ATOMIC>
 __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][kBK][kBM];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][kBK][kBN];
-  const int64_t u = blockIdx.x;
-  if (u >= p.n_units) return;
-  const int n_tiles = p.tiles_m * p.tiles_n;
-  const int64_t g = u / n_tiles;
-  const int t = static_cast<int>(u % n_tiles);
+  __shared__ __attribute__((aligned(16))) uint16_t la0[kBK][kBM];
+  __shared__ __attribute__((aligned(16))) uint16_t la1[kBK][kBM];
+  __shared__ __attribute__((aligned(16))) uint16_t la2[kBK][kBM];
+  __shared__ __attribute__((aligned(16))) uint16_t lb0[kBK][kBN];
+  __shared__ __attribute__((aligned(16))) uint16_t lb1[kBK][kBN];
+  __shared__ __attribute__((aligned(16))) uint16_t lb2[kBK][kBN];
+  int64_t g;
+  int mt, nt;
+  if (!unit_of(p, blockIdx.x, g, mt, nt)) return;
   Split sp;
   if (!find_split(p, g, sp)) return;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform by construction; readfirstlane lets the compiler keep it (and
+  // every LDS transfer base derived from it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int m0 = (t / p.tiles_n) * kBM;
-  const int n0 = (t % p.tiles_n) * kBN;
+  const int m0 = mt * kBM;
+  const int n0 = nt * kBN;
   const int r = lane & 31;
   const int kg = lane >> 5;
 
@@ -210,43 +289,34 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs p) {
   const int64_t r0 = sp.r0, r1 = sp.r1;
   const int32_t rows = static_cast<int32_t>(r1 - r0);
   Src src;
-  src.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.G + r0 * p.ldg), 0,
-                                             static_cast<int32_t>(rows * p.ldg * 2), kRsrcWord3);
-  src.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.X + r0 * p.ldx), 0,
-                                             static_cast<int32_t>(rows * p.ldx * 2), kRsrcWord3);
-  {
-    const int t = threadIdx.x;
-    src.krow_a = static_cast<int32_t>(p.ldg * 2);
-    src.krow_b = static_cast<int32_t>(p.ldx * 2);
-    src.voff_a = (t / (kBM / 8)) * src.krow_a + (m0 + (t % (kBM / 8)) * 8) * 2;
-    src.voff_b = (t / (kBN / 8)) * src.krow_b + (n0 + (t % (kBN / 8)) * 8) * 2;
-    src.step_a = (kThreads / (kBM / 8)) * src.krow_a;
-    src.step_b = (kThreads / (kBN / 8)) * src.krow_b;
+  src.ra = make_rsrc(p.G + r0 * p.ldg, static_cast<uint32_t>(rows * p.ldg * 2));
+  src.rb = make_rsrc(p.X + r0 * p.ldx, static_cast<uint32_t>(rows * p.ldx * 2));
+  src.krow_a = static_cast<int32_t>(p.ldg * 2);
+  src.krow_b = static_cast<int32_t>(p.ldx * 2);
+  src.voff_a = (lane / (kBM / 8)) * src.krow_a + (m0 + (lane % (kBM / 8)) * 8) * 2;
+  src.voff_b = (n0 + lane * 8) * 2;
+
+  // Three LDS buffers: while the matrix cores work on step s, the transfers of
+  // steps s+1 and s+2 are in flight. The loop is unrolled over the buffers so
+  // that each buffer is its own LDS object (exact wait counts) and every LDS
+  // address is a per-lane base plus a constant.
+  stage_issue(src, 0, la0, lb0, wave);
+  if (kBK < rows) stage_issue(src, kBK, la1, lb1, wave);
+#define DET_WGRAD_STEP(LA, LB, LA_NEXT2, LB_NEXT2, OFF)                              \
+  {                                                                                 \
+    const int32_t k = k0 + (OFF);                                                   \
+    if (k >= rows) break;                                                           \
+    if (k + kBK < rows) stage_wait<true>(); else stage_wait<false>();               \
+    if (k + 2 * kBK < rows) stage_issue(src, k + 2 * kBK, LA_NEXT2, LB_NEXT2, wave); \
+    mma_block(LA, LB, 0, r, kg, wave, acc);                                         \
+    if (k + 16 < rows) mma_block(LA, LB, 16, r, kg, wave, acc);                     \
   }
-  Stage st;
-  stage_load(src, 0, st);
-  stage_store(lds_a[0], lds_b[0], st);
-  __syncthreads();
-  if (kBK < rows) stage_load(src, kBK, st);
-  // K loop, unrolled over the two LDS buffers so that every LDS address is a
-  // per-lane base plus a constant
-  for (int32_t k = 0; k < rows; k += 2 * kBK) {
-    mma_block(lds_a[0], lds_b[0], 0, r, kg, wave, acc);
-    if (k + 16 < rows) mma_block(lds_a[0], lds_b[0], 16, r, kg, wave, acc);
-    if (k + kBK < rows) {
-      stage_store(lds_a[1], lds_b[1], st);
-      if (k + 2 * kBK < rows) stage_load(src, k + 2 * kBK, st);
-    }
-    __syncthreads();
-    if (k + kBK >= rows) break;
-    mma_block(lds_a[1], lds_b[1], 0, r, kg, wave, acc);
-    if (k + kBK + 16 < rows) mma_block(lds_a[1], lds_b[1], 16, r, kg, wave, acc);
-    if (k + 2 * kBK < rows) {
-      stage_store(lds_a[0], lds_b[0], st);
-      if (k + 3 * kBK < rows) stage_load(src, k + 3 * kBK, st);
-    }
-    __syncthreads();
+  for (int32_t k0 = 0; k0 < rows; k0 += 3 * kBK) {
+    DET_WGRAD_STEP(la0, lb0, la2, lb2, 0)
+    DET_WGRAD_STEP(la1, lb1, la0, lb0, kBK)
+    DET_WGRAD_STEP(la2, lb2, la1, lb1, 2 * kBK)
   }
+#undef DET_WGRAD_STEP
 
   // Epilogue: lane (r, kg), MFMA (i, j), accumulator q holds output
   // m = m0 + 4 * (8*(q/4) + 4*kg + q%4) + i,  n = n0 + 128*wave + 4*r + j.
@@ -415,7 +485,7 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
   p.tiles_m = static_cast<int>(M / kTileM);
   p.tiles_n = static_cast<int>(N / kTileN);
   p.max_splits = max_splits(T_total, E, c);
-  p.n_units = static_cast<int64_t>(p.tiles_m) * p.tiles_n * p.max_splits;
+  p.n_units = wgrad_grid(p.tiles_m, p.tiles_n, p.max_splits);
   p.scratch = (atomic || sb == 0) ? nullptr : reinterpret_cast<float*>(static_cast<char*>(ws) + DET_WS_HEADER_BYTES);
   if (p.n_units > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "wgrad: too many work units");
   const hipStream_t st = as_stream(stream);
