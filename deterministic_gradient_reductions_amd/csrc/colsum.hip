@@ -8,8 +8,8 @@
 // registers; the remaining tree levels run over LDS. The resulting tile slot
 // (one per head and gradient) goes to the workspace. A second kernel on the
 // same stream folds the slots of every head in tile order and adds the totals
-// into dA_log / ddt_bias (the page's "caller reduces them on the existing
-// stream"); the kernel boundary orders the slot writes before the fold without
+// into dA_log / ddt_bias (the page has the caller reduce the partials on the
+// same stream the backward runs on); the kernel boundary orders the slot writes before the fold without
 // any device-wide fence inside a kernel.
 //
 // The atomic arm computes the same tile slots and adds them into the outputs

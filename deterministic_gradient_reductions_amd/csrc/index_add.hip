@@ -1,6 +1,6 @@
 // det_index_add: out[ids[p]] += src[p] without float atomics (sparse-indexer dK,
-// Megatron-LM PR #7441, source 3: "stable sort + prefix sum" in place of the
-// atomic accumulation).
+// Megatron-LM PR #7441, source 3: a stable sort of the ids and a prefix sum of
+// their counts replace the atomic accumulation).
 //
 // Pipeline (all on `stream`, integer-only until step 5):
 //  1. count    per block of 4096 source positions, an LDS histogram of the ids

@@ -12,7 +12,9 @@
 // with v_perm_b32. Fragment i (i = 0..3) then holds output rows m0 + 4r + i
 // for lane slot r: one MFMA computes a strided 32x32 sub-tile, and 4 x 4 MFMAs
 // cover the wave's 128 x 128 output tile. G and X reach LDS in their memory
-// layout through coalesced 16-byte loads, double-buffered by K step.
+// layout through 16-byte buffer loads that write LDS directly (no register
+// round trip), over three LDS stages of 32 token rows, so two stages of loads
+// are in flight while the matrix cores work on the third.
 //
 // Canonical order (the oracle's): an expert's rows are cut into splits of
 // k_tile * ktiles_per_split rows counted from the expert's first row (one split
@@ -460,11 +462,9 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
   const size_t sb = scratch_bytes(T_total, E, M, N, c);
   const size_t need = (atomic || sb == 0) ? 0 : DET_WS_HEADER_BYTES + align_up(sb, 256);
   if (int s = check_workspace(ws, ws_bytes, need)) return s;
-  const Range out = range2d(main_grad, static_cast<int64_t>(E) * M, N, ld_m, 4);
   Range out_full;
   out_full.lo = reinterpret_cast<uintptr_t>(main_grad);
   out_full.hi = out_full.lo + static_cast<uintptr_t>(((E - 1) * ld_e + (M - 1) * ld_m + N) * 4);
-  (void)out;
   if (overlaps(out_full, range2d(G, T_total, M, ldg, 2)) || overlaps(out_full, range2d(X, T_total, N, ldx, 2)) ||
       overlaps(out_full, range1d(offs, (static_cast<size_t>(E) + 1) * 4)) || overlaps(out_full, range1d(ws, ws_bytes)))
     return set_error(DET_ERR_OVERLAP, "wgrad: main_grad overlaps an input or the workspace");

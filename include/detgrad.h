@@ -17,9 +17,9 @@
  *   synchronises with the host and keeps no state between calls; the caller
  *   owns every buffer, the workspace included.
  * - Outputs ACCUMULATE: out <- RN32(out + total), one rounding per element
- *   (cudnn-frontend PR #521: the slot reduction "accumulates ... rather than
- *   overwriting"; FlashInfer PR #8924: bitwise AccumulateGrad of the
- *   deterministic dW). An empty problem leaves every output bit unchanged.
+ *   (cudnn-frontend PR #521: the slot reduction adds into the existing output
+ *   instead of replacing it; FlashInfer PR #8924: bitwise AccumulateGrad of
+ *   the deterministic dW). An empty problem leaves every output bit unchanged.
  * - `atomic` must be exactly 0 or 1, anything else is DET_ERR_INVALID_ARG
  *   (FlashInfer PR #8924, mode rules: only an explicit value selects a route).
  * - With atomic = 0 the output bits are a function of the inputs and the tile
@@ -32,13 +32,14 @@
  * Workspace
  * ---------
  * The deterministic routes need device scratch of det_*_workspace_size()
- * bytes, 256-byte aligned. Its first 256 bytes hold small self-resetting
- * counters: call det_workspace_init() once on a new workspace (it enqueues a
- * tiny fill kernel on `stream`); afterwards every call leaves the counters at
- * zero again, so the workspace never needs another fill. The slot area is
- * never read before it is written, so it needs no initial value. One
- * workspace must not be used by two calls that can run at the same time
- * (for example on two streams without an event between them).
+ * bytes (0 when a route keeps its partials on chip), 256-byte aligned. A
+ * non-empty workspace starts with a 256-byte header; det_index_add keeps its
+ * bad-id counter there, which every call leaves at zero again. Call
+ * det_workspace_init() once on a new workspace (it enqueues a tiny fill
+ * kernel on `stream`); it never needs another fill. The slot area behind the
+ * header is never read before it is written in the same call, so it needs no
+ * initial value. One workspace must not be used by two calls that can run at
+ * the same time (for example on two streams without an event between them).
  */
 #ifndef DETGRAD_H
 #define DETGRAD_H
@@ -146,9 +147,10 @@ int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* count, void*
 
 /* ------------------------------------------------------------------------
  * det_grouped_dprob: dprob of a grouped-GEMM dsReLU backward.
- * cudnn-frontend PR #521 (deterministic dprob): one slot per N tile so every
- * (token, tile_n) pair has exactly one writer, subtile partials parked by
- * actual subtile, slots reduced in a fixed order, accumulating into dprob.
+ * cudnn-frontend PR #521 (deterministic dprob): each N tile of a token gets
+ * its own slot with a single writer, each subtile's partial is stored by its
+ * subtile index, and the slots are folded in one fixed order and added into
+ * the existing dprob.
  *
  *   dprob[m] += sum_n dY[m,n] * relu(C[m,n])^2     for offs[0] <= m < offs[E]
  *
@@ -194,10 +196,17 @@ int det_grouped_dprob(float* dprob, const void* dY, int64_t ldy, const void* C, 
  *            ld_m >= N, ld_e >= M*ld_m (so an expanded tensor is rejected).
  * offs: [E+1] int32 device array, non-decreasing, offs[E] <= T_total.
  *       Values are read on the device only; out-of-range offsets are clamped.
- * M, N must be multiples of 16 and ldg, ldx multiples of 8, G and X 16-byte
- * aligned (DET_ERR_UNSUPPORTED otherwise).
- * cfg:  NULL selects {block_m = 256, block_n = 256, k_tile = 512,
- *       ktiles_per_split = 0}. */
+ * M must be a multiple of 128 and N of 512 (the workgroup tile); ldg, ldx,
+ * ld_m and ld_e keep every row 16-byte aligned, as do G, X and main_grad;
+ * T_total * max(M, N) * 2 < 2^31 (32-bit buffer offsets). Otherwise
+ * DET_ERR_UNSUPPORTED.
+ * cfg:  NULL selects {block_m = 128, block_n = 512, k_tile = 512,
+ *       ktiles_per_split = 0}; block_m x block_n must be 128 x 512 and k_tile
+ *       512; ktiles_per_split in [0, 2^20].
+ * ws:   ktiles_per_split = 0 keeps each expert's partial in registers and
+ *       needs no workspace (size 0); otherwise the 256-byte header plus one
+ *       [M, N] float32 slot per possible split, ceil(T_total / (512 C)) + E
+ *       slots. atomic = 1 needs none. */
 typedef struct {
   int32_t block_m;
   int32_t block_n;

@@ -27,7 +27,13 @@ fp64        the exact mathematical definitions in float64, used to pin the
 brute       scalar, loop-by-loop restatements for tiny inputs (pins only).
 
 Parity status: every function here is pinned by CPU tests against fp64 sums,
-closed forms, exact-integer inputs, order-revealing probes or brute force,
-except ``wgrad.mfma_chain_model``, whose matrix-core model is "parity
-unpinned" (the pages say nothing about matrix-core internals).
+closed forms, exact-integer inputs, order-revealing probes or brute force.
+One step is not: the rounding inside a matrix-core multiply-accumulate chain
+(the wgrad split partial). The pages say nothing about matrix-core internals,
+so ``wgrad.grouped_wgrad_acc`` takes the chain as a parameter; its default,
+``chain_exact_rounded``, is the exact product rounded once, which every order
+reproduces when all partial sums are exactly representable (small-integer
+inputs). For general inputs the GPU chain is "parity unpinned": it is checked
+against float64 to a rel-L2 bound, and the split structure, the fold and the
+main_grad add around it are checked bit for bit.
 """

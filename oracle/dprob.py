@@ -1,11 +1,12 @@
 """Grouped-GEMM dsReLU backward dprob with per-N-tile slots (test infrastructure only).
 
 cudnn-frontend PR #521 (deterministic dprob in the grouped-GEMM dsReLU
-backward), first commit: dprob is a float reduction over n that was
-non-deterministic at two levels; the fix parks each subtile's partial in a slot
-indexed by the actual subtile, gives dprob one slot per N tile so every
-(token, tile_n) pair has exactly one writer, and reduces the slots in a fixed
-order, accumulating into dprob rather than overwriting it.
+backward), first commit: dprob, a float sum over n, varied from run to run
+both inside a CTA (the order of its N subtiles) and across CTAs (atomics on the
+same token). The fix stores each subtile's partial in its own slot, addressed
+by which subtile it is, allots dprob one slot per N tile so that no slot has
+two writers, folds the slots in one fixed order and adds the result to the
+existing dprob.
 
     dprob[m] += sum_n dY[m, n] * srelu(C[m, n]),   srelu(c) = relu(c)^2
 

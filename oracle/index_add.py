@@ -2,8 +2,8 @@
 
 Megatron-LM PR #7441 (DSv4 deterministic mode), source 3: the indexer backward
 accumulated dK with atomics; the fix computes it without atomics through a
-deterministic index_add, with a "stable sort + prefix sum" fallback, and
-padding slots are dropped.
+deterministic index_add whose fallback sorts the ids stably and takes a prefix
+sum of the counts, and padding slots are dropped.
 
     out[id] += src[p]   for every source row p with ids[p] = id >= 0
 
@@ -18,8 +18,9 @@ Canonical order (the reading taken here):
 4. fold the chunk partials of an id left to right and add the total once
    into out[id]. Ids with no rows are untouched.
 
-With L at least the longest run this is exactly the literal sequential
-"out[id] += src in stable sorted order" when out starts at +0.
+With L at least the longest run this is exactly the literal sequential loop
+that adds the source rows of each id into out[id] one by one, in stable id
+order, when out starts at +0.
 """
 from __future__ import annotations
 

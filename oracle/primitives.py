@@ -3,21 +3,22 @@
 The pages fix the pattern but not the in-tile order: each program/CTA writes
 its own FP32 partial into a slot, and the slots are then reduced in a fixed
 order on the caller's stream (Megatron-LM PR #8244, description; cudnn-frontend
-PR #521, first commit: "each subtile's partial is parked in a slot ... the
-wrapper reduces those slots in fixed order"). The readings taken here:
+PR #521, first commit: one slot per subtile, folded by the wrapper in a fixed
+order). The readings taken here:
 
 * inside a tile: the adjacent pairwise tree. Level one adds elements (2i, 2i+1),
   the next level adds neighbouring results, and so on to a single value;
   positions past the end of the data are -0.0;
 * across slots: a strict left-to-right fold starting from -0.0;
 * into the output: one add of the finished total, out <- RN32(out + total),
-  i.e. accumulate rather than overwrite (cudnn-frontend PR #521: the reduction
-  "accumulates into it rather than overwriting"; FlashInfer PR #8924: the result
+  i.e. accumulate rather than overwrite (cudnn-frontend PR #521: the slot
+  reduction adds into the existing output; FlashInfer PR #8924: the result
   equals AccumulateGrad of the deterministic dW).
 
 -0.0 is the exact additive identity of binary32 (x + -0.0 == x for every x,
 including -0.0), so padding never changes a bit and an empty set leaves the
-output bitwise unchanged (FlashInfer PR #8602 tests "empty groups bitwise").
+output bitwise unchanged (FlashInfer PR #8602, commits: its tests require an
+empty group to leave the output bit-identical).
 """
 from __future__ import annotations
 
