@@ -120,18 +120,15 @@ def build_workloads():
     T_total = int(wg.offs[-1])
     G, X, woffs, mg = bf(wg.G), bf(wg.X), i32(wg.offs), f32(wg.main_grad0)
     mg0 = mg.clone()
-    try:
-        wws = dg.Workspace(dg.det_grouped_wgrad_acc_workspace_size(T_total, 8, 1408, 2048))
-        out.append(Workload(
-            "wgrad",
-            lambda: dg.det_grouped_wgrad_acc(mg, G, X, woffs, ws=wws),
-            lambda: dg.det_grouped_wgrad_acc(mg, G, X, woffs, atomic=True),
-            lambda: mg.copy_(mg0),
-            lambda: mg.cpu().numpy(),
-            nbytes=T_total * (1408 + 2048) * 2 + 8 * 1408 * 2048 * 4 * 2,
-            flops=2.0 * 1408 * 2048 * T_total, bound="mfma"))
-    except dg.DetError as e:
-        log("wgrad not available: %s" % e)
+    wws = dg.Workspace(dg.det_grouped_wgrad_acc_workspace_size(T_total, 8, 1408, 2048))
+    out.append(Workload(
+        "wgrad",
+        lambda: dg.det_grouped_wgrad_acc(mg, G, X, woffs, ws=wws),
+        lambda: dg.det_grouped_wgrad_acc(mg, G, X, woffs, atomic=True),
+        lambda: mg.copy_(mg0),
+        lambda: mg.cpu().numpy(),
+        nbytes=T_total * (1408 + 2048) * 2 + 8 * 1408 * 2048 * 4 * 2,
+        flops=2.0 * 1408 * 2048 * T_total, bound="mfma"))
     return out
 
 

@@ -3,18 +3,25 @@
 // #8924: deterministic accumulate, bitwise the AccumulateGrad of the
 // deterministic dW, with expert offsets read on the device).
 //
-// Contraction on the matrix cores. G_e [T_e x M] and X_e [T_e x N] both have
-// the token index as their row index, so the reduction runs down the rows of
-// both operands, while v_mfma_f32_32x32x16_bf16 wants each lane to hold 8
-// consecutive k values of one output row (A) or column (B). Each lane therefore
-// reads 8 token rows x 4 consecutive columns (8 bytes per row, 32 lanes cover
-// 128 contiguous columns) from LDS and transposes the 8x4 block in registers
-// with v_perm_b32. Fragment i (i = 0..3) then holds output rows m0 + 4r + i
-// for lane slot r: one MFMA computes a strided 32x32 sub-tile, and 4 x 4 MFMAs
-// cover the wave's 128 x 128 output tile. G and X reach LDS in their memory
-// layout through 16-byte buffer loads that write LDS directly (no register
-// round trip), over three LDS stages of 32 token rows, so two stages of loads
-// are in flight while the matrix cores work on the third.
+// Contraction on the matrix cores (v_mfma_f32_32x32x16_bf16). G_e [T_e x M]
+// and X_e [T_e x N] both have the token index as their row index, so the
+// reduction runs down the rows of both operands, while the instruction wants
+// each lane to hold 8 consecutive k values of one output row (A) or column
+// (B). Each lane therefore holds 8 token rows x 4 consecutive columns (8 bytes
+// per row; 32 lanes cover 128 contiguous columns) and transposes the 8 x 4
+// block in registers with v_perm_b32. Fragment i (i = 0..3) then holds output
+// rows m0 + 4r + i for lane slot r: one MFMA computes a strided 32 x 32
+// sub-tile, and 4 x 4 MFMAs cover a wave's 128 x 128 output tile.
+//
+// Operand paths. A workgroup of W waves owns a 128 (m) x 128W (n) tile; wave
+// w owns the n columns n0 + 128w. The G block is shared by all waves, so it is
+// staged in LDS: 16-byte loads into registers three 32-row stages ahead, one
+// 16-byte LDS write per lane and stage, three LDS stages. The X block of a
+// wave is private to it, so it goes from global memory straight into
+// registers, six 16-row blocks ahead. This keeps LDS traffic to the G operand
+// alone (the LDS of one CU moves about 128 bytes per clock, less than both
+// operands need at the matrix-core rate). All loads are ordinary loads whose
+// waits the compiler places.
 //
 // Canonical order (the oracle's): an expert's rows are cut into splits of
 // k_tile * ktiles_per_split rows counted from the expert's first row (one split
@@ -22,7 +29,13 @@
 // rows in ascending 16-row blocks starting from +0.0 (rows past the split end
 // are zero). With one split the epilogue adds the partial into main_grad
 // directly; with several, each partial goes to scratch and a second kernel adds
-// (((Q0 + Q1) + Q2) + ...) into main_grad once.
+// (((Q0 + Q1) + Q2) + ...) into main_grad once. The tile shape and the order
+// in which workgroups take splits never change a bit.
+//
+// Scheduling. Experts differ in size, so splits are handed out largest expert
+// first (ties by expert index): the hardware dispatches workgroups in index
+// order to whichever CU frees up, which makes this a longest-job-first list
+// schedule.
 //
 // The atomic arm adds every split's partial into main_grad with float atomics.
 #include "common.hpp"
@@ -33,15 +46,36 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128;     // workgroup tile: 128 (m) x 512 (n), 4 waves of 128 x 128
-constexpr int kBN = 512;
-constexpr int kBK = 32;      // token rows per LDS stage
-constexpr int kWaveN = 128;
-constexpr int kThreads = 256;
-constexpr int kTileM = kBM;
-constexpr int kTileN = kBN;
+constexpr int kBM = 128;      // m columns of G per workgroup tile
+constexpr int kWaveN = 128;   // n columns of X per wave
+constexpr int kBlk = 16;      // token rows per MFMA block
+constexpr int kStage = 32;    // token rows per LDS stage of G (two blocks)
+constexpr int kAStages = 3;   // LDS stages of G
+constexpr int kBSlots = 6;    // 16-row X blocks held in registers per wave
 constexpr int kKTile = 512;
+constexpr int kTileM = kBM;
+constexpr int kXcds = 8;
+constexpr int kRankMaxE = 63;  // experts are ordered by size when E <= 63
+
+// Raw buffer descriptor word 3 of the gfx9 family (32-bit data format, no
+// swizzle); the range check returns zeros past num_records bytes.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+// Per-stage G: 32 rows x 128 columns x 2 bytes = 8 pieces of 1 KiB (4 rows of
+// 256 bytes each; one 16-byte load per lane), shared out over the waves.
+constexpr int kDmaA = kStage * kBM * 2 / 1024;
+constexpr int kBLoads = 8;  // 8-byte X loads per lane per 16-row block
+
+template <int W>
+struct Shape {
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kBN = kWaveN * W;
+  static constexpr int kALoads = kDmaA / W;  // 16-byte G loads per lane and stage
+  static_assert(kDmaA % W == 0, "G transfers must divide over the waves");
+};
 
 struct WgradArgs {
   float* mg;
@@ -52,46 +86,44 @@ struct WgradArgs {
   int64_t ldx;
   const int32_t* offs;
   int E;
-  int64_t T_total;
+  int T_total;
   int M, N;
-  int64_t split_rows;  // 0: one split per expert
+  int split_rows;  // 0: one split per expert
   int tiles_m, tiles_n;
-  int64_t n_units;  // tiles * max_splits
+  int64_t n_units;
   float* scratch;   // [max_splits][M][N]
   int64_t max_splits;
 };
 
-// Expert row range with clamping (offsets are device data and cannot be
-// validated on the host): b_e = clamp(offs[e], b_{e-1}, T_total).
+// One split of one expert. Expert boundaries come from device offsets and are
+// clamped monotone: b_e = clamp(offs[e], b_{e-1}, T_total), b_{-1} = 0.
 struct Split {
   int e;
-  int64_t g;       // global split index (scratch slot)
+  int64_t g;        // natural split index (expert order, then split order): scratch slot
   int64_t n_split;  // splits of this expert
-  int64_t r0, r1;
+  int r0, r1;       // token rows [r0, r1)
 };
 
-__device__ __forceinline__ bool find_split(const WgradArgs& p, int64_t g, Split& out) {
-  int64_t prev = 0, cum = 0;
-  int64_t b = p.offs[0];
-  b = b < 0 ? 0 : (b > p.T_total ? p.T_total : b);
-  prev = b;
+__device__ __forceinline__ int clamp_i(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+__device__ __forceinline__ int splits_of(int te, int split_rows) {
+  return te <= 0 ? 0 : (split_rows == 0 ? 1 : (te + split_rows - 1) / split_rows);
+}
+
+// Split q in natural order (experts ascending, splits ascending).
+__device__ bool split_natural(const WgradArgs& p, int64_t q, Split& out) {
+  int prev = clamp_i(p.offs[0], 0, p.T_total);
+  int64_t cum = 0;
   for (int e = 0; e < p.E; ++e) {
-    int64_t nb = p.offs[e + 1];
-    nb = nb < prev ? prev : (nb > p.T_total ? p.T_total : nb);
-    const int64_t te = nb - prev;
-    const int64_t se = te == 0 ? 0 : (p.split_rows == 0 ? 1 : (te + p.split_rows - 1) / p.split_rows);
-    if (g < cum + se) {
-      const int64_t s = g - cum;
+    const int nb = clamp_i(p.offs[e + 1], prev, p.T_total);
+    const int se = splits_of(nb - prev, p.split_rows);
+    if (q < cum + se) {
+      const int s = static_cast<int>(q - cum);
       out.e = e;
-      out.g = g;
+      out.g = q;
       out.n_split = se;
-      if (p.split_rows == 0) {
-        out.r0 = prev;
-        out.r1 = nb;
-      } else {
-        out.r0 = prev + s * p.split_rows;
-        out.r1 = out.r0 + p.split_rows < nb ? out.r0 + p.split_rows : nb;
-      }
+      out.r0 = p.split_rows == 0 ? prev : prev + s * p.split_rows;
+      out.r1 = p.split_rows == 0 ? nb : (out.r0 + p.split_rows < nb ? out.r0 + p.split_rows : nb);
       return true;
     }
     cum += se;
@@ -100,10 +132,60 @@ __device__ __forceinline__ bool find_split(const WgradArgs& p, int64_t g, Split&
   return false;
 }
 
+// Split q in size order: experts by decreasing row count (ties by index), each
+// expert's splits in ascending order. Lane e of the wave handles expert e.
+__device__ bool split_by_size(const WgradArgs& p, int64_t q, Split& out) {
+  if (p.E > kRankMaxE) return split_natural(p, q, out);
+  const int lane = threadIdx.x & 63;
+  const int E = p.E;
+  // b_j = min(T, max(0, offs[0..j])) for j = 0..E (lanes 0..E)
+  int b = lane <= E ? p.offs[lane] : 0;
+  b = b < 0 ? 0 : b;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(b, d);
+    if (lane >= d) b = b > t ? b : t;
+  }
+  b = b < p.T_total ? b : p.T_total;
+  const int end = __shfl_down(b, 1);
+  const int te = lane < E ? end - b : 0;
+  const int se = lane < E ? splits_of(te, p.split_rows) : 0;
+  // natural exclusive prefix of split counts (scratch slots)
+  int gs = se;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(gs, d);
+    if (lane >= d) gs += t;
+  }
+  gs -= se;
+  // position of this expert's first split in the size order
+  int pos = 0;
+  for (int j = 0; j < E; ++j) {
+    const int tj = __builtin_amdgcn_readlane(te, j);
+    const int sj = __builtin_amdgcn_readlane(se, j);
+    const bool before = tj > te || (tj == te && j < lane);
+    pos += before ? sj : 0;
+  }
+  const bool mine = lane < E && se > 0 && q >= pos && q < pos + se;
+  const uint64_t m = __ballot(mine);
+  if (m == 0) return false;
+  const int e = __builtin_ctzll(m);
+  const int e_pos = __builtin_amdgcn_readlane(pos, e);
+  const int e_b = __builtin_amdgcn_readlane(b, e);
+  const int e_end = __builtin_amdgcn_readlane(end, e);
+  const int s = static_cast<int>(q) - e_pos;
+  out.e = e;
+  out.g = static_cast<int64_t>(__builtin_amdgcn_readlane(gs, e)) + s;
+  out.n_split = __builtin_amdgcn_readlane(se, e);
+  out.r0 = p.split_rows == 0 ? e_b : e_b + s * p.split_rows;
+  out.r1 = p.split_rows == 0 ? e_end : (out.r0 + p.split_rows < e_end ? out.r0 + p.split_rows : e_end);
+  return true;
+}
+
 // MFMA operand of column c (0..3) of a lane's 8-row x 4-column block: dword q
 // packs rows 2q (low 16 bits) and 2q+1 (high 16 bits) of that column.
 template <int C>
-__device__ __forceinline__ bf16x8_t frag(const uint2 (&v)[8]) {
+__device__ __forceinline__ bf16x8_t frag(const u32x2_t* v) {
   constexpr uint32_t sel = (C & 1) ? 0x07060302u : 0x05040100u;
   u32x4_t d;
 #pragma unroll
@@ -115,93 +197,58 @@ __device__ __forceinline__ bf16x8_t frag(const uint2 (&v)[8]) {
   return __builtin_bit_cast(bf16x8_t, d);
 }
 
-// One K step of kBK token rows lands in LDS as row-major [k][m] and [k][n]
-// slabs (the layout of G and X in memory) through direct buffer-to-LDS loads:
-// each instruction moves 64 lanes x 16 bytes into 1 KiB of LDS in lane order,
-// so no registers hold the data in flight. The buffer resources cover the
-// split's rows only; rows past the split end read as zero. G: 8 instructions
-// per step (4 rows of 256 B each), X: 32 (one 1 KiB row each), 10 per wave.
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9-family raw buffer descriptor
-constexpr int kDmaA = kBK * kBM * 2 / 1024;     // 1 KiB transfers of G per step
-constexpr int kDmaB = kBK * kBN * 2 / 1024;     // 1 KiB transfers of X per step
-constexpr int kDmaPerWave = (kDmaA + kDmaB) / (kThreads / 64);
+typedef uint16_t StageA[kStage][kBM];
 
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor: base address, stride 0, num_records bytes.
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t num_records) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = static_cast<int32_t>(a & 0xFFFFFFFFu);
-  r[1] = static_cast<int32_t>((a >> 32) & 0xFFFFu);
-  r[2] = static_cast<int32_t>(num_records);
-  r[3] = static_cast<int32_t>(kRsrcWord3);
-  return r;
-}
-
-// LDS byte address of a __shared__ object (wave-uniform here).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  typedef __attribute__((address_space(3))) const char* lds_ptr_t;
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));  // generic -> LDS address space
-}
-
-// One 1 KiB transfer: every lane's 16 bytes at rsrc + voff + soff land at
-// LDS[m0 + 16 * lane]. Issued as inline assembly (as the composable-kernel
-// library does for its asynchronous copies) so that the compiler does not
-// insert conservative waits on these loads before unrelated LDS reads; the
-// kernel waits for them explicitly with s_waitcnt vmcnt.
-__device__ __forceinline__ void dma16(uint32_t lds, i32x4_t rsrc, int32_t voff, int32_t soff) {
-  asm volatile("s_mov_b32 m0, %0" : : "s"(lds) : "memory");
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
-
-struct Src {
-  i32x4_t ra, rb;           // G and X rows [r0, r1), rebased at r0
-  int32_t voff_a, voff_b;   // this lane's byte offset inside one transfer
-  int32_t krow_a, krow_b;   // bytes per token row
-};
-
-// Issue this wave's share of the transfers of the step starting at split row krel.
-__device__ __forceinline__ void stage_issue(const Src& src, int32_t krel, uint16_t (*la)[kBM], uint16_t (*lb)[kBN],
-                                            int wave) {
+// This wave's pieces of G stage `st` (token rows 32 st ..): piece i covers
+// rows 4i .. 4i+3; lane l loads row 4i + l/16, columns 8 (l % 16) .. + 7.
+template <int W>
+__device__ __forceinline__ void load_a(u32x4_t* v, __amdgpu_buffer_rsrc_t rsrc, int32_t voff, int32_t krow, int32_t st,
+                                       int wave) {
 #pragma unroll
-  for (int u = 0; u < kDmaA / 4; ++u) {
-    const int i = wave * (kDmaA / 4) + u;  // transfer i covers rows 4i .. 4i+3
-    dma16(lds_addr(&la[4 * i][0]), src.ra, src.voff_a, (krel + 4 * i) * src.krow_a);
-  }
-#pragma unroll
-  for (int u = 0; u < kDmaB / 4; ++u) {
-    const int i = wave * (kDmaB / 4) + u;  // transfer i covers row i
-    dma16(lds_addr(&lb[i][0]), src.rb, src.voff_b, (krel + i) * src.krow_b);
+  for (int u = 0; u < Shape<W>::kALoads; ++u) {
+    const int i = wave * Shape<W>::kALoads + u;
+    v[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, (st * kStage + 4 * i) * krow, 0);
   }
 }
 
-// Wait until this wave's transfers of the oldest in-flight step have landed
-// (the younger step's kDmaPerWave may still be pending), then meet the other
-// waves so that every wave's transfers of that step are visible.
-template <bool YOUNGER_PENDING>
-__device__ __forceinline__ void stage_wait() {
-  static_assert(kDmaPerWave == 10, "vmcnt literal below");
-  if (YOUNGER_PENDING)
-    asm volatile("s_waitcnt vmcnt(10)" : : : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-  __builtin_amdgcn_s_barrier();
+template <int W>
+__device__ __forceinline__ void write_a(StageA& la, const u32x4_t* v, int lane, int wave) {
+#pragma unroll
+  for (int u = 0; u < Shape<W>::kALoads; ++u) {
+    const int i = wave * Shape<W>::kALoads + u;
+    *reinterpret_cast<u32x4_t*>(&la[4 * i + lane / 16][8 * (lane % 16)]) = v[u];
+  }
 }
 
-// One 16-row MFMA block from LDS rows [row0, row0 + 16): lane (r, kg) reads
-// rows row0 + 8*kg + e of its 4 G columns (4r..4r+3) and its 4 X columns
-// (128*wave + 4r ..), transposes, and issues 4 x 4 MFMAs.
-__device__ __forceinline__ void mma_block(const uint16_t (*la)[kBM], const uint16_t (*lb)[kBN], int row0, int r,
-                                          int kg, int wave, f32x16_t (&acc)[4][4]) {
-  uint2 ra[8], rb[8];
+// The 8 X rows of 16-row block `blk` this lane needs: rows 16 blk + 8 kg + e.
+__device__ __forceinline__ void issue_b(u32x2_t* slot, __amdgpu_buffer_rsrc_t rsrc, int32_t voff, int32_t krow,
+                                        int32_t blk) {
+#pragma unroll
+  for (int e = 0; e < kBLoads; ++e) slot[e] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, (blk * kBlk + e) * krow, 0);
+}
+
+// The G rows of one LDS stage this lane needs: rows 8 kg + e (block 0, into
+// v[0..7]) and 16 + 8 kg + e (block 1, into v[8..15]), columns 4r .. 4r+3.
+__device__ __forceinline__ void read_a(const StageA& la, int r, int kg, u32x2_t* v) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    ra[e] = *reinterpret_cast<const uint2*>(&la[row0 + 8 * kg + e][4 * r]);
-    rb[e] = *reinterpret_cast<const uint2*>(&lb[row0 + 8 * kg + e][kWaveN * wave + 4 * r]);
+    v[e] = *reinterpret_cast<const u32x2_t*>(&la[8 * kg + e][4 * r]);
+    v[8 + e] = *reinterpret_cast<const u32x2_t*>(&la[16 + 8 * kg + e][4 * r]);
   }
-  const bf16x8_t fa[4] = {frag<0>(ra), frag<1>(ra), frag<2>(ra), frag<3>(ra)};
-  const bf16x8_t fb[4] = {frag<0>(rb), frag<1>(rb), frag<2>(rb), frag<3>(rb)};
+}
+
+// Pin the use of an X slot to this point of the program: volatile asm keeps
+// its place among the pipeline's other volatile asm (the stage syncs), so the
+// transposes and MFMAs that read the slot cannot be hoisted ahead of the stage
+// they belong to, and the compiler's wait for the slot's loads lands here.
+__device__ __forceinline__ void pin(u32x2_t* v) {
+#pragma unroll
+  for (int e = 0; e < kBLoads; ++e) asm volatile("" : "+v"(v[e]));
+}
+
+__device__ __forceinline__ void mma_block(const u32x2_t* a, const u32x2_t* b, f32x16_t (&acc)[4][4]) {
+  const bf16x8_t fa[4] = {frag<0>(a), frag<1>(a), frag<2>(a), frag<3>(a)};
+  const bf16x8_t fb[4] = {frag<0>(b), frag<1>(b), frag<2>(b), frag<3>(b)};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -213,29 +260,27 @@ __device__ __forceinline__ void mma_block(const uint16_t (*la)[kBM], const uint1
 // for every split, the tiles of n-tile column x % tiles_n and of its share of
 // the m-tiles; consecutive workgroups on one XCD are tiles of the same split
 // and column, so their X rows come from that XCD's L2 after the first read.
-// Every XCD gets a share of every expert, which keeps the XCDs balanced.
-constexpr int kXcds = 8;
-
-__device__ __forceinline__ bool unit_of(const WgradArgs& p, uint32_t u, int64_t& g, int& mt, int& nt) {
+// Every XCD gets a share of every split, which keeps the XCDs balanced.
+__device__ __forceinline__ bool unit_of(const WgradArgs& p, uint32_t u, int64_t& q, int& mt, int& nt) {
   const int x = static_cast<int>(u % kXcds);
   const int64_t slot = u / kXcds;
   const int NT = p.tiles_n, MT = p.tiles_m;
   if (kXcds % NT == 0) {
-    const int parts = kXcds / NT;           // m-tile parts per column
+    const int parts = kXcds / NT;  // m-tile parts per column
     const int part = x / NT;
     const int mlo = part * MT / parts, mhi = (part + 1) * MT / parts;
     const int per = mhi - mlo;
     if (per == 0) return false;
-    g = slot / per;
-    if (g >= p.max_splits) return false;
+    q = slot / per;
+    if (q >= p.max_splits) return false;
     mt = mlo + static_cast<int>(slot % per);
     nt = x % NT;
     return true;
   }
   // any other column count: plain split-major order
   const int64_t t = static_cast<int64_t>(u) % (static_cast<int64_t>(MT) * NT);
-  g = static_cast<int64_t>(u) / (static_cast<int64_t>(MT) * NT);
-  if (g >= p.max_splits) return false;
+  q = static_cast<int64_t>(u) / (static_cast<int64_t>(MT) * NT);
+  if (q >= p.max_splits) return false;
   mt = static_cast<int>(t / NT);
   nt = static_cast<int>(t % NT);
   return true;
@@ -254,29 +299,30 @@ __host__ int64_t wgrad_grid(int tiles_m, int tiles_n, int64_t max_splits) {
   return static_cast<int64_t>(tiles_m) * tiles_n * max_splits;
 }
 
-// One workgroup = 4 waves = a 128 (m) x 512 (n) output tile; wave w owns the
-// 128 x 128 columns n0 + 128w. K runs in steps of kBK rows through two LDS
-// buffers: while the matrix cores work on one, the next step's global loads
-// are in flight in registers and then written to the other.
-template <bool ATOMIC>
-__global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t la0[kBK][kBM];
-  __shared__ __attribute__((aligned(16))) uint16_t la1[kBK][kBM];
-  __shared__ __attribute__((aligned(16))) uint16_t la2[kBK][kBM];
-  __shared__ __attribute__((aligned(16))) uint16_t lb0[kBK][kBN];
-  __shared__ __attribute__((aligned(16))) uint16_t lb1[kBK][kBN];
-  __shared__ __attribute__((aligned(16))) uint16_t lb2[kBK][kBN];
-  int64_t g;
+// One workgroup = W waves = a 128 (m) x 128W (n) output tile; wave w owns the
+// 128 x 128 columns n0 + 128w.
+//
+// Pipeline per stage s (blocks 2s and 2s+1):
+//   block 2s:    MFMAs on G rows of stage s (registers) and X block 2s (slot),
+//                then X block 2s+6 into the freed slot
+//   G stage s+1: registers -> LDS stage (s+1) % 3; barrier
+//   G stage s+4: global -> the registers that stage s+1 came through
+//   G stage s+1: LDS -> registers
+//   block 2s+1:  MFMAs, then X block 2s+7 into the freed slot
+// The LDS stage written at stage s was last read at stage s-3, before two
+// barriers, and every LDS read of a stage follows the barrier after its write.
+template <int W, bool ATOMIC>
+__global__ __launch_bounds__(64 * W) void wgrad_kernel(WgradArgs p) {
+  __shared__ __attribute__((aligned(16))) StageA la[kAStages];
+  int64_t uq;
   int mt, nt;
-  if (!unit_of(p, blockIdx.x, g, mt, nt)) return;
+  if (!unit_of(p, blockIdx.x, uq, mt, nt)) return;
   Split sp;
-  if (!find_split(p, g, sp)) return;
-  // wave-uniform by construction; readfirstlane lets the compiler keep it (and
-  // every LDS transfer base derived from it) in scalar registers
+  if (!split_by_size(p, uq, sp)) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int m0 = mt * kBM;
-  const int n0 = nt * kBN;
+  const int n0 = nt * Shape<W>::kBN;
   const int r = lane & 31;
   const int kg = lane >> 5;
 
@@ -286,39 +332,73 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+      for (int c = 0; c < 16; ++c) acc[i][j][c] = 0.0f;
 
-  const int64_t r0 = sp.r0, r1 = sp.r1;
-  const int32_t rows = static_cast<int32_t>(r1 - r0);
-  Src src;
-  src.ra = make_rsrc(p.G + r0 * p.ldg, static_cast<uint32_t>(rows * p.ldg * 2));
-  src.rb = make_rsrc(p.X + r0 * p.ldx, static_cast<uint32_t>(rows * p.ldx * 2));
-  src.krow_a = static_cast<int32_t>(p.ldg * 2);
-  src.krow_b = static_cast<int32_t>(p.ldx * 2);
-  src.voff_a = (lane / (kBM / 8)) * src.krow_a + (m0 + (lane % (kBM / 8)) * 8) * 2;
-  src.voff_b = (n0 + lane * 8) * 2;
+  // Buffer resources cover the split's rows only: rows past its end read as
+  // zero, which is the zero padding of the last block.
+  const int32_t rows = sp.r1 - sp.r0;
+  const int32_t krow_a = static_cast<int32_t>(p.ldg * 2);
+  const int32_t krow_b = static_cast<int32_t>(p.ldx * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.G + static_cast<int64_t>(sp.r0) * p.ldg), 0, rows * krow_a, static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.X + static_cast<int64_t>(sp.r0) * p.ldx), 0, rows * krow_b, static_cast<int>(kRsrcWord3));
+  const int32_t voff_a = (lane / 16) * krow_a + (m0 + (lane % 16) * 8) * 2;
+  const int32_t voff_b = 8 * kg * krow_b + (n0 + kWaveN * wave + 4 * r) * 2;
 
-  // Three LDS buffers: while the matrix cores work on step s, the transfers of
-  // steps s+1 and s+2 are in flight. The loop is unrolled over the buffers so
-  // that each buffer is its own LDS object (exact wait counts) and every LDS
-  // address is a per-lane base plus a constant.
-  stage_issue(src, 0, la0, lb0, wave);
-  if (kBK < rows) stage_issue(src, kBK, la1, lb1, wave);
-#define DET_WGRAD_STEP(LA, LB, LA_NEXT2, LB_NEXT2, OFF)                              \
-  {                                                                                 \
-    const int32_t k = k0 + (OFF);                                                   \
-    if (k >= rows) break;                                                           \
-    if (k + kBK < rows) stage_wait<true>(); else stage_wait<false>();               \
-    if (k + 2 * kBK < rows) stage_issue(src, k + 2 * kBK, LA_NEXT2, LB_NEXT2, wave); \
-    mma_block(LA, LB, 0, r, kg, wave, acc);                                         \
-    if (k + 16 < rows) mma_block(LA, LB, 16, r, kg, wave, acc);                     \
+  u32x2_t bq[kBSlots][kBLoads];
+  u32x4_t ga[kAStages][Shape<W>::kALoads];
+  u32x2_t ra[16];
+
+  // prologue: G stages 0..2 and X blocks 0..5 in flight; G stage 0 to LDS,
+  // and its registers take G stage 3 (register set k holds the G stages
+  // congruent to k mod 3)
+  load_a<W>(ga[0], rsrc_a, voff_a, krow_a, 0, wave);
+#pragma unroll
+  for (int b = 0; b < kBSlots; ++b) {
+    issue_b(bq[b], rsrc_b, voff_b, krow_b, b);
+    if (b == 1) load_a<W>(ga[1], rsrc_a, voff_a, krow_a, 1, wave);
+    if (b == 3) load_a<W>(ga[2], rsrc_a, voff_a, krow_a, 2, wave);
   }
-  for (int32_t k0 = 0; k0 < rows; k0 += 3 * kBK) {
-    DET_WGRAD_STEP(la0, lb0, la2, lb2, 0)
-    DET_WGRAD_STEP(la1, lb1, la0, lb0, kBK)
-    DET_WGRAD_STEP(la2, lb2, la1, lb1, 2 * kBK)
+  write_a<W>(la[0], ga[0], lane, wave);
+  __syncthreads();
+  load_a<W>(ga[0], rsrc_a, voff_a, krow_a, kAStages, wave);
+  read_a(la[0], r, kg, ra);
+
+  // Three stages per iteration, so that every LDS stage and register slot is
+  // a compile-time index. Whole iterations (6 blocks inside the split) run
+  // without any branch between their MFMA blocks; the last, partial iteration
+  // runs the same stages with each MFMA block guarded. Every stage issues its
+  // loads even past the split end (those read zeros), so all paths through the
+  // loop issue the same loads and the compiler's waits stay loose.
+#define DET_WGRAD_STAGE(SI, GUARD)                                                         \
+  {                                                                                        \
+    const int32_t s = s0 + (SI);                                                           \
+    pin(bq[(2 * (SI)) % kBSlots]);                                                         \
+    if (!(GUARD) || s * kStage < rows) mma_block(&ra[0], bq[(2 * (SI)) % kBSlots], acc);   \
+    issue_b(bq[(2 * (SI)) % kBSlots], rsrc_b, voff_b, krow_b, 2 * s + 6);                  \
+    write_a<W>(la[((SI) + 1) % kAStages], ga[((SI) + 1) % kAStages], lane, wave);          \
+    __syncthreads();                                                                       \
+    load_a<W>(ga[((SI) + 1) % kAStages], rsrc_a, voff_a, krow_a, s + 1 + kAStages, wave);  \
+    u32x2_t rn[16];                                                                        \
+    read_a(la[((SI) + 1) % kAStages], r, kg, rn);                                          \
+    pin(bq[(2 * (SI) + 1) % kBSlots]);                                                     \
+    if (!(GUARD) || s * kStage + kBlk < rows) mma_block(&ra[8], bq[(2 * (SI) + 1) % kBSlots], acc); \
+    issue_b(bq[(2 * (SI) + 1) % kBSlots], rsrc_b, voff_b, krow_b, 2 * s + 7);              \
+    _Pragma("unroll") for (int v = 0; v < 16; ++v) ra[v] = rn[v];                          \
   }
-#undef DET_WGRAD_STEP
+  int32_t s0 = 0;
+  for (; (s0 + 3) * kStage <= rows; s0 += 3) {
+    DET_WGRAD_STAGE(0, false)
+    DET_WGRAD_STAGE(1, false)
+    DET_WGRAD_STAGE(2, false)
+  }
+  if (s0 * kStage < rows) {
+    DET_WGRAD_STAGE(0, true)
+    DET_WGRAD_STAGE(1, true)
+    DET_WGRAD_STAGE(2, true)
+  }
+#undef DET_WGRAD_STAGE
 
   // Epilogue: lane (r, kg), MFMA (i, j), accumulator q holds output
   // m = m0 + 4 * (8*(q/4) + 4*kg + q%4) + i,  n = n0 + 128*wave + 4*r + j.
@@ -391,12 +471,14 @@ __global__ __launch_bounds__(256) void wgrad_fold_kernel(WgradArgs p) {
   *reinterpret_cast<float4*>(d) = o;
 }
 
+constexpr int kDefaultBlockN = 256;
+
 int resolve(const det_wgrad_cfg* cfg, det_wgrad_cfg* out) {
-  det_wgrad_cfg c{kTileM, kTileN, kKTile, 0};
+  det_wgrad_cfg c{kTileM, kDefaultBlockN, kKTile, 0};
   if (cfg) c = *cfg;
-  if (c.block_m != kTileM || c.block_n != kTileN)
-    return set_error(DET_ERR_UNSUPPORTED, "wgrad: block_m x block_n must be %d x %d, got %d x %d", kTileM, kTileN,
-                     c.block_m, c.block_n);
+  if (c.block_m != kTileM || (c.block_n != 256 && c.block_n != 512))
+    return set_error(DET_ERR_UNSUPPORTED, "wgrad: block_m x block_n must be %d x 256 or %d x 512, got %d x %d", kTileM,
+                     kTileM, c.block_m, c.block_n);
   if (c.k_tile != kKTile) return set_error(DET_ERR_INVALID_ARG, "wgrad: k_tile must be %d, got %d", kKTile, c.k_tile);
   if (c.ktiles_per_split < 0 || c.ktiles_per_split > (1 << 20))
     return set_error(DET_ERR_INVALID_ARG, "wgrad: ktiles_per_split must be in [0, 2^20], got %d", c.ktiles_per_split);
@@ -404,15 +486,13 @@ int resolve(const det_wgrad_cfg* cfg, det_wgrad_cfg* out) {
   return DET_OK;
 }
 
-int check_shape(int64_t T_total, int32_t E, int64_t M, int64_t N) {
+int check_shape(int64_t T_total, int32_t E, int64_t M, int64_t N, const det_wgrad_cfg& c) {
   if (T_total < 0 || E < 0 || M < 0 || N < 0) return set_error(DET_ERR_INVALID_ARG, "wgrad: sizes must be >= 0");
-  if (M % kTileM || N % kTileN)
+  if (M % kTileM || N % c.block_n)
     return set_error(DET_ERR_UNSUPPORTED, "wgrad: M and N must be multiples of %d and %d, got %lld x %lld", kTileM,
-                     kTileN, static_cast<long long>(M), static_cast<long long>(N));
+                     c.block_n, static_cast<long long>(M), static_cast<long long>(N));
   if (M > (1 << 20) || N > (1 << 20) || E > 4096) return set_error(DET_ERR_UNSUPPORTED, "wgrad: problem too large");
-  // buffer loads use 32-bit byte offsets inside one split's rows
-  if (T_total * (M > N ? M : N) * 2 >= (1LL << 31))
-    return set_error(DET_ERR_UNSUPPORTED, "wgrad: T_total x max(M, N) too large for 32-bit offsets");
+  if (T_total >= (1LL << 30)) return set_error(DET_ERR_UNSUPPORTED, "wgrad: T_total too large");
   return DET_OK;
 }
 
@@ -436,9 +516,9 @@ extern "C" int det_grouped_wgrad_acc_workspace_size(int64_t T_total, int32_t E, 
                                                     const det_wgrad_cfg* cfg, int atomic, size_t* bytes) {
   if (int s = check_atomic_flag(atomic)) return s;
   if (!bytes) return set_error(DET_ERR_INVALID_ARG, "wgrad: bytes is NULL");
-  if (int s = check_shape(T_total, E, M, N)) return s;
   det_wgrad_cfg c;
   if (int s = resolve(cfg, &c)) return s;
+  if (int s = check_shape(T_total, E, M, N, c)) return s;
   const size_t sb = scratch_bytes(T_total, E, M, N, c);
   *bytes = (atomic || sb == 0) ? 0 : DET_WS_HEADER_BYTES + align_up(sb, 256);
   return ok();
@@ -449,9 +529,9 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
                                      int64_t M, int64_t N, const det_wgrad_cfg* cfg, void* ws, size_t ws_bytes,
                                      int atomic, void* stream) {
   if (int s = check_atomic_flag(atomic)) return s;
-  if (int s = check_shape(T_total, E, M, N)) return s;
   det_wgrad_cfg c;
   if (int s = resolve(cfg, &c)) return s;
+  if (int s = check_shape(T_total, E, M, N, c)) return s;
   if (E == 0 || M == 0 || N == 0 || T_total == 0) return ok();
   if (!main_grad || !G || !X || !offs) return set_error(DET_ERR_INVALID_ARG, "wgrad: NULL pointer");
   if (ld_m < N || ld_e < M * ld_m)
@@ -459,6 +539,10 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
   if (ldg < M || ldx < N) return set_error(DET_ERR_INVALID_ARG, "wgrad: need ldg >= M and ldx >= N");
   if (ldg % 8 || ldx % 8 || !aligned(G, 16) || !aligned(X, 16) || ld_m % 4 || ld_e % 4 || !aligned(main_grad, 16))
     return set_error(DET_ERR_UNSUPPORTED, "wgrad: rows of G, X and main_grad must be 16-byte aligned");
+  // buffer loads use 32-bit byte offsets inside one split, including the rows
+  // read ahead past its end (fewer than 512)
+  if ((T_total + 512) * (ldg > ldx ? ldg : ldx) * 2 >= (1LL << 31))
+    return set_error(DET_ERR_UNSUPPORTED, "wgrad: T_total x max(ldg, ldx) too large for 32-bit offsets");
   const size_t sb = scratch_bytes(T_total, E, M, N, c);
   const size_t need = (atomic || sb == 0) ? 0 : DET_WS_HEADER_BYTES + align_up(sb, 256);
   if (int s = check_workspace(ws, ws_bytes, need)) return s;
@@ -478,21 +562,30 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
   p.ldx = ldx;
   p.offs = offs;
   p.E = E;
-  p.T_total = T_total;
+  p.T_total = static_cast<int>(T_total);
   p.M = static_cast<int>(M);
   p.N = static_cast<int>(N);
-  p.split_rows = c.ktiles_per_split == 0 ? 0 : static_cast<int64_t>(c.k_tile) * c.ktiles_per_split;
+  p.split_rows = c.ktiles_per_split == 0 ? 0 : c.k_tile * c.ktiles_per_split;
   p.tiles_m = static_cast<int>(M / kTileM);
-  p.tiles_n = static_cast<int>(N / kTileN);
+  p.tiles_n = static_cast<int>(N / c.block_n);
   p.max_splits = max_splits(T_total, E, c);
   p.n_units = wgrad_grid(p.tiles_m, p.tiles_n, p.max_splits);
   p.scratch = (atomic || sb == 0) ? nullptr : reinterpret_cast<float*>(static_cast<char*>(ws) + DET_WS_HEADER_BYTES);
   if (p.n_units > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "wgrad: too many work units");
   const hipStream_t st = as_stream(stream);
-  if (atomic) {
-    hipLaunchKernelGGL(wgrad_kernel<true>, dim3(static_cast<uint32_t>(p.n_units)), dim3(kThreads), 0, st, p);
+  const dim3 grid(static_cast<uint32_t>(p.n_units));
+  if (c.block_n == 512) {
+    if (atomic)
+      hipLaunchKernelGGL((wgrad_kernel<4, true>), grid, dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((wgrad_kernel<4, false>), grid, dim3(256), 0, st, p);
   } else {
-    hipLaunchKernelGGL(wgrad_kernel<false>, dim3(static_cast<uint32_t>(p.n_units)), dim3(kThreads), 0, st, p);
+    if (atomic)
+      hipLaunchKernelGGL((wgrad_kernel<2, true>), grid, dim3(128), 0, st, p);
+    else
+      hipLaunchKernelGGL((wgrad_kernel<2, false>), grid, dim3(128), 0, st, p);
+  }
+  if (!atomic) {
     if (p.split_rows != 0) {
       const int64_t per_e = M * N / 4;
       hipLaunchKernelGGL(wgrad_fold_kernel, dim3(static_cast<uint32_t>(ceil_div(per_e, 256)), static_cast<uint32_t>(E)),

@@ -170,6 +170,16 @@ def test_wgrad_validation():
     assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 512, ctypes.byref(bad), 0, ctypes.byref(n)) == \
         dg.DET_ERR_UNSUPPORTED
     assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 100, 512, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 384, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
+    # the default 128 x 256 workgroup tile takes N in multiples of 256, the 128 x 512 tile in multiples of
+    # 512; other widths are refused
+    wide = dg.WgradCfg(128, 512, 512, 0)
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 768, None, 0, ctypes.byref(n)) == dg.DET_OK
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 768, ctypes.byref(wide), 0, ctypes.byref(n)) == \
+        dg.DET_ERR_UNSUPPORTED
+    odd = dg.WgradCfg(128, 384, 512, 0)
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 768, ctypes.byref(odd), 0, ctypes.byref(n)) == \
+        dg.DET_ERR_UNSUPPORTED
     MG, G, X, O = P(0x1000000), P(0x9000000), P(0xA000000), P(0xB000000)
     # an expanded main_grad (expert stride 0) is rejected
     assert L.det_grouped_wgrad_acc(MG, 0, 512, G, 128, X, 512, O, 2, 64, 128, 512, None, None, 0, 0, None) == \

@@ -27,18 +27,18 @@ pytestmark = pytest.mark.gpu
 M_, N_ = 256, 512  # small shapes: 2 x 2 workgroup tiles
 
 
-def cfg(C):
-    return dg.WgradCfg(128, 512, 512, C)
+def cfg(C, block_n=512):
+    return dg.WgradCfg(128, block_n, 512, C)
 
 
-def run(inp, C=0, atomic=False, mg0=None, offs=None, G=None, X=None):
+def run(inp, C=0, atomic=False, mg0=None, offs=None, G=None, X=None, block_n=512):
     import torch
     Gd = dev_bf16(inp.G) if G is None else G
     Xd = dev_bf16(inp.X) if X is None else X
     mg = dev_f32(inp.main_grad0 if mg0 is None else mg0)
     o = dev_i32(inp.offs if offs is None else offs)
     torch.cuda.synchronize()
-    dg.det_grouped_wgrad_acc(mg, Gd, Xd, o, cfg=cfg(C), atomic=atomic)
+    dg.det_grouped_wgrad_acc(mg, Gd, Xd, o, cfg=cfg(C, block_n), atomic=atomic)
     return host(mg)
 
 
@@ -85,6 +85,19 @@ def test_fold_of_gpu_partials_matches_oracle(C):
     for e in range(3):
         a, b = int(inp.offs[e]), int(inp.offs[e + 1])
         assert_bitwise(single[e], ow.fold_partials(inp.main_grad0[e], [gpu_partial(inp, G, X, a, b)]), "single")
+
+
+@pytest.mark.parametrize("C", [0, 1])
+def test_tile_width_does_not_change_bits(C):
+    """The 128 x 256 and 128 x 512 workgroup tiles give the same bits (the tile only shapes the launch)."""
+    inp = W.wgrad_inputs(E=5, M=M_, N=1024, tokens=[1500, 0, 33, 2049, 640], seed=8, out_init="normal")
+    G, X = dev_bf16(inp.G), dev_bf16(inp.X)
+    wide = run(inp, C, G=G, X=X, block_n=512)
+    narrow = run(inp, C, G=G, X=X, block_n=256)
+    note("wgrad C=%d: 128x512 vs 128x256 tiles" % C)
+    assert_bitwise(narrow, wide, "tile width")
+    ex = fp64.wgrad64(inp.main_grad0, inp.G, inp.X, inp.offs)
+    assert rel_l2(wide - inp.main_grad0, ex - inp.main_grad0) <= 1e-5
 
 
 def test_partial_is_independent_of_position():
