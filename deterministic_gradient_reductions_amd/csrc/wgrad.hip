@@ -90,6 +90,7 @@ struct WgradArgs {
   int M, N;
   int split_rows;  // 0: one split per expert
   int tiles_m, tiles_n;
+  int xcd_m, xcd_n;  // XCD cut of a split's tiles (0: plain order)
   int64_t n_units;
   float* scratch;   // [max_splits][M][N]
   int64_t max_splits;
@@ -256,47 +257,67 @@ __device__ __forceinline__ void mma_block(const u32x2_t* a, const u32x2_t* b, f3
 }
 
 // XCD-aware placement. Workgroups are dispatched to the 8 XCDs round-robin
-// (workgroup u runs on XCD u % 8), and each XCD has its own L2. XCD x takes,
-// for every split, the tiles of n-tile column x % tiles_n and of its share of
-// the m-tiles; consecutive workgroups on one XCD are tiles of the same split
-// and column, so their X rows come from that XCD's L2 after the first read.
-// Every XCD gets a share of every split, which keeps the XCDs balanced.
+// (workgroup u runs on XCD u % 8), and each XCD has its own L2. The tiles of
+// every split are cut into 8 rectangles, xcd_m (m-parts) x xcd_n (n-parts),
+// one per XCD; the host picks the cut that minimises the G and X bytes per
+// token row one XCD reads (its m-range of G plus its n-range of X), since the
+// workgroups of one rectangle share those rows through their XCD's L2. XCD x
+// takes its rectangle's tiles split after split, so every XCD gets the same
+// share of every split and the XCDs stay balanced.
 __device__ __forceinline__ bool unit_of(const WgradArgs& p, uint32_t u, int64_t& q, int& mt, int& nt) {
-  const int x = static_cast<int>(u % kXcds);
-  const int64_t slot = u / kXcds;
-  const int NT = p.tiles_n, MT = p.tiles_m;
-  if (kXcds % NT == 0) {
-    const int parts = kXcds / NT;  // m-tile parts per column
-    const int part = x / NT;
-    const int mlo = part * MT / parts, mhi = (part + 1) * MT / parts;
-    const int per = mhi - mlo;
+  if (p.xcd_m > 0) {
+    const int x = static_cast<int>(u % kXcds);
+    const int64_t slot = u / kXcds;
+    const int xm = x / p.xcd_n, xn = x % p.xcd_n;
+    const int mlo = xm * p.tiles_m / p.xcd_m, mhi = (xm + 1) * p.tiles_m / p.xcd_m;
+    const int nlo = xn * p.tiles_n / p.xcd_n, nhi = (xn + 1) * p.tiles_n / p.xcd_n;
+    const int per = (mhi - mlo) * (nhi - nlo);
     if (per == 0) return false;
     q = slot / per;
     if (q >= p.max_splits) return false;
-    mt = mlo + static_cast<int>(slot % per);
-    nt = x % NT;
+    const int t = static_cast<int>(slot % per);
+    mt = mlo + t / (nhi - nlo);
+    nt = nlo + t % (nhi - nlo);
     return true;
   }
-  // any other column count: plain split-major order
-  const int64_t t = static_cast<int64_t>(u) % (static_cast<int64_t>(MT) * NT);
-  q = static_cast<int64_t>(u) / (static_cast<int64_t>(MT) * NT);
+  // fewer tiles than XCDs: plain split-major order
+  const int64_t tiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
+  q = static_cast<int64_t>(u) / tiles;
   if (q >= p.max_splits) return false;
-  mt = static_cast<int>(t / NT);
-  nt = static_cast<int>(t % NT);
+  const int t = static_cast<int>(static_cast<int64_t>(u) % tiles);
+  mt = t / p.tiles_n;
+  nt = t % p.tiles_n;
   return true;
 }
 
-__host__ int64_t wgrad_grid(int tiles_m, int tiles_n, int64_t max_splits) {
-  if (kXcds % tiles_n == 0) {
-    const int parts = kXcds / tiles_n;
+// Host: choose the XCD cut and the grid size.
+__host__ void plan_xcds(WgradArgs& p, int block_m, int block_n) {
+  p.xcd_m = 0;
+  p.xcd_n = 0;
+  int64_t best = -1;
+  for (int pm = 1; pm <= kXcds; pm *= 2) {
+    const int pn = kXcds / pm;
+    if (pm > p.tiles_m || pn > p.tiles_n) continue;
+    const int64_t bytes = static_cast<int64_t>((p.tiles_m + pm - 1) / pm) * block_m * 2 +
+                          static_cast<int64_t>((p.tiles_n + pn - 1) / pn) * block_n * 2;
+    if (best < 0 || bytes < best) {
+      best = bytes;
+      p.xcd_m = pm;
+      p.xcd_n = pn;
+    }
+  }
+  if (p.xcd_m > 0) {
     int per_max = 0;
-    for (int part = 0; part < parts; ++part) {
-      const int per = (part + 1) * tiles_m / parts - part * tiles_m / parts;
+    for (int x = 0; x < kXcds; ++x) {
+      const int xm = x / p.xcd_n, xn = x % p.xcd_n;
+      const int per = ((xm + 1) * p.tiles_m / p.xcd_m - xm * p.tiles_m / p.xcd_m) *
+                      ((xn + 1) * p.tiles_n / p.xcd_n - xn * p.tiles_n / p.xcd_n);
       per_max = per > per_max ? per : per_max;
     }
-    return static_cast<int64_t>(kXcds) * per_max * max_splits;
+    p.n_units = static_cast<int64_t>(kXcds) * per_max * p.max_splits;
+  } else {
+    p.n_units = static_cast<int64_t>(p.tiles_m) * p.tiles_n * p.max_splits;
   }
-  return static_cast<int64_t>(tiles_m) * tiles_n * max_splits;
 }
 
 // One workgroup = W waves = a 128 (m) x 128W (n) output tile; wave w owns the
@@ -439,6 +460,293 @@ __global__ __launch_bounds__(64 * W) void wgrad_kernel(WgradArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 workgroup tile, both operands through LDS.
+//
+// Four waves in a 2 x 2 arrangement each own a 128 x 128 quarter, so every G
+// column block and every X column block is shared by two waves. Both operands
+// reach LDS through 16-byte buffer loads that write LDS directly (one 1 KiB
+// transfer per instruction, no registers in flight), four stages of 32 token
+// rows, three in flight. At the matrix-core rate a CU then needs about half of
+// its texture-address throughput (which is set by instructions, not bytes)
+// and three quarters of its LDS read bandwidth, but direct-to-LDS writes run
+// at about half the LDS read rate, so this kernel is bound by its LDS traffic
+// (transfers plus fragment reads). A fragments come from LDS through
+// the transposing 8-byte read (ds_read_b64_tr_b16: each lane gets 4 token rows
+// of one G column); X fragments through plain 8-byte reads and v_perm_b32, so
+// that each lane keeps 4 consecutive output columns for float4 epilogue
+// access. Fragments of the next 16-row block are read while the current
+// block's MFMAs run.
+//
+// Every load in the loop is one of these explicit transfers, issued the same
+// way on every path, so the vmcnt literals below count exactly: when stage s
+// waits for stage s+1, the transfers of stages s+2 and s+3 (8 per wave each)
+// may still be in flight.
+constexpr int kLTile = 256;
+constexpr int kLStages = 4;
+constexpr int kLPerWave = 8;  // transfers per wave and stage: 4 of G, 4 of X
+#define DET_WGRAD_L_VM_STEADY 16
+#define DET_WGRAD_L_VM_PROLOG 24
+#define DET_STR2(x) #x
+#define DET_STR(x) DET_STR2(x)
+static_assert(DET_WGRAD_L_VM_STEADY == 2 * kLPerWave && DET_WGRAD_L_VM_PROLOG == 3 * kLPerWave, "vmcnt literals");
+
+typedef uint16_t LStage[kStage][kLTile];  // 32 rows x 256 columns, 16 KiB
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t raw_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = static_cast<int32_t>(a & 0xFFFFFFFFu);
+  r[1] = static_cast<int32_t>((a >> 32) & 0xFFFFu);
+  r[2] = static_cast<int32_t>(num_records);
+  r[3] = static_cast<int32_t>(kRsrcWord3);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const char* lds_ptr_t;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));  // generic -> LDS address space
+}
+
+// One 1 KiB transfer: lane l's 16 bytes at rsrc + voff + soff land at
+// LDS[lds + 16 l]. Inline assembly, so that the compiler neither drops nor
+// reorders it and does not wait on it; the kernel waits with s_waitcnt vmcnt.
+__device__ __forceinline__ void dma16(uint32_t lds, i32x4_t rsrc, int32_t voff, int32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
+// LDS layout of a stage: row-major 32 x 512 bytes, with the 16-byte chunks of
+// row R permuted as chunk c -> c ^ swz(R). Without it, the transposing read
+// (4 lanes x 8 bytes from each of 4 consecutive rows 512 bytes apart) and the
+// 8-row X reads hit the same banks.
+#ifndef DET_WGRAD_SWZ_SHIFT
+#define DET_WGRAD_SWZ_SHIFT 1
+#endif
+__device__ __forceinline__ int swz(int row) { return DET_WGRAD_SWZ_SHIFT < 0 ? 0 : (row & 3) << DET_WGRAD_SWZ_SHIFT; }
+
+// Global byte offset (inside a stage's row pair) that lane l loads so that it
+// lands at LDS chunk l of a transfer: row 2i + l/32, physical chunk l % 32,
+// logical chunk (l % 32) ^ swz(row). Depends on the parity of i only.
+__device__ __forceinline__ int32_t dma_voff(int lane, int parity, int32_t krow, int col0) {
+  const int row = 2 * parity + (lane >> 5);
+  return (lane >> 5) * krow + (col0 + 8 * ((lane & 31) ^ swz(row))) * 2;
+}
+
+// This wave's transfers of stage `st`: transfer i covers rows 2i, 2i+1 of G
+// and of X. voff[p] is dma_voff for transfers of parity p.
+__device__ __forceinline__ void stage_dma(LStage& sa, LStage& sb, i32x4_t ra, i32x4_t rb, const int32_t (&voff_a)[2],
+                                          const int32_t (&voff_b)[2], int32_t krow_a, int32_t krow_b, int32_t st,
+                                          int wave) {
+#pragma unroll
+  for (int u = 0; u < kLPerWave / 2; ++u) {
+    const int i = wave * (kLPerWave / 2) + u;
+    dma16(lds_addr(&sa[2 * i][0]), ra, voff_a[u & 1], (st * kStage + 2 * i) * krow_a);
+  }
+#pragma unroll
+  for (int u = 0; u < kLPerWave / 2; ++u) {
+    const int i = wave * (kLPerWave / 2) + u;
+    dma16(lds_addr(&sb[2 * i][0]), rb, voff_b[u & 1], (st * kStage + 2 * i) * krow_b);
+  }
+}
+
+#define DET_WGRAD_L_SYNC(N)                                                         \
+  do {                                                                             \
+    asm volatile("s_waitcnt vmcnt(" DET_STR(N) ") lgkmcnt(0)" : : : "memory");     \
+    __builtin_amdgcn_s_barrier();                                                  \
+  } while (0)
+
+__device__ __forceinline__ u32x2_t tr_read(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) v4s_t* lp_t;
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp_t)(p)));
+}
+
+// Raw fragments of one 16-row block (rows row0 ..): a[2i], a[2i+1] are the
+// two 4-row halves of A fragment i (G columns gc + 32 i + lane % 32); b[e] is
+// X row row0 + 8 kg + e, columns xc + 4 r .. + 3.
+struct LFrag {
+  u32x2_t a[8];
+  u32x2_t b[8];
+};
+
+// Per-lane byte offsets inside a stage (row0 = 0) of the reads above; row0 =
+// 16 adds 16 * 512 bytes, since swz() depends on the row modulo 4 only.
+struct LOffs {
+  int a[4];  // A fragment i, first half (the second half is 4 rows = 2048 bytes on)
+  int b[4];  // X rows with row % 4 == e % 4 (rows 8 kg + e, e < 4; e + 4 adds 2048 bytes)
+};
+
+__device__ __forceinline__ LOffs lane_offsets(int lane, int gc, int xc) {
+  LOffs o;
+  const int g = lane >> 4, j = lane & 15;
+  const int ar = 8 * (g >> 1) + (j >> 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int col = gc + 16 * (g & 1) + 4 * (j & 3) + 32 * i;  // first of this lane's 4 columns
+    o.a[i] = ar * 512 + 16 * ((col >> 3) ^ swz(ar)) + 2 * (col & 7);
+  }
+  const int r = lane & 31, kg = lane >> 5;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = 8 * kg + e;
+    const int col = xc + 4 * r;
+    o.b[e] = row * 512 + 16 * ((col >> 3) ^ swz(row)) + 2 * (col & 7);
+  }
+  return o;
+}
+
+__device__ __forceinline__ void read_frag(const LStage& sa, const LStage& sb, int row0, const LOffs& o, LFrag& f) {
+  const char* pa = reinterpret_cast<const char*>(&sa[row0][0]);
+  const char* pb = reinterpret_cast<const char*>(&sb[row0][0]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.a[2 * i] = tr_read(reinterpret_cast<const uint16_t*>(pa + o.a[i]));
+    f.a[2 * i + 1] = tr_read(reinterpret_cast<const uint16_t*>(pa + o.a[i] + 4 * 512));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    f.b[e] = *reinterpret_cast<const u32x2_t*>(pb + o.b[e & 3] + (e >> 2) * 4 * 512);
+}
+
+// MFMAs of one block, ordered by X fragment so that each fragment's
+// transposes are needed only just before its first MFMA.
+__device__ __forceinline__ void mma_frag(const LFrag& f, f32x16_t (&acc)[4][4]) {
+  bf16x8_t fa[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4_t d;
+    d[0] = f.a[2 * i].x;
+    d[1] = f.a[2 * i].y;
+    d[2] = f.a[2 * i + 1].x;
+    d[3] = f.a[2 * i + 1].y;
+    fa[i] = __builtin_bit_cast(bf16x8_t, d);
+  }
+  const bf16x8_t fb[4] = {frag<0>(f.b), frag<1>(f.b), frag<2>(f.b), frag<3>(f.b)};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+}
+
+template <bool ATOMIC>
+__global__ __launch_bounds__(256) void wgrad_lds_kernel(WgradArgs p) {
+  __shared__ __attribute__((aligned(16))) LStage sa[kLStages];
+  __shared__ __attribute__((aligned(16))) LStage sb[kLStages];
+  int64_t uq;
+  int mt, nt;
+  if (!unit_of(p, blockIdx.x, uq, mt, nt)) return;
+  Split sp;
+  if (!split_by_size(p, uq, sp)) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = mt * kLTile, n0 = nt * kLTile;
+  // M is a multiple of 128, so a wave's 128 rows are all inside or all
+  // outside; a wave outside still runs the loop (its MFMAs read G columns past
+  // M and are discarded) so that no branch splits the MFMA schedule
+  const bool live = m0 + 128 * wm < p.M;
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[i][j][c] = 0.0f;
+
+  // Buffer resources cover the split's rows only: rows past its end read as
+  // zero (the zero padding of the last block); G columns past M of a row read
+  // the next row or zero and only feed waves that are not live.
+  const int32_t rows = sp.r1 - sp.r0;
+  const int32_t krow_a = static_cast<int32_t>(p.ldg * 2);
+  const int32_t krow_b = static_cast<int32_t>(p.ldx * 2);
+  const i32x4_t rsrc_a = raw_rsrc(p.G + static_cast<int64_t>(sp.r0) * p.ldg, static_cast<uint32_t>(rows * krow_a));
+  const i32x4_t rsrc_b = raw_rsrc(p.X + static_cast<int64_t>(sp.r0) * p.ldx, static_cast<uint32_t>(rows * krow_b));
+  const int32_t voff_a[2] = {dma_voff(lane, 0, krow_a, m0), dma_voff(lane, 1, krow_a, m0)};
+  const int32_t voff_b[2] = {dma_voff(lane, 0, krow_b, n0), dma_voff(lane, 1, krow_b, n0)};
+  const LOffs lo = lane_offsets(lane, 128 * wm, 128 * wn);
+
+#pragma unroll
+  for (int st = 0; st < kLStages; ++st) stage_dma(sa[st], sb[st], rsrc_a, rsrc_b, voff_a, voff_b, krow_a, krow_b, st, wave);
+  DET_WGRAD_L_SYNC(DET_WGRAD_L_VM_PROLOG);
+  // fragments of even blocks in fr[0], of odd blocks in fr[1]
+  LFrag fr[2];
+  read_frag(sa[0], sb[0], 0, lo, fr[0]);
+
+  // Four stages per iteration, so that every LDS stage is a compile-time
+  // index; only the MFMA blocks past the split end are skipped (in the last,
+  // partial iteration).
+#define DET_WGRAD_L_STAGE(SI, GUARD)                                                        \
+  {                                                                                         \
+    const int32_t s = s0 + (SI);                                                            \
+    read_frag(sa[(SI)], sb[(SI)], kBlk, lo, fr[1]);                                         \
+    if (!(GUARD) || s * kStage < rows) mma_frag(fr[0], acc);                                \
+    DET_WGRAD_L_SYNC(DET_WGRAD_L_VM_STEADY);                                                \
+    stage_dma(sa[(SI)], sb[(SI)], rsrc_a, rsrc_b, voff_a, voff_b, krow_a, krow_b, s + kLStages, wave); \
+    read_frag(sa[((SI) + 1) % kLStages], sb[((SI) + 1) % kLStages], 0, lo, fr[0]);          \
+    if (!(GUARD) || s * kStage + kBlk < rows) mma_frag(fr[1], acc);                         \
+  }
+  int32_t s0 = 0;
+  for (; (s0 + kLStages) * kStage <= rows; s0 += kLStages) {
+    DET_WGRAD_L_STAGE(0, false)
+    DET_WGRAD_L_STAGE(1, false)
+    DET_WGRAD_L_STAGE(2, false)
+    DET_WGRAD_L_STAGE(3, false)
+  }
+  if (s0 * kStage < rows) {
+    DET_WGRAD_L_STAGE(0, true)
+    DET_WGRAD_L_STAGE(1, true)
+    DET_WGRAD_L_STAGE(2, true)
+    DET_WGRAD_L_STAGE(3, true)
+  }
+#undef DET_WGRAD_L_STAGE
+  // transfers issued ahead of the last stage must land before the
+  // workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  if (!live) return;
+
+  // Epilogue: lane (r, kg), MFMA (i, j), accumulator c holds output
+  // m = m0 + 128 wm + 32 i + 8 (c/4) + 4 kg + c%4,  n = n0 + 128 wn + 4 r + j.
+  const int r = lane & 31, kg = lane >> 5;
+  const bool direct = sp.n_split == 1;
+  float* dst_base;
+  int64_t ld_m;
+  if (ATOMIC || direct) {
+    dst_base = p.mg + sp.e * p.ld_e;
+    ld_m = p.ld_m;
+  } else {
+    dst_base = p.scratch + sp.g * static_cast<int64_t>(p.M) * p.N;
+    ld_m = p.N;
+  }
+  const int nc = n0 + 128 * wn + 4 * r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int m = m0 + 128 * wm + 32 * i + 8 * (c / 4) + 4 * kg + (c % 4);
+      float* d = dst_base + static_cast<int64_t>(m) * ld_m + nc;
+      const float v0 = acc[i][0][c], v1 = acc[i][1][c], v2 = acc[i][2][c], v3 = acc[i][3][c];
+      if (ATOMIC) {
+        unsafeAtomicAdd(d + 0, v0);
+        unsafeAtomicAdd(d + 1, v1);
+        unsafeAtomicAdd(d + 2, v2);
+        unsafeAtomicAdd(d + 3, v3);
+      } else if (direct) {
+        float4 o = *reinterpret_cast<const float4*>(d);
+        o.x = o.x + v0; o.y = o.y + v1; o.z = o.z + v2; o.w = o.w + v3;
+        *reinterpret_cast<float4*>(d) = o;
+      } else {
+        *reinterpret_cast<float4*>(d) = make_float4(v0, v1, v2, v3);
+      }
+      if (c % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Fold of multi-split experts: main_grad[e] += ((Q0 + Q1) + ...) elementwise.
 __global__ __launch_bounds__(256) void wgrad_fold_kernel(WgradArgs p) {
   const int64_t per_e = static_cast<int64_t>(p.M) * p.N / 4;  // float4 per expert
@@ -476,9 +784,11 @@ constexpr int kDefaultBlockN = 256;
 int resolve(const det_wgrad_cfg* cfg, det_wgrad_cfg* out) {
   det_wgrad_cfg c{kTileM, kDefaultBlockN, kKTile, 0};
   if (cfg) c = *cfg;
-  if (c.block_m != kTileM || (c.block_n != 256 && c.block_n != 512))
-    return set_error(DET_ERR_UNSUPPORTED, "wgrad: block_m x block_n must be %d x 256 or %d x 512, got %d x %d", kTileM,
-                     kTileM, c.block_m, c.block_n);
+  const bool shape_ok = (c.block_m == 128 && (c.block_n == 256 || c.block_n == 512)) ||
+                        (c.block_m == kLTile && c.block_n == kLTile);
+  if (!shape_ok)
+    return set_error(DET_ERR_UNSUPPORTED, "wgrad: block_m x block_n must be 128 x 256, 128 x 512 or 256 x 256, got %d x %d",
+                     c.block_m, c.block_n);
   if (c.k_tile != kKTile) return set_error(DET_ERR_INVALID_ARG, "wgrad: k_tile must be %d, got %d", kKTile, c.k_tile);
   if (c.ktiles_per_split < 0 || c.ktiles_per_split > (1 << 20))
     return set_error(DET_ERR_INVALID_ARG, "wgrad: ktiles_per_split must be in [0, 2^20], got %d", c.ktiles_per_split);
@@ -566,15 +876,20 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
   p.M = static_cast<int>(M);
   p.N = static_cast<int>(N);
   p.split_rows = c.ktiles_per_split == 0 ? 0 : c.k_tile * c.ktiles_per_split;
-  p.tiles_m = static_cast<int>(M / kTileM);
+  p.tiles_m = static_cast<int>((M + c.block_m - 1) / c.block_m);
   p.tiles_n = static_cast<int>(N / c.block_n);
   p.max_splits = max_splits(T_total, E, c);
-  p.n_units = wgrad_grid(p.tiles_m, p.tiles_n, p.max_splits);
+  plan_xcds(p, c.block_m, c.block_n);
   p.scratch = (atomic || sb == 0) ? nullptr : reinterpret_cast<float*>(static_cast<char*>(ws) + DET_WS_HEADER_BYTES);
   if (p.n_units > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "wgrad: too many work units");
   const hipStream_t st = as_stream(stream);
   const dim3 grid(static_cast<uint32_t>(p.n_units));
-  if (c.block_n == 512) {
+  if (c.block_m == kLTile) {
+    if (atomic)
+      hipLaunchKernelGGL((wgrad_lds_kernel<true>), grid, dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((wgrad_lds_kernel<false>), grid, dim3(256), 0, st, p);
+  } else if (c.block_n == 512) {
     if (atomic)
       hipLaunchKernelGGL((wgrad_kernel<4, true>), grid, dim3(256), 0, st, p);
     else

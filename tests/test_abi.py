@@ -177,6 +177,9 @@ def test_wgrad_validation():
     assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 768, None, 0, ctypes.byref(n)) == dg.DET_OK
     assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 768, ctypes.byref(wide), 0, ctypes.byref(n)) == \
         dg.DET_ERR_UNSUPPORTED
+    square = dg.WgradCfg(256, 256, 512, 0)
+    assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 384, 768, ctypes.byref(square), 0, ctypes.byref(n)) == \
+        dg.DET_OK
     odd = dg.WgradCfg(128, 384, 512, 0)
     assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 768, ctypes.byref(odd), 0, ctypes.byref(n)) == \
         dg.DET_ERR_UNSUPPORTED

@@ -27,18 +27,21 @@ pytestmark = pytest.mark.gpu
 M_, N_ = 256, 512  # small shapes: 2 x 2 workgroup tiles
 
 
-def cfg(C, block_n=512):
-    return dg.WgradCfg(128, block_n, 512, C)
+TILES = [(128, 256), (128, 512), (256, 256)]
 
 
-def run(inp, C=0, atomic=False, mg0=None, offs=None, G=None, X=None, block_n=512):
+def cfg(C, block_n=512, block_m=128):
+    return dg.WgradCfg(block_m, block_n, 512, C)
+
+
+def run(inp, C=0, atomic=False, mg0=None, offs=None, G=None, X=None, block_n=512, block_m=128):
     import torch
     Gd = dev_bf16(inp.G) if G is None else G
     Xd = dev_bf16(inp.X) if X is None else X
     mg = dev_f32(inp.main_grad0 if mg0 is None else mg0)
     o = dev_i32(inp.offs if offs is None else offs)
     torch.cuda.synchronize()
-    dg.det_grouped_wgrad_acc(mg, Gd, Xd, o, cfg=cfg(C, block_n), atomic=atomic)
+    dg.det_grouped_wgrad_acc(mg, Gd, Xd, o, cfg=cfg(C, block_n, block_m), atomic=atomic)
     return host(mg)
 
 
@@ -88,16 +91,28 @@ def test_fold_of_gpu_partials_matches_oracle(C):
 
 
 @pytest.mark.parametrize("C", [0, 1])
-def test_tile_width_does_not_change_bits(C):
-    """The 128 x 256 and 128 x 512 workgroup tiles give the same bits (the tile only shapes the launch)."""
-    inp = W.wgrad_inputs(E=5, M=M_, N=1024, tokens=[1500, 0, 33, 2049, 640], seed=8, out_init="normal")
+def test_tile_shape_does_not_change_bits(C):
+    """128x256, 128x512 and 256x256 workgroup tiles give the same bits (the tile only shapes the launch).
+
+    M = 384 leaves the 256-row tile a 128-row tail, whose second half of waves has no rows.
+    """
+    inp = W.wgrad_inputs(E=5, M=384, N=1024, tokens=[1500, 0, 33, 2049, 640], seed=8, out_init="normal")
     G, X = dev_bf16(inp.G), dev_bf16(inp.X)
-    wide = run(inp, C, G=G, X=X, block_n=512)
-    narrow = run(inp, C, G=G, X=X, block_n=256)
-    note("wgrad C=%d: 128x512 vs 128x256 tiles" % C)
-    assert_bitwise(narrow, wide, "tile width")
+    outs = [run(inp, C, G=G, X=X, block_m=bm, block_n=bn) for bm, bn in TILES]
+    note("wgrad C=%d: tiles %s" % (C, TILES))
+    for (bm, bn), o in zip(TILES[1:], outs[1:]):
+        assert_bitwise(o, outs[0], "tile %dx%d" % (bm, bn))
     ex = fp64.wgrad64(inp.main_grad0, inp.G, inp.X, inp.offs)
-    assert rel_l2(wide - inp.main_grad0, ex - inp.main_grad0) <= 1e-5
+    assert rel_l2(outs[0] - inp.main_grad0, ex - inp.main_grad0) <= 1e-5
+
+
+@pytest.mark.parametrize("bm,bn", TILES)
+def test_exact_integer_inputs_every_tile(bm, bn):
+    inp = W.wgrad_inputs(E=4, M=384, N=512, tokens=[700, 0, 1300, 17], seed=9, integer=True, out_init="normal")
+    note("wgrad exact integers tile %dx%d" % (bm, bn))
+    got = run(inp, 0, block_m=bm, block_n=bn)
+    assert np.array_equal(got.astype(np.float64), fp64.wgrad64(inp.main_grad0, inp.G, inp.X, inp.offs))
+    assert_bitwise(got[1], inp.main_grad0[1], "empty expert")
 
 
 def test_partial_is_independent_of_position():
