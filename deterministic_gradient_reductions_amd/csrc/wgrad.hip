@@ -461,193 +461,167 @@ __global__ __launch_bounds__(64 * W) void wgrad_kernel(WgradArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// 256 x 256 workgroup tile, both operands through LDS.
+// 256 x 256 workgroup tile, operands transposed on their way into LDS.
 //
 // Four waves in a 2 x 2 arrangement each own a 128 x 128 quarter, so every G
-// column block and every X column block is shared by two waves. Both operands
-// reach LDS through 16-byte buffer loads that write LDS directly (one 1 KiB
-// transfer per instruction, no registers in flight), four stages of 32 token
-// rows, three in flight. At the matrix-core rate a CU then needs about half of
-// its texture-address throughput (which is set by instructions, not bytes)
-// and three quarters of its LDS read bandwidth, but direct-to-LDS writes run
-// at about half the LDS read rate, so this kernel is bound by its LDS traffic
-// (transfers plus fragment reads). A fragments come from LDS through
-// the transposing 8-byte read (ds_read_b64_tr_b16: each lane gets 4 token rows
-// of one G column); X fragments through plain 8-byte reads and v_perm_b32, so
-// that each lane keeps 4 consecutive output columns for float4 epilogue
-// access. Fragments of the next 16-row block are read while the current
-// block's MFMAs run.
+// column block and every X column block feeds two waves. A stage is 64 token
+// rows. Each of the 256 lanes loads an 8-row x 8-column block of G and one of
+// X (eight 16-byte loads each), turns each block around in registers with
+// v_perm_b32 into eight 16-byte vectors (8 consecutive token rows of one
+// column: exactly what one MFMA operand lane holds), and stores the vectors to
+// LDS with 16-byte writes. Every MFMA fragment is then a single 16-byte LDS
+// read per lane. Plain 16-byte LDS reads are the fastest LDS access on gfx950
+// (the transposing 8-byte read moves less than half as many bytes per clock),
+// and a 128 x 128 wave tile needs 64 bytes per clock per CU of fragment reads
+// at the matrix-core rate.
 //
-// Every load in the loop is one of these explicit transfers, issued the same
-// way on every path, so the vmcnt literals below count exactly: when stage s
-// waits for stage s+1, the transfers of stages s+2 and s+3 (8 per wave each)
-// may still be in flight.
-constexpr int kLTile = 256;
-constexpr int kLStages = 4;
-constexpr int kLPerWave = 8;  // transfers per wave and stage: 4 of G, 4 of X
-#define DET_WGRAD_L_VM_STEADY 16
-#define DET_WGRAD_L_VM_PROLOG 24
-#define DET_STR2(x) #x
-#define DET_STR(x) DET_STR2(x)
-static_assert(DET_WGRAD_L_VM_STEADY == 2 * kLPerWave && DET_WGRAD_L_VM_PROLOG == 3 * kLPerWave, "vmcnt literals");
+// LDS layout of one operand and stage: [k-group 8][column 256][8 rows] bf16,
+// the vector of column c stored at slot c ^ (((c >> 4) ^ ((c >> 1) & 4)) & 7)
+// (a permutation of the low three bits of c inside each group of 8). Every 8
+// consecutive lanes of a store (columns 8 apart) and of a fragment read (32
+// consecutive columns) then cover 8 distinct 16-byte bank groups, and every 16
+// consecutive lanes 16 distinct ones, so neither access has bank conflicts
+// whether the LDS serves a 16-byte access 8 or 16 lanes per pass.
+//
+// Pipeline: two LDS buffers per operand. While the MFMAs of stage s run from
+// one buffer, the loads of stage s+1 (issued right after the previous
+// barrier) land in registers, are transposed and written to the other buffer
+// after the stage's second block; one barrier per stage.
+constexpr int kTT = 256;                 // tile edge (m and n)
+constexpr int kTRows = 64;               // token rows per stage
+constexpr int kTGroups = kTRows / 8;     // 8-row k-groups per stage
+constexpr int kTGroupBytes = kTT * 16;   // bytes of one k-group of one operand
+typedef uint32_t TStage[kTGroups][kTT][4];  // 32 KiB
 
-typedef uint16_t LStage[kStage][kLTile];  // 32 rows x 256 columns, 16 KiB
-typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int tslot(int c) { return c ^ (((c >> 4) ^ ((c >> 1) & 4)) & 7); }
 
-__device__ __forceinline__ i32x4_t raw_rsrc(const void* base, uint32_t num_records) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = static_cast<int32_t>(a & 0xFFFFFFFFu);
-  r[1] = static_cast<int32_t>((a >> 32) & 0xFFFFu);
-  r[2] = static_cast<int32_t>(num_records);
-  r[3] = static_cast<int32_t>(kRsrcWord3);
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  typedef __attribute__((address_space(3))) const char* lds_ptr_t;
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));  // generic -> LDS address space
-}
-
-// One 1 KiB transfer: lane l's 16 bytes at rsrc + voff + soff land at
-// LDS[lds + 16 l]. Inline assembly, so that the compiler neither drops nor
-// reorders it and does not wait on it; the kernel waits with s_waitcnt vmcnt.
-__device__ __forceinline__ void dma16(uint32_t lds, i32x4_t rsrc, int32_t voff, int32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory");
-}
-
-// LDS layout of a stage: row-major 32 x 512 bytes, with the 16-byte chunks of
-// row R permuted as chunk c -> c ^ swz(R). Without it, the transposing read
-// (4 lanes x 8 bytes from each of 4 consecutive rows 512 bytes apart) and the
-// 8-row X reads hit the same banks.
-#ifndef DET_WGRAD_SWZ_SHIFT
-#define DET_WGRAD_SWZ_SHIFT 1
-#endif
-__device__ __forceinline__ int swz(int row) { return DET_WGRAD_SWZ_SHIFT < 0 ? 0 : (row & 3) << DET_WGRAD_SWZ_SHIFT; }
-
-// Global byte offset (inside a stage's row pair) that lane l loads so that it
-// lands at LDS chunk l of a transfer: row 2i + l/32, physical chunk l % 32,
-// logical chunk (l % 32) ^ swz(row). Depends on the parity of i only.
-__device__ __forceinline__ int32_t dma_voff(int lane, int parity, int32_t krow, int col0) {
-  const int row = 2 * parity + (lane >> 5);
-  return (lane >> 5) * krow + (col0 + 8 * ((lane & 31) ^ swz(row))) * 2;
-}
-
-// This wave's transfers of stage `st`: transfer i covers rows 2i, 2i+1 of G
-// and of X. voff[p] is dma_voff for transfers of parity p.
-__device__ __forceinline__ void stage_dma(LStage& sa, LStage& sb, i32x4_t ra, i32x4_t rb, const int32_t (&voff_a)[2],
-                                          const int32_t (&voff_b)[2], int32_t krow_a, int32_t krow_b, int32_t st,
-                                          int wave) {
-#pragma unroll
-  for (int u = 0; u < kLPerWave / 2; ++u) {
-    const int i = wave * (kLPerWave / 2) + u;
-    dma16(lds_addr(&sa[2 * i][0]), ra, voff_a[u & 1], (st * kStage + 2 * i) * krow_a);
-  }
-#pragma unroll
-  for (int u = 0; u < kLPerWave / 2; ++u) {
-    const int i = wave * (kLPerWave / 2) + u;
-    dma16(lds_addr(&sb[2 * i][0]), rb, voff_b[u & 1], (st * kStage + 2 * i) * krow_b);
-  }
-}
-
-#define DET_WGRAD_L_SYNC(N)                                                         \
-  do {                                                                             \
-    asm volatile("s_waitcnt vmcnt(" DET_STR(N) ") lgkmcnt(0)" : : : "memory");     \
-    __builtin_amdgcn_s_barrier();                                                  \
-  } while (0)
-
-__device__ __forceinline__ u32x2_t tr_read(const uint16_t* p) {
-  typedef __attribute__((address_space(3))) v4s_t* lp_t;
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp_t)(p)));
-}
-
-// Raw fragments of one 16-row block (rows row0 ..): a[2i], a[2i+1] are the
-// two 4-row halves of A fragment i (G columns gc + 32 i + lane % 32); b[e] is
-// X row row0 + 8 kg + e, columns xc + 4 r .. + 3.
-struct LFrag {
-  u32x2_t a[8];
-  u32x2_t b[8];
-};
-
-// Per-lane byte offsets inside a stage (row0 = 0) of the reads above; row0 =
-// 16 adds 16 * 512 bytes, since swz() depends on the row modulo 4 only.
-struct LOffs {
-  int a[4];  // A fragment i, first half (the second half is 4 rows = 2048 bytes on)
-  int b[4];  // X rows with row % 4 == e % 4 (rows 8 kg + e, e < 4; e + 4 adds 2048 bytes)
-};
-
-__device__ __forceinline__ LOffs lane_offsets(int lane, int gc, int xc) {
-  LOffs o;
-  const int g = lane >> 4, j = lane & 15;
-  const int ar = 8 * (g >> 1) + (j >> 2);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int col = gc + 16 * (g & 1) + 4 * (j & 3) + 32 * i;  // first of this lane's 4 columns
-    o.a[i] = ar * 512 + 16 * ((col >> 3) ^ swz(ar)) + 2 * (col & 7);
-  }
-  const int r = lane & 31, kg = lane >> 5;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = 8 * kg + e;
-    const int col = xc + 4 * r;
-    o.b[e] = row * 512 + 16 * ((col >> 3) ^ swz(row)) + 2 * (col & 7);
-  }
-  return o;
-}
-
-__device__ __forceinline__ void read_frag(const LStage& sa, const LStage& sb, int row0, const LOffs& o, LFrag& f) {
-  const char* pa = reinterpret_cast<const char*>(&sa[row0][0]);
-  const char* pb = reinterpret_cast<const char*>(&sb[row0][0]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f.a[2 * i] = tr_read(reinterpret_cast<const uint16_t*>(pa + o.a[i]));
-    f.a[2 * i + 1] = tr_read(reinterpret_cast<const uint16_t*>(pa + o.a[i] + 4 * 512));
-  }
+// Stage s of one operand: lane rows 8 rg .. 8 rg + 7 (relative to the split
+// start), columns 8 c8 .. 8 c8 + 7 of the tile (voff holds both).
+__device__ __forceinline__ void t_load(u32x4_t (&v)[8], __amdgpu_buffer_rsrc_t rsrc, int32_t voff, int32_t krow,
+                                       int32_t s) {
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    f.b[e] = *reinterpret_cast<const u32x2_t*>(pb + o.b[e & 3] + (e >> 2) * 4 * 512);
+    v[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, (s * kTRows + e) * krow, 0));
 }
 
-// MFMAs of one block, ordered by X fragment so that each fragment's
-// transposes are needed only just before its first MFMA.
-__device__ __forceinline__ void mma_frag(const LFrag& f, f32x16_t (&acc)[4][4]) {
-  bf16x8_t fa[4];
+// v[e] holds row e, dword q = columns 2q (low half) and 2q + 1 (high half).
+// Column i's vector: dword q = rows 2q (low half) and 2q + 1 (high half).
+__device__ __forceinline__ void t_store(TStage& st, const u32x4_t (&v)[8], int rg, int c8) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+    u32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(v[2 * q + 1][i >> 1], v[2 * q][i >> 1], sel);
+    *reinterpret_cast<u32x4_t*>(&st[rg][tslot(8 * c8 + i)][0]) = o;
+  }
+}
+
+struct TFrag {
+  bf16x8_t a[4];
+  bf16x8_t b[4];
+};
+
+// Fragments of 16-row block `blk` of the stage pair at `base` (A at base,
+// B one stage further): lane (r, kg) reads k-group 2 blk + kg of columns
+// 32 i + r of its quarter (offsets precomputed, B's include the stage size).
+__device__ __forceinline__ void t_frag(const char* base, int blk, const int (&oa)[4], const int (&ob)[4], TFrag& f) {
+  const char* pb = base + blk * 2 * kTGroupBytes;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    u32x4_t d;
-    d[0] = f.a[2 * i].x;
-    d[1] = f.a[2 * i].y;
-    d[2] = f.a[2 * i + 1].x;
-    d[3] = f.a[2 * i + 1].y;
-    fa[i] = __builtin_bit_cast(bf16x8_t, d);
+    f.a[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(pb + oa[i]));
+    f.b[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(pb + ob[i]));
   }
-  const bf16x8_t fb[4] = {frag<0>(f.b), frag<1>(f.b), frag<2>(f.b), frag<3>(f.b)};
+}
+
+__device__ __forceinline__ void t_mma(const TFrag& f, f32x16_t (&acc)[4][4]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Epilogue of one wave: lane (r, kg), MFMA (i, j), accumulator c holds output
+// row m = mw + 32 i + 8 (c/4) + 4 kg + c%4 and column n = nw + 32 j + r, so a
+// wave instruction covers two 128-byte row segments. MODE 0 adds into the
+// destination (one rounding per element), 1 stores, 2 adds with float
+// atomics. Each quarter i moves 64 values per lane with all loads in flight.
+template <int MODE>
+__device__ __forceinline__ void t_epilogue(float* dst, int64_t ld, int mw, int nw, int r, int kg,
+                                           const f32x16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float* row0 = dst + static_cast<int64_t>(mw + 32 * i + 4 * kg) * ld + nw + r;
+    if (MODE == 0) {
+      float v[16][4];
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[c][j] = row0[static_cast<int64_t>(8 * (c / 4) + (c % 4)) * ld + 32 * j];
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          row0[static_cast<int64_t>(8 * (c / 4) + (c % 4)) * ld + 32 * j] = v[c][j] + acc[i][j][c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float* d = row0 + static_cast<int64_t>(8 * (c / 4) + (c % 4)) * ld + 32 * j;
+          if (MODE == 1)
+            *d = acc[i][j][c];
+          else
+            unsafeAtomicAdd(d, acc[i][j][c]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Transpose and store column i (0..7) of a lane's 8 x 8 block into the stage
+// at `st` (see t_store).
+__device__ __forceinline__ void t_store_col(char* st, const u32x4_t (&v)[8], int rg, int c8, int i) {
+  const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+  u32x4_t o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(v[2 * q + 1][i >> 1], v[2 * q][i >> 1], sel);
+  *reinterpret_cast<u32x4_t*>(st + (rg * kTT + tslot(8 * c8 + i)) * 16) = o;
+}
+
+// Fragment q of block `blk` (q < 4: A fragment q, else B fragment q - 4).
+__device__ __forceinline__ void t_frag1(const char* base, int blk, const int (&oa)[4], const int (&ob)[4], int q,
+                                        TFrag& f) {
+  const char* pb = base + blk * 2 * kTGroupBytes;
+  if (q < 4)
+    f.a[q] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(pb + oa[q]));
+  else
+    f.b[q - 4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(pb + ob[q - 4]));
+}
+
+__device__ __forceinline__ void t_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
 }
 
 template <bool ATOMIC>
-__global__ __launch_bounds__(256) void wgrad_lds_kernel(WgradArgs p) {
-  __shared__ __attribute__((aligned(16))) LStage sa[kLStages];
-  __shared__ __attribute__((aligned(16))) LStage sb[kLStages];
+__global__ __launch_bounds__(256) void wgrad_tl_kernel(WgradArgs p) {
+  // [stage buffer 2][operand 2]: A (G) of buffer b at 2b, B (X) at 2b + 1
+  __shared__ __attribute__((aligned(16))) TStage lds[4];
   int64_t uq;
   int mt, nt;
   if (!unit_of(p, blockIdx.x, uq, mt, nt)) return;
   Split sp;
   if (!split_by_size(p, uq, sp)) return;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = mt * kLTile, n0 = nt * kLTile;
+  const int m0 = mt * kTT, n0 = nt * kTT;
   // M is a multiple of 128, so a wave's 128 rows are all inside or all
-  // outside; a wave outside still runs the loop (its MFMAs read G columns past
-  // M and are discarded) so that no branch splits the MFMA schedule
+  // outside M. A wave outside runs the same program (its MFMAs read G
+  // columns past M and are discarded), so that the workgroup stays in step
+  // and no branch splits the MFMA schedule; it stores nothing.
   const bool live = m0 + 128 * wm < p.M;
 
   f32x16_t acc[4][4];
@@ -659,91 +633,112 @@ __global__ __launch_bounds__(256) void wgrad_lds_kernel(WgradArgs p) {
       for (int c = 0; c < 16; ++c) acc[i][j][c] = 0.0f;
 
   // Buffer resources cover the split's rows only: rows past its end read as
-  // zero (the zero padding of the last block); G columns past M of a row read
-  // the next row or zero and only feed waves that are not live.
+  // zero (the zero padding of the last block). G columns past M (the last
+  // m tile when M % 256 == 128) read the next row or zero and only feed the
+  // waves that are not live.
   const int32_t rows = sp.r1 - sp.r0;
   const int32_t krow_a = static_cast<int32_t>(p.ldg * 2);
   const int32_t krow_b = static_cast<int32_t>(p.ldx * 2);
-  const i32x4_t rsrc_a = raw_rsrc(p.G + static_cast<int64_t>(sp.r0) * p.ldg, static_cast<uint32_t>(rows * krow_a));
-  const i32x4_t rsrc_b = raw_rsrc(p.X + static_cast<int64_t>(sp.r0) * p.ldx, static_cast<uint32_t>(rows * krow_b));
-  const int32_t voff_a[2] = {dma_voff(lane, 0, krow_a, m0), dma_voff(lane, 1, krow_a, m0)};
-  const int32_t voff_b[2] = {dma_voff(lane, 0, krow_b, n0), dma_voff(lane, 1, krow_b, n0)};
-  const LOffs lo = lane_offsets(lane, 128 * wm, 128 * wn);
-
-#pragma unroll
-  for (int st = 0; st < kLStages; ++st) stage_dma(sa[st], sb[st], rsrc_a, rsrc_b, voff_a, voff_b, krow_a, krow_b, st, wave);
-  DET_WGRAD_L_SYNC(DET_WGRAD_L_VM_PROLOG);
-  // fragments of even blocks in fr[0], of odd blocks in fr[1]
-  LFrag fr[2];
-  read_frag(sa[0], sb[0], 0, lo, fr[0]);
-
-  // Four stages per iteration, so that every LDS stage is a compile-time
-  // index; only the MFMA blocks past the split end are skipped (in the last,
-  // partial iteration).
-#define DET_WGRAD_L_STAGE(SI, GUARD)                                                        \
-  {                                                                                         \
-    const int32_t s = s0 + (SI);                                                            \
-    read_frag(sa[(SI)], sb[(SI)], kBlk, lo, fr[1]);                                         \
-    if (!(GUARD) || s * kStage < rows) mma_frag(fr[0], acc);                                \
-    DET_WGRAD_L_SYNC(DET_WGRAD_L_VM_STEADY);                                                \
-    stage_dma(sa[(SI)], sb[(SI)], rsrc_a, rsrc_b, voff_a, voff_b, krow_a, krow_b, s + kLStages, wave); \
-    read_frag(sa[((SI) + 1) % kLStages], sb[((SI) + 1) % kLStages], 0, lo, fr[0]);          \
-    if (!(GUARD) || s * kStage + kBlk < rows) mma_frag(fr[1], acc);                         \
-  }
-  int32_t s0 = 0;
-  for (; (s0 + kLStages) * kStage <= rows; s0 += kLStages) {
-    DET_WGRAD_L_STAGE(0, false)
-    DET_WGRAD_L_STAGE(1, false)
-    DET_WGRAD_L_STAGE(2, false)
-    DET_WGRAD_L_STAGE(3, false)
-  }
-  if (s0 * kStage < rows) {
-    DET_WGRAD_L_STAGE(0, true)
-    DET_WGRAD_L_STAGE(1, true)
-    DET_WGRAD_L_STAGE(2, true)
-    DET_WGRAD_L_STAGE(3, true)
-  }
-#undef DET_WGRAD_L_STAGE
-  // transfers issued ahead of the last stage must land before the
-  // workgroup's LDS is released
-  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-  if (!live) return;
-
-  // Epilogue: lane (r, kg), MFMA (i, j), accumulator c holds output
-  // m = m0 + 128 wm + 32 i + 8 (c/4) + 4 kg + c%4,  n = n0 + 128 wn + 4 r + j.
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.G + static_cast<int64_t>(sp.r0) * p.ldg), 0, rows * krow_a, static_cast<int>(kRsrcWord3));
+  const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.X + static_cast<int64_t>(sp.r0) * p.ldx), 0, rows * krow_b, static_cast<int>(kRsrcWord3));
+  const int c8 = t & 31, rg = t >> 5;
+  const int32_t voff_a = rg * 8 * krow_a + (m0 + 8 * c8) * 2;
+  const int32_t voff_b = rg * 8 * krow_b + (n0 + 8 * c8) * 2;
   const int r = lane & 31, kg = lane >> 5;
-  const bool direct = sp.n_split == 1;
-  float* dst_base;
-  int64_t ld_m;
-  if (ATOMIC || direct) {
-    dst_base = p.mg + sp.e * p.ld_e;
-    ld_m = p.ld_m;
-  } else {
-    dst_base = p.scratch + sp.g * static_cast<int64_t>(p.M) * p.N;
-    ld_m = p.N;
-  }
-  const int nc = n0 + 128 * wn + 4 * r;
+  int oa[4], ob[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int m = m0 + 128 * wm + 32 * i + 8 * (c / 4) + 4 * kg + (c % 4);
-      float* d = dst_base + static_cast<int64_t>(m) * ld_m + nc;
-      const float v0 = acc[i][0][c], v1 = acc[i][1][c], v2 = acc[i][2][c], v3 = acc[i][3][c];
-      if (ATOMIC) {
-        unsafeAtomicAdd(d + 0, v0);
-        unsafeAtomicAdd(d + 1, v1);
-        unsafeAtomicAdd(d + 2, v2);
-        unsafeAtomicAdd(d + 3, v3);
-      } else if (direct) {
-        float4 o = *reinterpret_cast<const float4*>(d);
-        o.x = o.x + v0; o.y = o.y + v1; o.z = o.z + v2; o.w = o.w + v3;
-        *reinterpret_cast<float4*>(d) = o;
-      } else {
-        *reinterpret_cast<float4*>(d) = make_float4(v0, v1, v2, v3);
-      }
-      if (c % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-    }
+    oa[i] = kg * kTGroupBytes + tslot(128 * wm + 32 * i + r) * 16;
+    ob[i] = static_cast<int>(sizeof(TStage)) + kg * kTGroupBytes + tslot(128 * wn + 32 * i + r) * 16;
+  }
+  char* const lbase = reinterpret_cast<char*>(&lds[0][0][0][0]);
+  constexpr int kPair = 2 * static_cast<int>(sizeof(TStage));
+  constexpr int kOpB = static_cast<int>(sizeof(TStage));
+
+  // Stage k's rows live in register set k & 1 from their loads until their
+  // transposition, which happens during stage k - 1: loads are issued about
+  // two stages ahead of their use.
+  u32x4_t ra[2][8], rb[2][8];
+  t_load(ra[0], rsrc_a, voff_a, krow_a, 0);
+  t_load(rb[0], rsrc_b, voff_b, krow_b, 0);
+  t_load(ra[1], rsrc_a, voff_a, krow_a, 1);
+  t_load(rb[1], rsrc_b, voff_b, krow_b, 1);
+  t_store(lds[0], ra[0], rg, c8);
+  t_store(lds[1], rb[0], rg, c8);
+  t_load(ra[0], rsrc_a, voff_a, krow_a, 2);
+  t_load(rb[0], rsrc_b, voff_b, krow_b, 2);
+  __syncthreads();
+
+  TFrag fb[2];
+  t_frag(lbase, 0, oa, ob, fb[0]);
+
+  // Full stages (all four blocks inside the split). The 64 MFMAs of stage s
+  // are issue slots k = 0..63 (block k / 16, MFMA (i, j) = (k % 16 / 4,
+  // k % 4)); the other work of the stage is spread over them so that the
+  // matrix pipe never waits for it:
+  //   slots 16b .. 16b+7 (b < 3): the 8 fragments of block b + 1
+  //   odd slots 1 .. 15: G columns of stage s + 1 (registers) -> the other
+  //                      buffer (every wave finished reading it before the
+  //                      previous barrier); odd slots 17 .. 31: X columns
+  //   slots 16, 20, .. 44: G loads of stage s + 3 into the registers just
+  //                        freed; slots 34, 38, .. 62: X loads (one load
+  //                        per two slots, so the memory pipe never backs up
+  //                        into the instruction stream)
+  //   slot 51: barrier (every wave has written the other buffer and read
+  //            the last fragments of this one)
+  //   slots 52 .. 59: the fragments of block 0 of stage s + 1
+  // Scheduling fences between slots keep this order.
+#define DET_WGRAD_T_STAGE(P)                                                                                    \
+  {                                                                                                             \
+    const int cur = (P) * kPair;                                                                                \
+    const int nxt = kPair - cur;                                                                                \
+    _Pragma("unroll") for (int k = 0; k < 64; ++k) {                                                            \
+      const int b = k / 16, q = k % 16;                                                                         \
+      acc[q / 4][q % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[b & 1].a[q / 4], fb[b & 1].b[q % 4],       \
+                                                                  acc[q / 4][q % 4], 0, 0, 0);                  \
+      if (b < 3 && q < 8) t_frag1(lbase + cur, b + 1, oa, ob, q, fb[(b + 1) & 1]);                              \
+      if (k < 16 && (k & 1)) t_store_col(lbase + nxt, ra[(P) ^ 1], rg, c8, k >> 1);                            \
+      if (k >= 16 && k < 32 && (k & 1)) t_store_col(lbase + nxt + kOpB, rb[(P) ^ 1], rg, c8, (k - 16) >> 1);   \
+      if (k >= 16 && k < 48 && (k % 4) == 0)                                                                    \
+        ra[(P) ^ 1][(k - 16) / 4] = __builtin_bit_cast(                                                         \
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a, ((s + 3) * kTRows + (k - 16) / 4) * krow_a, 0)); \
+      if (k >= 34 && (k % 4) == 2)                                                                              \
+        rb[(P) ^ 1][(k - 34) / 4] = __builtin_bit_cast(                                                         \
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, ((s + 3) * kTRows + (k - 34) / 4) * krow_b, 0)); \
+      if (k == 51) t_sync();                                                                                    \
+      if (k >= 52 && k < 60) t_frag1(lbase + nxt, 0, oa, ob, k - 52, fb[0]);                                    \
+      __builtin_amdgcn_sched_barrier(0);                                                                        \
+    }                                                                                                           \
+    ++s;                                                                                                        \
+  }
+  int s = 0;
+  const int full = rows / kTRows;
+  while (s + 1 < full) {
+    DET_WGRAD_T_STAGE(0)
+    DET_WGRAD_T_STAGE(1)
+  }
+  if (s < full) DET_WGRAD_T_STAGE(0)
+#undef DET_WGRAD_T_STAGE
+  // Last, partial stage: blocks inside the split only.
+  if (s * kTRows < rows) {
+    const int cur = (s & 1) * kPair;
+    const int nb = (rows - s * kTRows + kBlk - 1) / kBlk;
+    t_mma(fb[0], acc);
+    if (nb > 1) { t_frag(lbase + cur, 1, oa, ob, fb[1]); t_mma(fb[1], acc); }
+    if (nb > 2) { t_frag(lbase + cur, 2, oa, ob, fb[0]); t_mma(fb[0], acc); }
+    if (nb > 3) { t_frag(lbase + cur, 3, oa, ob, fb[1]); t_mma(fb[1], acc); }
+  }
+  if (!live) return;
+
+  const int mw = m0 + 128 * wm, nw = n0 + 128 * wn;
+  if (ATOMIC) {
+    t_epilogue<2>(p.mg + sp.e * p.ld_e, p.ld_m, mw, nw, r, kg, acc);
+  } else if (sp.n_split == 1) {
+    t_epilogue<0>(p.mg + sp.e * p.ld_e, p.ld_m, mw, nw, r, kg, acc);
+  } else {
+    t_epilogue<1>(p.scratch + sp.g * static_cast<int64_t>(p.M) * p.N, p.N, mw, nw, r, kg, acc);
   }
 }
 
@@ -779,13 +774,11 @@ __global__ __launch_bounds__(256) void wgrad_fold_kernel(WgradArgs p) {
   *reinterpret_cast<float4*>(d) = o;
 }
 
-constexpr int kDefaultBlockN = 256;
-
 int resolve(const det_wgrad_cfg* cfg, det_wgrad_cfg* out) {
-  det_wgrad_cfg c{kTileM, kDefaultBlockN, kKTile, 0};
+  det_wgrad_cfg c{kTT, kTT, kKTile, 0};
   if (cfg) c = *cfg;
   const bool shape_ok = (c.block_m == 128 && (c.block_n == 256 || c.block_n == 512)) ||
-                        (c.block_m == kLTile && c.block_n == kLTile);
+                        (c.block_m == kTT && c.block_n == kTT);
   if (!shape_ok)
     return set_error(DET_ERR_UNSUPPORTED, "wgrad: block_m x block_n must be 128 x 256, 128 x 512 or 256 x 256, got %d x %d",
                      c.block_m, c.block_n);
@@ -884,11 +877,11 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
   if (p.n_units > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "wgrad: too many work units");
   const hipStream_t st = as_stream(stream);
   const dim3 grid(static_cast<uint32_t>(p.n_units));
-  if (c.block_m == kLTile) {
+  if (c.block_m == kTT) {
     if (atomic)
-      hipLaunchKernelGGL((wgrad_lds_kernel<true>), grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL((wgrad_tl_kernel<true>), grid, dim3(256), 0, st, p);
     else
-      hipLaunchKernelGGL((wgrad_lds_kernel<false>), grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL((wgrad_tl_kernel<false>), grid, dim3(256), 0, st, p);
   } else if (c.block_n == 512) {
     if (atomic)
       hipLaunchKernelGGL((wgrad_kernel<4, true>), grid, dim3(256), 0, st, p);

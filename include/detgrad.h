@@ -200,10 +200,10 @@ int det_grouped_dprob(float* dprob, const void* dY, int64_t ldy, const void* C, 
  * ldx, ld_m and ld_e keep every row 16-byte aligned, as do G, X and
  * main_grad; T_total < 2^30 and (T_total + 512) * max(ldg, ldx) * 2 < 2^31
  * (32-bit buffer offsets). Otherwise DET_ERR_UNSUPPORTED.
- * cfg:  NULL selects {block_m = 128, block_n = 256, k_tile = 512,
- *       ktiles_per_split = 0}; block_m must be 128, block_n 256 or 512 (the
- *       tile only shapes the launch: both give the same bits), k_tile 512,
- *       ktiles_per_split in [0, 2^20].
+ * cfg:  NULL selects {block_m = 256, block_n = 256, k_tile = 512,
+ *       ktiles_per_split = 0}; block_m x block_n must be 256 x 256, 128 x 256
+ *       or 128 x 512 (the tile only shapes the launch: all give the same
+ *       bits), k_tile 512, ktiles_per_split in [0, 2^20].
  * ws:   ktiles_per_split = 0 keeps each expert's partial in registers and
  *       needs no workspace (size 0); otherwise the 256-byte header plus one
  *       [M, N] float32 slot per possible split, ceil(T_total / (512 C)) + E
