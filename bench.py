@@ -260,10 +260,14 @@ def main():
     import torch
     torch.cuda.init()
     wls = build_workloads()
-    flush_buf = torch.empty(1024 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    # Cold cache: read a 1 GiB buffer (4x the 256 MB last-level cache) between
+    # timed runs. A read leaves only clean lines behind, so the timed kernel
+    # pays no write-back of someone else's dirty data.
+    flush_buf = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def flush():
-        flush_buf.fill_(1.0)
+        torch.sum(flush_buf, dim=0, out=flush_sink)
 
     log("workloads ready: %s" % [w.name for w in wls])
     stream = torch.cuda.current_stream()

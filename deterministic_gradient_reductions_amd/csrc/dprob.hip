@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kWG) void dprob_atomic_kernel(float* __restrict__ d
 }
 
 int check_cfg(const det_dprob_cfg* cfg, det_dprob_cfg* out) {
-  det_dprob_cfg c{kTileN, 16};
+  det_dprob_cfg c{kTileN, 4};
   if (cfg) c = *cfg;
   if (c.tile_n != kTileN) return set_error(DET_ERR_INVALID_ARG, "dprob: tile_n must be %d, got %d", kTileN, c.tile_n);
   if (c.rows_per_wg < 1 || c.rows_per_wg > 1024)

@@ -39,7 +39,7 @@ constexpr int kMaxDim = 512;
 constexpr int kSegBlocks = 32;   // blocks per prefix segment
 
 struct Layout {
-  size_t hist, segtot, count, seg_off, chunk_off, perm, scratch, total;
+  size_t hist, segtot, count, seg_off, chunk_off, chunk_desc, perm, scratch, total;
   int64_t nblk, nseg, max_chunks;
 };
 
@@ -54,6 +54,7 @@ Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L) {
   l.count = o;     o = align_up(o + static_cast<size_t>(n_rows) * 4, 256);
   l.seg_off = o;   o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
   l.chunk_off = o; o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
+  l.chunk_desc = o; o = align_up(o + static_cast<size_t>(l.max_chunks) * 16, 256);
   l.perm = o;      o = align_up(o + static_cast<size_t>(n_src) * 4, 256);
   l.scratch = o;   o = align_up(o + static_cast<size_t>(l.max_chunks * dim) * 4, 256);
   l.total = o;
@@ -61,29 +62,33 @@ Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L) {
 }
 
 // Lanes of one wave holding the same id find each other with one ballot per
-// id bit; returns the mask of those lanes (0 for invalid lanes).
-__device__ __forceinline__ uint64_t match_peers(int32_t id, bool valid, int id_bits) {
+// id bit (ids are below 2^14); returns the mask of those lanes (0 for invalid
+// lanes). Invalid lanes are never in a mask: the first ballot drops them.
+constexpr int kIdBits = 14;
+static_assert((1 << kIdBits) >= kMaxRows, "ids must fit in kIdBits bits");
+
+__device__ __forceinline__ uint64_t match_peers(int32_t id, bool valid) {
   uint64_t peers = __ballot(valid);
-  for (int bit = 0; bit < id_bits; ++bit) {
-    const bool set = valid && ((id >> bit) & 1);
+#pragma unroll
+  for (int bit = 0; bit < kIdBits; ++bit) {
+    const bool set = (id >> bit) & 1;
     const uint64_t m = __ballot(set);
     peers &= set ? m : ~m;
   }
   return valid ? peers : 0ull;
 }
 
-// ---- 1. count. One LDS increment per distinct id per wave (the hot Zipf
-// key would otherwise serialise dozens of LDS atomics per instruction).
+// ---- 1. count. Integer LDS atomics: the counts are exact in any order (the
+// hot Zipf key makes a few lanes of an instruction share an address, which
+// the LDS serialises; that is far cheaper than matching lanes first).
 __global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                int id_bits, uint32_t* __restrict__ hist,
-                                                uint32_t* __restrict__ bad_accum) {
+                                                uint32_t* __restrict__ hist, uint32_t* __restrict__ bad_accum) {
   extern __shared__ uint32_t lds_hist[];
   for (int k = threadIdx.x; k < n_rows; k += 256) lds_hist[k] = 0u;
   __syncthreads();
   const int64_t b = blockIdx.x;
   const int64_t p0 = b * kBlockPos;
   const int64_t p1 = p0 + kBlockPos < n_src ? p0 + kBlockPos : n_src;
-  const uint64_t lt = __lanemask_lt();
   uint32_t bad = 0;
   constexpr int kPer = kBlockPos / 256;
   int32_t idv[kPer];
@@ -95,10 +100,10 @@ __global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids,
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int32_t id = idv[u];
-    const bool valid = id >= 0 && id < n_rows;
-    if (!valid && id != -1) ++bad;
-    const uint64_t peers = match_peers(id, valid, id_bits);
-    if (valid && (peers & lt) == 0) atomicAdd(&lds_hist[id], static_cast<uint32_t>(__popcll(peers)));
+    if (id >= 0 && id < n_rows)
+      atomicAdd(&lds_hist[id], 1u);
+    else if (id != -1)
+      ++bad;
   }
   __syncthreads();
   uint32_t* row = hist + b * n_rows;
@@ -145,89 +150,123 @@ __global__ __launch_bounds__(256) void ia_prefix_tot(uint32_t* __restrict__ segt
   count[k] = run;
 }
 
-// ---- 3. scan over ids (single workgroup of 1024 threads)
-__global__ __launch_bounds__(1024) void ia_scan(const uint32_t* __restrict__ count, int n_rows, int L,
+// ceil(n / L) for n < 2^31 + L with a reciprocal computed on the host,
+// rcp = floor((2^32 - 1) / L): the estimate is low by at most 2 and is
+// corrected exactly (a hardware integer division does not exist).
+__device__ __forceinline__ uint32_t ceil_div_rcp(uint32_t n, uint32_t L, uint32_t rcp) {
+  const uint32_t m = n + L - 1;
+  uint32_t q = __umulhi(m, rcp);
+  uint32_t r = m - q * L;
+  while (r >= L) {
+    ++q;
+    r -= L;
+  }
+  return q;
+}
+
+// ---- 3. scan over ids (single workgroup of 1024 threads): exclusive scans of
+// the counts (segment offsets) and of ceil(count / L) (chunk offsets). Thread
+// t owns ids [t * per, (t + 1) * per). Integer sums only: exact in any order.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(1024) void ia_scan(const uint32_t* __restrict__ count, int n_rows, int L, uint32_t rcp,
                                                 uint32_t* __restrict__ seg_off, uint32_t* __restrict__ chunk_off,
                                                 uint32_t* __restrict__ hdr) {
-  __shared__ uint32_t s_seg[1024];
-  __shared__ uint32_t s_chk[1024];
-  const int per = (n_rows + 1023) / 1024;
-  const int k0 = threadIdx.x * per;
+  __shared__ uint32_t w_seg[16], w_chk[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (n_rows + 1023) / 1024;  // <= 16
+  const int k0 = tid * per;
+  uint32_t c[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = (i < per && k0 + i < n_rows) ? count[k0 + i] : 0u;
   uint32_t seg = 0, chk = 0;
-  for (int i = 0; i < per; ++i) {
-    const int k = k0 + i;
-    if (k < n_rows) {
-      const uint32_t c = count[k];
-      seg += c;
-      chk += (c + L - 1) / L;
-    }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    seg += c[i];
+    chk += ceil_div_rcp(c[i], L, rcp);
   }
-  s_seg[threadIdx.x] = seg;
-  s_chk[threadIdx.x] = chk;
+  const uint32_t iseg = wave_incl_scan(seg, lane), ichk = wave_incl_scan(chk, lane);
+  if (lane == 63) {
+    w_seg[wave] = iseg;
+    w_chk[wave] = ichk;
+  }
   __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 per-thread totals (integers: exact)
-  for (int off = 1; off < 1024; off *= 2) {
-    const uint32_t a = threadIdx.x >= off ? s_seg[threadIdx.x - off] : 0u;
-    const uint32_t c = threadIdx.x >= off ? s_chk[threadIdx.x - off] : 0u;
-    __syncthreads();
-    s_seg[threadIdx.x] += a;
-    s_chk[threadIdx.x] += c;
-    __syncthreads();
+  uint32_t run_seg = iseg - seg, run_chk = ichk - chk;
+  for (int w = 0; w < wave; ++w) {
+    run_seg += w_seg[w];
+    run_chk += w_chk[w];
   }
-  uint32_t run_seg = threadIdx.x ? s_seg[threadIdx.x - 1] : 0u;
-  uint32_t run_chk = threadIdx.x ? s_chk[threadIdx.x - 1] : 0u;
-  for (int i = 0; i < per; ++i) {
-    const int k = k0 + i;
-    if (k < n_rows) {
-      seg_off[k] = run_seg;
-      chunk_off[k] = run_chk;
-      const uint32_t c = count[k];
-      run_seg += c;
-      run_chk += (c + L - 1) / L;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < per && k0 + i < n_rows) {
+      seg_off[k0 + i] = run_seg;
+      chunk_off[k0 + i] = run_chk;
     }
+    run_seg += c[i];
+    run_chk += ceil_div_rcp(c[i], L, rcp);
   }
-  if (threadIdx.x == 1023) {
-    seg_off[n_rows] = s_seg[1023];
-    chunk_off[n_rows] = s_chk[1023];
+  if (tid == 1023) {
+    seg_off[n_rows] = run_seg;
+    chunk_off[n_rows] = run_chk;
     hdr[1] = hdr[0];  // bad ids of this call
     hdr[0] = 0u;      // reset the accumulator for the next call
   }
 }
 
-// ---- 4. stable scatter. All 256 threads stage the block's ids and, for every
-// id, its first destination (segment offset + prefix of earlier segments +
-// prefix of earlier blocks of this segment) in LDS; then wave 0 alone walks
-// the block in order, 64 positions at a time, so the walk touches global
-// memory only to write perm. Within one wave the LDS read of an id's base
+// ---- 3b. chunk descriptors: desc[c] = {id, first sorted row, rows, chunks of
+// the id}, so a gather wave starts from one 16-byte load. One wave per id; a
+// hot id owns thousands of chunks, written 64 at a time.
+__global__ __launch_bounds__(256) void ia_chunks(const uint32_t* __restrict__ chunk_off,
+                                                 const uint32_t* __restrict__ seg_off, int n_rows, int L,
+                                                 int64_t n_src, int4* __restrict__ desc) {
+  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (k >= n_rows) return;
+  const uint32_t c0 = chunk_off[k], c1 = chunk_off[k + 1];
+  const uint32_t s0 = seg_off[k];
+  uint32_t s1 = seg_off[k + 1];
+  if (s1 > static_cast<uint64_t>(n_src)) s1 = static_cast<uint32_t>(n_src);
+  for (uint32_t c = c0 + (threadIdx.x & 63); c < c1; c += 64) {
+    const uint32_t r0 = s0 + (c - c0) * static_cast<uint32_t>(L);
+    const uint32_t len = r0 + static_cast<uint32_t>(L) < s1 ? static_cast<uint32_t>(L) : (s1 > r0 ? s1 - r0 : 0u);
+    desc[c] = make_int4(k, static_cast<int>(r0), static_cast<int>(len), static_cast<int>(c1 - c0));
+  }
+}
+
+// ---- 4. stable scatter. The block's 4096 positions are cut into NW
+// sub-blocks, one per walking wave. Pass 1: each walking wave counts the ids
+// of its sub-block into its own LDS table (integer LDS atomics: exact in any
+// order). Pass 2: for every id, the first destination of each sub-block =
+// segment offset + earlier segments + earlier blocks of this segment + the
+// counts of the earlier sub-blocks. Pass 3: each walking wave walks its
+// sub-block in order, 64 positions at a time; lanes holding the same id find
+// each other with one ballot per id bit, so a lane's rank among equal ids is
+// its order inside the batch plus the id's running count: a stable counting
+// sort, perm[dest] = p. Within one wave the LDS read of an id's running count
 // precedes its leader's update in program order, so no barrier is needed.
+template <int NW>
 __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                  int id_bits, const uint32_t* __restrict__ prefix,
+                                                  int tab_ld, const uint32_t* __restrict__ prefix,
                                                   const uint32_t* __restrict__ segbase,
                                                   const uint32_t* __restrict__ seg_off, int32_t* __restrict__ perm) {
   extern __shared__ uint32_t lds[];
-  uint32_t* base = lds;                                     // [n_rows]
-  int32_t* lid = reinterpret_cast<int32_t*>(lds + n_rows);  // [kBlockPos]
-  const int tid = threadIdx.x;
+  uint32_t* tab = lds;                                           // [NW][tab_ld], tab_ld = n_rows rounded up to 4
+  int32_t* lid = reinterpret_cast<int32_t*>(lds + NW * tab_ld);  // [kBlockPos]
+  constexpr int kSub = kBlockPos / NW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t b = blockIdx.x;
-  const uint32_t* pre = prefix + b * n_rows;
-  const uint32_t* sb = segbase + (b / kSegBlocks) * n_rows;
-  for (int k0 = 0; k0 < n_rows; k0 += 256 * 8) {
-    uint32_t v0[8], v1[8], v2[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + tid + 256 * u;
-      v0[u] = k < n_rows ? seg_off[k] : 0u;
-      v1[u] = k < n_rows ? sb[k] : 0u;
-      v2[u] = k < n_rows ? pre[k] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + tid + 256 * u;
-      if (k < n_rows) base[k] = v0[u] + v1[u] + v2[u];
-    }
-  }
   const int64_t p0 = b * kBlockPos;
   const int64_t p1 = p0 + kBlockPos < n_src ? p0 + kBlockPos : n_src;
+  {
+    uint4* t4 = reinterpret_cast<uint4*>(tab);
+    for (int k = tid; k < NW * tab_ld / 4; k += 256) t4[k] = make_uint4(0u, 0u, 0u, 0u);
+  }
   {
     constexpr int kPer = kBlockPos / 256;
     int32_t v[kPer];
@@ -240,22 +279,115 @@ __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ id
     for (int u = 0; u < kPer; ++u) lid[tid + 256 * u] = v[u];
   }
   __syncthreads();
-  if (tid >= 64) return;
-  const int lane = tid;
+  if (wave < NW) {
+    uint32_t* t = tab + wave * tab_ld;
+#pragma unroll 4
+    for (int off = wave * kSub; off < (wave + 1) * kSub; off += 64) {
+      const int32_t id = lid[off + lane];
+      if (id >= 0 && id < n_rows) atomicAdd(&t[id], 1u);
+    }
+  }
+  __syncthreads();
+  const uint32_t* pre = prefix + b * n_rows;
+  const uint32_t* sb = segbase + (b / kSegBlocks) * n_rows;
+  // only ids present in the block need a base (absent ids are never read in
+  // the walk), so the global loads are predicated on the counts
+  for (int k0 = 0; k0 < n_rows; k0 += 256 * 16) {
+    uint32_t c[16][NW];
+    bool present[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int k = k0 + tid + 256 * u;
+      uint32_t any = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        c[u][w] = k < n_rows ? tab[w * tab_ld + k] : 0u;
+        any |= c[u][w];
+      }
+      present[u] = any != 0;
+    }
+    uint32_t base[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int k = k0 + tid + 256 * u;
+      base[u] = present[u] ? seg_off[k] + sb[k] + pre[k] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int k = k0 + tid + 256 * u;
+      if (present[u]) {
+        uint32_t run = base[u];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          tab[w * tab_ld + k] = run;
+          run += c[u][w];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (wave >= NW) return;
+  uint32_t* t = tab + wave * tab_ld;
   const uint64_t lt = __lanemask_lt();
-  for (int64_t off = 0; p0 + off < p1; off += 64) {
-    const int32_t id = lid[off + lane];
-    const bool valid = id >= 0 && id < n_rows;
-    const uint64_t peers = match_peers(id, valid, id_bits);
-    if (valid) {
-      const uint32_t old = base[id];
-      const uint64_t dest = static_cast<uint64_t>(old) + static_cast<uint32_t>(__popcll(peers & lt));
-      if (dest < static_cast<uint64_t>(n_src)) perm[dest] = static_cast<int32_t>(p0 + off + lane);
+  // the lane matches of all batches first (independent of each other), then
+  // the short in-order chain of running-count reads and leader updates
+  constexpr int kSteps = kSub / 64;
+  int32_t sid[kSteps];
+  uint32_t rank[kSteps], cnt[kSteps];
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) sid[q] = lid[wave * kSub + 64 * q + lane];
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) {
+    const bool valid = sid[q] >= 0 && sid[q] < n_rows;
+    const uint64_t peers = match_peers(sid[q], valid);
+    rank[q] = static_cast<uint32_t>(__popcll(peers & lt));
+    // the lowest lane of each group carries the group size; -1 marks non-leaders and invalid lanes
+    cnt[q] = (valid && (peers & lt) == 0) ? static_cast<uint32_t>(__popcll(peers)) : 0xFFFFFFFFu;
+    if (!valid) sid[q] = -1;
+    // materialise the per-lane results here, so that the compiler does not
+    // carry the ballot masks into the chain below
+    asm volatile("" : "+v"(rank[q]), "+v"(cnt[q]), "+v"(sid[q]));
+  }
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) {
+    const int32_t id = sid[q];
+    if (id >= 0) {
+      const uint32_t old = t[id];
+      const uint64_t dest = static_cast<uint64_t>(old) + rank[q];
+      if (dest < static_cast<uint64_t>(n_src))
+        perm[dest] = static_cast<int32_t>(p0 + wave * kSub + 64 * q + lane);
       __builtin_amdgcn_wave_barrier();
-      if ((peers & lt) == 0) base[id] = old + static_cast<uint32_t>(__popcll(peers));
+      if (cnt[q] != 0xFFFFFFFFu) t[id] = old + cnt[q];
     }
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// Walking waves of the scatter: as many as fit while two workgroups still
+// share a CU's 160 KiB of LDS (one count table per walking wave plus the
+// block's ids), so that all blocks of the workload run in one round.
+int scatter_waves(int64_t n_rows) {
+  const int64_t pad_rows = (n_rows + 3) / 4 * 4;
+  for (int nw = 4; nw > 1; nw /= 2)
+    if (static_cast<int64_t>(nw) * pad_rows * 4 + kBlockPos * 4 <= 80 * 1024) return nw;
+  return 1;
+}
+
+template <int NW>
+void launch_scatter(int64_t nblk, int n_rows, hipStream_t st, const int32_t* ids, int64_t n_src,
+                    const uint32_t* hist, const uint32_t* segtot, const uint32_t* seg_off, int32_t* perm) {
+  const int pad_rows = (n_rows + 3) / 4 * 4;  // table rows padded for 16-byte zeroing
+  const size_t lds = static_cast<size_t>(NW) * pad_rows * 4 + kBlockPos * 4;
+  if (lds > 64 * 1024) {
+    static bool raised = false;  // allow up to the 160 KiB of a gfx950 workgroup, once per process
+    if (!raised) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(ia_scatter<NW>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL(ia_scatter<NW>, dim3(static_cast<uint32_t>(nblk)), dim3(256), lds, st, ids, n_src, n_rows,
+                     pad_rows, hist, segtot, seg_off, perm);
 }
 
 // Binary search: the id whose chunk range [chunk_off[k], chunk_off[k+1]) holds c.
@@ -374,6 +506,10 @@ __device__ __forceinline__ void add_bf16(float (&acc)[4], uint2 v) {
   acc[2] = acc[2] + bf16_lo(v.y); acc[3] = acc[3] + bf16_hi(v.y);
 }
 __device__ __forceinline__ void add_bf16(float (&acc)[8], uint4 v) { add8_bf16(acc, v); }
+// bf16 -0.0 in every element: adding it leaves an fp32 accumulator unchanged bit for bit
+__device__ __forceinline__ uint32_t neg_zero_vec(uint32_t) { return 0x80008000u; }
+__device__ __forceinline__ uint2 neg_zero_vec(uint2) { return make_uint2(0x80008000u, 0x80008000u); }
+__device__ __forceinline__ uint4 neg_zero_vec(uint4) { return make_uint4(0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u); }
 __device__ __forceinline__ uint32_t zero_vec(uint32_t) { return 0u; }
 __device__ __forceinline__ uint2 zero_vec(uint2) { return make_uint2(0u, 0u); }
 __device__ __forceinline__ uint4 zero_vec(uint4) { return make_uint4(0u, 0u, 0u, 0u); }
@@ -381,23 +517,24 @@ __device__ __forceinline__ uint4 zero_vec(uint4) { return make_uint4(0u, 0u, 0u,
 template <int DPL>
 __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict__ src, int64_t src_ld, int dim,
                                                       const int32_t* __restrict__ perm,
-                                                      const uint32_t* __restrict__ seg_off,
-                                                      const uint32_t* __restrict__ chunk_off, int n_rows, int L,
+                                                      const uint32_t* __restrict__ chunk_off,
+                                                      const int4* __restrict__ desc, int n_rows,
                                                       float* __restrict__ out, int64_t out_ld,
                                                       float* __restrict__ scratch, int64_t n_src,
                                                       int64_t max_chunks) {
   typedef typename RowVec<DPL>::T V;
   const int lane = threadIdx.x & 63;
   const uint32_t c = static_cast<uint32_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (c >= max_chunks) return;  // wave-uniform
+  // the descriptor load does not wait for the chunk count: entries past the
+  // count are read but never used
   const uint32_t n_chunks = chunk_off[n_rows];
-  if (c >= n_chunks || c >= max_chunks) return;  // wave-uniform
-  const int k = chunk_owner(chunk_off, n_rows, c);
-  const uint32_t j = c - chunk_off[k];
-  const uint32_t r0 = seg_off[k] + j * static_cast<uint32_t>(L);
-  uint32_t r_end = seg_off[k + 1];
-  if (r_end > static_cast<uint64_t>(n_src)) r_end = static_cast<uint32_t>(n_src);
-  const int len = static_cast<int>(r0 + static_cast<uint32_t>(L) < r_end ? static_cast<uint32_t>(L)
-                                                                          : (r_end > r0 ? r_end - r0 : 0u));
+  const int4 dsc = desc[c];
+  if (c >= n_chunks) return;  // wave-uniform
+  const int k = dsc.x;
+  const uint32_t r0 = static_cast<uint32_t>(dsc.y);
+  const int len = dsc.z;
+  const uint32_t nk = static_cast<uint32_t>(dsc.w);
   const int d0 = DPL * lane;
   float acc[DPL];
 #pragma unroll
@@ -409,7 +546,17 @@ __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict
     const int32_t x = perm[ok ? r0 + 64 * i + lane : r0];
     pos[i] = ok ? x : 0;
   }
-  // rows whose loads are in flight together: 64 / 32 / 16 for 4 / 8 / 16-byte rows
+  // a single-chunk id adds into out directly: its out row is fetched now,
+  // while the row loads are in flight
+  float* const dst = nk == 1 ? out + static_cast<int64_t>(k) * out_ld + d0 : scratch + static_cast<int64_t>(c) * dim + d0;
+  float o[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) o[i] = nk == 1 ? dst[i] : 0.0f;
+  // rows whose loads are in flight together: 64 / 32 / 16 for 4 / 8 / 16-byte rows.
+  // A row's position is read from its lane with readlane (wave-uniform, so
+  // the row address is scalar); rows past the chunk end load a valid row and
+  // add -0.0 instead, which leaves every value bitwise unchanged, so the
+  // adds need no branches.
   constexpr int kB = 128 / DPL;
 #pragma unroll
   for (int i = 0; i < kPosPerLane; ++i) {
@@ -419,19 +566,16 @@ __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict
       V v[kB];
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        int64_t p = __shfl(pos[i], h + u, 64);
-        p = (p >= 0 && p < n_src) ? p : 0;  // always a valid row; masked below
+        int64_t p = __builtin_amdgcn_readlane(pos[i], h + u);
+        p = (p >= 0 && p < n_src) ? p : 0;  // always a valid row
         v[u] = *reinterpret_cast<const V*>(src + p * src_ld + d0);
       }
 #pragma unroll
-      for (int u = 0; u < kB; ++u)
-        if (64 * i + h + u < len) add_bf16(acc, v[u]);
+      for (int u = 0; u < kB; ++u) add_bf16(acc, 64 * i + h + u < len ? v[u] : neg_zero_vec(v[u]));
     }
   }
-  const uint32_t nk = chunk_off[k + 1] - chunk_off[k];
-  float* dst = nk == 1 ? out + static_cast<int64_t>(k) * out_ld + d0 : scratch + static_cast<int64_t>(c) * dim + d0;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) dst[i] = (nk == 1 ? dst[i] + acc[i] : acc[i]);
+  for (int i = 0; i < DPL; ++i) dst[i] = (nk == 1 ? o[i] + acc[i] : acc[i]);
 }
 
 // Chunks longer than GS * 16 rows (a large chunk_rows setting): one lane group
@@ -486,11 +630,12 @@ __global__ __launch_bounds__(256) void ia_gather_long(const uint16_t* __restrict
 }
 
 // ---- 6. fold of multi-chunk ids: one workgroup per id. A round is a block
-// of R = floor(1024 / (dim/4)) chunk partials (at most 16 KiB); every thread
-// loads up to 4 float4 of a round, kAhead rounds are in flight in registers, each round is staged in
-// LDS, and one thread per group of 4 dims folds it left to right.
-constexpr int kAhead = 4;
-constexpr int kRoundF4 = 1024;  // float4 per round
+// of R = 4096 / dim chunk partials (16 KiB); all 256 threads load it (4
+// float4 each, kAhead rounds in flight in registers) and stage it in LDS, and
+// thread t folds dimensions t and t + 256 (dim <= 512) left to right: one
+// dependent add chain per dimension, spread over as many lanes as possible.
+constexpr int kAhead = 8;
+constexpr int kRoundF = 4096;  // floats per round
 
 __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chunk_off, int n_rows, int dim,
                                                const float* __restrict__ scratch, float* __restrict__ out,
@@ -499,66 +644,67 @@ __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chun
   if (k >= n_rows) return;
   const uint32_t c0 = chunk_off[k], c1 = chunk_off[k + 1];
   if (c1 - c0 < 2) return;
-  __shared__ float4 stage[kRoundF4];
-  const int quads = dim / 4;
-  const int R = kRoundF4 / quads;  // chunks per round
+  __shared__ float4 stage4[kRoundF / 4];
+  const float* stage = reinterpret_cast<const float*>(stage4);
   const int tid = threadIdx.x;
+  const uint32_t R = static_cast<uint32_t>(kRoundF / dim);  // chunks per round (dim <= 512: R >= 8)
   const uint32_t n = c1 - c0;
   const uint32_t rounds = (n + R - 1) / R;
   const float4* base = reinterpret_cast<const float4*>(scratch + static_cast<int64_t>(c0) * dim);
-  float4 acc = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
-  // four named register buffers (rounds r, r+1, r+2, r+3 in flight)
-  float4 b0[4], b1[4], b2[4], b3[4];
-  const uint32_t round_f4 = static_cast<uint32_t>(R * quads);  // <= kRoundF4
-  const uint32_t total_f4 = n * static_cast<uint32_t>(quads);
+  const uint32_t round_f4 = R * static_cast<uint32_t>(dim) / 4;  // <= kRoundF / 4
+  const uint32_t total_f4 = n * static_cast<uint32_t>(dim) / 4;
+  static_assert(kMaxDim <= 512, "two dimensions per thread");
+  float acc[2] = {-0.0f, -0.0f};
+  float4 buf[kAhead][4];
   // unconditional loads from a clamped (always valid) index, then a select:
   // no branches, so the loads of several rounds stay in flight together
   auto load = [&](uint32_t rd, float4 (&v)[4]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t j = tid + 256 * s;      // float4 index inside the round
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t j = tid + 256 * q;      // float4 index inside the round
       const uint32_t e = rd * round_f4 + j;  // float4 index from c0
       const bool ok = rd < rounds && j < round_f4 && e < total_f4;
       const float4 x = base[ok ? e : 0u];
-      v[s] = ok ? x : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      v[q] = ok ? x : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
   };
   auto consume = [&](uint32_t rd, float4 (&v)[4]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) stage[tid + 256 * s] = v[s];
+    for (int q = 0; q < 4; ++q) stage4[tid + 256 * q] = v[q];
     __syncthreads();
     load(rd + kAhead, v);
-    if (tid < quads) {
-      const uint32_t m = n - rd * R < static_cast<uint32_t>(R) ? n - rd * R : static_cast<uint32_t>(R);
-      uint32_t i = 0;
-      for (; i + 8 <= m; i += 8) {  // 8 LDS reads in flight ahead of the dependent adds
-        float4 q[8];
+    const uint32_t m = n - rd * R < R ? n - rd * R : R;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) q[u] = stage[(i + u) * quads + tid];
+    for (int h = 0; h < 2; ++h) {
+      const int d = tid + 256 * h;
+      if (d < dim) {
+        uint32_t i = 0;
+        for (; i + 8 <= m; i += 8) {  // 8 LDS reads in flight ahead of the dependent adds
+          float x[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          acc.x = acc.x + q[u].x; acc.y = acc.y + q[u].y; acc.z = acc.z + q[u].z; acc.w = acc.w + q[u].w;
+          for (int u = 0; u < 8; ++u) x[u] = stage[(i + u) * dim + d];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc[h] = acc[h] + x[u];
         }
-      }
-      for (; i < m; ++i) {
-        const float4 q = stage[i * quads + tid];
-        acc.x = acc.x + q.x; acc.y = acc.y + q.y; acc.z = acc.z + q.z; acc.w = acc.w + q.w;
+        for (; i < m; ++i) acc[h] = acc[h] + stage[i * dim + d];
       }
     }
     __syncthreads();
   };
-  load(0, b0); load(1, b1); load(2, b2); load(3, b3);
-  for (uint32_t rd = 0; rd < rounds; rd += kAhead) {
-    consume(rd, b0);
-    if (rd + 1 < rounds) consume(rd + 1, b1);
-    if (rd + 2 < rounds) consume(rd + 2, b2);
-    if (rd + 3 < rounds) consume(rd + 3, b3);
+#pragma unroll
+  for (int q = 0; q < kAhead; ++q) load(q, buf[q]);
+  for (uint32_t rd0 = 0; rd0 < rounds; rd0 += kAhead) {
+#pragma unroll
+    for (int q = 0; q < kAhead; ++q)
+      if (rd0 + q < rounds) consume(rd0 + q, buf[q]);
   }
-  if (tid < quads) {
-    float* d = out + static_cast<int64_t>(k) * out_ld + 4 * tid;
-    float4 o = *reinterpret_cast<const float4*>(d);
-    o.x = o.x + acc.x; o.y = o.y + acc.y; o.z = o.z + acc.z; o.w = o.w + acc.w;
-    *reinterpret_cast<float4*>(d) = o;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int d = tid + 256 * h;
+    if (d < dim) {
+      float* o = out + static_cast<int64_t>(k) * out_ld + d;
+      *o = *o + acc[h];
+    }
   }
 }
 
@@ -665,27 +811,23 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   auto* count = reinterpret_cast<uint32_t*>(w + l.count);
   auto* seg_off = reinterpret_cast<uint32_t*>(w + l.seg_off);
   auto* chunk_off = reinterpret_cast<uint32_t*>(w + l.chunk_off);
+  auto* chunk_desc = reinterpret_cast<int4*>(w + l.chunk_desc);
   auto* perm = reinterpret_cast<int32_t*>(w + l.perm);
   auto* scratch = reinterpret_cast<float*>(w + l.scratch);
-  int id_bits = 0;
-  while ((1LL << id_bits) < n_rows) ++id_bits;
   const size_t lds_count = static_cast<size_t>(n_rows) * 4;
-  const size_t lds_scatter = lds_count + kBlockPos * 4;
-  if (lds_scatter > 64 * 1024) {
-    static bool raised = false;  // allow up to the 160 KiB of a gfx950 workgroup once per process
-    if (!raised) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(ia_scatter),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      raised = true;
-    }
-  }
   auto* segtot = reinterpret_cast<uint32_t*>(w + l.segtot);
-  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, id_bits, hist, hdr);
+  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, hist, hdr);
   hipLaunchKernelGGL(ia_prefix_seg, dim3(ceil_div(n_rows, 256), l.nseg), dim3(256), 0, st, hist, l.nblk, nr, segtot);
   hipLaunchKernelGGL(ia_prefix_tot, dim3(ceil_div(n_rows, 256)), dim3(256), 0, st, segtot, l.nseg, nr, count);
-  hipLaunchKernelGGL(ia_scan, dim3(1), dim3(1024), 0, st, count, nr, L, seg_off, chunk_off, hdr);
-  hipLaunchKernelGGL(ia_scatter, dim3(l.nblk), dim3(256), lds_scatter, st, ids, n_src, nr, id_bits, hist, segtot,
-                     seg_off, perm);
+  const uint32_t rcp = static_cast<uint32_t>(0xFFFFFFFFull / static_cast<uint64_t>(L));
+  hipLaunchKernelGGL(ia_scan, dim3(1), dim3(1024), 0, st, count, nr, L, rcp, seg_off, chunk_off, hdr);
+  hipLaunchKernelGGL(ia_chunks, dim3(static_cast<uint32_t>(ceil_div(n_rows, 4))), dim3(256), 0, st, chunk_off,
+                     seg_off, nr, L, n_src, chunk_desc);
+  switch (scatter_waves(n_rows)) {
+    case 4: launch_scatter<4>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
+    case 2: launch_scatter<2>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
+    default: launch_scatter<1>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
+  }
   const int64_t grid_g = ceil_div(l.max_chunks, 256 / gs);
 #define DET_IA_TAIL(G)                                                                                           \
   if (gs == G) {                                                                                                 \
@@ -701,8 +843,8 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
     const int64_t grid_w = ceil_div(l.max_chunks, 4);
 #define DET_IA_WAVE(D)                                                                                          \
   if (dpl == D)                                                                                                 \
-    hipLaunchKernelGGL(ia_gather_wave<D>, dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim, perm, seg_off, \
-                       chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);
+    hipLaunchKernelGGL(ia_gather_wave<D>, dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim, perm, chunk_off, \
+                       chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks);
     DET_IA_WAVE(2) DET_IA_WAVE(4) DET_IA_WAVE(8)
 #undef DET_IA_WAVE
   } else {

@@ -619,9 +619,7 @@ __global__ __launch_bounds__(256) void wgrad_tl_kernel(WgradArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = mt * kTT, n0 = nt * kTT;
   // M is a multiple of 128, so a wave's 128 rows are all inside or all
-  // outside M. A wave outside runs the same program (its MFMAs read G
-  // columns past M and are discarded), so that the workgroup stays in step
-  // and no branch splits the MFMA schedule; it stores nothing.
+  // outside M; a wave outside stores nothing.
   const bool live = m0 + 128 * wm < p.M;
 
   f32x16_t acc[4][4];
@@ -690,14 +688,15 @@ __global__ __launch_bounds__(256) void wgrad_tl_kernel(WgradArgs p) {
   //            the last fragments of this one)
   //   slots 52 .. 59: the fragments of block 0 of stage s + 1
   // Scheduling fences between slots keep this order.
-#define DET_WGRAD_T_STAGE(P)                                                                                    \
+#define DET_WGRAD_T_STAGE(P, MMA)                                                                               \
   {                                                                                                             \
     const int cur = (P) * kPair;                                                                                \
     const int nxt = kPair - cur;                                                                                \
     _Pragma("unroll") for (int k = 0; k < 64; ++k) {                                                            \
       const int b = k / 16, q = k % 16;                                                                         \
-      acc[q / 4][q % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[b & 1].a[q / 4], fb[b & 1].b[q % 4],       \
-                                                                  acc[q / 4][q % 4], 0, 0, 0);                  \
+      if (MMA)                                                                                                  \
+        acc[q / 4][q % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[b & 1].a[q / 4], fb[b & 1].b[q % 4],     \
+                                                                    acc[q / 4][q % 4], 0, 0, 0);                \
       if (b < 3 && q < 8) t_frag1(lbase + cur, b + 1, oa, ob, q, fb[(b + 1) & 1]);                              \
       if (k < 16 && (k & 1)) t_store_col(lbase + nxt, ra[(P) ^ 1], rg, c8, k >> 1);                            \
       if (k >= 16 && k < 32 && (k & 1)) t_store_col(lbase + nxt + kOpB, rb[(P) ^ 1], rg, c8, (k - 16) >> 1);   \
@@ -713,16 +712,27 @@ __global__ __launch_bounds__(256) void wgrad_tl_kernel(WgradArgs p) {
     }                                                                                                           \
     ++s;                                                                                                        \
   }
+  // A wave past M (the second half of the last m tile when M % 256 == 128)
+  // runs the same stages without MFMAs: it still moves its share of both
+  // operands and meets every barrier.
   int s = 0;
   const int full = rows / kTRows;
-  while (s + 1 < full) {
-    DET_WGRAD_T_STAGE(0)
-    DET_WGRAD_T_STAGE(1)
+  if (live) {
+    while (s + 1 < full) {
+      DET_WGRAD_T_STAGE(0, true)
+      DET_WGRAD_T_STAGE(1, true)
+    }
+    if (s < full) DET_WGRAD_T_STAGE(0, true)
+  } else {
+    while (s + 1 < full) {
+      DET_WGRAD_T_STAGE(0, false)
+      DET_WGRAD_T_STAGE(1, false)
+    }
+    if (s < full) DET_WGRAD_T_STAGE(0, false)
   }
-  if (s < full) DET_WGRAD_T_STAGE(0)
 #undef DET_WGRAD_T_STAGE
   // Last, partial stage: blocks inside the split only.
-  if (s * kTRows < rows) {
+  if (live && s * kTRows < rows) {
     const int cur = (s & 1) * kPair;
     const int nb = (rows - s * kTRows + kBlk - 1) / kBlk;
     t_mma(fb[0], acc);

@@ -163,7 +163,7 @@ int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* count, void*
  *
  * dY, C: [M, N] bf16, row strides ldy, ldc >= N (elements).
  * dprob: [M] float32, accumulated.
- * cfg:   NULL = {tile_n = 128, rows_per_wg = 16}; tile_n must be 128;
+ * cfg:   NULL = {tile_n = 128, rows_per_wg = 4}; tile_n must be 128;
  *        rows_per_wg in [1, 1024] only shapes the launch.
  * ws:    the deterministic route keeps every slot on chip and needs no
  *        workspace (size 0); ws may be NULL. */
