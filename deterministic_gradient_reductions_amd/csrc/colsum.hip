@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
 // kPiece tiles so that all their loads are in flight together; then one thread
 // per (head, gradient) runs the strictly sequential fold over the piece.
 constexpr int kFoldHeads = 32;
-constexpr int kPiece = 128;
+constexpr int kPiece = 256;
 
 __global__ __launch_bounds__(kWG) void colsum_fold_kernel(const float* __restrict__ slot1,
                                                           const float* __restrict__ slot2, int64_t S, int64_t H,
@@ -225,18 +225,19 @@ using namespace detgrad;
 
 // Shape-only selector (the deterministic route never times kernels to pick a
 // tile: the page replaces timing-based autotuning by a block-size rule).
-// block_h: the smallest of {8,16,32} covering H (all heads in one tile when
-// H <= 32). block_t: the largest of {256,128,64} that still yields at least one
-// workgroup per compute unit (256 CUs) in total, else 64.
+// block_h never changes a bit, so it is the smallest, 8: more workgroups hide
+// the latency of the per-element transcendental chains. block_t: the largest
+// of {256, 128} that still yields at least four workgroups per compute unit
+// (1024 on 256 CUs), else 64.
 extern "C" int det_colsum_select_cfg(int64_t T, int64_t H, det_colsum_cfg* out) {
   if (!out) return set_error(DET_ERR_INVALID_ARG, "colsum: out is NULL");
   if (T < 0 || H < 0) return set_error(DET_ERR_INVALID_ARG, "colsum: T and H must be >= 0");
   det_colsum_cfg c;
-  c.block_h = H <= 8 ? 8 : (H <= 16 ? 16 : 32);
+  c.block_h = 8;
   const int64_t hb = ceil_div(H > 0 ? H : 1, c.block_h);
   c.block_t = 64;
   for (int bt : {256, 128}) {
-    if (ceil_div(T, bt) * hb >= 256) {
+    if (ceil_div(T, bt) * hb >= 1024) {
       c.block_t = bt;
       break;
     }

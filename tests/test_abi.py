@@ -88,18 +88,20 @@ def test_dprob_validation():
 
 def test_colsum_validation_and_selector():
     L = lib()
-    # shape-only rule: block_h covers H; block_t the largest of 256/128/64 that
-    # still gives >= 256 workgroups, else 64
+    # shape-only rule: block_h = 8; block_t the largest of 256/128 that still
+    # gives >= 1024 workgroups, else 64
     c = dg.det_colsum_select_cfg(16384, 32)
-    assert (c.block_t, c.block_h) == (64, 32)
+    assert (c.block_t, c.block_h) == (64, 8)
     c = dg.det_colsum_select_cfg(4096, 16)
-    assert (c.block_t, c.block_h) == (64, 16)
+    assert (c.block_t, c.block_h) == (64, 8)
     c = dg.det_colsum_select_cfg(16384 * 4, 32)
-    assert (c.block_t, c.block_h) == (256, 32)
-    c = dg.det_colsum_select_cfg(32768, 5)
+    assert (c.block_t, c.block_h) == (256, 8)
+    c = dg.det_colsum_select_cfg(16384 * 2, 32)
     assert (c.block_t, c.block_h) == (128, 8)
+    c = dg.det_colsum_select_cfg(32768, 5)
+    assert (c.block_t, c.block_h) == (64, 8)
     c = dg.det_colsum_select_cfg(1000, 100)
-    assert (c.block_t, c.block_h) == (64, 32)
+    assert (c.block_t, c.block_h) == (64, 8)
     bad = dg.ColsumCfg(96, 16)
     assert L.det_colsum(FAKE, 16, 1, FAKE, 16, 1, 0, FAKE, FAKE, 16, 16, FAKE, FAKE, ctypes.byref(bad), None, 0, 0,
                         None) == dg.DET_ERR_INVALID_ARG
