@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 256 * 1024 * 1024
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
@@ -45,6 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reps", type=int, default=50, help="timed repetitions per kernel for the per-kernel stats")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the measurements, copy a 256 MiB buffer three times (a kernel of known traffic, "
+                         "against which hardware byte counters are scaled)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     return ap.parse_args()
 
@@ -351,6 +355,14 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if args.copy_calibration:
+        # a plain copy of known size: reads and writes exactly COPY_BYTES each
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of %d bytes" % COPY_BYTES)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(res), flush=True)
