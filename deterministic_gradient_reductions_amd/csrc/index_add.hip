@@ -39,7 +39,7 @@ constexpr int kMaxDim = 512;
 constexpr int kSegBlocks = 32;   // blocks per prefix segment
 
 struct Layout {
-  size_t hist, segtot, count, seg_off, chunk_off, chunk_desc, perm, scratch, total;
+  size_t hist, segtot, count, seg_off, chunk_off, full_off, chunk_desc, perm, scratch, total;
   int64_t nblk, nseg, max_chunks;
 };
 
@@ -54,6 +54,7 @@ Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L) {
   l.count = o;     o = align_up(o + static_cast<size_t>(n_rows) * 4, 256);
   l.seg_off = o;   o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
   l.chunk_off = o; o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
+  l.full_off = o;  o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
   l.chunk_desc = o; o = align_up(o + static_cast<size_t>(l.max_chunks) * 16, 256);
   l.perm = o;      o = align_up(o + static_cast<size_t>(n_src) * 4, 256);
   l.scratch = o;   o = align_up(o + static_cast<size_t>(l.max_chunks * dim) * 4, 256);
@@ -178,64 +179,83 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 
 __global__ __launch_bounds__(1024) void ia_scan(const uint32_t* __restrict__ count, int n_rows, int L, uint32_t rcp,
                                                 uint32_t* __restrict__ seg_off, uint32_t* __restrict__ chunk_off,
-                                                uint32_t* __restrict__ hdr) {
-  __shared__ uint32_t w_seg[16], w_chk[16];
+                                                uint32_t* __restrict__ full_off, uint32_t* __restrict__ hdr) {
+  __shared__ uint32_t w_seg[16], w_chk[16], w_full[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (n_rows + 1023) / 1024;  // <= 16
   const int k0 = tid * per;
   uint32_t c[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) c[i] = (i < per && k0 + i < n_rows) ? count[k0 + i] : 0u;
-  uint32_t seg = 0, chk = 0;
+  // per id: count, ceil(count / L) chunks, of which (count % L != 0) is partial
+  uint32_t seg = 0, chk = 0, ful = 0, nc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
+    nc[i] = ceil_div_rcp(c[i], L, rcp);
     seg += c[i];
-    chk += ceil_div_rcp(c[i], L, rcp);
+    chk += nc[i];
+    ful += nc[i] - (nc[i] * static_cast<uint32_t>(L) != c[i] ? 1u : 0u);
   }
-  const uint32_t iseg = wave_incl_scan(seg, lane), ichk = wave_incl_scan(chk, lane);
+  const uint32_t iseg = wave_incl_scan(seg, lane), ichk = wave_incl_scan(chk, lane), iful = wave_incl_scan(ful, lane);
   if (lane == 63) {
     w_seg[wave] = iseg;
     w_chk[wave] = ichk;
+    w_full[wave] = iful;
   }
   __syncthreads();
-  uint32_t run_seg = iseg - seg, run_chk = ichk - chk;
+  uint32_t run_seg = iseg - seg, run_chk = ichk - chk, run_ful = iful - ful;
   for (int w = 0; w < wave; ++w) {
     run_seg += w_seg[w];
     run_chk += w_chk[w];
+    run_ful += w_full[w];
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if (i < per && k0 + i < n_rows) {
       seg_off[k0 + i] = run_seg;
       chunk_off[k0 + i] = run_chk;
+      full_off[k0 + i] = run_ful;
     }
     run_seg += c[i];
-    run_chk += ceil_div_rcp(c[i], L, rcp);
+    run_chk += nc[i];
+    run_ful += nc[i] - (nc[i] * static_cast<uint32_t>(L) != c[i] ? 1u : 0u);
   }
   if (tid == 1023) {
     seg_off[n_rows] = run_seg;
     chunk_off[n_rows] = run_chk;
+    full_off[n_rows] = run_ful;
     hdr[1] = hdr[0];  // bad ids of this call
     hdr[0] = 0u;      // reset the accumulator for the next call
   }
 }
 
-// ---- 3b. chunk descriptors: desc[c] = {id, first sorted row, rows, chunks of
-// the id}, so a gather wave starts from one 16-byte load. One wave per id; a
-// hot id owns thousands of chunks, written 64 at a time.
+// ---- 3b. chunk descriptors {id, first sorted row, rows, scratch slot}, so a
+// gather wave starts from one 16-byte load. The gather takes them in list
+// order, so the list puts the chunks of L rows first and the shorter last
+// chunks of the ids after them: the waves that start last are the short ones,
+// and the end of the kernel is not left to a few long chunks. The scratch
+// slot is the chunk's canonical index (chunk_off[id] + j, where the fold
+// reads it), or -1 for the single chunk of an id (added into out directly).
+// One wave per id; a hot id owns thousands of chunks, written 64 at a time.
 __global__ __launch_bounds__(256) void ia_chunks(const uint32_t* __restrict__ chunk_off,
+                                                 const uint32_t* __restrict__ full_off,
                                                  const uint32_t* __restrict__ seg_off, int n_rows, int L,
                                                  int64_t n_src, int4* __restrict__ desc) {
   const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (k >= n_rows) return;
   const uint32_t c0 = chunk_off[k], c1 = chunk_off[k + 1];
+  const uint32_t f0 = full_off[k], n_full = full_off[n_rows];
   const uint32_t s0 = seg_off[k];
   uint32_t s1 = seg_off[k + 1];
   if (s1 > static_cast<uint64_t>(n_src)) s1 = static_cast<uint32_t>(n_src);
   for (uint32_t c = c0 + (threadIdx.x & 63); c < c1; c += 64) {
-    const uint32_t r0 = s0 + (c - c0) * static_cast<uint32_t>(L);
+    const uint32_t j = c - c0;
+    const uint32_t r0 = s0 + j * static_cast<uint32_t>(L);
     const uint32_t len = r0 + static_cast<uint32_t>(L) < s1 ? static_cast<uint32_t>(L) : (s1 > r0 ? s1 - r0 : 0u);
-    desc[c] = make_int4(k, static_cast<int>(r0), static_cast<int>(len), static_cast<int>(c1 - c0));
+    // full chunks keep their order among full chunks; an id's partial chunk
+    // is its last, numbered among the partial chunks (c0 - f0 before it)
+    const uint32_t at = len == static_cast<uint32_t>(L) ? f0 + j : n_full + (c0 - f0);
+    desc[at] = make_int4(k, static_cast<int>(r0), static_cast<int>(len), c1 - c0 == 1 ? -1 : static_cast<int>(c));
   }
 }
 
@@ -514,7 +534,7 @@ __device__ __forceinline__ uint32_t zero_vec(uint32_t) { return 0u; }
 __device__ __forceinline__ uint2 zero_vec(uint2) { return make_uint2(0u, 0u); }
 __device__ __forceinline__ uint4 zero_vec(uint4) { return make_uint4(0u, 0u, 0u, 0u); }
 
-template <int DPL>
+template <int DPL, int NPOS>
 __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict__ src, int64_t src_ld, int dim,
                                                       const int32_t* __restrict__ perm,
                                                       const uint32_t* __restrict__ chunk_off,
@@ -524,42 +544,44 @@ __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict
                                                       int64_t max_chunks) {
   typedef typename RowVec<DPL>::T V;
   const int lane = threadIdx.x & 63;
-  const uint32_t c = static_cast<uint32_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (c >= max_chunks) return;  // wave-uniform
+  const uint32_t w = static_cast<uint32_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (w >= max_chunks) return;  // wave-uniform
   // the descriptor load does not wait for the chunk count: entries past the
   // count are read but never used
   const uint32_t n_chunks = chunk_off[n_rows];
-  const int4 dsc = desc[c];
-  if (c >= n_chunks) return;  // wave-uniform
+  const int4 dsc = desc[w];
+  if (w >= n_chunks) return;  // wave-uniform
   const int k = dsc.x;
   const uint32_t r0 = static_cast<uint32_t>(dsc.y);
   const int len = dsc.z;
-  const uint32_t nk = static_cast<uint32_t>(dsc.w);
+  const int slot = dsc.w;  // canonical chunk index, or -1: the id's only chunk
   const int d0 = DPL * lane;
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = -0.0f;
-  int32_t pos[kPosPerLane];
+  // NPOS * 64 >= the chunk length: positions beyond len are never read
+  int32_t pos[NPOS];
 #pragma unroll
-  for (int i = 0; i < kPosPerLane; ++i) {
+  for (int i = 0; i < NPOS; ++i) {
     const bool ok = 64 * i + lane < len;
     const int32_t x = perm[ok ? r0 + 64 * i + lane : r0];
     pos[i] = ok ? x : 0;
   }
   // a single-chunk id adds into out directly: its out row is fetched now,
   // while the row loads are in flight
-  float* const dst = nk == 1 ? out + static_cast<int64_t>(k) * out_ld + d0 : scratch + static_cast<int64_t>(c) * dim + d0;
+  float* const dst = slot < 0 ? out + static_cast<int64_t>(k) * out_ld + d0 : scratch + static_cast<int64_t>(slot) * dim + d0;
   float o[DPL];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) o[i] = nk == 1 ? dst[i] : 0.0f;
-  // rows whose loads are in flight together: 64 / 32 / 16 for 4 / 8 / 16-byte rows.
+  for (int i = 0; i < DPL; ++i) o[i] = slot < 0 ? dst[i] : 0.0f;
+  // rows whose loads are in flight together: 32 / 16 / 8 for 4 / 8 / 16-byte rows
+  // (few registers, so eight waves fit on a SIMD).
   // A row's position is read from its lane with readlane (wave-uniform, so
   // the row address is scalar); rows past the chunk end load a valid row and
   // add -0.0 instead, which leaves every value bitwise unchanged, so the
   // adds need no branches.
-  constexpr int kB = 128 / DPL;
+  constexpr int kB = 64 / DPL;
 #pragma unroll
-  for (int i = 0; i < kPosPerLane; ++i) {
+  for (int i = 0; i < NPOS; ++i) {
 #pragma unroll
     for (int h = 0; h < 64; h += kB) {
       if (64 * i + h >= len) continue;  // wave-uniform skip
@@ -575,7 +597,7 @@ __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict
     }
   }
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) dst[i] = (nk == 1 ? o[i] + acc[i] : acc[i]);
+  for (int i = 0; i < DPL; ++i) dst[i] = (slot < 0 ? o[i] + acc[i] : acc[i]);
 }
 
 // Chunks longer than GS * 16 rows (a large chunk_rows setting): one lane group
@@ -820,9 +842,10 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   hipLaunchKernelGGL(ia_prefix_seg, dim3(ceil_div(n_rows, 256), l.nseg), dim3(256), 0, st, hist, l.nblk, nr, segtot);
   hipLaunchKernelGGL(ia_prefix_tot, dim3(ceil_div(n_rows, 256)), dim3(256), 0, st, segtot, l.nseg, nr, count);
   const uint32_t rcp = static_cast<uint32_t>(0xFFFFFFFFull / static_cast<uint64_t>(L));
-  hipLaunchKernelGGL(ia_scan, dim3(1), dim3(1024), 0, st, count, nr, L, rcp, seg_off, chunk_off, hdr);
+  auto* full_off = reinterpret_cast<uint32_t*>(w + l.full_off);
+  hipLaunchKernelGGL(ia_scan, dim3(1), dim3(1024), 0, st, count, nr, L, rcp, seg_off, chunk_off, full_off, hdr);
   hipLaunchKernelGGL(ia_chunks, dim3(static_cast<uint32_t>(ceil_div(n_rows, 4))), dim3(256), 0, st, chunk_off,
-                     seg_off, nr, L, n_src, chunk_desc);
+                     full_off, seg_off, nr, L, n_src, chunk_desc);
   switch (scatter_waves(n_rows)) {
     case 4: launch_scatter<4>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
     case 2: launch_scatter<2>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
@@ -841,11 +864,14 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   const int dpl = (dim % 64 == 0) ? static_cast<int>(dim / 64) : 0;
   if ((dpl == 2 || dpl == 4 || dpl == 8) && L <= 64 * kPosPerLane) {
     const int64_t grid_w = ceil_div(l.max_chunks, 4);
-#define DET_IA_WAVE(D)                                                                                          \
-  if (dpl == D)                                                                                                 \
-    hipLaunchKernelGGL(ia_gather_wave<D>, dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim, perm, chunk_off, \
-                       chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks);
-    DET_IA_WAVE(2) DET_IA_WAVE(4) DET_IA_WAVE(8)
+    // position registers per lane sized to the chunk length (fewer registers, more waves per SIMD)
+#define DET_IA_WAVE(D, NP)                                                                                      \
+  if (dpl == D && L <= 64 * NP && (NP == 4 || L > 64 * (NP / 2)))                                               \
+    hipLaunchKernelGGL((ia_gather_wave<D, NP>), dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim, perm,     \
+                       chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks);
+    DET_IA_WAVE(2, 4) DET_IA_WAVE(2, 8) DET_IA_WAVE(2, 16)
+    DET_IA_WAVE(4, 4) DET_IA_WAVE(4, 8) DET_IA_WAVE(4, 16)
+    DET_IA_WAVE(8, 4) DET_IA_WAVE(8, 8) DET_IA_WAVE(8, 16)
 #undef DET_IA_WAVE
   } else {
     DET_IA_TAIL(1) DET_IA_TAIL(2) DET_IA_TAIL(4) DET_IA_TAIL(8) DET_IA_TAIL(16) DET_IA_TAIL(32) DET_IA_TAIL(64)
