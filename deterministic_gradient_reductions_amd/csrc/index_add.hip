@@ -152,35 +152,58 @@ __global__ __launch_bounds__(256) void ia_prefix_tot(uint32_t* __restrict__ segt
 }
 
 // ceil(n / L) for n < 2^31 + L with a reciprocal computed on the host,
-// rcp = floor((2^32 - 1) / L): the estimate is low by at most 2 and is
-// corrected exactly (a hardware integer division does not exist).
+// rcp = floor((2^32 - 1) / L): the quotient estimate is low by at most 2 and
+// is corrected exactly with two compare-and-subtract steps (no branches; a
+// hardware integer division does not exist).
 __device__ __forceinline__ uint32_t ceil_div_rcp(uint32_t n, uint32_t L, uint32_t rcp) {
   const uint32_t m = n + L - 1;
   uint32_t q = __umulhi(m, rcp);
   uint32_t r = m - q * L;
-  while (r >= L) {
-    ++q;
-    r -= L;
-  }
+  const uint32_t c1 = r >= L ? 1u : 0u;
+  q += c1;
+  r -= c1 * L;
+  q += r >= L ? 1u : 0u;
   return q;
 }
 
 // ---- 3. scan over ids (single workgroup of 1024 threads): exclusive scans of
-// the counts (segment offsets) and of ceil(count / L) (chunk offsets). Thread
-// t owns ids [t * per, (t + 1) * per). Integer sums only: exact in any order.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
+// the counts (segment offsets), of ceil(count / L) (chunk offsets) and of
+// floor(count / L) (full chunks). Thread t owns ids [t * per, (t + 1) * per).
+// Integer sums only: exact in any order. The scans run on DPP row shifts and
+// row broadcasts in registers; LDS is used once, for the 16 wave totals (an
+// LDS round trip costs far more than the arithmetic here).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_add(uint32_t v) {
+  // lanes without a source lane read 0 (the `old` operand)
+  return v + static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Inclusive scan over the 64 lanes: shifts by 1, 2, 4, 8 inside each row of
+// 16, then the last lane of row 0 into row 1 and 3 (row_bcast:15) and of row
+// 1 into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v = dpp_add<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Inclusive scan over the 16 lanes of row 0 (the other rows are ignored).
+__device__ __forceinline__ uint32_t row_incl_scan(uint32_t v) {
+  v = dpp_add<0x111, 0xF>(v);
+  v = dpp_add<0x112, 0xF>(v);
+  v = dpp_add<0x114, 0xF>(v);
+  v = dpp_add<0x118, 0xF>(v);
   return v;
 }
 
 __global__ __launch_bounds__(1024) void ia_scan(const uint32_t* __restrict__ count, int n_rows, int L, uint32_t rcp,
                                                 uint32_t* __restrict__ seg_off, uint32_t* __restrict__ chunk_off,
                                                 uint32_t* __restrict__ full_off, uint32_t* __restrict__ hdr) {
-  __shared__ uint32_t w_seg[16], w_chk[16], w_full[16];
+  __shared__ uint32_t w_tot[3][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (n_rows + 1023) / 1024;  // <= 16
   const int k0 = tid * per;
@@ -196,19 +219,23 @@ __global__ __launch_bounds__(1024) void ia_scan(const uint32_t* __restrict__ cou
     chk += nc[i];
     ful += nc[i] - (nc[i] * static_cast<uint32_t>(L) != c[i] ? 1u : 0u);
   }
-  const uint32_t iseg = wave_incl_scan(seg, lane), ichk = wave_incl_scan(chk, lane), iful = wave_incl_scan(ful, lane);
+  const uint32_t iseg = wave_incl_scan(seg), ichk = wave_incl_scan(chk), iful = wave_incl_scan(ful);
   if (lane == 63) {
-    w_seg[wave] = iseg;
-    w_chk[wave] = ichk;
-    w_full[wave] = iful;
+    w_tot[0][wave] = iseg;
+    w_tot[1][wave] = ichk;
+    w_tot[2][wave] = iful;
   }
   __syncthreads();
-  uint32_t run_seg = iseg - seg, run_chk = ichk - chk, run_ful = iful - ful;
-  for (int w = 0; w < wave; ++w) {
-    run_seg += w_seg[w];
-    run_chk += w_chk[w];
-    run_ful += w_full[w];
+  if (wave == 0 && lane < 16) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const uint32_t t = w_tot[q][lane];
+      w_tot[q][lane] = row_incl_scan(t) - t;  // exclusive prefix of the wave totals
+    }
   }
+  __syncthreads();
+  uint32_t run_seg = iseg - seg + w_tot[0][wave], run_chk = ichk - chk + w_tot[1][wave],
+           run_ful = iful - ful + w_tot[2][wave];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if (i < per && k0 + i < n_rows) {
@@ -260,16 +287,28 @@ __global__ __launch_bounds__(256) void ia_chunks(const uint32_t* __restrict__ ch
 }
 
 // ---- 4. stable scatter. The block's 4096 positions are cut into NW
-// sub-blocks, one per walking wave. Pass 1: each walking wave counts the ids
-// of its sub-block into its own LDS table (integer LDS atomics: exact in any
-// order). Pass 2: for every id, the first destination of each sub-block =
-// segment offset + earlier segments + earlier blocks of this segment + the
-// counts of the earlier sub-blocks. Pass 3: each walking wave walks its
-// sub-block in order, 64 positions at a time; lanes holding the same id find
-// each other with one ballot per id bit, so a lane's rank among equal ids is
-// its order inside the batch plus the id's running count: a stable counting
-// sort, perm[dest] = p. Within one wave the LDS read of an id's running count
-// precedes its leader's update in program order, so no barrier is needed.
+// sub-blocks, one per walking wave.
+//   match:  all four waves take the block's 64-position batches in turn; the
+//           lanes holding the same id find each other with one ballot per id
+//           bit, which gives each lane its rank among equal ids of the batch
+//           and the group size; (id, rank, group size at the lowest lane of
+//           the group) is packed in place of the id.
+//   count:  each walking wave adds the group sizes of its sub-block into its
+//           own LDS table (one add per distinct id and batch: exact in any
+//           order).
+//   bases:  for every id present in the block, the first destination of each
+//           sub-block = segment offset + earlier segments + earlier blocks +
+//           the counts of the earlier sub-blocks (global loads for present
+//           ids, issued without branches).
+//   chain:  each walking wave walks its sub-block in order, batch by batch:
+//           perm[base + rank] = p, then the group's lowest lane advances the
+//           id's running count: a stable counting sort. Within one wave the
+//           LDS read of an id's running count precedes its leader's update in
+//           program order, so no barrier is needed.
+// Packed match result: id (14 bits) | rank << 14 (6 bits) | size << 20 (7
+// bits, 0 except at the group's lowest lane); -1 for ids out of range.
+constexpr uint32_t kPackRank = 14, kPackSize = 20;
+
 template <int NW>
 __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
                                                   int tab_ld, const uint32_t* __restrict__ prefix,
@@ -279,6 +318,7 @@ __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ id
   uint32_t* tab = lds;                                           // [NW][tab_ld], tab_ld = n_rows rounded up to 4
   int32_t* lid = reinterpret_cast<int32_t*>(lds + NW * tab_ld);  // [kBlockPos]
   constexpr int kSub = kBlockPos / NW;
+  constexpr int kBatches = kBlockPos / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t b = blockIdx.x;
   const int64_t p0 = b * kBlockPos;
@@ -299,19 +339,39 @@ __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ id
     for (int u = 0; u < kPer; ++u) lid[tid + 256 * u] = v[u];
   }
   __syncthreads();
+  {
+    const uint64_t lt = __lanemask_lt();
+    constexpr int kMine = kBatches / 4;  // batches per wave
+    int32_t x[kMine];
+#pragma unroll
+    for (int q = 0; q < kMine; ++q) x[q] = lid[(wave + 4 * q) * 64 + lane];
+#pragma unroll
+    for (int q = 0; q < kMine; ++q) {
+      const int32_t id = x[q];
+      const bool valid = id >= 0 && id < n_rows;
+      const uint64_t peers = match_peers(id, valid);
+      const uint32_t rank = static_cast<uint32_t>(__popcll(peers & lt));
+      const uint32_t size = (valid && rank == 0) ? static_cast<uint32_t>(__popcll(peers)) : 0u;
+      x[q] = valid ? static_cast<int32_t>(static_cast<uint32_t>(id) | (rank << kPackRank) | (size << kPackSize)) : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kMine; ++q) lid[(wave + 4 * q) * 64 + lane] = x[q];
+  }
+  __syncthreads();
   if (wave < NW) {
     uint32_t* t = tab + wave * tab_ld;
 #pragma unroll 4
     for (int off = wave * kSub; off < (wave + 1) * kSub; off += 64) {
-      const int32_t id = lid[off + lane];
-      if (id >= 0 && id < n_rows) atomicAdd(&t[id], 1u);
+      const int32_t xv = lid[off + lane];
+      const uint32_t size = (static_cast<uint32_t>(xv) >> kPackSize) & 0x7Fu;
+      if (xv >= 0 && size != 0) atomicAdd(&t[xv & 0x3FFF], size);
     }
   }
   __syncthreads();
   const uint32_t* pre = prefix + b * n_rows;
   const uint32_t* sb = segbase + (b / kSegBlocks) * n_rows;
   // only ids present in the block need a base (absent ids are never read in
-  // the walk), so the global loads are predicated on the counts
+  // the walk); absent ids load entry 0 instead, so the loads need no branches
   for (int k0 = 0; k0 < n_rows; k0 += 256 * 16) {
     uint32_t c[16][NW];
     bool present[16];
@@ -329,8 +389,8 @@ __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ id
     uint32_t base[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const int k = k0 + tid + 256 * u;
-      base[u] = present[u] ? seg_off[k] + sb[k] + pre[k] : 0u;
+      const int kk = present[u] ? k0 + tid + 256 * u : 0;
+      base[u] = seg_off[kk] + sb[kk] + pre[kk];
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -348,36 +408,20 @@ __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ id
   __syncthreads();
   if (wave >= NW) return;
   uint32_t* t = tab + wave * tab_ld;
-  const uint64_t lt = __lanemask_lt();
-  // the lane matches of all batches first (independent of each other), then
-  // the short in-order chain of running-count reads and leader updates
   constexpr int kSteps = kSub / 64;
-  int32_t sid[kSteps];
-  uint32_t rank[kSteps], cnt[kSteps];
-#pragma unroll
-  for (int q = 0; q < kSteps; ++q) sid[q] = lid[wave * kSub + 64 * q + lane];
 #pragma unroll
   for (int q = 0; q < kSteps; ++q) {
-    const bool valid = sid[q] >= 0 && sid[q] < n_rows;
-    const uint64_t peers = match_peers(sid[q], valid);
-    rank[q] = static_cast<uint32_t>(__popcll(peers & lt));
-    // the lowest lane of each group carries the group size; -1 marks non-leaders and invalid lanes
-    cnt[q] = (valid && (peers & lt) == 0) ? static_cast<uint32_t>(__popcll(peers)) : 0xFFFFFFFFu;
-    if (!valid) sid[q] = -1;
-    // materialise the per-lane results here, so that the compiler does not
-    // carry the ballot masks into the chain below
-    asm volatile("" : "+v"(rank[q]), "+v"(cnt[q]), "+v"(sid[q]));
-  }
-#pragma unroll
-  for (int q = 0; q < kSteps; ++q) {
-    const int32_t id = sid[q];
-    if (id >= 0) {
+    const int32_t xv = lid[wave * kSub + 64 * q + lane];
+    if (xv >= 0) {
+      const int32_t id = xv & 0x3FFF;
+      const uint32_t rank = (static_cast<uint32_t>(xv) >> kPackRank) & 0x3Fu;
+      const uint32_t size = (static_cast<uint32_t>(xv) >> kPackSize) & 0x7Fu;
       const uint32_t old = t[id];
-      const uint64_t dest = static_cast<uint64_t>(old) + rank[q];
+      const uint64_t dest = static_cast<uint64_t>(old) + rank;
       if (dest < static_cast<uint64_t>(n_src))
         perm[dest] = static_cast<int32_t>(p0 + wave * kSub + 64 * q + lane);
       __builtin_amdgcn_wave_barrier();
-      if (cnt[q] != 0xFFFFFFFFu) t[id] = old + cnt[q];
+      if (size != 0) t[id] = old + size;
     }
     __builtin_amdgcn_wave_barrier();
   }
