@@ -695,81 +695,149 @@ __global__ __launch_bounds__(256) void ia_gather_long(const uint16_t* __restrict
   }
 }
 
-// ---- 6. fold of multi-chunk ids: one workgroup per id. A round is a block
-// of R = 4096 / dim chunk partials (16 KiB); all 256 threads load it (4
-// float4 each, kAhead rounds in flight in registers) and stage it in LDS, and
-// thread t folds dimensions t and t + 256 (dim <= 512) left to right: one
-// dependent add chain per dimension, spread over as many lanes as possible.
-constexpr int kAhead = 8;
-constexpr int kRoundF = 4096;  // floats per round
+// ---- 6. fold of multi-chunk ids. One workgroup per compute unit owns the
+// ids k = blockIdx.x + gridDim.x j (at most 64: n_rows <= 64 gridDim.x); lane j
+// of each wave reads that id's chunk range in one go, and the workgroup folds
+// the ids with several chunks one after another.
+//
+// Lane d adds dimension d of the id's chunk partials left to right: one
+// dependent add chain per dimension (d and d + 256 when dim > 256), fed from
+// LDS. An id's partials (contiguous in scratch from slot chunk_off[k]) pass
+// through LDS in rounds of R chunks, transposed to [dim][R] so that one
+// 16-byte LDS read gives a lane four consecutive chunks of its dimension:
+// each thread loads 4 x 4 blocks (4 chunks x 4 dims, four 16-byte loads),
+// turns them around in registers and stores four 16-byte vectors. The
+// 16-byte column blocks of row d are XOR-swizzled by d (fold_swz), so that
+// neither the reads nor the stores have bank conflicts. The next round's loads are in
+// flight in registers (two rounds ahead) while a round is added; the two LDS
+// buffers alternate.
+constexpr int kFoldGrid = 256;  // workgroups (one per compute unit)
+static_assert(kFoldGrid * 64 >= kMaxRows, "a fold workgroup owns at most 64 ids");
+constexpr int kFoldFloats = 8192;  // floats per LDS round buffer (32 KiB): dim * R
+constexpr int kFoldBlocks = 2;     // 4 x 4 blocks per thread and round (512 blocks of 16 floats)
 
+__device__ __forceinline__ int fold_round(int dim) {
+  const int r = kFoldFloats / dim;  // 16 .. 1024 for dim in [8, 512]
+  return r < 64 ? r : 64;
+}
+
+// Swizzle of the 16-byte column blocks of dimension row d: a bijection of the
+// low bits of d for 16 consecutive rows, so that both accesses are free of
+// bank conflicts: the reads (16 lanes = 16 consecutive rows, one block each)
+// and the stores (16 lanes = 4-dim groups g, rows 4 g + e, one block each).
+__device__ __forceinline__ int fold_swz(int d, int nb) { return ((d >> 2) ^ ((d & 3) << 2)) & (nb - 1); }
+
+// Dimension row `row` (R chunks, swizzled 16-byte blocks) added into a, left
+// to right: a full round with all 16 block reads issued ahead of the adds,
+// a partial (last) round one chunk at a time.
+__device__ __forceinline__ float fold_row(const float* row, int d, int R, int nb, int m, float a) {
+  if (m == R && nb == 16) {
+    float4 x[16];
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) x[cb] = *reinterpret_cast<const float4*>(row + 4 * (cb ^ fold_swz(d, 16)));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) {
+      a = a + x[cb].x;
+      a = a + x[cb].y;
+      a = a + x[cb].z;
+      a = a + x[cb].w;
+    }
+    return a;
+  }
+  for (int c = 0; c < m; ++c) a = a + row[4 * ((c >> 2) ^ fold_swz(d, nb)) + (c & 3)];
+  return a;
+}
+
+template <bool TWO>
 __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chunk_off, int n_rows, int dim,
                                                const float* __restrict__ scratch, float* __restrict__ out,
                                                int64_t out_ld) {
-  const int k = blockIdx.x;
-  if (k >= n_rows) return;
-  const uint32_t c0 = chunk_off[k], c1 = chunk_off[k + 1];
-  if (c1 - c0 < 2) return;
-  __shared__ float4 stage4[kRoundF / 4];
-  const float* stage = reinterpret_cast<const float*>(stage4);
-  const int tid = threadIdx.x;
-  const uint32_t R = static_cast<uint32_t>(kRoundF / dim);  // chunks per round (dim <= 512: R >= 8)
-  const uint32_t n = c1 - c0;
-  const uint32_t rounds = (n + R - 1) / R;
-  const float4* base = reinterpret_cast<const float4*>(scratch + static_cast<int64_t>(c0) * dim);
-  const uint32_t round_f4 = R * static_cast<uint32_t>(dim) / 4;  // <= kRoundF / 4
-  const uint32_t total_f4 = n * static_cast<uint32_t>(dim) / 4;
+  __shared__ __attribute__((aligned(16))) float buf[2][kFoldFloats];
   static_assert(kMaxDim <= 512, "two dimensions per thread");
-  float acc[2] = {-0.0f, -0.0f};
-  float4 buf[kAhead][4];
-  // unconditional loads from a clamped (always valid) index, then a select:
-  // no branches, so the loads of several rounds stay in flight together
-  auto load = [&](uint32_t rd, float4 (&v)[4]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int R = fold_round(dim);   // chunks per round, a multiple of 16
+  const int nb = R / 4;            // 16-byte column blocks per dimension row
+  const int d4 = dim / 4;          // 4-dim groups per chunk
+  const int blocks = nb * d4;      // 4 x 4 blocks per round (<= 512)
+  const int kj = blockIdx.x + gridDim.x * lane;
+  const uint32_t lo_j = kj < n_rows ? chunk_off[kj] : 0u, hi_j = kj < n_rows ? chunk_off[kj + 1] : 0u;
+  uint64_t todo = __ballot(hi_j - lo_j >= 2);  // the same in every wave
+  while (todo) {
+    const int j = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int k = blockIdx.x + gridDim.x * j;
+    const uint32_t c0 = __builtin_amdgcn_readlane(lo_j, j), c1 = __builtin_amdgcn_readlane(hi_j, j);
+    const int n = static_cast<int>(c1 - c0);
+    const int rounds = (n + R - 1) / R;
+    // partials past the id's last chunk read as zero and are never added
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(scratch + static_cast<int64_t>(c0) * dim), 0, n * dim * 4, 0x00020000);
+    // two register sets: the loads of rounds r + 1 and r + 2 are in flight while round r is added
+    float4 va[kFoldBlocks][4], vb[kFoldBlocks][4];
+    // block b = cb * d4 + g: chunks 4 cb .. 4 cb + 3 of the round, dims 4 g .. 4 g + 3
+    auto load = [&](float4 (&v)[kFoldBlocks][4], int r) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t j = tid + 256 * q;      // float4 index inside the round
-      const uint32_t e = rd * round_f4 + j;  // float4 index from c0
-      const bool ok = rd < rounds && j < round_f4 && e < total_f4;
-      const float4 x = base[ok ? e : 0u];
-      v[q] = ok ? x : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
-  };
-  auto consume = [&](uint32_t rd, float4 (&v)[4]) {
+      for (int q = 0; q < kFoldBlocks; ++q) {
+        const int b = tid + 256 * q;
+        const int cb = b / d4, g = b % d4;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) stage4[tid + 256 * q] = v[q];
-    __syncthreads();
-    load(rd + kAhead, v);
-    const uint32_t m = n - rd * R < R ? n - rd * R : R;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int d = tid + 256 * h;
-      if (d < dim) {
-        uint32_t i = 0;
-        for (; i + 8 <= m; i += 8) {  // 8 LDS reads in flight ahead of the dependent adds
-          float x[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) x[u] = stage[(i + u) * dim + d];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) acc[h] = acc[h] + x[u];
+        for (int e = 0; e < 4; ++e) {
+          const int off = b < blocks ? ((r * R + 4 * cb + e) * dim + 4 * g) * 4 : 0x7FFFFFF0;
+          v[q][e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
         }
-        for (; i < m; ++i) acc[h] = acc[h] + stage[i * dim + d];
       }
-    }
+    };
+    auto store = [&](const float4 (&v)[kFoldBlocks][4], int r) {
+      float* const bb = buf[r & 1];
+#pragma unroll
+      for (int q = 0; q < kFoldBlocks; ++q) {
+        const int b = tid + 256 * q;
+        if (b < blocks) {
+          const int cb = b / d4, g = b % d4;
+          const float4 t0 = make_float4(v[q][0].x, v[q][1].x, v[q][2].x, v[q][3].x);
+          const float4 t1 = make_float4(v[q][0].y, v[q][1].y, v[q][2].y, v[q][3].y);
+          const float4 t2 = make_float4(v[q][0].z, v[q][1].z, v[q][2].z, v[q][3].z);
+          const float4 t3 = make_float4(v[q][0].w, v[q][1].w, v[q][2].w, v[q][3].w);
+          const int d = 4 * g;
+          *reinterpret_cast<float4*>(bb + (d + 0) * R + 4 * (cb ^ fold_swz(d + 0, nb))) = t0;
+          *reinterpret_cast<float4*>(bb + (d + 1) * R + 4 * (cb ^ fold_swz(d + 1, nb))) = t1;
+          *reinterpret_cast<float4*>(bb + (d + 2) * R + 4 * (cb ^ fold_swz(d + 2, nb))) = t2;
+          *reinterpret_cast<float4*>(bb + (d + 3) * R + 4 * (cb ^ fold_swz(d + 3, nb))) = t3;
+        }
+      }
+    };
+    __syncthreads();  // the previous id's reads of both buffers are done
+    load(va, 0);
+    if (rounds > 1) load(vb, 1);
+    store(va, 0);
+    if (rounds > 2) load(va, 2);
     __syncthreads();
-  };
-#pragma unroll
-  for (int q = 0; q < kAhead; ++q) load(q, buf[q]);
-  for (uint32_t rd0 = 0; rd0 < rounds; rd0 += kAhead) {
-#pragma unroll
-    for (int q = 0; q < kAhead; ++q)
-      if (rd0 + q < rounds) consume(rd0 + q, buf[q]);
+    float a0 = -0.0f, a1 = -0.0f;
+    // round r: add buffer r & 1; then round r + 1 (registers of parity (r + 1) & 1)
+    // goes to the other buffer and those registers take the loads of round r + 3
+#define DET_IA_FOLD_ROUND(r, vnext)                                                       \
+  {                                                                                        \
+    const float* const bb = buf[(r) & 1];                                                  \
+    const int m = n - (r) * R < R ? n - (r) * R : R;                                       \
+    if (tid < dim) a0 = fold_row(bb + tid * R, tid, R, nb, m, a0);                         \
+    if (TWO && tid + 256 < dim) a1 = fold_row(bb + (tid + 256) * R, tid + 256, R, nb, m, a1); \
+    if ((r) + 1 < rounds) {                                                                \
+      store(vnext, (r) + 1);                                                               \
+      if ((r) + 3 < rounds) load(vnext, (r) + 3);                                          \
+    }                                                                                      \
+    __syncthreads();                                                                       \
   }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int d = tid + 256 * h;
-    if (d < dim) {
-      float* o = out + static_cast<int64_t>(k) * out_ld + d;
-      *o = *o + acc[h];
+    for (int r = 0; r < rounds; r += 2) {
+      DET_IA_FOLD_ROUND(r, vb)
+      if (r + 1 >= rounds) break;
+      DET_IA_FOLD_ROUND(r + 1, va)
+    }
+#undef DET_IA_FOLD_ROUND
+    if (tid < dim) {
+      float* const o = out + static_cast<int64_t>(k) * out_ld;
+      o[tid] = o[tid] + a0;
+      if (TWO && tid + 256 < dim) o[tid + 256] = o[tid + 256] + a1;
     }
   }
 }
@@ -921,8 +989,11 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
     DET_IA_TAIL(1) DET_IA_TAIL(2) DET_IA_TAIL(4) DET_IA_TAIL(8) DET_IA_TAIL(16) DET_IA_TAIL(32) DET_IA_TAIL(64)
   }
 #undef DET_IA_TAIL
-  hipLaunchKernelGGL(ia_fold, dim3(static_cast<uint32_t>(n_rows)), dim3(256), 0, st, chunk_off, nr, (int)dim, scratch,
-                     out, out_ld);
+  const dim3 fold_grid(static_cast<uint32_t>(n_rows < kFoldGrid ? n_rows : kFoldGrid));
+  if (dim > 256)
+    hipLaunchKernelGGL(ia_fold<true>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
+  else
+    hipLaunchKernelGGL(ia_fold<false>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
   return check_launch("det_index_add");
 }
 
