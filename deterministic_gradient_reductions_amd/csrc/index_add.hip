@@ -37,9 +37,10 @@ constexpr int kMaxRows = 16384;  // LDS histogram capacity (64 KiB)
 constexpr int kMaxDim = 512;
 
 constexpr int kSegBlocks = 32;   // blocks per prefix segment
+constexpr int kMaxGroups = kMaxRows / 256;  // workgroups of the offsets kernel (one thread per id)
 
 struct Layout {
-  size_t hist, segtot, count, seg_off, chunk_off, full_off, chunk_desc, perm, scratch, total;
+  size_t hist, segtot, pub, seg_off, chunk_off, full_off, chunk_desc, perm, scratch, total;
   int64_t nblk, nseg, max_chunks;
 };
 
@@ -51,7 +52,7 @@ Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L) {
   size_t o = DET_WS_HEADER_BYTES;
   l.hist = o;      o = align_up(o + static_cast<size_t>(l.nblk * n_rows) * 4, 256);
   l.segtot = o;    o = align_up(o + static_cast<size_t>(l.nseg * n_rows) * 4, 256);
-  l.count = o;     o = align_up(o + static_cast<size_t>(n_rows) * 4, 256);
+  l.pub = o;       o = align_up(o + static_cast<size_t>(3 * kMaxGroups) * 4, 256);
   l.seg_off = o;   o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
   l.chunk_off = o; o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
   l.full_off = o;  o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
@@ -83,8 +84,14 @@ __device__ __forceinline__ uint64_t match_peers(int32_t id, bool valid) {
 // hot Zipf key makes a few lanes of an instruction share an address, which
 // the LDS serialises; that is far cheaper than matching lanes first).
 __global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                uint32_t* __restrict__ hist, uint32_t* __restrict__ bad_accum) {
+                                                uint32_t* __restrict__ hist, uint32_t* __restrict__ hdr,
+                                                uint32_t* __restrict__ pub) {
   extern __shared__ uint32_t lds_hist[];
+  // the offsets kernel's exchange words start unpublished, its timeout flag clear
+  if (blockIdx.x == 0) {
+    if (threadIdx.x < 3 * kMaxGroups) pub[threadIdx.x] = 0u;
+    if (threadIdx.x == 0) hdr[2] = 0u;
+  }
   for (int k = threadIdx.x; k < n_rows; k += 256) lds_hist[k] = 0u;
   __syncthreads();
   const int64_t b = blockIdx.x;
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids,
   __syncthreads();
   uint32_t* row = hist + b * n_rows;
   for (int k = threadIdx.x; k < n_rows; k += 256) row[k] = lds_hist[k];
-  if (bad) atomicAdd(bad_accum, bad);
+  if (bad) atomicAdd(hdr, bad);
 }
 
 // ---- 2a. per id and segment of kSegBlocks blocks: exclusive prefix over the
@@ -132,25 +139,6 @@ __global__ __launch_bounds__(256) void ia_prefix_seg(uint32_t* __restrict__ hist
   segtot[seg * n_rows + k] = run;
 }
 
-// ---- 2b. per id: exclusive prefix over segments (in place) and the total.
-__global__ __launch_bounds__(256) void ia_prefix_tot(uint32_t* __restrict__ segtot, int64_t nseg, int n_rows,
-                                                     uint32_t* __restrict__ count) {
-  const int k = blockIdx.x * 256 + threadIdx.x;
-  if (k >= n_rows) return;
-  uint32_t run = 0;
-  for (int64_t s0 = 0; s0 < nseg; s0 += 16) {
-    uint32_t c[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) c[j] = (s0 + j < nseg) ? segtot[(s0 + j) * n_rows + k] : 0u;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (s0 + j < nseg) segtot[(s0 + j) * n_rows + k] = run;
-      run += c[j];
-    }
-  }
-  count[k] = run;
-}
-
 // ceil(n / L) for n < 2^31 + L with a reciprocal computed on the host,
 // rcp = floor((2^32 - 1) / L): the quotient estimate is low by at most 2 and
 // is corrected exactly with two compare-and-subtract steps (no branches; a
@@ -166,12 +154,28 @@ __device__ __forceinline__ uint32_t ceil_div_rcp(uint32_t n, uint32_t L, uint32_
   return q;
 }
 
-// ---- 3. scan over ids (single workgroup of 1024 threads): exclusive scans of
-// the counts (segment offsets), of ceil(count / L) (chunk offsets) and of
-// floor(count / L) (full chunks). Thread t owns ids [t * per, (t + 1) * per).
-// Integer sums only: exact in any order. The scans run on DPP row shifts and
-// row broadcasts in registers; LDS is used once, for the 16 wave totals (an
-// LDS round trip costs far more than the arithmetic here).
+// ---- 3. offsets and chunk descriptors, one thread per id and 256 ids per
+// workgroup. Thread k adds up id k's segment totals (leaving their exclusive
+// prefix in place) to its count c, with n = ceil(c / L) chunks of which
+// f = floor(c / L) are full. Then the exclusive scans over ids of c (segment
+// offsets), n (chunk offsets) and f (full chunks): a workgroup scans its own
+// ids, publishes its three totals in the workspace (the top bit marks a
+// published word: totals stay below 2^31; the count kernel of the same call
+// clears the words) and reads every workgroup's totals for its prefix and the
+// grand totals. Integer sums only: exact in any order. Every workgroup
+// publishes before it waits and there are at most 64 of them, so all of them
+// are resident together and the waits end; a wait is bounded all the same,
+// and a timeout is recorded in header word 2.
+//
+// Then the 16-byte descriptors {id, first sorted row, rows, scratch slot} of
+// every chunk, so a gather wave starts from one load. The gather takes them
+// in list order, so the list puts the chunks of L rows first and the shorter
+// last chunks of the ids after them: the waves that start last are the short
+// ones. The scratch slot is the chunk's canonical index (chunk offset + j,
+// where the fold reads it), or -1 for the only chunk of an id (added into out
+// directly).
+
+// Integer scans on DPP row shifts and row broadcasts in registers.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint32_t dpp_add(uint32_t v) {
   // lanes without a source lane read 0 (the `old` operand)
@@ -200,89 +204,120 @@ __device__ __forceinline__ uint32_t row_incl_scan(uint32_t v) {
   return v;
 }
 
-__global__ __launch_bounds__(1024) void ia_scan(const uint32_t* __restrict__ count, int n_rows, int L, uint32_t rcp,
-                                                uint32_t* __restrict__ seg_off, uint32_t* __restrict__ chunk_off,
-                                                uint32_t* __restrict__ full_off, uint32_t* __restrict__ hdr) {
-  __shared__ uint32_t w_tot[3][16];
+constexpr uint32_t kPublished = 0x80000000u;
+constexpr int kSpinLimit = 1 << 20;
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_incl_scan(v)), 63));
+}
+
+__global__ __launch_bounds__(256) void ia_offsets(uint32_t* __restrict__ segtot, int64_t nseg, int n_rows, int L,
+                                                  uint32_t rcp, int64_t n_src, uint32_t* __restrict__ pub,
+                                                  uint32_t* __restrict__ seg_off, uint32_t* __restrict__ chunk_off,
+                                                  uint32_t* __restrict__ full_off, int4* __restrict__ desc,
+                                                  uint32_t* __restrict__ hdr) {
+  __shared__ uint32_t w_tot[3][4];
+  __shared__ uint32_t g_tot[2][3];  // [0]: workgroups before this one, [1]: all
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (n_rows + 1023) / 1024;  // <= 16
-  const int k0 = tid * per;
-  uint32_t c[16];
+  const int b = blockIdx.x, ng = gridDim.x;
+  const int k = b * 256 + tid;
+  uint32_t c = 0;
+  if (k < n_rows) {
+    for (int64_t s0 = 0; s0 < nseg; s0 += 16) {
+      uint32_t v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) c[i] = (i < per && k0 + i < n_rows) ? count[k0 + i] : 0u;
-  // per id: count, ceil(count / L) chunks, of which (count % L != 0) is partial
-  uint32_t seg = 0, chk = 0, ful = 0, nc[16];
+      for (int j = 0; j < 16; ++j) v[j] = (s0 + j < nseg) ? segtot[(s0 + j) * n_rows + k] : 0u;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    nc[i] = ceil_div_rcp(c[i], L, rcp);
-    seg += c[i];
-    chk += nc[i];
-    ful += nc[i] - (nc[i] * static_cast<uint32_t>(L) != c[i] ? 1u : 0u);
+      for (int j = 0; j < 16; ++j) {
+        if (s0 + j < nseg) segtot[(s0 + j) * n_rows + k] = c;
+        c += v[j];
+      }
+    }
   }
-  const uint32_t iseg = wave_incl_scan(seg), ichk = wave_incl_scan(chk), iful = wave_incl_scan(ful);
+  const uint32_t nc = ceil_div_rcp(c, L, rcp);
+  const uint32_t fc = nc - (nc * static_cast<uint32_t>(L) != c ? 1u : 0u);
+  const uint32_t i0 = wave_incl_scan(c), i1 = wave_incl_scan(nc), i2 = wave_incl_scan(fc);
   if (lane == 63) {
-    w_tot[0][wave] = iseg;
-    w_tot[1][wave] = ichk;
-    w_tot[2][wave] = iful;
+    w_tot[0][wave] = i0;
+    w_tot[1][wave] = i1;
+    w_tot[2][wave] = i2;
   }
   __syncthreads();
-  if (wave == 0 && lane < 16) {
+  uint32_t e0 = i0 - c, e1 = i1 - nc, e2 = i2 - fc;  // exclusive prefix inside the workgroup
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const uint32_t t = w_tot[q][lane];
-      w_tot[q][lane] = row_incl_scan(t) - t;  // exclusive prefix of the wave totals
+  for (int w = 0; w < 3; ++w)
+    if (w < wave) {
+      e0 += w_tot[0][w];
+      e1 += w_tot[1][w];
+      e2 += w_tot[2][w];
+    }
+  if (wave == 0) {
+    if (lane < 3) {
+      const uint32_t t = w_tot[lane][0] + w_tot[lane][1] + w_tot[lane][2] + w_tot[lane][3];
+      __hip_atomic_store(pub + lane * kMaxGroups + b, t | kPublished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // lane j waits for workgroup j's three totals
+    uint32_t v0 = 0, v1 = 0, v2 = 0;
+    if (lane < ng) {
+      int spins = 0;
+      do {
+        v0 = __hip_atomic_load(pub + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v1 = __hip_atomic_load(pub + kMaxGroups + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v2 = __hip_atomic_load(pub + 2 * kMaxGroups + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } while ((v0 & v1 & v2 & kPublished) == 0u && ++spins < kSpinLimit);
+      if ((v0 & v1 & v2 & kPublished) == 0u) hdr[2] = 1u;
+      v0 &= ~kPublished;
+      v1 &= ~kPublished;
+      v2 &= ~kPublished;
+    }
+    const uint32_t p0 = wave_sum(lane < b ? v0 : 0u), p1 = wave_sum(lane < b ? v1 : 0u),
+                   p2 = wave_sum(lane < b ? v2 : 0u);
+    const uint32_t a0 = wave_sum(v0), a1 = wave_sum(v1), a2 = wave_sum(v2);
+    if (lane == 0) {
+      g_tot[0][0] = p0; g_tot[0][1] = p1; g_tot[0][2] = p2;
+      g_tot[1][0] = a0; g_tot[1][1] = a1; g_tot[1][2] = a2;
     }
   }
   __syncthreads();
-  uint32_t run_seg = iseg - seg + w_tot[0][wave], run_chk = ichk - chk + w_tot[1][wave],
-           run_ful = iful - ful + w_tot[2][wave];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i < per && k0 + i < n_rows) {
-      seg_off[k0 + i] = run_seg;
-      chunk_off[k0 + i] = run_chk;
-      full_off[k0 + i] = run_ful;
-    }
-    run_seg += c[i];
-    run_chk += nc[i];
-    run_ful += nc[i] - (nc[i] * static_cast<uint32_t>(L) != c[i] ? 1u : 0u);
+  const uint32_t seg = g_tot[0][0] + e0, chk = g_tot[0][1] + e1, ful = g_tot[0][2] + e2;
+  const uint32_t n_full = g_tot[1][2];
+  if (k < n_rows) {
+    seg_off[k] = seg;
+    chunk_off[k] = chk;
+    full_off[k] = ful;
   }
-  if (tid == 1023) {
-    seg_off[n_rows] = run_seg;
-    chunk_off[n_rows] = run_chk;
-    full_off[n_rows] = run_ful;
+  if (b == 0 && tid == 0) {
+    seg_off[n_rows] = g_tot[1][0];
+    chunk_off[n_rows] = g_tot[1][1];
+    full_off[n_rows] = n_full;
     hdr[1] = hdr[0];  // bad ids of this call
     hdr[0] = 0u;      // reset the accumulator for the next call
   }
-}
-
-// ---- 3b. chunk descriptors {id, first sorted row, rows, scratch slot}, so a
-// gather wave starts from one 16-byte load. The gather takes them in list
-// order, so the list puts the chunks of L rows first and the shorter last
-// chunks of the ids after them: the waves that start last are the short ones,
-// and the end of the kernel is not left to a few long chunks. The scratch
-// slot is the chunk's canonical index (chunk_off[id] + j, where the fold
-// reads it), or -1 for the single chunk of an id (added into out directly).
-// One wave per id; a hot id owns thousands of chunks, written 64 at a time.
-__global__ __launch_bounds__(256) void ia_chunks(const uint32_t* __restrict__ chunk_off,
-                                                 const uint32_t* __restrict__ full_off,
-                                                 const uint32_t* __restrict__ seg_off, int n_rows, int L,
-                                                 int64_t n_src, int4* __restrict__ desc) {
-  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (k >= n_rows) return;
-  const uint32_t c0 = chunk_off[k], c1 = chunk_off[k + 1];
-  const uint32_t f0 = full_off[k], n_full = full_off[n_rows];
-  const uint32_t s0 = seg_off[k];
-  uint32_t s1 = seg_off[k + 1];
-  if (s1 > static_cast<uint64_t>(n_src)) s1 = static_cast<uint32_t>(n_src);
-  for (uint32_t c = c0 + (threadIdx.x & 63); c < c1; c += 64) {
-    const uint32_t j = c - c0;
-    const uint32_t r0 = s0 + j * static_cast<uint32_t>(L);
+  // descriptors: a thread writes those of its own id when it has at most
+  // kDescSerial chunks (most ids have one); the wave writes those of its ids
+  // with more, 64 chunks at a time (a hot id owns thousands)
+  constexpr uint32_t kDescSerial = 4;
+  const uint32_t s1 = static_cast<uint64_t>(seg) + c > static_cast<uint64_t>(n_src) ? static_cast<uint32_t>(n_src)
+                                                                                     : seg + c;
+  auto put = [&](int id, uint32_t s0, uint32_t s1, uint32_t c0, uint32_t nj, uint32_t f0, uint32_t i) {
+    const uint32_t r0 = s0 + i * static_cast<uint32_t>(L);
     const uint32_t len = r0 + static_cast<uint32_t>(L) < s1 ? static_cast<uint32_t>(L) : (s1 > r0 ? s1 - r0 : 0u);
     // full chunks keep their order among full chunks; an id's partial chunk
     // is its last, numbered among the partial chunks (c0 - f0 before it)
-    const uint32_t at = len == static_cast<uint32_t>(L) ? f0 + j : n_full + (c0 - f0);
-    desc[at] = make_int4(k, static_cast<int>(r0), static_cast<int>(len), c1 - c0 == 1 ? -1 : static_cast<int>(c));
+    const uint32_t at = len == static_cast<uint32_t>(L) ? f0 + i : n_full + (c0 - f0);
+    desc[at] = make_int4(id, static_cast<int>(r0), static_cast<int>(len), nj == 1 ? -1 : static_cast<int>(c0 + i));
+  };
+  if (k < n_rows && nc <= kDescSerial)
+    for (uint32_t i = 0; i < nc; ++i) put(k, seg, s1, chk, nc, ful, i);
+  uint64_t big = __ballot(k < n_rows && nc > kDescSerial);
+  while (big) {
+    const int j = __builtin_ctzll(big);
+    big &= big - 1;
+    const int kj = __builtin_amdgcn_readlane(k, j);
+    const uint32_t s0j = __builtin_amdgcn_readlane(seg, j), s1j = __builtin_amdgcn_readlane(s1, j);
+    const uint32_t c0j = __builtin_amdgcn_readlane(chk, j), nj = __builtin_amdgcn_readlane(nc, j);
+    const uint32_t f0j = __builtin_amdgcn_readlane(ful, j);
+    for (uint32_t i = lane; i < nj; i += 64) put(kj, s0j, s1j, c0j, nj, f0j, i);
   }
 }
 
@@ -695,116 +730,103 @@ __global__ __launch_bounds__(256) void ia_gather_long(const uint16_t* __restrict
   }
 }
 
-// ---- 6. fold of multi-chunk ids. One workgroup per compute unit owns the
-// ids k = blockIdx.x + gridDim.x j (at most 64: n_rows <= 64 gridDim.x); lane j
-// of each wave reads that id's chunk range in one go, and the workgroup folds
-// the ids with several chunks one after another.
+// ---- 6. fold of multi-chunk ids. The dimensions are cut into slices of DS
+// (8, 16 or 32) and a workgroup owns one slice of the ids k = gi + groups j
+// (at most 64 ids per group: n_rows <= 64 groups); lane j of each wave reads
+// that id's chunk range in one go, and the workgroup folds the ids with
+// several chunks one after another. The slices of one id run on different
+// compute units, so the longest run (the hottest key) is spread over
+// dim / DS of them.
 //
-// Lane d adds dimension d of the id's chunk partials left to right: one
-// dependent add chain per dimension (d and d + 256 when dim > 256), fed from
-// LDS. An id's partials (contiguous in scratch from slot chunk_off[k]) pass
-// through LDS in rounds of R chunks, transposed to [dim][R] so that one
-// 16-byte LDS read gives a lane four consecutive chunks of its dimension:
-// each thread loads 4 x 4 blocks (4 chunks x 4 dims, four 16-byte loads),
-// turns them around in registers and stores four 16-byte vectors. The
-// 16-byte column blocks of row d are XOR-swizzled by d (fold_swz), so that
-// neither the reads nor the stores have bank conflicts. The next round's loads are in
-// flight in registers (two rounds ahead) while a round is added; the two LDS
-// buffers alternate.
-constexpr int kFoldGrid = 256;  // workgroups (one per compute unit)
-static_assert(kFoldGrid * 64 >= kMaxRows, "a fold workgroup owns at most 64 ids");
-constexpr int kFoldFloats = 8192;  // floats per LDS round buffer (32 KiB): dim * R
-constexpr int kFoldBlocks = 2;     // 4 x 4 blocks per thread and round (512 blocks of 16 floats)
+// Lane d of wave 0 adds dimension d of the slice, left to right over the id's
+// chunk partials: one dependent add chain per dimension, fed from LDS. The
+// partials (contiguous in scratch from slot chunk_off[k]) pass through LDS in
+// rounds of R = 8192 / DS chunks, transposed to [DS][R] so that one 16-byte
+// LDS read gives a lane four consecutive chunks of its dimension. Every
+// thread loads two 4 x 4 blocks per round (4 chunks x 4 dims, four 16-byte
+// loads each), turns them around in registers and stores four 16-byte
+// vectors; chunks past the id's last one are stored as -0.0, which leaves a
+// chain bitwise unchanged, so every round is added in whole groups of 64
+// chunks. The 16-byte column blocks of row d are XOR-swizzled (fold_swz), so
+// that neither the reads nor the stores have bank conflicts. The loads of the
+// next two rounds are in flight in registers while a round is added; the two
+// LDS buffers alternate.
+constexpr int kFoldGroups = 256;  // id groups
+static_assert(kFoldGroups * 64 >= kMaxRows, "a fold group owns at most 64 ids");
+constexpr int kFoldFloats = 8192;  // floats per LDS round buffer (32 KiB): DS * R
 
-__device__ __forceinline__ int fold_round(int dim) {
-  const int r = kFoldFloats / dim;  // 16 .. 1024 for dim in [8, 512]
-  return r < 64 ? r : 64;
+inline int fold_slice(int64_t dim) { return dim % 32 == 0 ? 32 : (dim % 16 == 0 ? 16 : 8); }
+
+// Column-block swizzle of dimension row d (a value below 16, XORed into the
+// low four bits of the block index). With D4 = DS / 4 dim groups per chunk,
+// 16 consecutive store lanes are 16 / D4 consecutive column blocks times the
+// D4 groups: the group g = d / 4 fills the block bits above those the lanes'
+// own blocks vary in. The 16 rows a read covers differ in g % 4 and d % 4,
+// which fill the remaining bits.
+template <int DS>
+__device__ __forceinline__ int fold_swz(int d) {
+  constexpr int s = DS == 32 ? 1 : (DS == 16 ? 2 : 3);
+  const int e = d & 3;
+  const int ee = DS == 32 ? ((e & 1) | ((e >> 1) << 3)) : e;
+  return ((d >> 2) << s) ^ ee;
 }
 
-// Swizzle of the 16-byte column blocks of dimension row d: a bijection of the
-// low bits of d for 16 consecutive rows, so that both accesses are free of
-// bank conflicts: the reads (16 lanes = 16 consecutive rows, one block each)
-// and the stores (16 lanes = 4-dim groups g, rows 4 g + e, one block each).
-__device__ __forceinline__ int fold_swz(int d, int nb) { return ((d >> 2) ^ ((d & 3) << 2)) & (nb - 1); }
-
-// Dimension row `row` (R chunks, swizzled 16-byte blocks) added into a, left
-// to right: a full round with all 16 block reads issued ahead of the adds,
-// a partial (last) round one chunk at a time.
-__device__ __forceinline__ float fold_row(const float* row, int d, int R, int nb, int m, float a) {
-  if (m == R && nb == 16) {
-    float4 x[16];
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb) x[cb] = *reinterpret_cast<const float4*>(row + 4 * (cb ^ fold_swz(d, 16)));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb) {
-      a = a + x[cb].x;
-      a = a + x[cb].y;
-      a = a + x[cb].z;
-      a = a + x[cb].w;
-    }
-    return a;
-  }
-  for (int c = 0; c < m; ++c) a = a + row[4 * ((c >> 2) ^ fold_swz(d, nb)) + (c & 3)];
-  return a;
-}
-
-template <bool TWO>
+template <int DS>
 __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chunk_off, int n_rows, int dim,
                                                const float* __restrict__ scratch, float* __restrict__ out,
                                                int64_t out_ld) {
+  constexpr int R = kFoldFloats / DS;  // chunks per round
+  constexpr int D4 = DS / 4;           // 4-dim groups per chunk of the slice
+  static_assert((R / 4) * D4 == 512, "two 4 x 4 blocks per thread and round");
   __shared__ __attribute__((aligned(16))) float buf[2][kFoldFloats];
-  static_assert(kMaxDim <= 512, "two dimensions per thread");
   const int tid = threadIdx.x, lane = tid & 63;
-  const int R = fold_round(dim);   // chunks per round, a multiple of 16
-  const int nb = R / 4;            // 16-byte column blocks per dimension row
-  const int d4 = dim / 4;          // 4-dim groups per chunk
-  const int blocks = nb * d4;      // 4 x 4 blocks per round (<= 512)
-  const int kj = blockIdx.x + gridDim.x * lane;
+  const int parts = dim / DS;
+  const int groups = static_cast<int>(gridDim.x) / parts;
+  const int gi = static_cast<int>(blockIdx.x) / parts;
+  const int d0 = DS * (static_cast<int>(blockIdx.x) % parts);
+  const int kj = gi + groups * lane;
   const uint32_t lo_j = kj < n_rows ? chunk_off[kj] : 0u, hi_j = kj < n_rows ? chunk_off[kj + 1] : 0u;
   uint64_t todo = __ballot(hi_j - lo_j >= 2);  // the same in every wave
   while (todo) {
     const int j = __builtin_ctzll(todo);
     todo &= todo - 1;
-    const int k = blockIdx.x + gridDim.x * j;
+    const int k = gi + groups * j;
     const uint32_t c0 = __builtin_amdgcn_readlane(lo_j, j), c1 = __builtin_amdgcn_readlane(hi_j, j);
     const int n = static_cast<int>(c1 - c0);
     const int rounds = (n + R - 1) / R;
-    // partials past the id's last chunk read as zero and are never added
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(scratch + static_cast<int64_t>(c0) * dim), 0, n * dim * 4, 0x00020000);
-    // two register sets: the loads of rounds r + 1 and r + 2 are in flight while round r is added
-    float4 va[kFoldBlocks][4], vb[kFoldBlocks][4];
-    // block b = cb * d4 + g: chunks 4 cb .. 4 cb + 3 of the round, dims 4 g .. 4 g + 3
-    auto load = [&](float4 (&v)[kFoldBlocks][4], int r) {
+    // block b = cb * D4 + g: chunks 4 cb .. 4 cb + 3 of the round, dims 4 g .. 4 g + 3 of the slice
+    float4 va[2][4], vb[2][4];
+    auto load = [&](float4 (&v)[2][4], int r) {
+      // one buffer resource per round (offsets stay below R * dim * 4 <= 2 MiB);
+      // partials past the id's last chunk read as zero (stored as -0.0)
+      const int left = n - r * R;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(scratch + (static_cast<int64_t>(c0) + static_cast<int64_t>(r) * R) * dim + d0), 0,
+          ((left < R ? left : R) * dim - d0) * 4, 0x00020000);
 #pragma unroll
-      for (int q = 0; q < kFoldBlocks; ++q) {
+      for (int q = 0; q < 2; ++q) {
         const int b = tid + 256 * q;
-        const int cb = b / d4, g = b % d4;
+        const int cb = b / D4, g = b % D4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int off = b < blocks ? ((r * R + 4 * cb + e) * dim + 4 * g) * 4 : 0x7FFFFFF0;
-          v[q][e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-        }
+        for (int e = 0; e < 4; ++e)
+          v[q][e] = __builtin_bit_cast(
+              float4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((4 * cb + e) * dim + 4 * g) * 4, 0, 0));
       }
     };
-    auto store = [&](const float4 (&v)[kFoldBlocks][4], int r) {
+    auto store = [&](const float4 (&v)[2][4], int r) {
       float* const bb = buf[r & 1];
 #pragma unroll
-      for (int q = 0; q < kFoldBlocks; ++q) {
+      for (int q = 0; q < 2; ++q) {
         const int b = tid + 256 * q;
-        if (b < blocks) {
-          const int cb = b / d4, g = b % d4;
-          const float4 t0 = make_float4(v[q][0].x, v[q][1].x, v[q][2].x, v[q][3].x);
-          const float4 t1 = make_float4(v[q][0].y, v[q][1].y, v[q][2].y, v[q][3].y);
-          const float4 t2 = make_float4(v[q][0].z, v[q][1].z, v[q][2].z, v[q][3].z);
-          const float4 t3 = make_float4(v[q][0].w, v[q][1].w, v[q][2].w, v[q][3].w);
-          const int d = 4 * g;
-          *reinterpret_cast<float4*>(bb + (d + 0) * R + 4 * (cb ^ fold_swz(d + 0, nb))) = t0;
-          *reinterpret_cast<float4*>(bb + (d + 1) * R + 4 * (cb ^ fold_swz(d + 1, nb))) = t1;
-          *reinterpret_cast<float4*>(bb + (d + 2) * R + 4 * (cb ^ fold_swz(d + 2, nb))) = t2;
-          *reinterpret_cast<float4*>(bb + (d + 3) * R + 4 * (cb ^ fold_swz(d + 3, nb))) = t3;
-        }
+        const int cb = b / D4, g = b % D4;
+        float4 w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = r * R + 4 * cb + e < n ? v[q][e] : make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
+        const int d = 4 * g;
+        *reinterpret_cast<float4*>(bb + (d + 0) * R + 4 * (cb ^ fold_swz<DS>(d + 0))) = make_float4(w[0].x, w[1].x, w[2].x, w[3].x);
+        *reinterpret_cast<float4*>(bb + (d + 1) * R + 4 * (cb ^ fold_swz<DS>(d + 1))) = make_float4(w[0].y, w[1].y, w[2].y, w[3].y);
+        *reinterpret_cast<float4*>(bb + (d + 2) * R + 4 * (cb ^ fold_swz<DS>(d + 2))) = make_float4(w[0].z, w[1].z, w[2].z, w[3].z);
+        *reinterpret_cast<float4*>(bb + (d + 3) * R + 4 * (cb ^ fold_swz<DS>(d + 3))) = make_float4(w[0].w, w[1].w, w[2].w, w[3].w);
       }
     };
     __syncthreads();  // the previous id's reads of both buffers are done
@@ -813,20 +835,34 @@ __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chun
     store(va, 0);
     if (rounds > 2) load(va, 2);
     __syncthreads();
-    float a0 = -0.0f, a1 = -0.0f;
-    // round r: add buffer r & 1; then round r + 1 (registers of parity (r + 1) & 1)
-    // goes to the other buffer and those registers take the loads of round r + 3
-#define DET_IA_FOLD_ROUND(r, vnext)                                                       \
-  {                                                                                        \
-    const float* const bb = buf[(r) & 1];                                                  \
-    const int m = n - (r) * R < R ? n - (r) * R : R;                                       \
-    if (tid < dim) a0 = fold_row(bb + tid * R, tid, R, nb, m, a0);                         \
-    if (TWO && tid + 256 < dim) a1 = fold_row(bb + (tid + 256) * R, tid + 256, R, nb, m, a1); \
-    if ((r) + 1 < rounds) {                                                                \
-      store(vnext, (r) + 1);                                                               \
-      if ((r) + 3 < rounds) load(vnext, (r) + 3);                                          \
-    }                                                                                      \
-    __syncthreads();                                                                       \
+    float a = -0.0f;
+    const int f = fold_swz<DS>(tid & (DS - 1));
+    // round r: add buffer r & 1 in groups of 64 chunks; then round r + 1
+    // (registers of parity (r + 1) & 1) goes to the other buffer and those
+    // registers take the loads of round r + 3
+#define DET_IA_FOLD_ROUND(r, vnext)                                                     \
+  {                                                                                      \
+    const float* const row = buf[(r) & 1] + (tid & (DS - 1)) * R;                        \
+    const int m = n - (r) * R < R ? n - (r) * R : R;                                     \
+    if (tid < DS) {                                                                      \
+      for (int h = 0; h < (m + 63) / 64; ++h) {                                          \
+        float4 x[16];                                                                    \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i)                                   \
+          x[i] = *reinterpret_cast<const float4*>(row + 4 * (16 * h + (i ^ f)));         \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                 \
+          a = a + x[i].x;                                                                \
+          a = a + x[i].y;                                                                \
+          a = a + x[i].z;                                                                \
+          a = a + x[i].w;                                                                \
+        }                                                                                \
+      }                                                                                  \
+    }                                                                                    \
+    if ((r) + 1 < rounds) {                                                              \
+      store(vnext, (r) + 1);                                                             \
+      if ((r) + 3 < rounds) load(vnext, (r) + 3);                                        \
+    }                                                                                    \
+    __syncthreads();                                                                     \
   }
     for (int r = 0; r < rounds; r += 2) {
       DET_IA_FOLD_ROUND(r, vb)
@@ -834,10 +870,9 @@ __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chun
       DET_IA_FOLD_ROUND(r + 1, va)
     }
 #undef DET_IA_FOLD_ROUND
-    if (tid < dim) {
-      float* const o = out + static_cast<int64_t>(k) * out_ld;
-      o[tid] = o[tid] + a0;
-      if (TWO && tid + 256 < dim) o[tid + 256] = o[tid + 256] + a1;
+    if (tid < DS) {
+      float* const o = out + static_cast<int64_t>(k) * out_ld + d0 + tid;
+      *o = *o + a;
     }
   }
 }
@@ -942,22 +977,20 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   char* w = static_cast<char*>(ws);
   auto* hdr = reinterpret_cast<uint32_t*>(w);
   auto* hist = reinterpret_cast<uint32_t*>(w + l.hist);
-  auto* count = reinterpret_cast<uint32_t*>(w + l.count);
+  auto* pub = reinterpret_cast<uint32_t*>(w + l.pub);
   auto* seg_off = reinterpret_cast<uint32_t*>(w + l.seg_off);
   auto* chunk_off = reinterpret_cast<uint32_t*>(w + l.chunk_off);
+  auto* full_off = reinterpret_cast<uint32_t*>(w + l.full_off);
   auto* chunk_desc = reinterpret_cast<int4*>(w + l.chunk_desc);
   auto* perm = reinterpret_cast<int32_t*>(w + l.perm);
   auto* scratch = reinterpret_cast<float*>(w + l.scratch);
   const size_t lds_count = static_cast<size_t>(n_rows) * 4;
   auto* segtot = reinterpret_cast<uint32_t*>(w + l.segtot);
-  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, hist, hdr);
+  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, hist, hdr, pub);
   hipLaunchKernelGGL(ia_prefix_seg, dim3(ceil_div(n_rows, 256), l.nseg), dim3(256), 0, st, hist, l.nblk, nr, segtot);
-  hipLaunchKernelGGL(ia_prefix_tot, dim3(ceil_div(n_rows, 256)), dim3(256), 0, st, segtot, l.nseg, nr, count);
   const uint32_t rcp = static_cast<uint32_t>(0xFFFFFFFFull / static_cast<uint64_t>(L));
-  auto* full_off = reinterpret_cast<uint32_t*>(w + l.full_off);
-  hipLaunchKernelGGL(ia_scan, dim3(1), dim3(1024), 0, st, count, nr, L, rcp, seg_off, chunk_off, full_off, hdr);
-  hipLaunchKernelGGL(ia_chunks, dim3(static_cast<uint32_t>(ceil_div(n_rows, 4))), dim3(256), 0, st, chunk_off,
-                     full_off, seg_off, nr, L, n_src, chunk_desc);
+  hipLaunchKernelGGL(ia_offsets, dim3(static_cast<uint32_t>(ceil_div(n_rows, 256))), dim3(256), 0, st, segtot, l.nseg,
+                     nr, L, rcp, n_src, pub, seg_off, chunk_off, full_off, chunk_desc, hdr);
   switch (scatter_waves(n_rows)) {
     case 4: launch_scatter<4>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
     case 2: launch_scatter<2>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
@@ -989,22 +1022,26 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
     DET_IA_TAIL(1) DET_IA_TAIL(2) DET_IA_TAIL(4) DET_IA_TAIL(8) DET_IA_TAIL(16) DET_IA_TAIL(32) DET_IA_TAIL(64)
   }
 #undef DET_IA_TAIL
-  const dim3 fold_grid(static_cast<uint32_t>(n_rows < kFoldGrid ? n_rows : kFoldGrid));
-  if (dim > 256)
-    hipLaunchKernelGGL(ia_fold<true>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
+  const int ds = fold_slice(dim);
+  const dim3 fold_grid(static_cast<uint32_t>((n_rows < kFoldGroups ? n_rows : kFoldGroups) * (dim / ds)));
+  if (ds == 32)
+    hipLaunchKernelGGL(ia_fold<32>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
+  else if (ds == 16)
+    hipLaunchKernelGGL(ia_fold<16>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
   else
-    hipLaunchKernelGGL(ia_fold<false>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
+    hipLaunchKernelGGL(ia_fold<8>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
   return check_launch("det_index_add");
 }
 
 extern "C" int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* count, void* stream) {
   if (!count) return set_error(DET_ERR_INVALID_ARG, "index_add_bad_ids: count is NULL");
   if (int s = check_workspace(ws, ws_bytes, DET_WS_HEADER_BYTES)) return s;
-  uint32_t v = 0;
+  uint32_t v[2] = {0u, 0u};  // header words 1 (bad ids of the last call) and 2 (exchange timeout)
   const hipStream_t st = as_stream(stream);
-  hipError_t e = hipMemcpyAsync(&v, static_cast<const char*>(ws) + 4, 4, hipMemcpyDeviceToHost, st);
+  hipError_t e = hipMemcpyAsync(v, static_cast<const char*>(ws) + 4, 8, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return set_error(DET_ERR_HIP, "index_add_bad_ids: %s", hipGetErrorString(e));
-  *count = v;
+  if (v[1] != 0u) return set_error(DET_ERR_HIP, "index_add: the offsets kernel timed out waiting for a workgroup");
+  *count = v[0];
   return ok();
 }

@@ -142,7 +142,10 @@ int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t out_ld, const
                   const void* src, int64_t src_ld, int src_dtype, const det_index_add_cfg* cfg, void* ws,
                   size_t ws_bytes, int atomic, void* stream);
 /* Number of ids dropped as out of range (not -1) by the last det_index_add
- * that used this workspace. Synchronises `stream`; for tests and debugging. */
+ * that used this workspace. Synchronises `stream`; for tests and debugging.
+ * Returns DET_ERR_HIP if that call's offsets kernel gave up waiting for the
+ * totals of one of its workgroups (a bounded wait that never times out when
+ * the GPU schedules all of them; the result of such a call is not valid). */
 int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* count, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -36,7 +36,8 @@ def small(P, n_rows, dim, seed, pad=0.05, out_init="normal"):
 
 
 @pytest.mark.parametrize("P,n_rows,dim", [(5000, 64, 128), (20000, 1000, 128), (3000, 7, 8), (9000, 300, 64),
-                                          (4097, 8192, 128), (1, 1, 16), (12345, 513, 512), (8192, 16384, 24)])
+                                          (4097, 8192, 128), (1, 1, 16), (12345, 513, 512), (8192, 16384, 24),
+                                          (20000, 5, 40), (30000, 3, 48)])
 @pytest.mark.parametrize("L", [1, 7, 256])
 def test_parity_small(P, n_rows, dim, L):
     note("index_add P=%d rows=%d dim=%d L=%d" % (P, n_rows, dim, L))
