@@ -754,6 +754,7 @@ __global__ __launch_bounds__(256) void ia_gather_long(const uint16_t* __restrict
 constexpr int kFoldGroups = 256;  // id groups
 static_assert(kFoldGroups * 64 >= kMaxRows, "a fold group owns at most 64 ids");
 constexpr int kFoldFloats = 8192;  // floats per LDS round buffer (32 KiB): DS * R
+constexpr int kFoldDirect = 32;    // ids with at most this many chunks are folded by one wave
 
 inline int fold_slice(int64_t dim) { return dim % 32 == 0 ? 32 : (dim % 16 == 0 ? 16 : 8); }
 
@@ -776,27 +777,58 @@ __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chun
                                                const float* __restrict__ scratch, float* __restrict__ out,
                                                int64_t out_ld) {
   constexpr int R = kFoldFloats / DS;  // chunks per round
+  constexpr int NG = R / 64;           // groups of 64 chunks per round
   constexpr int D4 = DS / 4;           // 4-dim groups per chunk of the slice
-  static_assert((R / 4) * D4 == 512, "two 4 x 4 blocks per thread and round");
+  static_assert((R / 4) * D4 == 512, "512 4 x 4 blocks per round");
   __shared__ __attribute__((aligned(16))) float buf[2][kFoldFloats];
   const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int parts = dim / DS;
   const int groups = static_cast<int>(gridDim.x) / parts;
   const int gi = static_cast<int>(blockIdx.x) / parts;
   const int d0 = DS * (static_cast<int>(blockIdx.x) % parts);
   const int kj = gi + groups * lane;
   const uint32_t lo_j = kj < n_rows ? chunk_off[kj] : 0u, hi_j = kj < n_rows ? chunk_off[kj + 1] : 0u;
-  uint64_t todo = __ballot(hi_j - lo_j >= 2);  // the same in every wave
-  while (todo) {
-    const int j = __builtin_ctzll(todo);
-    todo &= todo - 1;
+  const uint32_t nj = hi_j - lo_j;
+  // the same masks in every wave
+  uint64_t small = __ballot(nj >= 2 && nj <= kFoldDirect);
+  uint64_t big = __ballot(nj > kFoldDirect);
+
+  // ids with at most kFoldDirect chunks: one wave each, in turn; lane d loads
+  // dimension d of every chunk partial at once and adds them left to right
+  // (chunks past the last add -0.0, which changes no bit)
+  for (int i = 0; small; small &= small - 1, ++i) {
+    if ((i & 3) != wave) continue;
+    const int j = __builtin_ctzll(small);
     const int k = gi + groups * j;
-    const uint32_t c0 = __builtin_amdgcn_readlane(lo_j, j), c1 = __builtin_amdgcn_readlane(hi_j, j);
-    const int n = static_cast<int>(c1 - c0);
+    const uint32_t c0 = __builtin_amdgcn_readlane(lo_j, j);
+    const int n = static_cast<int>(__builtin_amdgcn_readlane(nj, j));
+    if (lane < DS) {
+      const float* p = scratch + static_cast<int64_t>(c0) * dim + d0 + lane;
+      float x[kFoldDirect];
+#pragma unroll
+      for (int c = 0; c < kFoldDirect; ++c) x[c] = c < n ? p[static_cast<int64_t>(c) * dim] : -0.0f;
+      float a = -0.0f;
+#pragma unroll
+      for (int c = 0; c < kFoldDirect; ++c) a = a + x[c];
+      float* const o = out + static_cast<int64_t>(k) * out_ld + d0 + lane;
+      *o = *o + a;
+    }
+  }
+
+  // longer runs: the whole workgroup; waves 1..3 stage the rounds through LDS,
+  // wave 0 runs the add chains
+  const int u = tid - 64;  // staging thread (waves 1..3): blocks u, u + 192 and (u < 128) u + 384
+  while (big) {
+    const int j = __builtin_ctzll(big);
+    big &= big - 1;
+    const int k = gi + groups * j;
+    const uint32_t c0 = __builtin_amdgcn_readlane(lo_j, j);
+    const int n = static_cast<int>(__builtin_amdgcn_readlane(nj, j));
     const int rounds = (n + R - 1) / R;
     // block b = cb * D4 + g: chunks 4 cb .. 4 cb + 3 of the round, dims 4 g .. 4 g + 3 of the slice
-    float4 va[2][4], vb[2][4];
-    auto load = [&](float4 (&v)[2][4], int r) {
+    float4 va[3][4], vb[3][4];
+    auto load = [&](float4 (&v)[3][4], int r) {
       // one buffer resource per round (offsets stay below R * dim * 4 <= 2 MiB);
       // partials past the id's last chunk read as zero (stored as -0.0)
       const int left = n - r * R;
@@ -804,8 +836,9 @@ __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chun
           const_cast<float*>(scratch + (static_cast<int64_t>(c0) + static_cast<int64_t>(r) * R) * dim + d0), 0,
           ((left < R ? left : R) * dim - d0) * 4, 0x00020000);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int b = tid + 256 * q;
+      for (int q = 0; q < 3; ++q) {
+        if (q == 2 && wave == 3) break;
+        const int b = u + 192 * q;
         const int cb = b / D4, g = b % D4;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -813,11 +846,12 @@ __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chun
               float4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((4 * cb + e) * dim + 4 * g) * 4, 0, 0));
       }
     };
-    auto store = [&](const float4 (&v)[2][4], int r) {
+    auto store = [&](const float4 (&v)[3][4], int r) {
       float* const bb = buf[r & 1];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int b = tid + 256 * q;
+      for (int q = 0; q < 3; ++q) {
+        if (q == 2 && wave == 3) break;
+        const int b = u + 192 * q;
         const int cb = b / D4, g = b % D4;
         float4 w[4];
 #pragma unroll
@@ -829,36 +863,58 @@ __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chun
         *reinterpret_cast<float4*>(bb + (d + 3) * R + 4 * (cb ^ fold_swz<DS>(d + 3))) = make_float4(w[0].w, w[1].w, w[2].w, w[3].w);
       }
     };
+    // 64-chunk group h of dimension row `row`: 16 16-byte reads
+    const int f = fold_swz<DS>(lane & (DS - 1));
+    auto rd = [&](float4 (&x)[16], const float* row, int h) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = *reinterpret_cast<const float4*>(row + 4 * (16 * h + (i ^ f)));
+    };
+    auto add = [&](const float4 (&x)[16], float a) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        a = a + x[i].x;
+        a = a + x[i].y;
+        a = a + x[i].z;
+        a = a + x[i].w;
+      }
+      return a;
+    };
     __syncthreads();  // the previous id's reads of both buffers are done
-    load(va, 0);
-    if (rounds > 1) load(vb, 1);
-    store(va, 0);
-    if (rounds > 2) load(va, 2);
+    if (wave != 0) {
+      load(va, 0);
+      if (rounds > 1) load(vb, 1);
+      store(va, 0);
+      if (rounds > 2) load(va, 2);
+    }
     __syncthreads();
     float a = -0.0f;
-    const int f = fold_swz<DS>(tid & (DS - 1));
-    // round r: add buffer r & 1 in groups of 64 chunks; then round r + 1
-    // (registers of parity (r + 1) & 1) goes to the other buffer and those
-    // registers take the loads of round r + 3
+    // round r: wave 0 adds buffer r & 1, 64 chunks per group with the next
+    // group's reads in flight; meanwhile round r + 1 (registers of parity
+    // (r + 1) & 1) goes to the other buffer and those registers take the
+    // loads of round r + 3
 #define DET_IA_FOLD_ROUND(r, vnext)                                                     \
   {                                                                                      \
-    const float* const row = buf[(r) & 1] + (tid & (DS - 1)) * R;                        \
-    const int m = n - (r) * R < R ? n - (r) * R : R;                                     \
-    if (tid < DS) {                                                                      \
-      for (int h = 0; h < (m + 63) / 64; ++h) {                                          \
-        float4 x[16];                                                                    \
-        _Pragma("unroll") for (int i = 0; i < 16; ++i)                                   \
-          x[i] = *reinterpret_cast<const float4*>(row + 4 * (16 * h + (i ^ f)));         \
-        __builtin_amdgcn_sched_barrier(0);                                               \
-        _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                 \
-          a = a + x[i].x;                                                                \
-          a = a + x[i].y;                                                                \
-          a = a + x[i].z;                                                                \
-          a = a + x[i].w;                                                                \
+    if (wave == 0) {                                                                     \
+      if (lane < DS) {                                                                   \
+        const float* const row = buf[(r) & 1] + lane * R;                                \
+        const int m = n - (r) * R < R ? n - (r) * R : R;                                 \
+        const int ng = (m + 63) / 64;                                                    \
+        float4 xa[16], xb[16];                                                           \
+        rd(xa, row, 0);                                                                  \
+        _Pragma("unroll") for (int h = 0; h < NG; h += 2) {                              \
+          if (h < ng) {                                                                  \
+            if (h + 1 < ng) rd(xb, row, h + 1);                                          \
+            __builtin_amdgcn_sched_barrier(0);                                           \
+            a = add(xa, a);                                                              \
+          }                                                                              \
+          if (h + 1 < ng) {                                                              \
+            if (h + 2 < ng) rd(xa, row, h + 2);                                          \
+            __builtin_amdgcn_sched_barrier(0);                                           \
+            a = add(xb, a);                                                              \
+          }                                                                              \
         }                                                                                \
       }                                                                                  \
-    }                                                                                    \
-    if ((r) + 1 < rounds) {                                                              \
+    } else if ((r) + 1 < rounds) {                                                       \
       store(vnext, (r) + 1);                                                             \
       if ((r) + 3 < rounds) load(vnext, (r) + 3);                                        \
     }                                                                                    \
@@ -870,8 +926,8 @@ __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chun
       DET_IA_FOLD_ROUND(r + 1, va)
     }
 #undef DET_IA_FOLD_ROUND
-    if (tid < DS) {
-      float* const o = out + static_cast<int64_t>(k) * out_ld + d0 + tid;
+    if (wave == 0 && lane < DS) {
+      float* const o = out + static_cast<int64_t>(k) * out_ld + d0 + lane;
       *o = *o + a;
     }
   }
