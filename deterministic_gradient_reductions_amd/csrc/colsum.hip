@@ -117,59 +117,50 @@ __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
 }
 
 // Phase 2: fold the tile slots of every head left to right and add the totals.
-// One workgroup per 32 heads. The slots are staged through LDS in pieces of
-// kPiece tiles so that all their loads are in flight together; then one thread
-// per (head, gradient) runs the strictly sequential fold over the piece.
-constexpr int kFoldHeads = 32;
-constexpr int kPiece = 256;
+// One wave per (head, gradient). Lane j loads tiles j, j + 64, j + 128 and
+// j + 192 of a round of 256 tiles (the next round's loads are in flight while
+// a round is added; tiles past S read as -0.0, which leaves the sum bitwise
+// unchanged). The values are then added in tile order through readlane: one
+// dependent add per tile, the same in every lane.
+constexpr int kFoldRound = 256;
 
-__global__ __launch_bounds__(kWG) void colsum_fold_kernel(const float* __restrict__ slot1,
-                                                          const float* __restrict__ slot2, int64_t S, int64_t H,
-                                                          float* __restrict__ dA_log, float* __restrict__ ddt_bias) {
-  __shared__ float buf[2][kPiece][kFoldHeads];
-  const int tid = threadIdx.x;
-  const int64_t h0 = static_cast<int64_t>(blockIdx.x) * kFoldHeads;
-  const int which = tid / kFoldHeads;  // 0: dA_log, 1: ddt_bias (threads 0..63 fold)
-  const int hl = tid % kFoldHeads;
-  float tot = -0.0f;
-  for (int64_t i0 = 0; i0 < S; i0 += kPiece) {
-    const int64_t n = S - i0 < kPiece ? S - i0 : kPiece;
-    // every thread issues all of its loads before the first LDS store
-    constexpr int kPer = kPiece * kFoldHeads / kWG;
-    float v1[kPer], v2[kPer];
+__device__ __forceinline__ void fold_load(float (&v)[4], const float* s, int64_t i0, int64_t S, int64_t H,
+                                          int lane) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int j = tid + u * kWG;
-      const int64_t i = i0 + j / kFoldHeads;
-      const int64_t h = h0 + j % kFoldHeads;
-      const bool ok = h < H && j < n * kFoldHeads;
-      v1[u] = ok ? slot1[i * H + h] : 0.0f;
-      v2[u] = ok ? slot2[i * H + h] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int j = tid + u * kWG;
-      buf[0][j / kFoldHeads][j % kFoldHeads] = v1[u];
-      buf[1][j / kFoldHeads][j % kFoldHeads] = v2[u];
-    }
-    __syncthreads();
-    if (tid < 2 * kFoldHeads) {
-      int64_t i = 0;
-      for (; i + 8 <= n; i += 8) {
-        float b[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) b[u] = buf[which][i + u][hl];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) tot = tot + b[u];
-      }
-      for (; i < n; ++i) tot = tot + buf[which][i][hl];
-    }
-    __syncthreads();
+  for (int q = 0; q < 4; ++q) {
+    const int64_t i = i0 + lane + 64 * q;
+    v[q] = i < S ? s[i * H] : -0.0f;
   }
-  const int64_t h = h0 + hl;
-  if (tid < 2 * kFoldHeads && h < H) {
-    float* o = which == 0 ? dA_log : ddt_bias;
-    o[h] = o[h] + tot;
+}
+
+__device__ __forceinline__ float fold_add(const float (&v)[4], float tot) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < 64; ++j) tot = tot + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[q]), j));
+  return tot;
+}
+
+__global__ __launch_bounds__(64) void colsum_fold_kernel(const float* __restrict__ slot1,
+                                                         const float* __restrict__ slot2, int64_t S, int64_t H,
+                                                         float* __restrict__ dA_log, float* __restrict__ ddt_bias) {
+  const int lane = threadIdx.x;
+  const int64_t h = blockIdx.x;
+  const bool second = blockIdx.y != 0;
+  const float* const s = (second ? slot2 : slot1) + h;
+  float tot = -0.0f;
+  float va[4], vb[4];
+  fold_load(va, s, 0, S, H, lane);
+  for (int64_t i0 = 0; i0 < S; i0 += 2 * kFoldRound) {
+    if (i0 + kFoldRound < S) fold_load(vb, s, i0 + kFoldRound, S, H, lane);
+    tot = fold_add(va, tot);
+    if (i0 + kFoldRound >= S) break;
+    if (i0 + 2 * kFoldRound < S) fold_load(va, s, i0 + 2 * kFoldRound, S, H, lane);
+    tot = fold_add(vb, tot);
+  }
+  if (lane == 0) {
+    float* const o = (second ? ddt_bias : dA_log) + h;
+    *o = *o + tot;
   }
 }
 
@@ -192,8 +183,8 @@ void launch_one(const ColsumArgs& p, int atomic, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((colsum_kernel<R, BH, true>), grid, dim3(kWG), 0, st, p);
   } else {
     hipLaunchKernelGGL((colsum_kernel<R, BH, false>), grid, dim3(kWG), 0, st, p);
-    hipLaunchKernelGGL(colsum_fold_kernel, dim3(static_cast<uint32_t>(ceil_div(p.H, kFoldHeads))), dim3(kWG), 0, st,
-                       p.slot1, p.slot2, static_cast<int64_t>(grid.x), p.H, p.dA_log, p.ddt_bias);
+    hipLaunchKernelGGL(colsum_fold_kernel, dim3(static_cast<uint32_t>(p.H), 2), dim3(64), 0, st, p.slot1, p.slot2,
+                       static_cast<int64_t>(grid.x), p.H, p.dA_log, p.ddt_bias);
   }
 }
 
