@@ -36,7 +36,12 @@ constexpr int kBlockPos = 4096;  // source positions per count/scatter block
 constexpr int kMaxRows = 16384;  // LDS histogram capacity (64 KiB)
 constexpr int kMaxDim = 512;
 
-constexpr int kSegBlocks = 32;   // blocks per prefix segment
+constexpr int kSegBlocks = 16;   // blocks per prefix segment
+// block counts and their prefix inside a segment are stored as 16-bit words
+static_assert((kSegBlocks - 1) * kBlockPos <= 0xFFFF, "a segment prefix must fit in 16 bits");
+
+// Row stride of the block histograms (16-bit entries): rows start 16-byte aligned.
+inline __host__ __device__ int hist_stride(int64_t n_rows) { return static_cast<int>((n_rows + 7) / 8 * 8); }
 constexpr int kMaxGroups = kMaxRows / 256;  // workgroups of the offsets kernel (one thread per id)
 
 struct Layout {
@@ -50,7 +55,7 @@ Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L) {
   l.nseg = ceil_div(l.nblk, kSegBlocks);
   l.max_chunks = n_src / L + (n_rows < n_src ? n_rows : n_src) + 1;
   size_t o = DET_WS_HEADER_BYTES;
-  l.hist = o;      o = align_up(o + static_cast<size_t>(l.nblk * n_rows) * 4, 256);
+  l.hist = o;      o = align_up(o + static_cast<size_t>(l.nblk * hist_stride(n_rows)) * 2, 256);
   l.segtot = o;    o = align_up(o + static_cast<size_t>(l.nseg * n_rows) * 4, 256);
   l.pub = o;       o = align_up(o + static_cast<size_t>(3 * kMaxGroups) * 4, 256);
   l.seg_off = o;   o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
@@ -84,15 +89,15 @@ __device__ __forceinline__ uint64_t match_peers(int32_t id, bool valid) {
 // hot Zipf key makes a few lanes of an instruction share an address, which
 // the LDS serialises; that is far cheaper than matching lanes first).
 __global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                uint32_t* __restrict__ hist, uint32_t* __restrict__ hdr,
-                                                uint32_t* __restrict__ pub) {
+                                                int hist_ld, uint16_t* __restrict__ hist,
+                                                uint32_t* __restrict__ hdr, uint32_t* __restrict__ pub) {
   extern __shared__ uint32_t lds_hist[];
   // the offsets kernel's exchange words start unpublished, its timeout flag clear
   if (blockIdx.x == 0) {
     if (threadIdx.x < 3 * kMaxGroups) pub[threadIdx.x] = 0u;
     if (threadIdx.x == 0) hdr[2] = 0u;
   }
-  for (int k = threadIdx.x; k < n_rows; k += 256) lds_hist[k] = 0u;
+  for (int k = threadIdx.x; k < hist_ld; k += 256) lds_hist[k] = 0u;
   __syncthreads();
   const int64_t b = blockIdx.x;
   const int64_t p0 = b * kBlockPos;
@@ -114,26 +119,30 @@ __global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids,
       ++bad;
   }
   __syncthreads();
-  uint32_t* row = hist + b * n_rows;
-  for (int k = threadIdx.x; k < n_rows; k += 256) row[k] = lds_hist[k];
+  // counts are at most kBlockPos: eight 16-bit entries per 16-byte store
+  uint4* row = reinterpret_cast<uint4*>(hist + b * hist_ld);
+  for (int k8 = threadIdx.x; k8 < hist_ld / 8; k8 += 256) {
+    const uint32_t* c = lds_hist + 8 * k8;
+    row[k8] = make_uint4(c[0] | c[1] << 16, c[2] | c[3] << 16, c[4] | c[5] << 16, c[6] | c[7] << 16);
+  }
   if (bad) atomicAdd(hdr, bad);
 }
 
 // ---- 2a. per id and segment of kSegBlocks blocks: exclusive prefix over the
 // segment's blocks (in place) and the segment total.
-__global__ __launch_bounds__(256) void ia_prefix_seg(uint32_t* __restrict__ hist, int64_t nblk, int n_rows,
-                                                     uint32_t* __restrict__ segtot) {
+__global__ __launch_bounds__(256) void ia_prefix_seg(uint16_t* __restrict__ hist, int hist_ld, int64_t nblk,
+                                                     int n_rows, uint32_t* __restrict__ segtot) {
   const int k = blockIdx.x * 256 + threadIdx.x;
   const int64_t seg = blockIdx.y;
   if (k >= n_rows) return;
   const int64_t b0 = seg * kSegBlocks;
   uint32_t c[kSegBlocks];
 #pragma unroll
-  for (int j = 0; j < kSegBlocks; ++j) c[j] = (b0 + j < nblk) ? hist[(b0 + j) * n_rows + k] : 0u;
+  for (int j = 0; j < kSegBlocks; ++j) c[j] = (b0 + j < nblk) ? hist[(b0 + j) * hist_ld + k] : 0u;
   uint32_t run = 0;
 #pragma unroll
   for (int j = 0; j < kSegBlocks; ++j) {
-    if (b0 + j < nblk) hist[(b0 + j) * n_rows + k] = run;
+    if (b0 + j < nblk) hist[(b0 + j) * hist_ld + k] = static_cast<uint16_t>(run);
     run += c[j];
   }
   segtot[seg * n_rows + k] = run;
@@ -346,7 +355,7 @@ constexpr uint32_t kPackRank = 14, kPackSize = 20;
 
 template <int NW>
 __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                  int tab_ld, const uint32_t* __restrict__ prefix,
+                                                  int tab_ld, int hist_ld, const uint16_t* __restrict__ prefix,
                                                   const uint32_t* __restrict__ segbase,
                                                   const uint32_t* __restrict__ seg_off, int32_t* __restrict__ perm) {
   extern __shared__ uint32_t lds[];
@@ -403,7 +412,7 @@ __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ id
     }
   }
   __syncthreads();
-  const uint32_t* pre = prefix + b * n_rows;
+  const uint16_t* pre = prefix + b * hist_ld;
   const uint32_t* sb = segbase + (b / kSegBlocks) * n_rows;
   // only ids present in the block need a base (absent ids are never read in
   // the walk); absent ids load entry 0 instead, so the loads need no branches
@@ -474,7 +483,7 @@ int scatter_waves(int64_t n_rows) {
 
 template <int NW>
 void launch_scatter(int64_t nblk, int n_rows, hipStream_t st, const int32_t* ids, int64_t n_src,
-                    const uint32_t* hist, const uint32_t* segtot, const uint32_t* seg_off, int32_t* perm) {
+                    const uint16_t* hist, const uint32_t* segtot, const uint32_t* seg_off, int32_t* perm) {
   const int pad_rows = (n_rows + 3) / 4 * 4;  // table rows padded for 16-byte zeroing
   const size_t lds = static_cast<size_t>(NW) * pad_rows * 4 + kBlockPos * 4;
   if (lds > 64 * 1024) {
@@ -486,7 +495,7 @@ void launch_scatter(int64_t nblk, int n_rows, hipStream_t st, const int32_t* ids
     }
   }
   hipLaunchKernelGGL(ia_scatter<NW>, dim3(static_cast<uint32_t>(nblk)), dim3(256), lds, st, ids, n_src, n_rows,
-                     pad_rows, hist, segtot, seg_off, perm);
+                     pad_rows, hist_stride(n_rows), hist, segtot, seg_off, perm);
 }
 
 // Binary search: the id whose chunk range [chunk_off[k], chunk_off[k+1]) holds c.
@@ -1032,7 +1041,8 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   }
   char* w = static_cast<char*>(ws);
   auto* hdr = reinterpret_cast<uint32_t*>(w);
-  auto* hist = reinterpret_cast<uint32_t*>(w + l.hist);
+  auto* hist = reinterpret_cast<uint16_t*>(w + l.hist);
+  const int hist_ld = hist_stride(n_rows);
   auto* pub = reinterpret_cast<uint32_t*>(w + l.pub);
   auto* seg_off = reinterpret_cast<uint32_t*>(w + l.seg_off);
   auto* chunk_off = reinterpret_cast<uint32_t*>(w + l.chunk_off);
@@ -1040,10 +1050,11 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   auto* chunk_desc = reinterpret_cast<int4*>(w + l.chunk_desc);
   auto* perm = reinterpret_cast<int32_t*>(w + l.perm);
   auto* scratch = reinterpret_cast<float*>(w + l.scratch);
-  const size_t lds_count = static_cast<size_t>(n_rows) * 4;
+  const size_t lds_count = static_cast<size_t>(hist_ld) * 4;
   auto* segtot = reinterpret_cast<uint32_t*>(w + l.segtot);
-  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, hist, hdr, pub);
-  hipLaunchKernelGGL(ia_prefix_seg, dim3(ceil_div(n_rows, 256), l.nseg), dim3(256), 0, st, hist, l.nblk, nr, segtot);
+  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, hist_ld, hist, hdr, pub);
+  hipLaunchKernelGGL(ia_prefix_seg, dim3(ceil_div(n_rows, 256), l.nseg), dim3(256), 0, st, hist, hist_ld, l.nblk, nr,
+                     segtot);
   const uint32_t rcp = static_cast<uint32_t>(0xFFFFFFFFull / static_cast<uint64_t>(L));
   hipLaunchKernelGGL(ia_offsets, dim3(static_cast<uint32_t>(ceil_div(n_rows, 256))), dim3(256), 0, st, segtot, l.nseg,
                      nr, L, rcp, n_src, pub, seg_off, chunk_off, full_off, chunk_desc, hdr);
