@@ -116,3 +116,21 @@ def wgrad_exact_integer(main_grad0, G, X, offs):
                     s += int(_w(G[r][i])) * int(_w(X[r][j]))
                 out[e, i, j] = F(out[e, i, j] + F(s))
     return out
+
+
+def dbias(dbias0, dA, offs, block_m):
+    M = len(dA)
+    N = len(dA[0]) if M else 0
+    out = [[F(v) for v in row] for row in dbias0]
+    b = []
+    for e, o in enumerate(offs):
+        lo = 0 if e == 0 else b[-1]
+        b.append(min(max(int(o), lo), M))
+    for e in range(len(b) - 1):
+        if b[e + 1] <= b[e]:
+            continue
+        for n in range(N):
+            col = [_w(dA[m][n]) for m in range(b[e], b[e + 1])]
+            slots = [tree(t) for t in padded_tiles(col, block_m)]
+            out[e][n] = F(out[e][n] + fold(slots))
+    return np.array(out, np.float32).reshape(np.asarray(dbias0).shape)

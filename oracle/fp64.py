@@ -63,3 +63,18 @@ def wgrad64(main_grad0, G_bits, X_bits, offs, experts=None):
         if hi > lo:
             out[e] += widen(G_bits[lo:hi]).T @ widen(X_bits[lo:hi])
     return out
+
+
+def dbias64(dbias0, dA_bits, offs):
+    out = np.asarray(dbias0, np.float64).copy()
+    absum = np.zeros_like(out)
+    M = dA_bits.shape[0]
+    prev = 0
+    b = []
+    for e, o in enumerate(np.asarray(offs, np.int64)):
+        v = int(min(max(int(o), 0 if e == 0 else prev), M)); b.append(v); prev = v
+    for e in range(len(b) - 1):
+        x = widen(dA_bits[b[e]:b[e + 1]])
+        out[e] += x.sum(0)
+        absum[e] = np.abs(x).sum(0)
+    return out, absum

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from oracle import brute, colsum as oc, dprob as od, fp64, index_add as oi, wgrad as ow
+from oracle import brute, colsum as oc, dbias as odb, dprob as od, fp64, index_add as oi, wgrad as ow
 from oracle.primitives import widen_bf16
 
 U = 2.0 ** -24
@@ -92,6 +92,100 @@ def test_dprob_invariants():
     # empty problem leaves the output bitwise unchanged
     e = od.grouped_dprob(inp.dprob0, inp.dY, inp.C, np.array([4, 4, 4], np.int32))
     assert np.array_equal(bits(e), bits(inp.dprob0))
+
+
+# ----------------------------------------------------------------------- dbias
+@pytest.mark.parametrize("M,N,BM", [(4096, 64, 128), (777, 33, 64), (300, 8, 256), (5, 3, 64)])
+def test_dbias_fp64_bound(M, N, BM):
+    inp = W.dbias_inputs(M=M, N=N, E=5, min_tokens=1, seed=17, out_init="normal")
+    got = odb.grouped_dbias(inp.dbias0, inp.dA, inp.offs, BM)
+    exact, absum = fp64.dbias64(inp.dbias0, inp.dA, inp.offs)
+    n_tiles = max(len(t) for t in odb.tile_ranges(inp.offs, M, BM))
+    d = int(np.log2(BM)) + n_tiles + 1  # tree depth + fold length + final add
+    bound = gamma(d) * (absum + np.abs(inp.dbias0)) + 2.0 ** -149
+    assert np.all(np.abs(got - exact) <= bound)
+    assert rel_l2(got, exact) <= 1e-5
+
+
+def test_dbias_exact_integers():
+    inp = W.dbias_inputs(M=3000, N=40, E=6, min_tokens=1, seed=19, integer=True)
+    d0 = np.random.default_rng(5).integers(-100, 100, inp.dbias0.shape).astype(np.float32)
+    got = odb.grouped_dbias(d0, inp.dA, inp.offs, 128)
+    x = widen_bf16(inp.dA).astype(np.int64)
+    exact = d0.astype(np.int64).copy()
+    for e in range(len(inp.offs) - 1):
+        exact[e] += x[inp.offs[e]:inp.offs[e + 1]].sum(0)
+    assert np.array_equal(got.astype(np.int64), exact)
+
+
+def test_dbias_order_probe():
+    """+-2^40 at two rows of one expert: the count of 1.0s absorbed reveals the
+    tree inside a tile and the left fold across tiles."""
+    BM, rows = 64, 640
+    cases = [(0, 1), (0, 63), (5, 40), (64, 65), (10, 300), (0, 639), (200, 500)]
+    N = len(cases)
+    x = np.ones((rows, N), np.float32)
+    for j, (p, q) in enumerate(cases):
+        x[p, j], x[q, j] = 2.0 ** 40, -(2.0 ** 40)
+    got = odb.grouped_dbias(np.zeros((1, N), np.float32), W.bf16_bits(x), np.array([0, rows], np.int32), BM)
+    n_t = rows // BM
+    for j, (p, q) in enumerate(cases):
+        tp, tq = p // BM, q // BM
+        if tp == tq:
+            want = (BM - 2 ** int((p % BM) ^ (q % BM)).bit_length()) + BM * (n_t - 1)
+        else:
+            want = BM * (n_t - 1 - tq)
+        assert got[0, j] == want, (p, q, got[0, j], want)
+
+
+def test_dbias_brute_force_and_offsets():
+    inp = W.dbias_inputs(M=50, N=5, E=4, min_tokens=1, seed=23, out_init="normal")
+    for offs in (inp.offs, np.array([3, 20, 20, 9, 44], np.int32), np.array([-5, 7, 60, 2, 70], np.int32)):
+        for BM in (8, 16, 64):
+            got = odb.grouped_dbias(inp.dbias0, inp.dA, offs, BM)
+            ref = brute.dbias(inp.dbias0, inp.dA, offs, BM)
+            assert np.array_equal(bits(got), bits(ref)), (offs, BM)
+    # clamped monotone bounds: an expert whose range is empty keeps its row bitwise
+    got = odb.grouped_dbias(inp.dbias0, inp.dA, np.array([3, 20, 20, 9, 44], np.int32), 16)
+    assert np.array_equal(bits(got[1]), bits(inp.dbias0[1]))
+    assert np.array_equal(bits(got[2]), bits(inp.dbias0[2]))
+
+
+def test_dbias_aligned_experts_are_absolute_m_blocks():
+    """With every expert starting on a block boundary, the tiles are the absolute
+    M blocks: slots from the whole matrix cut into blocks, folded per expert."""
+    BM = 32
+    inp = W.dbias_inputs(M=320, N=7, E=3, min_tokens=1, seed=29, out_init="normal")
+    offs = np.array([0, 64, 64, 320], np.int32)
+    got = odb.grouped_dbias(inp.dbias0, inp.dA, offs, BM)
+    x = widen_bf16(inp.dA)
+    blocks = [x[r:r + BM] for r in range(0, 320, BM)]
+    slots = []
+    for blk in blocks:
+        v = blk.astype(np.float32)
+        while v.shape[0] > 1:
+            v = (v[0::2] + v[1::2]).astype(np.float32)
+        slots.append(v[0])
+    want = inp.dbias0.copy()
+    for e, (lo, hi) in enumerate([(0, 2), (2, 2), (2, 10)]):
+        if hi > lo:
+            t = np.float32(-0.0) * np.ones(7, np.float32)
+            for s_ in slots[lo:hi]:
+                t = (t + s_).astype(np.float32)
+            want[e] = (want[e] + t).astype(np.float32)
+    assert np.array_equal(bits(got), bits(want))
+
+
+def test_dbias_invariants():
+    inp = W.dbias_inputs(M=1000, N=16, E=4, min_tokens=1, seed=31, out_init="normal")
+    z = odb.grouped_dbias(np.full(inp.dbias0.shape, -0.0, np.float32), inp.dA, inp.offs, 128)
+    full = odb.grouped_dbias(inp.dbias0, inp.dA, inp.offs, 128)
+    assert np.array_equal(bits(full), bits(inp.dbias0 + z))  # accumulate = one add of the total
+    dA8 = W.bf16_bits(widen_bf16(inp.dA) * np.float32(8))
+    z8 = odb.grouped_dbias(np.zeros(inp.dbias0.shape, np.float32), dA8, inp.offs, 128)
+    assert np.array_equal(z8, z * np.float32(8))
+    e = odb.grouped_dbias(inp.dbias0, inp.dA, np.array([7] * 5, np.int32), 128)
+    assert np.array_equal(bits(e), bits(inp.dbias0))
 
 
 # ---------------------------------------------------------------------- colsum

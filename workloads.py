@@ -151,6 +151,35 @@ def dprob_inputs(M: int = 16384, N: int = 2048, E: int = 8, min_tokens: int = 25
     return DprobInputs(M, N, offs, dY, C, d0)
 
 
+# -------------------------------------------------------------------------- dbias
+@dataclass
+class DbiasInputs:
+    """Grouped dsReLU backward dbias inputs: per-expert column sums of dA."""
+    M: int
+    N: int
+    offs: np.ndarray    # int32 [E+1] expert row offsets
+    dA: np.ndarray      # uint16 [M, N]
+    dbias0: np.ndarray  # float32 [E, N]
+
+
+def dbias_inputs(M: int = 16384, N: int = 2048, E: int = 8, min_tokens: int = 256, seed: int = 6,
+                 out_init: str = "zero", integer: bool = False) -> DbiasInputs:
+    """Expert sizes as for dprob (min_tokens + a uniform multinomial); dA ~ N(0, 1)
+    (or small integers in [-4, 4]); dbias0 zero or N(0, 1)."""
+    counts = expert_counts(M, E, min_tokens, seed, 0) if M >= E * min_tokens else \
+        np.array([M // E + (1 if e < M % E else 0) for e in range(E)], np.int64)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    if integer:
+        dA = bf16_bits(_rng(seed, 1).integers(-4, 5, size=(M, N)).astype(np.float32))
+    else:
+        dA = bf16_bits(_rng(seed, 1).standard_normal((M, N), dtype=np.float32))
+    if out_init == "zero":
+        d0 = np.zeros((E, N), np.float32)
+    else:
+        d0 = _rng(seed, 2).standard_normal((E, N), dtype=np.float32)
+    return DbiasInputs(M, N, offs, dA, d0)
+
+
 # -------------------------------------------------------------------------- wgrad
 @dataclass
 class WgradInputs:
