@@ -12,6 +12,7 @@ Functions (same names as the C ABI):
     det_index_add(out, ids, src, cfg=None, atomic=False)
     det_grouped_dprob(dprob, dY, C, offs, cfg=None, atomic=False)
     det_grouped_wgrad_acc(main_grad, G, X, offs, cfg=None, atomic=False)
+    det_grouped_dbias(dbias, dA, offs, cfg=None, atomic=False)
 Every function accepts ``ws=`` (a Workspace or a uint8 device tensor) and
 ``stream=`` (a torch.cuda.Stream); by default a cached per-stream workspace
 and torch's current stream are used.
@@ -26,7 +27,8 @@ __all__ = [
     "lib", "library_path", "DetError", "ColsumCfg", "IndexAddCfg", "DprobCfg", "WgradCfg", "Workspace",
     "det_abi_version", "det_colsum", "det_colsum_select_cfg", "det_colsum_workspace_size", "det_index_add",
     "det_index_add_workspace_size", "det_index_add_bad_ids", "det_grouped_dprob", "det_grouped_dprob_workspace_size",
-    "det_grouped_wgrad_acc", "det_grouped_wgrad_acc_workspace_size", "det_workspace_init", "det_detmath_eval",
+    "det_grouped_wgrad_acc", "det_grouped_wgrad_acc_workspace_size", "det_grouped_dbias",
+    "det_grouped_dbias_workspace_size", "det_workspace_init", "det_detmath_eval",
     "DET_OK", "DET_ERR_INVALID_ARG", "DET_ERR_UNSUPPORTED", "DET_ERR_WORKSPACE", "DET_ERR_OVERLAP", "DET_ERR_HIP",
 ]
 
@@ -53,6 +55,10 @@ class IndexAddCfg(ctypes.Structure):
 
 class DprobCfg(ctypes.Structure):
     _fields_ = [("tile_n", ctypes.c_int32), ("rows_per_wg", ctypes.c_int32)]
+
+
+class DbiasCfg(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32)]
 
 
 class WgradCfg(ctypes.Structure):
@@ -84,6 +90,10 @@ _SIGS = {
     "det_grouped_wgrad_acc_workspace_size": ([_I64, _I32, _I64, _I64, ctypes.POINTER(WgradCfg), _INT,
                                               ctypes.POINTER(_SZ)], _INT),
     "det_detmath_eval": ([_P, _P, _I64, _INT, _P], _INT),
+    "det_grouped_dbias_workspace_size": ([_I64, _I64, _I32, ctypes.POINTER(DbiasCfg), _INT, ctypes.POINTER(_SZ)],
+                                         _INT),
+    "det_grouped_dbias": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I32, ctypes.POINTER(DbiasCfg), _P, _SZ, _INT, _P],
+                          _INT),
     "det_grouped_wgrad_acc": ([_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I32, _I64, _I64, _I64,
                                ctypes.POINTER(WgradCfg), _P, _SZ, _INT, _P], _INT),
 }
@@ -259,6 +269,27 @@ def det_grouped_dprob(dprob, dY, C, offs, cfg: DprobCfg | None = None, atomic=Fa
     _check(lib().det_grouped_dprob(_ptr(dprob), _ptr(dY), dY.stride(0), _ptr(C), C.stride(0), M, N, _ptr(offs),
                                    offs.numel() - 1, ctypes.byref(cfg) if cfg else None, wp, wn,
                                    _atomic_flag(atomic), _stream_handle(stream)))
+
+
+# ---------------------------------------------------------------------- dbias
+def det_grouped_dbias_workspace_size(M: int, N: int, E: int, cfg: DbiasCfg | None = None, atomic=False) -> int:
+    n = _SZ()
+    _check(lib().det_grouped_dbias_workspace_size(M, N, E, ctypes.byref(cfg) if cfg else None, _atomic_flag(atomic),
+                                                  ctypes.byref(n)))
+    return n.value
+
+
+def det_grouped_dbias(dbias, dA, offs, cfg: DbiasCfg | None = None, atomic=False, ws=None, stream=None) -> None:
+    """dbias[e] += column sums of dA[offs[e]:offs[e+1]]; dA bf16 [M, N], dbias fp32 [E, N]."""
+    M, N = dA.shape
+    E = offs.numel() - 1
+    if dA.stride(1) != 1 or dbias.stride(1) != 1:
+        raise ValueError("dA and dbias must have unit column stride")
+    need = det_grouped_dbias_workspace_size(M, N, E, cfg, atomic) if atomic in (0, 1, False, True) else 0
+    wp, wn = _workspace(need, ws, stream)
+    _check(lib().det_grouped_dbias(_ptr(dbias), dbias.stride(0), _ptr(dA), dA.stride(0), M, N, _ptr(offs), E,
+                                   ctypes.byref(cfg) if cfg else None, wp, wn, _atomic_flag(atomic),
+                                   _stream_handle(stream)))
 
 
 # ---------------------------------------------------------------------- wgrad

@@ -181,6 +181,47 @@ int det_grouped_dprob(float* dprob, const void* dY, int64_t ldy, const void* C, 
                       int atomic, void* stream);
 
 /* ------------------------------------------------------------------------
+ * det_grouped_dbias: dbias of a grouped-GEMM dsReLU backward.
+ * cudnn-frontend PR #521, the commit that extends the determinism flag to
+ * dbias: dbias contends across M tiles, so each (M block, column) gets its
+ * own float32 slot with a single writer, followed by a per-expert segment sum
+ * of the slots; experts start on M-tile boundaries, so no tile holds rows of
+ * two experts.
+ *
+ *   dbias[e][n] += sum_{offs[e] <= m < offs[e+1]} dA[m][n]
+ *
+ * Canonical order: expert bounds b_0 = clamp(offs[0], 0, M), b_e =
+ * clamp(offs[e], b_{e-1}, M) (read on the device only); expert e's rows cut
+ * into tiles of block_m rows counted from b_e (with block_m-aligned experts
+ * these are the absolute M blocks); per tile and column the adjacent pairwise
+ * tree of its block_m values (rows past the expert are -0.0); the expert's
+ * tile slots folded left to right; one add into dbias[e][n]. An expert with
+ * no rows leaves dbias[e] untouched. block_m changes the bits; block_n only
+ * shapes the launch.
+ *
+ * dA:    [M, N] bf16, row stride lda >= N; N and lda multiples of 8 and dA
+ *        16-byte aligned (DET_ERR_UNSUPPORTED otherwise).
+ * dbias: [E, N] float32, row stride ld_e >= N, accumulated.
+ * offs:  [E+1] int32 device array; E <= 65535.
+ * cfg:   NULL = {block_m = 128, block_n = 512}; block_m in {64, 128, 256},
+ *        block_n must be 512.
+ * ws:    the deterministic route needs det_grouped_dbias_workspace_size()
+ *        bytes: the header, the per-expert tile starts and one float32 slot
+ *        per possible tile and column, (ceil(M / block_m) + E) x N.
+ *        atomic = 1 needs none (the tile partials are added with float
+ *        atomics). */
+typedef struct {
+  int32_t block_m;
+  int32_t block_n;
+} det_dbias_cfg;
+
+int det_grouped_dbias_workspace_size(int64_t M, int64_t N, int32_t E, const det_dbias_cfg* cfg, int atomic,
+                                     size_t* bytes);
+int det_grouped_dbias(float* dbias, int64_t ld_e, const void* dA, int64_t lda, int64_t M, int64_t N,
+                      const int32_t* offs, int32_t E, const det_dbias_cfg* cfg, void* ws, size_t ws_bytes, int atomic,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
  * det_grouped_wgrad_acc: main_grad[e] += G_e^T X_e with fixed-order split-K.
  * FlashInfer PR #8602 (fused fp32 weight-gradient accumulate into main_grad)
  * and #8924 (deterministic accumulate: bitwise AccumulateGrad of the

@@ -86,6 +86,33 @@ def test_dprob_validation():
     assert L.det_grouped_dprob_workspace_size(16384, 2048, None, 0, ctypes.byref(n)) == dg.DET_OK and n.value == 0
 
 
+def test_dbias_validation():
+    L = lib()
+    n = ctypes.c_size_t(0)
+    # workspace: header + tile starts + (ceil(M/128) + E) x N slots; none for the atomic arm
+    assert L.det_grouped_dbias_workspace_size(16384, 2048, 8, None, 0, ctypes.byref(n)) == dg.DET_OK
+    assert n.value == 256 + 256 + (128 + 8) * 2048 * 4
+    assert L.det_grouped_dbias_workspace_size(16384, 2048, 8, None, 1, ctypes.byref(n)) == dg.DET_OK and n.value == 0
+    assert L.det_grouped_dbias_workspace_size(16384, 2048, 8, None, 2, ctypes.byref(n)) == dg.DET_ERR_INVALID_ARG
+    for cfg in (dg.DbiasCfg(96, 512), dg.DbiasCfg(128, 256)):
+        assert L.det_grouped_dbias_workspace_size(64, 64, 2, ctypes.byref(cfg), 0, ctypes.byref(n)) == \
+            dg.DET_ERR_INVALID_ARG
+    big = 1 << 22
+    # negative sizes, ld < N, N not a multiple of 8, NULL pointers, workspace too small
+    assert L.det_grouped_dbias(FAKE, 64, FAKE, 64, -1, 64, FAKE, 2, None, FAKE, big, 0, None) == dg.DET_ERR_INVALID_ARG
+    assert L.det_grouped_dbias(FAKE, 32, FAKE, 64, 16, 64, FAKE, 2, None, FAKE, big, 0, None) == dg.DET_ERR_INVALID_ARG
+    assert L.det_grouped_dbias(FAKE, 64, FAKE, 60, 16, 60, FAKE, 2, None, FAKE, big, 0, None) == dg.DET_ERR_UNSUPPORTED
+    assert L.det_grouped_dbias(None, 64, FAKE, 64, 16, 64, FAKE, 2, None, FAKE, big, 0, None) == dg.DET_ERR_INVALID_ARG
+    assert L.det_grouped_dbias(FAKE, 64, FAKE, 64, 16, 64, FAKE, 2, None, FAKE, 512, 0, None) == dg.DET_ERR_WORKSPACE
+    # output overlapping an input
+    base = 0x400000
+    assert L.det_grouped_dbias(P(base + 64), 64, P(base), 64, 16, 64, P(base + 65536), 2, None, None, 0, 1, None) == \
+        dg.DET_ERR_OVERLAP
+    # empty problems: OK with nothing launched
+    assert L.det_grouped_dbias(None, 64, None, 64, 0, 64, None, 2, None, None, 0, 0, None) == dg.DET_OK
+    assert L.det_grouped_dbias(None, 64, None, 64, 16, 64, None, 0, None, None, 0, 0, None) == dg.DET_OK
+
+
 def test_colsum_validation_and_selector():
     L = lib()
     # shape-only rule: block_h = 8; block_t the largest of 256/128 that still
