@@ -11,10 +11,12 @@
 // of the expert's slots, added once into dbias.
 //
 // Tile kernel: a workgroup owns one tile (block_m rows of one expert) and 512
-// columns. Lane l of each wave holds 8 consecutive columns (one 16-byte load
-// per row, fully coalesced); wave w takes the w-th quarter of the tile's rows
-// and reduces it with the adjacent pairwise tree in registers (rows past the
-// expert's end are -0.0); the four quarter values meet in LDS as
+// columns; consecutive workgroups take the column blocks of one tile. Lane l
+// of each wave holds 8 consecutive columns (one 16-byte load per row, fully
+// coalesced); wave w takes the w-th quarter of the tile's rows and reduces it
+// with the adjacent pairwise tree, fed row by row into a stack of partial
+// sums while the next 16 rows' loads are in flight (rows past the expert's
+// end are -0.0); the four quarter values meet in LDS as
 // ((q0 + q1) + (q2 + q3)), the top two levels of the same tree. The slot (or,
 // on the atomic arm, a float atomic add into dbias) is written once.
 // Fold kernel: one thread per (expert, column) adds the expert's slots left to
@@ -30,82 +32,107 @@ namespace {
 
 constexpr int kCols = 512;  // columns per workgroup: 64 lanes x 8
 
+// Inclusive scans over the 64 lanes on DPP (row shifts by 1, 2, 4, 8, then
+// the last lane of row 0 into rows 1 and 3 and of row 1 into rows 2 and 3);
+// lanes without a source read 0, the identity of both (the values are >= 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_src(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ uint32_t scan_add(uint32_t v) {
+  v += dpp_src<0x111, 0xF>(v); v += dpp_src<0x112, 0xF>(v); v += dpp_src<0x114, 0xF>(v);
+  v += dpp_src<0x118, 0xF>(v); v += dpp_src<0x142, 0xA>(v); v += dpp_src<0x143, 0xC>(v);
+  return v;
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t scan_max(uint32_t v) {
+  v = umax(v, dpp_src<0x111, 0xF>(v)); v = umax(v, dpp_src<0x112, 0xF>(v)); v = umax(v, dpp_src<0x114, 0xF>(v));
+  v = umax(v, dpp_src<0x118, 0xF>(v)); v = umax(v, dpp_src<0x142, 0xA>(v)); v = umax(v, dpp_src<0x143, 0xC>(v));
+  return v;
+}
+// the value of the lane below, `fill` in lane 0 (DPP wave_shr:1 with the fill
+// as the old value; computed with every lane active, never under a branch)
+__device__ __forceinline__ uint32_t from_lane_below(uint32_t v, uint32_t fill) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(fill), static_cast<int>(v), 0x138, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int j) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), j));
+}
+__device__ __forceinline__ uint32_t clamp_off(int32_t o, uint32_t M) {
+  const uint32_t v = o < 0 ? 0u : static_cast<uint32_t>(o);
+  return v < M ? v : M;
+}
+
 // Expert tile table, computed by every workgroup from the device offsets:
 // b_e = min(M, max(0, offs[0..e])) (clamped monotone), tiles_e =
 // ceil((b_{e+1} - b_e) / block_m), tile_start_e = sum of tiles before e.
-// Returns the expert of global tile t (or -1 past the last tile) and its rows.
-__device__ bool tile_of(const int32_t* __restrict__ offs, int E, int64_t M, int bm, int64_t t, int& e_out,
-                        int64_t& r0, int64_t& r1) {
+// Returns the expert of global tile t (false past the last tile) and its rows.
+__device__ bool tile_of(const int32_t* __restrict__ offs, int E, uint32_t M, int log_bm, uint32_t t, int& e_out,
+                        uint32_t& r0, uint32_t& r1) {
   const int lane = threadIdx.x & 63;
-  int64_t run_b = offs[0];  // b of the first expert of this chunk
-  run_b = run_b < 0 ? 0 : (run_b < M ? run_b : M);
-  int64_t run_t = 0;        // tiles before this chunk
+  const uint32_t bm = 1u << log_bm;
+  uint32_t run_b = clamp_off(offs[0], M);  // b of the first expert of the chunk
+  uint32_t run_t = 0;                      // tiles before the chunk
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
-    // running max of the offsets inside the chunk (lanes past E repeat the last bound)
-    int64_t v = e < E + 1 ? static_cast<int64_t>(offs[e < E ? e + 1 : E]) : 0;
-    v = v < 0 ? 0 : v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int64_t u = __shfl_up(v, d);
-      if (lane >= d) v = v > u ? v : u;
-    }
-    int64_t b1 = v > run_b ? v : run_b;   // b_{e+1}
-    b1 = b1 < M ? b1 : M;
-    int64_t b0 = __shfl_up(b1, 1);
-    if (lane == 0) b0 = run_b;             // b_e
-    const int64_t nt = (e < E && b1 > b0) ? (b1 - b0 + bm - 1) / bm : 0;
-    int64_t incl = nt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int64_t u = __shfl_up(incl, d);
-      if (lane >= d) incl += u;
-    }
-    const int64_t first = run_t + incl - nt;
+    // b_{e+1}: running max of the offsets (lanes past E repeat offs[E])
+    const uint32_t b1 = umax(scan_max(clamp_off(offs[e < E ? e + 1 : E], M)), run_b);
+    const uint32_t b0 = from_lane_below(b1, run_b);
+    const uint32_t nt = (e < E && b1 > b0) ? (b1 - b0 + bm - 1) >> log_bm : 0u;
+    const uint32_t incl = scan_add(nt);
+    const uint32_t first = run_t + incl - nt;
     const uint64_t hit = __ballot(e < E && t >= first && t < first + nt);
     if (hit) {
       const int j = __builtin_ctzll(hit);
       e_out = e0 + j;
-      const int64_t f = __shfl(first, j), lo = __shfl(b0, j), hi = __shfl(b1, j);
-      r0 = lo + (t - f) * bm;
+      r0 = lane_value(b0, j) + ((t - lane_value(first, j)) << log_bm);
+      const uint32_t hi = lane_value(b1, j);
       r1 = r0 + bm < hi ? r0 + bm : hi;
       return true;
     }
-    run_t += __shfl(incl, 63);
-    run_b = __shfl(b1, 63);
-    if (run_b < 0) run_b = 0;
+    run_t += lane_value(incl, 63);
+    run_b = lane_value(b1, 63);
   }
   return false;
 }
 
-// Pairwise tree over Q rows of 8 columns held as Q x 8 floats: in place, level by level.
-template <int Q>
-__device__ __forceinline__ void tree_rows(float (&x)[Q][8]) {
+// Rows of one piece: 16-byte loads of 8 columns; a row at or past the
+// tile's end r1 loads row `safe` (< r1; a whole piece can lie past r1) and is
+// replaced by -0.0 when it is added.
+template <int P>
+__device__ __forceinline__ void load_piece(uint4 (&v)[P], const uint16_t* __restrict__ dA, int64_t lda, int64_t a,
+                                           int64_t r1, int64_t safe, int64_t col) {
 #pragma unroll
-  for (int s = 1; s < Q; s <<= 1)
-#pragma unroll
-    for (int r = 0; r < Q; r += 2 * s)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) x[r][c] = x[r][c] + x[r + s][c];
-}
-
-// Rows [a, a + Q) of the tile (absolute row index base + i), -0.0 at rows >= r1.
-template <int Q>
-__device__ __forceinline__ void load_rows(float (&x)[Q][8], const uint16_t* __restrict__ dA, int64_t lda,
-                                          int64_t a, int64_t r1, int64_t col) {
-  uint4 v[Q];
-#pragma unroll
-  for (int i = 0; i < Q; ++i) {
-    const int64_t r = a + i < r1 ? a + i : a;  // a < r1 always: a valid row
+  for (int i = 0; i < P; ++i) {
+    const int64_t r = a + i < r1 ? a + i : safe;
     v[i] = *reinterpret_cast<const uint4*>(dA + r * lda + col);
   }
+}
+
+// Adds the rows of piece p (rows p P .. p P + P - 1 of the wave's quarter) to
+// the adjacent pairwise tree kept as a stack of partial sums: row i goes in
+// as the right operand of every completed level (i's trailing one bits), so
+// the stack ends holding exactly the tree of all Q rows.
+template <int P, int LQ>
+__device__ __forceinline__ void push_piece(float (&stk)[LQ + 1][8], const uint4 (&v)[P], int p, int64_t a,
+                                           int64_t r1) {
 #pragma unroll
-  for (int i = 0; i < Q; ++i) {
+  for (int i = 0; i < P; ++i) {
+    const int idx = p * P + i;
     const bool in = a + i < r1;  // wave-uniform
-    x[i][0] = in ? bf16_lo(v[i].x) : -0.0f; x[i][1] = in ? bf16_hi(v[i].x) : -0.0f;
-    x[i][2] = in ? bf16_lo(v[i].y) : -0.0f; x[i][3] = in ? bf16_hi(v[i].y) : -0.0f;
-    x[i][4] = in ? bf16_lo(v[i].z) : -0.0f; x[i][5] = in ? bf16_hi(v[i].z) : -0.0f;
-    x[i][6] = in ? bf16_lo(v[i].w) : -0.0f; x[i][7] = in ? bf16_hi(v[i].w) : -0.0f;
+    float c[8];
+    c[0] = in ? bf16_lo(v[i].x) : -0.0f; c[1] = in ? bf16_hi(v[i].x) : -0.0f;
+    c[2] = in ? bf16_lo(v[i].y) : -0.0f; c[3] = in ? bf16_hi(v[i].y) : -0.0f;
+    c[4] = in ? bf16_lo(v[i].z) : -0.0f; c[5] = in ? bf16_hi(v[i].z) : -0.0f;
+    c[6] = in ? bf16_lo(v[i].w) : -0.0f; c[7] = in ? bf16_hi(v[i].w) : -0.0f;
+    int l = 0;
+#pragma unroll
+    for (; l < LQ && ((idx >> l) & 1); ++l)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) c[k] = stk[l][k] + c[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) stk[l][k] = c[k];
   }
 }
 
@@ -114,72 +141,67 @@ template <int Q, bool ATOMIC>
 __global__ __launch_bounds__(256) void dbias_tile_kernel(const uint16_t* __restrict__ dA, int64_t lda, int64_t M,
                                                          int64_t N, const int32_t* __restrict__ offs, int E,
                                                          float* __restrict__ slots, int32_t* __restrict__ tstart,
-                                                         float* __restrict__ dbias, int64_t ld_e) {
+                                                         float* __restrict__ dbias, int64_t ld_e, int ncb) {
   constexpr int BM = 4 * Q;
-  constexpr int P = Q < 32 ? Q : 32;  // rows per piece
+  constexpr int LOG_BM = BM == 64 ? 6 : (BM == 128 ? 7 : 8);
+  static_assert((1 << LOG_BM) == BM, "block_m is 64, 128 or 256");
+  constexpr int P = 16;  // rows per piece: the next piece's loads are in flight while one is added
+  constexpr int NP = Q / P;
+  constexpr int LQ = Q == 16 ? 4 : (Q == 32 ? 5 : 6);
+  static_assert((1 << LQ) == Q && Q % P == 0, "Q is 16, 32 or 64");
+  const uint32_t Mu = static_cast<uint32_t>(M);
   __shared__ float part[4][kCols + 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the tile table for the fold: tile starts per expert (and the total),
   // written by the first workgroup whether or not any expert has rows
-  if (!ATOMIC && blockIdx.x == 0 && blockIdx.y == 0 && wave == 0) {
-    int64_t run_b = 0, run_t = 0;
+  // workgroup w: tile w / ncb, column block w % ncb (the column blocks of a
+  // tile run side by side, so the workgroups in flight read whole rows)
+  const uint32_t cb = blockIdx.x % ncb;
+  if (!ATOMIC && blockIdx.x == 0 && wave == 0) {
+    uint32_t run_b = 0, run_t = 0;
     for (int e0 = 0; e0 <= E; e0 += 64) {
       const int ee = e0 + lane;
-      int64_t v = ee < E + 1 ? static_cast<int64_t>(offs[ee]) : 0;
-      v = v < 0 ? 0 : v;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int64_t u = __shfl_up(v, d);
-        if (lane >= d) v = v > u ? v : u;
-      }
-      int64_t b = v > run_b ? v : run_b;
-      b = b < M ? b : M;                    // b_ee
-      int64_t bp = __shfl_up(b, 1);
-      if (lane == 0) bp = e0 == 0 ? b : run_b;  // b_{ee-1} (b_0 for ee = 0: no tiles before it)
-      const int64_t nt = (ee >= 1 && ee <= E && b > bp) ? (b - bp + BM - 1) / BM : 0;  // tiles of expert ee-1
-      int64_t incl = nt;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int64_t u = __shfl_up(incl, d);
-        if (lane >= d) incl += u;
-      }
+      const uint32_t b = umax(scan_max(clamp_off(ee <= E ? offs[ee] : 0, Mu)), run_b);  // b_ee
+      const uint32_t bp = from_lane_below(b, e0 == 0 ? b : run_b);                     // b_{ee-1}
+      const uint32_t nt = (ee >= 1 && ee <= E && b > bp) ? (b - bp + BM - 1) / BM : 0u;  // tiles of expert ee-1
+      const uint32_t incl = scan_add(nt);
       if (ee <= E) tstart[ee] = static_cast<int32_t>(run_t + incl);  // tiles of experts before ee
-      run_t += __shfl(incl, 63);
-      run_b = __shfl(b, 63);
+      run_t += lane_value(incl, 63);
+      run_b = lane_value(b, 63);
     }
   }
-  const int64_t t = blockIdx.x;
+  const uint32_t t = blockIdx.x / ncb;
   int e;
-  int64_t r0, r1;
-  if (!tile_of(offs, E, M, BM, t, e, r0, r1)) return;  // past the last tile (the grid covers the worst case)
-  const int64_t col = static_cast<int64_t>(blockIdx.y) * kCols + 8 * lane;
+  uint32_t r0, r1;
+  if (!tile_of(offs, E, Mu, LOG_BM, t, e, r0, r1)) return;  // past the last tile (the grid covers the worst case)
+  const int64_t col = static_cast<int64_t>(cb) * kCols + 8 * lane;
   const bool live = col < N;  // N % 8 == 0: a lane's 8 columns are all inside or all outside
   float q[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) q[c] = -0.0f;
   const int64_t a0 = r0 + static_cast<int64_t>(wave) * Q;
   if (live && a0 < r1) {
+    float stk[LQ + 1][8];
+    uint4 va[P], vb[P];
+    load_piece<P>(va, dA, lda, a0, r1, a0, col);
 #pragma unroll
-    for (int p = 0; p < Q / P; ++p) {
-      const int64_t a = a0 + p * P;
-      float x[P][8];
-      if (a < r1) {
-        load_rows<P>(x, dA, lda, a, r1, col);
-        tree_rows<P>(x);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) x[0][c] = -0.0f;
+    for (int p = 0; p < NP; p += 2) {
+      if (p + 1 < NP) load_piece<P>(vb, dA, lda, a0 + (p + 1) * P, r1, a0, col);
+      push_piece<P, LQ>(stk, va, p, a0 + p * P, r1);
+      if (p + 1 < NP) {
+        if (p + 2 < NP) load_piece<P>(va, dA, lda, a0 + (p + 2) * P, r1, a0, col);
+        push_piece<P, LQ>(stk, vb, p + 1, a0 + (p + 1) * P, r1);
       }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) q[c] = p == 0 ? x[0][c] : q[c] + x[0][c];
     }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) q[c] = stk[LQ][c];
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) part[wave][8 * lane + c] = q[c];
   __syncthreads();
   // the top two tree levels: thread i combines column i of the four quarters
   for (int i = threadIdx.x; i < kCols; i += 256) {
-    const int64_t n = static_cast<int64_t>(blockIdx.y) * kCols + i;
+    const int64_t n = static_cast<int64_t>(cb) * kCols + i;
     if (n >= N) break;
     const float s = (part[0][i] + part[1][i]) + (part[2][i] + part[3][i]);
     if (ATOMIC)
@@ -253,12 +275,13 @@ extern "C" int det_grouped_dbias(float* dbias, int64_t ld_e, const void* dA, int
   if (int s = check_cfg(cfg, &c)) return s;
   if (M == 0 || N == 0 || E == 0) return ok();  // no rows or no columns: dbias unchanged
   if (!dbias || !dA || !offs) return set_error(DET_ERR_INVALID_ARG, "dbias: NULL pointer");
+  if (M > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "dbias: M must be < 2^31");
   if (lda < N || ld_e < N) return set_error(DET_ERR_INVALID_ARG, "dbias: lda and ld_e must be >= N");
   if (N % 8 || lda % 8 || !aligned(dA, 16))
     return set_error(DET_ERR_UNSUPPORTED, "dbias: N and lda must be multiples of 8 and dA 16-byte aligned");
   if (E > 65535) return set_error(DET_ERR_UNSUPPORTED, "dbias: E must be <= 65535");
   const int64_t nt = max_tiles(M, E, c.block_m);
-  if (nt > 0x7FFFFFFF || ceil_div(N, kCols) > 65535 || nt * N > (int64_t(1) << 40))
+  if (nt * ceil_div(N, kCols) > 0x7FFFFFFF || nt * N > (int64_t(1) << 40))
     return set_error(DET_ERR_UNSUPPORTED, "dbias: problem too large");
   const size_t need = atomic ? 0 : ws_bytes_for(M, N, E, c.block_m);
   if (int s = check_workspace(ws, ws_bytes, need)) return s;
@@ -272,15 +295,16 @@ extern "C" int det_grouped_dbias(float* dbias, int64_t ld_e, const void* dA, int
   auto* tstart = atomic ? nullptr : reinterpret_cast<int32_t*>(w + DET_WS_HEADER_BYTES);
   auto* slots = atomic ? nullptr
                        : reinterpret_cast<float*>(w + DET_WS_HEADER_BYTES + align_up(static_cast<size_t>(E + 1) * 4, 256));
-  const dim3 grid(static_cast<uint32_t>(nt), static_cast<uint32_t>(ceil_div(N, kCols)));
+  const int ncb = static_cast<int>(ceil_div(N, kCols));
+  const dim3 grid(static_cast<uint32_t>(nt * ncb));
 #define DET_DBIAS_LAUNCH(Q)                                                                                       \
   if (c.block_m == 4 * Q) {                                                                                       \
     if (atomic)                                                                                                   \
       hipLaunchKernelGGL((dbias_tile_kernel<Q, true>), grid, dim3(256), 0, st, a, lda, M, N, offs, E, slots,      \
-                         tstart, dbias, ld_e);                                                                    \
+                         tstart, dbias, ld_e, ncb);                                                               \
     else                                                                                                          \
       hipLaunchKernelGGL((dbias_tile_kernel<Q, false>), grid, dim3(256), 0, st, a, lda, M, N, offs, E, slots,     \
-                         tstart, dbias, ld_e);                                                                    \
+                         tstart, dbias, ld_e, ncb);                                                               \
   }
   DET_DBIAS_LAUNCH(16) DET_DBIAS_LAUNCH(32) DET_DBIAS_LAUNCH(64)
 #undef DET_DBIAS_LAUNCH

@@ -51,13 +51,16 @@ def test_offsets_clamped_and_empty_experts():
         assert_bitwise(got, odb.grouped_dbias(inp.dbias0, inp.dA, offs, 128), "dbias offs")
 
 
-def test_full_size_parity_and_non_default_stream():
+@pytest.mark.parametrize("BM", [128, 64, 256])
+def test_full_size_parity_and_non_default_stream(BM):
+    """Full size, every block_m: the last tile of the last expert ends at M, so
+    a wave whose later row pieces lie past the tile must not read past M."""
     import torch
     inp = W.dbias_inputs(seed=6, out_init="normal")  # 16384 x 2048, E = 8
-    note("dbias full size on a side stream")
+    note("dbias full size block_m=%d on a side stream" % BM)
     s = torch.cuda.Stream()
-    got = run(inp, stream=s)
-    assert_bitwise(got, odb.grouped_dbias(inp.dbias0, inp.dA, inp.offs, 128), "dbias full")
+    got = run(inp, block_m=BM, stream=s)
+    assert_bitwise(got, odb.grouped_dbias(inp.dbias0, inp.dA, inp.offs, BM), "dbias full")
 
 
 def test_replay_under_load_and_atomic_arm():
