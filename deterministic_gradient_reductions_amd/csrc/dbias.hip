@@ -222,12 +222,13 @@ __global__ __launch_bounds__(256) void dbias_fold_kernel(const float* __restrict
   const int64_t t0 = tstart[e], t1 = tstart[e + 1];
   if (t1 <= t0) return;  // no rows: dbias[e] bitwise unchanged
   float tot = -0.0f;
-  for (int64_t t = t0; t < t1; t += 8) {
-    float v[8];
+  // 32 slots' loads in flight at a time (an expert of 4096 rows has 32 tiles of 128)
+  for (int64_t t = t0; t < t1; t += 32) {
+    float v[32];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = t + i < t1 ? slots[(t + i) * N + n] : -0.0f;
+    for (int i = 0; i < 32; ++i) v[i] = t + i < t1 ? slots[(t + i) * N + n] : -0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tot = tot + v[i];
+    for (int i = 0; i < 32; ++i) tot = tot + v[i];
   }
   float* const o = dbias + static_cast<int64_t>(e) * ld_e + n;
   *o = *o + tot;
