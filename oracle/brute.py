@@ -19,6 +19,11 @@ def _w(bits) -> np.float32:
     return np.array([int(bits) << 16], np.uint32).view(np.float32)[0]
 
 
+def _gate(v) -> np.float32:
+    """A gate input: a float32 value as is, else bf16 bits widened."""
+    return v if isinstance(v, np.float32) else _w(v)
+
+
 def tree(vals):
     """Recursive halving: tree(v) = tree(left half) + tree(right half)."""
     if len(vals) == 1:
@@ -66,11 +71,11 @@ def colsum(a, dg, A_log, dt_bias, dA0, ddt0, block_t):
         nA = -detmath.exp32(np.float32(A_log[h]))[()]
         t1, t2 = [], []
         for t in range(T):
-            x = F(_w(a[t][h]) + F(dt_bias[h]))
+            x = F(_gate(a[t][h]) + F(dt_bias[h]))
             e = detmath.exp32(F(-abs(x)))[()]
             sp = detmath.softplus_from(np.float32(x), np.float32(e))[()]
             sg = detmath.sigmoid_from(np.float32(x), np.float32(e))[()]
-            d = _w(dg[t][h])
+            d = _gate(dg[t][h])
             t1.append(F(d * F(nA * sp)))
             t2.append(F(d * F(nA * sg)))
         r1.append(F(F(dA0[h]) + fold([tree(x) for x in padded_tiles(t1, block_t)])))

@@ -30,10 +30,17 @@ from . import detmath
 from .primitives import accumulate, pairwise, sequential, tiles, widen_bf16
 
 
+def gate_input(x) -> np.ndarray:
+    """Gate inputs arrive as bf16 bit patterns (uint16, widened exactly) or as
+    float32 values (the GDN gate page tests both input precisions)."""
+    x = np.asarray(x)
+    return x.astype(np.float32) if x.dtype == np.float32 else widen_bf16(x)
+
+
 def gate_terms(a_bits, dg_bits, A_log, dt_bias):
     """Elementwise terms (t1, t2), each [T, H] float32."""
-    a = widen_bf16(a_bits)
-    dg = widen_bf16(dg_bits)
+    a = gate_input(a_bits)
+    dg = gate_input(dg_bits)
     A_log = np.asarray(A_log, np.float32)
     dt_bias = np.asarray(dt_bias, np.float32)
     x = (a + dt_bias[None, :]).astype(np.float32)

@@ -17,8 +17,8 @@ def widen(bits) -> np.ndarray:
 
 
 def gate_terms64(a_bits, dg_bits, A_log, dt_bias):
-    a = widen(a_bits)
-    dg = widen(dg_bits)
+    a = np.asarray(a_bits, np.float64) if np.asarray(a_bits).dtype == np.float32 else widen(a_bits)
+    dg = np.asarray(dg_bits, np.float64) if np.asarray(dg_bits).dtype == np.float32 else widen(dg_bits)
     x = a + np.asarray(dt_bias, np.float64)[None, :]
     nA = -np.exp(np.asarray(A_log, np.float64))[None, :]
     sp = np.where(x > 20.0, x, np.logaddexp(0.0, x))

@@ -190,8 +190,9 @@ def test_dbias_invariants():
 
 # ---------------------------------------------------------------------- colsum
 @pytest.mark.parametrize("T,H,BT", [(4096, 16, 128), (1000, 32, 64), (333, 8, 256), (1, 4, 64)])
-def test_colsum_fp64_bound(T, H, BT):
-    inp = W.gate_inputs(T, H, seed=2, out_init="normal")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_colsum_fp64_bound(T, H, BT, dtype):
+    inp = W.gate_inputs(T, H, seed=2, out_init="normal", dtype=dtype)
     r1, r2 = oc.colsum(inp.a, inp.dg, inp.A_log, inp.dt_bias, inp.dA_log0, inp.ddt_bias0, BT)
     e1, e2, a1, a2 = fp64.colsum64(inp.a, inp.dg, inp.A_log, inp.dt_bias, inp.dA_log0, inp.ddt_bias0)
     S = -(-T // BT)
@@ -203,12 +204,25 @@ def test_colsum_fp64_bound(T, H, BT):
         assert rel_l2(got, ex) <= 1e-5
 
 
-def test_colsum_brute_force():
-    inp = W.gate_inputs(37, 3, seed=5, out_init="normal")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_colsum_brute_force(dtype):
+    inp = W.gate_inputs(37, 3, seed=5, out_init="normal", dtype=dtype)
     for BT in (8, 64):
         r = oc.colsum(inp.a, inp.dg, inp.A_log, inp.dt_bias, inp.dA_log0, inp.ddt_bias0, BT)
         b = brute.colsum(inp.a, inp.dg, inp.A_log, inp.dt_bias, inp.dA_log0, inp.ddt_bias0, BT)
         assert np.array_equal(bits(r[0]), bits(b[0])) and np.array_equal(bits(r[1]), bits(b[1]))
+
+
+def test_colsum_f32_inputs_with_bf16_values_match_bf16_inputs():
+    """float32 inputs holding bf16-representable values must give the same bits as
+    the bf16 inputs (the widening is exact), and other float32 values must not."""
+    b = W.gate_inputs(300, 5, seed=6, out_init="normal")
+    f = W.gate_inputs(300, 5, seed=6, out_init="normal", dtype="f32")
+    rb = oc.colsum(b.a, b.dg, b.A_log, b.dt_bias, b.dA_log0, b.ddt_bias0, 64)
+    rf = oc.colsum(widen_bf16(b.a), widen_bf16(b.dg), b.A_log, b.dt_bias, b.dA_log0, b.ddt_bias0, 64)
+    assert np.array_equal(bits(rb[0]), bits(rf[0])) and np.array_equal(bits(rb[1]), bits(rf[1]))
+    rr = oc.colsum(f.a, f.dg, f.A_log, f.dt_bias, f.dA_log0, f.ddt_bias0, 64)
+    assert not np.array_equal(bits(rr[0]), bits(rb[0]))
 
 
 def test_colsum_order_probe_through_dg():

@@ -51,8 +51,8 @@ class GateInputs:
     """
     T: int
     H: int
-    a: np.ndarray          # uint16 [T, H]
-    dg_base: np.ndarray    # uint16 [T, 2H]
+    a: np.ndarray          # uint16 [T, H] bf16 bits (or float32 values)
+    dg_base: np.ndarray    # uint16 [T, 2H] bf16 bits (or float32 values)
     A_log: np.ndarray      # float32 [H]
     dt_bias: np.ndarray    # float32 [H]
     dA_log0: np.ndarray    # float32 [H] initial accumulator
@@ -63,9 +63,15 @@ class GateInputs:
         return self.dg_base[:, self.H:]
 
 
-def gate_inputs(T: int, H: int, seed: int = 1, out_init: str = "zero") -> GateInputs:
-    a = bf16_bits(_rng(seed, 0).standard_normal((T, H), dtype=np.float32))
-    dg_base = bf16_bits(_rng(seed, 1).standard_normal((T, 2 * H), dtype=np.float32))
+def gate_inputs(T: int, H: int, seed: int = 1, out_init: str = "zero", dtype: str = "bf16") -> GateInputs:
+    """``dtype="f32"`` keeps ``a`` and ``dg_base`` as float32 values (the same
+    draws, not rounded to bf16) instead of bf16 bit patterns."""
+    a = _rng(seed, 0).standard_normal((T, H), dtype=np.float32)
+    dg_base = _rng(seed, 1).standard_normal((T, 2 * H), dtype=np.float32)
+    if dtype == "bf16":
+        a, dg_base = bf16_bits(a), bf16_bits(dg_base)
+    elif dtype != "f32":
+        raise ValueError("dtype must be bf16 or f32")
     A_log = _rng(seed, 2).uniform(-2.0, 1.0, H).astype(np.float32)
     dt_bias = _rng(seed, 3).uniform(-1.0, 1.0, H).astype(np.float32)
     if out_init == "zero":
