@@ -26,9 +26,9 @@ namespace {
 constexpr int kWG = 256;
 
 struct ColsumArgs {
-  const uint16_t* a;
+  const void* a;     // bf16 bits or float32 values (the kernel's input type)
   int64_t a_st, a_sh;
-  const uint16_t* dg;
+  const void* dg;
   int64_t dg_st, dg_sh;
   const float* A_log;
   const float* dt_bias;
@@ -50,8 +50,14 @@ __device__ __forceinline__ float tree_regs(float (&v)[N]) {
   return v[0];
 }
 
-template <int R, int BH, bool ATOMIC>
+// Gate inputs: bf16 (widened exactly) or float32.
+__device__ __forceinline__ float gate_in(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float gate_in(const float* p, int64_t i) { return p[i]; }
+
+template <int R, int BH, bool ATOMIC, typename TIn>
 __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
+  const TIn* const pa = static_cast<const TIn*>(p.a);
+  const TIn* const pdg = static_cast<const TIn*>(p.dg);
   constexpr int kBT = R * kWG / BH;   // rows per tile
   constexpr int kNB = kWG / BH;       // row blocks per tile (threads per head)
   __shared__ float red1[kWG];
@@ -72,8 +78,8 @@ __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
     for (int i = 0; i < R; ++i) {
       const int64_t t = r0 + i;
       if (t < p.T) {
-        const float x = bf16_to_f32(p.a[t * p.a_st + h * p.a_sh]) + bias;
-        const float d = bf16_to_f32(p.dg[t * p.dg_st + h * p.dg_sh]);
+        const float x = gate_in(pa, t * p.a_st + h * p.a_sh) + bias;
+        const float d = gate_in(pdg, t * p.dg_st + h * p.dg_sh);
         const float e = dm::exp32(dm::neg_abs(x));
         const float sp = dm::softplus_e(x, e);
         const float sg = dm::sigmoid_e(x, e);
@@ -176,22 +182,23 @@ size_t ws_bytes_for(int64_t T, int64_t H, const det_colsum_cfg& c) {
   return DET_WS_HEADER_BYTES + align_up(static_cast<size_t>(S * H) * 4, 256) * 2;
 }
 
-template <int BT, int BH>
+template <int BT, int BH, typename TIn>
 void launch_one(const ColsumArgs& p, int atomic, dim3 grid, hipStream_t st) {
   constexpr int R = BT * BH / kWG;
   if (atomic) {
-    hipLaunchKernelGGL((colsum_kernel<R, BH, true>), grid, dim3(kWG), 0, st, p);
+    hipLaunchKernelGGL((colsum_kernel<R, BH, true, TIn>), grid, dim3(kWG), 0, st, p);
   } else {
-    hipLaunchKernelGGL((colsum_kernel<R, BH, false>), grid, dim3(kWG), 0, st, p);
+    hipLaunchKernelGGL((colsum_kernel<R, BH, false, TIn>), grid, dim3(kWG), 0, st, p);
     hipLaunchKernelGGL(colsum_fold_kernel, dim3(static_cast<uint32_t>(p.H), 2), dim3(64), 0, st, p.slot1, p.slot2,
                        static_cast<int64_t>(grid.x), p.H, p.dA_log, p.ddt_bias);
   }
 }
 
-void launch(const ColsumArgs& p, const det_colsum_cfg& c, int atomic, hipStream_t st) {
+void launch(const ColsumArgs& p, const det_colsum_cfg& c, int atomic, bool f32_in, hipStream_t st) {
   const dim3 grid(static_cast<uint32_t>(ceil_div(p.T, c.block_t)), static_cast<uint32_t>(ceil_div(p.H, c.block_h)));
 #define DET_COLSUM_CASE(bt, bh) \
-  if (c.block_t == bt && c.block_h == bh) return launch_one<bt, bh>(p, atomic, grid, st);
+  if (c.block_t == bt && c.block_h == bh)                                                                 \
+    return f32_in ? launch_one<bt, bh, float>(p, atomic, grid, st) : launch_one<bt, bh, uint16_t>(p, atomic, grid, st);
   DET_COLSUM_CASE(64, 8) DET_COLSUM_CASE(64, 16) DET_COLSUM_CASE(64, 32)
   DET_COLSUM_CASE(128, 8) DET_COLSUM_CASE(128, 16) DET_COLSUM_CASE(128, 32)
   DET_COLSUM_CASE(256, 8) DET_COLSUM_CASE(256, 16) DET_COLSUM_CASE(256, 32)
@@ -255,7 +262,6 @@ extern "C" int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void*
   if (T < 0 || H < 0) return set_error(DET_ERR_INVALID_ARG, "colsum: T and H must be >= 0");
   if (in_dtype != DET_BF16 && in_dtype != DET_F32)
     return set_error(DET_ERR_INVALID_ARG, "colsum: unknown dtype %d", in_dtype);
-  if (in_dtype != DET_BF16) return set_error(DET_ERR_UNSUPPORTED, "colsum: only bf16 inputs are implemented");
   det_colsum_cfg c;
   if (int s = resolve_cfg(T, H, cfg, &c)) return s;
   if (T == 0 || H == 0) return ok();
@@ -268,17 +274,18 @@ extern "C" int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void*
   const size_t need = atomic ? 0 : ws_bytes_for(T, H, c);
   if (int s = check_workspace(ws, ws_bytes, need)) return s;
   const Range o1 = range1d(dA_log, H * 4), o2 = range1d(ddt_bias, H * 4);
-  const Range ins[] = {range_strided(a, T, H, a_st, a_sh, 2), range_strided(dg, T, H, dg_st, dg_sh, 2),
+  const size_t esz = in_dtype == DET_F32 ? 4 : 2;
+  const Range ins[] = {range_strided(a, T, H, a_st, a_sh, esz), range_strided(dg, T, H, dg_st, dg_sh, esz),
                        range1d(A_log, H * 4), range1d(dt_bias, H * 4), range1d(ws, ws_bytes)};
   if (overlaps(o1, o2)) return set_error(DET_ERR_OVERLAP, "colsum: dA_log overlaps ddt_bias");
   for (const Range& r : ins)
     if (overlaps(o1, r) || overlaps(o2, r))
       return set_error(DET_ERR_OVERLAP, "colsum: an output overlaps an input or the workspace");
   ColsumArgs p;
-  p.a = static_cast<const uint16_t*>(a);
+  p.a = a;
   p.a_st = a_st;
   p.a_sh = a_sh;
-  p.dg = static_cast<const uint16_t*>(dg);
+  p.dg = dg;
   p.dg_st = dg_st;
   p.dg_sh = dg_sh;
   p.A_log = A_log;
@@ -291,6 +298,6 @@ extern "C" int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void*
   const size_t slot_bytes = align_up(static_cast<size_t>(ceil_div(T, c.block_t) * H) * 4, 256);
   p.slot1 = atomic ? nullptr : reinterpret_cast<float*>(w + DET_WS_HEADER_BYTES);
   p.slot2 = atomic ? nullptr : reinterpret_cast<float*>(w + DET_WS_HEADER_BYTES + slot_bytes);
-  launch(p, c, atomic, as_stream(stream));
+  launch(p, c, atomic, in_dtype == DET_F32, as_stream(stream));
   return check_launch("det_colsum");
 }

@@ -96,7 +96,8 @@ int det_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *
  * a, dg: [T, H] with element strides (st, sh) >= 1, any layout (for example
  *        a column slice of a wider tensor, or a transposed view); dtype
- *        DET_BF16 (DET_F32 returns DET_ERR_UNSUPPORTED).
+ *        DET_BF16 (widened exactly) or DET_F32, the same for both (the page
+ *        tests both input precisions).
  * A_log, dt_bias: [H] float32, contiguous. dA_log, ddt_bias: [H] float32,
  *        accumulated, must not overlap the inputs, each other or ws.
  * cfg:   NULL selects det_colsum_select_cfg(T, H). block_t in {64,128,256},

@@ -132,9 +132,11 @@ def test_colsum_validation_and_selector():
     bad = dg.ColsumCfg(96, 16)
     assert L.det_colsum(FAKE, 16, 1, FAKE, 16, 1, 0, FAKE, FAKE, 16, 16, FAKE, FAKE, ctypes.byref(bad), None, 0, 0,
                         None) == dg.DET_ERR_INVALID_ARG
-    # fp32 inputs: not implemented yet
+    # unknown input dtype; fp32 inputs pass validation (a missing workspace is the first error here)
+    assert L.det_colsum(FAKE, 16, 1, FAKE, 16, 1, 7, FAKE, FAKE, 16, 16, FAKE, FAKE, None, None, 0, 0, None) == \
+        dg.DET_ERR_INVALID_ARG
     assert L.det_colsum(FAKE, 16, 1, FAKE, 16, 1, 1, FAKE, FAKE, 16, 16, FAKE, FAKE, None, None, 0, 0, None) == \
-        dg.DET_ERR_UNSUPPORTED
+        dg.DET_ERR_WORKSPACE
     # workspace too small / missing / misaligned
     n = dg.det_colsum_workspace_size(1000, 16)
     assert n >= 256 + 2 * 16 * 4 * (1000 // 256)

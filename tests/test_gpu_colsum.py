@@ -46,12 +46,13 @@ def test_detmath_bitwise(fn):
 def run(inp, cfg=None, atomic=False, transpose=False, dA0=None, ddt0=None, ws=None):
     import torch
     T, H = inp.a.shape
-    a = dev_bf16(inp.a)
-    dgb = dev_bf16(inp.dg_base)
+    dev_in = dev_f32 if inp.a.dtype == np.float32 else dev_bf16  # float32 values or bf16 bits
+    a = dev_in(inp.a)
+    dgb = dev_in(inp.dg_base)
     d = dgb[:, H:]  # strided view: row stride 2H, offset H
     if transpose:
-        a = dev_bf16(np.ascontiguousarray(inp.a.T)).t()
-        d = dev_bf16(np.ascontiguousarray(inp.dg.T)).t()
+        a = dev_in(np.ascontiguousarray(inp.a.T)).t()
+        d = dev_in(np.ascontiguousarray(inp.dg.T)).t()
     o1 = dev_f32(inp.dA_log0 if dA0 is None else dA0)
     o2 = dev_f32(inp.ddt_bias0 if ddt0 is None else ddt0)
     torch.cuda.synchronize()
@@ -145,3 +146,22 @@ def test_block_h_never_changes_bits():
     for bh in (16, 32):
         r = run(inp, cfg=dg.ColsumCfg(128, bh))
         assert_bitwise(r[0], base[0], "bh"); assert_bitwise(r[1], base[1], "bh")
+
+
+@pytest.mark.parametrize("T,H,bt", [(16384, 32, 64), (16323, 32, 128), (1000, 40, 256), (70001, 3, 64)])
+def test_f32_inputs(T, H, bt):
+    """float32 a and dg (strided dg view, tails, multi-round folds): bitwise against the oracle."""
+    inp = W.gate_inputs(T, H, seed=12, out_init="normal", dtype="f32")
+    note("colsum f32 inputs T=%d H=%d block_t=%d" % (T, H, bt))
+    r1, r2 = run(inp, cfg=dg.ColsumCfg(bt, 8))
+    w1, w2 = oracle(inp, bt)
+    assert_bitwise(r1, w1, "dA_log f32"); assert_bitwise(r2, w2, "ddt_bias f32")
+
+
+def test_f32_inputs_transposed_and_atomic_arm():
+    inp = W.gate_inputs(777, 12, seed=13, out_init="normal", dtype="f32")
+    r1, r2 = run(inp, cfg=dg.ColsumCfg(128, 16), transpose=True)
+    w1, w2 = oracle(inp, 128)
+    assert_bitwise(r1, w1, "dA_log f32 T"); assert_bitwise(r2, w2, "ddt_bias f32 T")
+    a1, a2 = run(inp, cfg=dg.ColsumCfg(128, 16), atomic=True)
+    assert rel_l2(a1 - inp.dA_log0, w1 - inp.dA_log0) <= 1e-5 and rel_l2(a2 - inp.ddt_bias0, w2 - inp.ddt_bias0) <= 1e-5
