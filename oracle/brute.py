@@ -20,7 +20,7 @@ def _w(bits) -> np.float32:
 
 
 def _gate(v) -> np.float32:
-    """A gate input: a float32 value as is, else bf16 bits widened."""
+    """An input element: a float32 value as is, else bf16 bits widened."""
     return v if isinstance(v, np.float32) else _w(v)
 
 
@@ -94,7 +94,7 @@ def index_add(out0, ids, src, chunk_rows):
         for d in range(D):
             parts = []
             for s in range(0, len(rows), chunk_rows):
-                parts.append(fold([_w(src[p][d]) for p in rows[s:s + chunk_rows]]))
+                parts.append(fold([_gate(src[p][d]) for p in rows[s:s + chunk_rows]]))
             out[i][d] = F(out[i][d] + fold(parts))
     return np.array(out, np.float32)
 
@@ -105,7 +105,7 @@ def literal_sequential_index_add(out0, ids, src):
     out = np.array(out0, np.float32, copy=True)
     for i, p in sorted([(int(i), p) for p, i in enumerate(ids) if 0 <= int(i) < n_rows], key=lambda t: t[0]):
         for d in range(out.shape[1]):
-            out[i, d] = F(out[i, d] + _w(src[p][d]))
+            out[i, d] = F(out[i, d] + _gate(src[p][d]))
     return out
 
 

@@ -47,7 +47,8 @@ def index_add64(out0, ids, src_bits):
     out = np.asarray(out0, np.float64).copy()
     ids = np.asarray(ids, np.int64)
     ok = (ids >= 0) & (ids < out.shape[0])
-    src = widen(src_bits[ok])
+    sb = np.asarray(src_bits)[ok]
+    src = sb.astype(np.float64) if sb.dtype == np.float32 else widen(sb)
     absum = np.zeros_like(out)
     np.add.at(out, ids[ok], src)
     np.add.at(absum, ids[ok], np.abs(src))

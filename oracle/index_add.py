@@ -63,7 +63,8 @@ def index_add(out0, ids, src_bits, chunk_rows: int):
     perm, counts = stable_order(ids, n_rows)
     if len(perm) == 0:
         return out
-    src = widen_bf16(src_bits)
+    src = np.asarray(src_bits)
+    src = src.astype(np.float32) if src.dtype == np.float32 else widen_bf16(src)  # float32 values or bf16 bits
     keys, part, n_chunks = chunk_partials(src, perm, counts, chunk_rows)
     first = np.concatenate([[0], np.cumsum(n_chunks)])
     present = np.nonzero(counts)[0]

@@ -261,17 +261,20 @@ def test_colsum_invariants():
 
 
 # -------------------------------------------------------------------- index_add
-def small_index_inputs(seed=1, P=3000, n_rows=64, dim=16, pad=0.05, out_init="normal"):
+def small_index_inputs(seed=1, P=3000, n_rows=64, dim=16, pad=0.05, out_init="normal", dtype="bf16"):
     ids = W.zipf_ids(P, n_rows, 1.1, pad, seed)
     rng = np.random.default_rng(seed)
-    src = W.bf16_bits(rng.standard_normal((P, dim)).astype(np.float32) * np.float32(0.02))
+    src = rng.standard_normal((P, dim)).astype(np.float32) * np.float32(0.02)
+    if dtype == "bf16":
+        src = W.bf16_bits(src)
     out0 = rng.standard_normal((n_rows, dim)).astype(np.float32) if out_init == "normal" else np.zeros((n_rows, dim), np.float32)
     return ids, src, out0
 
 
 @pytest.mark.parametrize("L", [1, 4, 64, 100000])
-def test_index_add_fp64_bound(L):
-    ids, src, out0 = small_index_inputs()
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_index_add_fp64_bound(L, dtype):
+    ids, src, out0 = small_index_inputs(dtype=dtype)
     got = oi.index_add(out0, ids, src, L)
     exact, absum = fp64.index_add64(out0, ids, src)
     counts = np.bincount(ids[ids >= 0], minlength=64)
@@ -280,8 +283,9 @@ def test_index_add_fp64_bound(L):
     assert np.all(np.abs(got - exact) <= bound)
 
 
-def test_index_add_brute_force_and_literal():
-    ids, src, out0 = small_index_inputs(seed=4, P=500, n_rows=16, dim=4)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_index_add_brute_force_and_literal(dtype):
+    ids, src, out0 = small_index_inputs(seed=4, P=500, n_rows=16, dim=4, dtype=dtype)
     for L in (1, 3, 16):
         assert np.array_equal(bits(oi.index_add(out0, ids, src, L)), bits(brute.index_add(out0, ids, src, L)))
     z = np.zeros_like(out0)

@@ -93,7 +93,7 @@ class IndexAddInputs:
     n_rows: int
     dim: int
     ids: np.ndarray   # int32 [P]
-    src: np.ndarray   # uint16 [P, D]
+    src: np.ndarray   # uint16 [P, D] bf16 bits (or float32 values)
     out0: np.ndarray  # float32 [n_rows, D]
 
 
@@ -114,10 +114,15 @@ def zipf_ids(P: int, n_rows: int, s: float, pad_frac: float, seed: int, tensor_i
 
 def index_add_inputs(Q: int = 4096, K: int = 512, n_rows: int = 8192, dim: int = 128, seed: int = 3,
                      zipf_s: float = 1.1, pad_frac: float = 0.05, src_std: float = 0.02,
-                     out_init: str = "zero") -> IndexAddInputs:
+                     out_init: str = "zero", dtype: str = "bf16") -> IndexAddInputs:
+    """``dtype="f32"`` keeps ``src`` as float32 values (the same draws)."""
     P = Q * K
     ids = zipf_ids(P, n_rows, zipf_s, pad_frac, seed, 0)
-    src = bf16_bits(_rng(seed, 1).standard_normal((P, dim), dtype=np.float32) * np.float32(src_std))
+    src = _rng(seed, 1).standard_normal((P, dim), dtype=np.float32) * np.float32(src_std)
+    if dtype == "bf16":
+        src = bf16_bits(src)
+    elif dtype != "f32":
+        raise ValueError("dtype must be bf16 or f32")
     if out_init == "zero":
         out0 = np.zeros((n_rows, dim), np.float32)
     else:
