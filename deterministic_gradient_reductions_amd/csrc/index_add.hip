@@ -524,14 +524,48 @@ __device__ __forceinline__ void store_add8(float* dst, const float (&acc)[8]) {
   *reinterpret_cast<float4*>(dst + 4) = b;
 }
 
+// Eight consecutive source elements of one row: bf16 (one 16-byte load,
+// widened exactly) or float32 (two 16-byte loads).
+template <typename E>
+struct Row8;
+template <>
+struct Row8<uint16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void clear() { v = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ void add_to(float (&acc)[8]) const { add8_bf16(acc, v); }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t w = i < 2 ? v.x : (i < 4 ? v.y : (i < 6 ? v.z : v.w));
+    return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+};
+template <>
+struct Row8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void clear() { a = b = make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
+  __device__ __forceinline__ void add_to(float (&acc)[8]) const {
+    acc[0] = acc[0] + a.x; acc[1] = acc[1] + a.y; acc[2] = acc[2] + a.z; acc[3] = acc[3] + a.w;
+    acc[4] = acc[4] + b.x; acc[5] = acc[5] + b.y; acc[6] = acc[6] + b.z; acc[7] = acc[7] + b.w;
+  }
+  __device__ __forceinline__ float get(int i) const {
+    const float4& q = i < 4 ? a : b;
+    const int r = i & 3;
+    return r == 0 ? q.x : (r == 1 ? q.y : (r == 2 ? q.z : q.w));
+  }
+};
+
 // ---- 5. chunk gather-sum. GS lanes per chunk, 8 dims per lane. The chunk's
 // source positions (at most 16 per lane, GS * 16 rows) are loaded once,
 // handed out by lane shuffles; the rows are then read up to 16 at a time (all
 // their loads in flight) and folded in order.
 constexpr int kPosPerLane = 16;  // chunk capacity of ia_gather: GS * 16 rows (longer chunks: ia_gather_long)
 
-template <int GS>
-__global__ __launch_bounds__(256) void ia_gather(const uint16_t* __restrict__ src, int64_t src_ld, int dim,
+template <int GS, typename E>
+__global__ __launch_bounds__(256) void ia_gather(const E* __restrict__ src, int64_t src_ld, int dim,
                                                  const int32_t* __restrict__ perm,
                                                  const uint32_t* __restrict__ seg_off,
                                                  const uint32_t* __restrict__ chunk_off, int n_rows, int L,
@@ -570,16 +604,19 @@ __global__ __launch_bounds__(256) void ia_gather(const uint16_t* __restrict__ sr
     for (int h = 0; h < GS; h += kBatch) {
       if (GS * i + h >= static_cast<int>(len)) continue;  // skipped when no lane of the wave needs it
       // rows GS*i + h .. GS*i + h + kBatch - 1 of the chunk
-      uint4 v[kBatch];
+      Row8<E> v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int64_t p = __shfl(pos[i], h + u, GS);
         const bool ok = active && GS * i + h + u < static_cast<int>(len) && p >= 0 && p < n_src;
-        v[u] = ok ? *reinterpret_cast<const uint4*>(src + p * src_ld + d0) : make_uint4(0u, 0u, 0u, 0u);
+        if (ok)
+          v[u].load(src + p * src_ld + d0);
+        else
+          v[u].clear();
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
-        if (active && GS * i + h + u < static_cast<int>(len)) add8_bf16(acc, v[u]);
+        if (active && GS * i + h + u < static_cast<int>(len)) v[u].add_to(acc);
     }
   }
   if (!active) return;
@@ -690,8 +727,8 @@ __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict
 
 // Chunks longer than GS * 16 rows (a large chunk_rows setting): one lane group
 // walks the rows with the permutation read as it goes.
-template <int GS>
-__global__ __launch_bounds__(256) void ia_gather_long(const uint16_t* __restrict__ src, int64_t src_ld, int dim,
+template <int GS, typename E>
+__global__ __launch_bounds__(256) void ia_gather_long(const E* __restrict__ src, int64_t src_ld, int dim,
                                                       const int32_t* __restrict__ perm,
                                                       const uint32_t* __restrict__ seg_off,
                                                       const uint32_t* __restrict__ chunk_off, int n_rows, int L,
@@ -716,17 +753,20 @@ __global__ __launch_bounds__(256) void ia_gather_long(const uint16_t* __restrict
   for (int i = 0; i < 8; ++i) acc[i] = -0.0f;
   constexpr int kU = 8;
   for (uint32_t r = r0; r < r1; r += kU) {
-    uint4 v[kU];
+    Row8<E> v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (active && r + u < r1) {
         const int64_t p = perm[r + u];
-        v[u] = (p >= 0 && p < n_src) ? *reinterpret_cast<const uint4*>(src + p * src_ld + d0) : make_uint4(0u, 0u, 0u, 0u);
+        if (p >= 0 && p < n_src)
+          v[u].load(src + p * src_ld + d0);
+        else
+          v[u].clear();
       }
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-      if (active && r + u < r1) add8_bf16(acc, v[u]);
+      if (active && r + u < r1) v[u].add_to(acc);
   }
   if (!active) return;
   const uint32_t nk = chunk_off[k + 1] - chunk_off[k];
@@ -943,9 +983,9 @@ __global__ __launch_bounds__(256) void ia_fold(const uint32_t* __restrict__ chun
 }
 
 // ---- atomic arm: per-element float atomics, no sort
-template <int GS>
+template <int GS, typename E>
 __global__ __launch_bounds__(256) void ia_atomic(const int32_t* __restrict__ ids, int64_t n_src,
-                                                 const uint16_t* __restrict__ src, int64_t src_ld, int dim, int n_rows,
+                                                 const E* __restrict__ src, int64_t src_ld, int dim, int n_rows,
                                                  float* __restrict__ out, int64_t out_ld) {
   const int g = threadIdx.x / GS;
   const int lg = threadIdx.x % GS;
@@ -954,12 +994,11 @@ __global__ __launch_bounds__(256) void ia_atomic(const int32_t* __restrict__ ids
   const int32_t id = ids[p];
   if (id < 0 || id >= n_rows) return;
   const int d0 = 8 * lg;
-  const uint4 v = *reinterpret_cast<const uint4*>(src + p * src_ld + d0);
+  Row8<E> v;
+  v.load(src + p * src_ld + d0);
   float* o = out + static_cast<int64_t>(id) * out_ld + d0;
-  unsafeAtomicAdd(o + 0, bf16_lo(v.x)); unsafeAtomicAdd(o + 1, bf16_hi(v.x));
-  unsafeAtomicAdd(o + 2, bf16_lo(v.y)); unsafeAtomicAdd(o + 3, bf16_hi(v.y));
-  unsafeAtomicAdd(o + 4, bf16_lo(v.z)); unsafeAtomicAdd(o + 5, bf16_hi(v.z));
-  unsafeAtomicAdd(o + 6, bf16_lo(v.w)); unsafeAtomicAdd(o + 7, bf16_hi(v.w));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) unsafeAtomicAdd(o + i, v.get(i));
 }
 
 int group_size(int64_t dim) {
@@ -1013,7 +1052,6 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   if (int s = resolve(cfg, &L)) return s;
   if (src_dtype != DET_BF16 && src_dtype != DET_F32)
     return set_error(DET_ERR_INVALID_ARG, "index_add: unknown dtype %d", src_dtype);
-  if (src_dtype != DET_BF16) return set_error(DET_ERR_UNSUPPORTED, "index_add: only bf16 src is implemented");
   if (n_src == 0 || n_rows == 0 || dim == 0) return ok();
   if (!out || !ids || !src) return set_error(DET_ERR_INVALID_ARG, "index_add: NULL pointer");
   if (out_ld < dim || src_ld < dim) return set_error(DET_ERR_INVALID_ARG, "index_add: out_ld and src_ld must be >= dim");
@@ -1023,17 +1061,24 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   const size_t need = atomic ? 0 : l.total;
   if (int s = check_workspace(ws, ws_bytes, need)) return s;
   const Range o = range2d(out, n_rows, dim, out_ld, 4);
-  if (overlaps(o, range1d(ids, n_src * 4)) || overlaps(o, range2d(src, n_src, dim, src_ld, 2)) ||
+  if (overlaps(o, range1d(ids, n_src * 4)) || overlaps(o, range2d(src, n_src, dim, src_ld, src_dtype == DET_F32 ? 4 : 2)) ||
       overlaps(o, range1d(ws, ws_bytes)))
     return set_error(DET_ERR_OVERLAP, "index_add: out overlaps an input or the workspace");
   const hipStream_t st = as_stream(stream);
   const auto* s16 = static_cast<const uint16_t*>(src);
+  const auto* s32 = static_cast<const float*>(src);
+  const bool f32 = src_dtype == DET_F32;
   const int gs = group_size(dim);
   const int nr = static_cast<int>(n_rows);
   if (atomic) {
     const int64_t grid = ceil_div(n_src, 256 / gs);
 #define DET_IA_ATOMIC(G) \
-  if (gs == G) hipLaunchKernelGGL(ia_atomic<G>, dim3(grid), dim3(256), 0, st, ids, n_src, s16, src_ld, (int)dim, nr, out, out_ld);
+  if (gs == G && f32)                                                                                           \
+    hipLaunchKernelGGL((ia_atomic<G, float>), dim3(grid), dim3(256), 0, st, ids, n_src, s32, src_ld, (int)dim, nr, out, \
+                       out_ld);                                                                                  \
+  if (gs == G && !f32)                                                                                          \
+    hipLaunchKernelGGL((ia_atomic<G, uint16_t>), dim3(grid), dim3(256), 0, st, ids, n_src, s16, src_ld, (int)dim, nr, \
+                       out, out_ld);
     DET_IA_ATOMIC(1) DET_IA_ATOMIC(2) DET_IA_ATOMIC(4) DET_IA_ATOMIC(8) DET_IA_ATOMIC(16) DET_IA_ATOMIC(32)
     DET_IA_ATOMIC(64)
 #undef DET_IA_ATOMIC
@@ -1064,17 +1109,24 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
     default: launch_scatter<1>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
   }
   const int64_t grid_g = ceil_div(l.max_chunks, 256 / gs);
-#define DET_IA_TAIL(G)                                                                                           \
+#define DET_IA_TAIL_T(G, E, S)                                                                                  \
   if (gs == G) {                                                                                                 \
     if (L <= G * kPosPerLane)                                                                                    \
-      hipLaunchKernelGGL(ia_gather<G>, dim3(grid_g), dim3(256), 0, st, s16, src_ld, (int)dim, perm, seg_off,   \
+      hipLaunchKernelGGL((ia_gather<G, E>), dim3(grid_g), dim3(256), 0, st, S, src_ld, (int)dim, perm, seg_off,  \
                          chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);                           \
     else                                                                                                         \
-      hipLaunchKernelGGL(ia_gather_long<G>, dim3(grid_g), dim3(256), 0, st, s16, src_ld, (int)dim, perm,       \
+      hipLaunchKernelGGL((ia_gather_long<G, E>), dim3(grid_g), dim3(256), 0, st, S, src_ld, (int)dim, perm,      \
                          seg_off, chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);                  \
   }
+#define DET_IA_TAIL(G)                   \
+  if (f32) {                             \
+    DET_IA_TAIL_T(G, float, s32)         \
+  } else {                               \
+    DET_IA_TAIL_T(G, uint16_t, s16)      \
+  }
   const int dpl = (dim % 64 == 0) ? static_cast<int>(dim / 64) : 0;
-  if ((dpl == 2 || dpl == 4 || dpl == 8) && L <= 64 * kPosPerLane) {
+  // the one-wave-per-chunk gather is for bf16 rows; float32 rows take the lane-group gather
+  if (!f32 && (dpl == 2 || dpl == 4 || dpl == 8) && L <= 64 * kPosPerLane) {
     const int64_t grid_w = ceil_div(l.max_chunks, 4);
     // position registers per lane sized to the chunk length (fewer registers, more waves per SIMD)
 #define DET_IA_WAVE(D, NP)                                                                                      \
@@ -1089,6 +1141,7 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
     DET_IA_TAIL(1) DET_IA_TAIL(2) DET_IA_TAIL(4) DET_IA_TAIL(8) DET_IA_TAIL(16) DET_IA_TAIL(32) DET_IA_TAIL(64)
   }
 #undef DET_IA_TAIL
+#undef DET_IA_TAIL_T
   const int ds = fold_slice(dim);
   const dim3 fold_grid(static_cast<uint32_t>((n_rows < kFoldGroups ? n_rows : kFoldGroups) * (dim / ds)));
   if (ds == 32)

@@ -128,7 +128,8 @@ int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_
  * (det_index_add_bad_ids). Ids with no rows leave out[id] untouched.
  *
  * out:  [n_rows, dim] float32, row stride out_ld >= dim (elements).
- * ids:  [n_src] int32. src: [n_src, dim], row stride src_ld >= dim, DET_BF16.
+ * ids:  [n_src] int32. src: [n_src, dim], row stride src_ld >= dim, DET_BF16
+ *       (widened exactly) or DET_F32 (the page tests the indexer dK in both).
  * dim must be a multiple of 8; out_ld, src_ld multiples of 8; src and out
  * 16-byte aligned (DET_ERR_UNSUPPORTED otherwise). n_rows <= 16384, dim <= 512.
  * cfg:  NULL = {chunk_rows = 256}; chunk_rows in [1, 65536].

@@ -172,13 +172,14 @@ def test_index_add_validation():
     assert L.det_index_add_workspace_size(100, 16, 16385, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
     bad = dg.IndexAddCfg(0)
     assert L.det_index_add_workspace_size(100, 16, 10, ctypes.byref(bad), 0, ctypes.byref(n)) == dg.DET_ERR_INVALID_ARG
-    # out_ld < dim; misaligned src; overlap; fp32 src unsupported; workspace missing
+    # out_ld < dim; misaligned src; overlap; unknown src dtype; workspace missing (bf16 and fp32 src)
     O, I, S = P(0x100000), P(0x200000), P(0x300000)
     assert L.det_index_add(O, 10, 16, 8, I, 100, S, 16, 0, None, None, 0, 1, None) == dg.DET_ERR_INVALID_ARG
     assert L.det_index_add(O, 10, 16, 16, I, 100, P(0x300008), 16, 0, None, None, 0, 1, None) == dg.DET_ERR_UNSUPPORTED
     assert L.det_index_add(O, 10, 16, 16, P(0x100010), 100, S, 16, 0, None, None, 0, 1, None) == dg.DET_ERR_OVERLAP
-    assert L.det_index_add(O, 10, 16, 16, I, 100, S, 16, 1, None, None, 0, 1, None) == dg.DET_ERR_UNSUPPORTED
+    assert L.det_index_add(O, 10, 16, 16, I, 100, S, 16, 5, None, None, 0, 1, None) == dg.DET_ERR_INVALID_ARG
     assert L.det_index_add(O, 10, 16, 16, I, 100, S, 16, 0, None, None, 0, 0, None) == dg.DET_ERR_WORKSPACE
+    assert L.det_index_add(O, 10, 16, 16, I, 100, S, 16, 1, None, None, 0, 0, None) == dg.DET_ERR_WORKSPACE
     # empty problems return OK without touching anything
     assert L.det_index_add(None, 10, 16, 16, None, 0, None, 16, 0, None, None, 0, 0, None) == dg.DET_OK
 

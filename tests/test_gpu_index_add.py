@@ -14,11 +14,12 @@ pytestmark = pytest.mark.gpu
 def run(ids, src, out0, L=None, atomic=False, ws=None, src_pad=0):
     import torch
     P, D = src.shape
+    dev_src = dev_f32 if src.dtype == np.float32 else dev_bf16  # float32 values or bf16 bits
     if src_pad:
-        sb = np.zeros((P, D + src_pad), np.uint16); sb[:, :D] = src
-        s = dev_bf16(sb)[:, :D]
+        sb = np.zeros((P, D + src_pad), src.dtype); sb[:, :D] = src
+        s = dev_src(sb)[:, :D]
     else:
-        s = dev_bf16(src)
+        s = dev_src(src)
     o = dev_f32(out0)
     i = dev_i32(ids)
     torch.cuda.synchronize()
@@ -26,10 +27,12 @@ def run(ids, src, out0, L=None, atomic=False, ws=None, src_pad=0):
     return host(o)
 
 
-def small(P, n_rows, dim, seed, pad=0.05, out_init="normal"):
+def small(P, n_rows, dim, seed, pad=0.05, out_init="normal", dtype="bf16"):
     ids = W.zipf_ids(P, n_rows, 1.1, pad, seed)
     rng = np.random.default_rng(seed + 100)
-    src = W.bf16_bits(rng.standard_normal((P, dim)).astype(np.float32) * np.float32(0.02))
+    src = rng.standard_normal((P, dim)).astype(np.float32) * np.float32(0.02)
+    if dtype == "bf16":
+        src = W.bf16_bits(src)
     out0 = rng.standard_normal((n_rows, dim)).astype(np.float32) if out_init == "normal" else \
         np.zeros((n_rows, dim), np.float32)
     return ids, src, out0
@@ -123,3 +126,25 @@ def test_exact_integer_sources():
     for atomic in (False, True):
         got = run(ids, src, out0, 128, atomic=atomic)
         assert np.array_equal((got * 256).astype(np.int64), exact)
+
+
+@pytest.mark.parametrize("P,n_rows,dim,L", [(5000, 64, 128, 7), (20000, 1000, 128, 256), (3000, 7, 8, 1),
+                                            (9000, 300, 64, 256), (12345, 513, 512, 64), (8192, 16384, 24, 7),
+                                            (4000, 50, 128, 65536)])
+def test_f32_sources(P, n_rows, dim, L):
+    """float32 source rows (the lane-group gather and the long-chunk gather), bitwise."""
+    note("index_add f32 src P=%d rows=%d dim=%d L=%d" % (P, n_rows, dim, L))
+    ids, src, out0 = small(P, n_rows, dim, seed=P % 89, dtype="f32")
+    got = run(ids, src, out0, L)
+    assert_bitwise(got, oi.index_add(out0, ids, src, L), "index_add f32")
+    got = run(ids, src, out0, L, src_pad=8)
+    assert_bitwise(got, oi.index_add(out0, ids, src, L), "index_add f32 row stride")
+
+
+def test_f32_sources_full_size_and_atomic_arm():
+    inp = W.index_add_inputs(seed=3, out_init="normal", dtype="f32")
+    note("index_add full size with float32 sources")
+    want = oi.index_add(inp.out0, inp.ids, inp.src, 256)
+    assert_bitwise(run(inp.ids, inp.src, inp.out0, 256), want, "index_add f32 full")
+    a = run(inp.ids, inp.src, inp.out0, atomic=True)
+    assert rel_l2(a - inp.out0, want - inp.out0) <= 1e-5
