@@ -139,3 +139,31 @@ def dbias(dbias0, dA, offs, block_m):
             slots = [tree(t) for t in padded_tiles(col, block_m)]
             out[e][n] = F(out[e][n] + fold(slots))
     return np.array(out, np.float32).reshape(np.asarray(dbias0).shape)
+
+
+def topk_canonical(ids, logits):
+    """Per row: insertion sort of (id, slot) with padding last, then the softmax
+    in that order, one scalar at a time."""
+    Q, K = len(ids), len(ids[0])
+    io = np.zeros((Q, K), np.int32); lo = np.zeros((Q, K), np.float32); po = np.zeros((Q, K), np.float32)
+    for q in range(Q):
+        order = []
+        for j in range(K):
+            key = (0 if int(ids[q][j]) >= 0 else 1, int(ids[q][j]) if int(ids[q][j]) >= 0 else 0, j)
+            pos = len(order)
+            while pos > 0 and order[pos - 1][0] > key:
+                pos -= 1
+            order.insert(pos, (key, j))
+        for r, (_, j) in enumerate(order):
+            io[q, r] = ids[q][j]; lo[q, r] = logits[q][j]
+        nv = sum(1 for j in range(K) if int(ids[q][j]) >= 0)
+        if nv == 0:
+            continue
+        m = lo[q, 0]
+        for r in range(1, nv):
+            m = lo[q, r] if lo[q, r] > m else m
+        e = [detmath.exp32(np.float32(F(lo[q, r] - m)))[()] for r in range(nv)]
+        S = fold(e)
+        for r in range(nv):
+            po[q, r] = F(F(e[r]) / S)
+    return io, lo, po

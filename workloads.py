@@ -191,6 +191,31 @@ def dbias_inputs(M: int = 16384, N: int = 2048, E: int = 8, min_tokens: int = 25
     return DbiasInputs(M, N, offs, dA, d0)
 
 
+# ------------------------------------------------------------- compact top-k
+@dataclass
+class TopkInputs:
+    """Compact indexer top-k rows: ids (distinct per row, in a shuffled slot order,
+    -1 padding) and their logits."""
+    ids: np.ndarray     # int32 [Q, K]
+    logits: np.ndarray  # float32 [Q, K]
+
+
+def topk_inputs(Q: int = 4096, K: int = 512, n_keys: int = 8192, pad_frac: float = 0.05, seed: int = 7,
+                distinct: bool = True) -> TopkInputs:
+    """Per row: K keys drawn without replacement (with replacement when
+    ``distinct`` is False), i.i.d. padding slots, logits ~ N(0, 1); the slot
+    order is a random shuffle, as a run-dependent selection order would be."""
+    rng = _rng(seed, 0)
+    if distinct:
+        ids = np.argsort(rng.random((Q, n_keys)), axis=1)[:, :K].astype(np.int32)
+    else:
+        ids = rng.integers(0, n_keys, size=(Q, K)).astype(np.int32)
+    pad = _rng(seed, 1).random((Q, K)) < pad_frac
+    ids = np.where(pad, np.int32(-1), ids)
+    logits = _rng(seed, 2).standard_normal((Q, K), dtype=np.float32)
+    return TopkInputs(ids, logits)
+
+
 # -------------------------------------------------------------------------- wgrad
 @dataclass
 class WgradInputs:
