@@ -13,6 +13,7 @@ Functions (same names as the C ABI):
     det_grouped_dprob(dprob, dY, C, offs, cfg=None, atomic=False)
     det_grouped_wgrad_acc(main_grad, G, X, offs, cfg=None, atomic=False)
     det_grouped_dbias(dbias, dA, offs, cfg=None, atomic=False)
+    det_topk_canonicalize(ids, logits, ids_out, logits_out, probs)
 Every function accepts ``ws=`` (a Workspace or a uint8 device tensor) and
 ``stream=`` (a torch.cuda.Stream); by default a cached per-stream workspace
 and torch's current stream are used.
@@ -28,7 +29,7 @@ __all__ = [
     "det_abi_version", "det_colsum", "det_colsum_select_cfg", "det_colsum_workspace_size", "det_index_add",
     "det_index_add_workspace_size", "det_index_add_bad_ids", "det_grouped_dprob", "det_grouped_dprob_workspace_size",
     "det_grouped_wgrad_acc", "det_grouped_wgrad_acc_workspace_size", "det_grouped_dbias",
-    "det_grouped_dbias_workspace_size", "det_workspace_init", "det_detmath_eval",
+    "det_grouped_dbias_workspace_size", "det_topk_canonicalize", "det_workspace_init", "det_detmath_eval",
     "DET_OK", "DET_ERR_INVALID_ARG", "DET_ERR_UNSUPPORTED", "DET_ERR_WORKSPACE", "DET_ERR_OVERLAP", "DET_ERR_HIP",
 ]
 
@@ -90,6 +91,7 @@ _SIGS = {
     "det_grouped_wgrad_acc_workspace_size": ([_I64, _I32, _I64, _I64, ctypes.POINTER(WgradCfg), _INT,
                                               ctypes.POINTER(_SZ)], _INT),
     "det_detmath_eval": ([_P, _P, _I64, _INT, _P], _INT),
+    "det_topk_canonicalize": ([_P, _P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
     "det_grouped_dbias_workspace_size": ([_I64, _I64, _I32, ctypes.POINTER(DbiasCfg), _INT, ctypes.POINTER(_SZ)],
                                          _INT),
     "det_grouped_dbias": ([_P, _I64, _P, _I64, _I64, _I64, _P, _I32, ctypes.POINTER(DbiasCfg), _P, _SZ, _INT, _P],
@@ -290,6 +292,20 @@ def det_grouped_dbias(dbias, dA, offs, cfg: DbiasCfg | None = None, atomic=False
     _check(lib().det_grouped_dbias(_ptr(dbias), dbias.stride(0), _ptr(dA), dA.stride(0), M, N, _ptr(offs), E,
                                    ctypes.byref(cfg) if cfg else None, wp, wn, _atomic_flag(atomic),
                                    _stream_handle(stream)))
+
+
+# ------------------------------------------------------------- compact top-k
+def det_topk_canonicalize(ids, logits, ids_out, logits_out, probs, stream=None) -> None:
+    """Per row of the [Q, K] compact top-k: ids sorted (padding last), logits permuted alike,
+    softmax recomputed in that order. ids int32, logits and outputs float32 (ids_out int32)."""
+    Q, K = ids.shape
+    if ids.stride(1) != 1 or logits.stride(1) != 1 or ids.stride(0) != logits.stride(0):
+        raise ValueError("ids and logits need unit column stride and one row stride")
+    if not (ids_out.stride(0) == logits_out.stride(0) == probs.stride(0)) or \
+            ids_out.stride(1) != 1 or logits_out.stride(1) != 1 or probs.stride(1) != 1:
+        raise ValueError("outputs need unit column stride and one row stride")
+    _check(lib().det_topk_canonicalize(_ptr(ids), _ptr(logits), Q, K, ids.stride(0), _ptr(ids_out),
+                                       _ptr(logits_out), _ptr(probs), probs.stride(0), _stream_handle(stream)))
 
 
 # ---------------------------------------------------------------------- wgrad

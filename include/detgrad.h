@@ -268,6 +268,31 @@ int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_m, const vo
                           const det_wgrad_cfg* cfg, void* ws, size_t ws_bytes, int atomic, void* stream);
 
 /* ------------------------------------------------------------------------
+ * det_topk_canonicalize: canonical order of a compact indexer top-k.
+ * Megatron-LM PR #7441 (DSv4 deterministic mode), source 1: the compact
+ * indexer top-k returns each row's ids in a run-dependent slot order and
+ * accumulates its softmax in that order; the fix sorts the ids of every row
+ * with the padding last, permutes the logits with the same permutation,
+ * recomputes the softmax in that order, and makes all-padding rows zero.
+ *
+ * Canonical order per row: slots with a valid id (>= 0) by ascending id,
+ * equal ids by ascending slot, then the padding slots (negative ids) by slot.
+ * ids_out and logits_out are the row's ids and logits in that order. With
+ * m = the largest valid logit, e_j = exp32(logit_j - m) (the fixed float32
+ * sequence of det_colsum), S = the left-to-right sum of the e_j in that order,
+ * probs_j = e_j / S (one correctly rounded division) for valid slots and +0.0
+ * for padding; a row with no valid id gets all +0.0. Distinct ids in any slot
+ * order give the same bits.
+ *
+ * ids: [Q, K] int32, logits: [Q, K] float32, row stride ld >= K (elements).
+ * ids_out: [Q, K] int32, logits_out, probs: [Q, K] float32, row stride
+ *          ld_out >= K; outputs must not overlap the inputs or each other.
+ * K <= 1024 (DET_ERR_UNSUPPORTED otherwise). No workspace. The entry point is
+ * deterministic by construction and has no atomic arm. */
+int det_topk_canonicalize(const int32_t* ids, const float* logits, int64_t Q, int64_t K, int64_t ld,
+                          int32_t* ids_out, float* logits_out, float* probs, int64_t ld_out, void* stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics (tests only). det_detmath_eval evaluates the device versions of
  * the gate's exp / log1p / softplus / sigmoid sequences elementwise:
  * fn = 0 exp32, 1 log1p32, 2 softplus32, 3 sigmoid32. x, y: [n] float32

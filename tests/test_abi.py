@@ -113,6 +113,22 @@ def test_dbias_validation():
     assert L.det_grouped_dbias(None, 64, None, 64, 16, 64, None, 0, None, None, 0, 0, None) == dg.DET_OK
 
 
+def test_topk_validation():
+    L = lib()
+    Z = P(0x500000)
+    assert L.det_topk_canonicalize(FAKE, FAKE, -1, 8, 8, FAKE, FAKE, FAKE, 8, None) == dg.DET_ERR_INVALID_ARG
+    assert L.det_topk_canonicalize(FAKE, FAKE, 4, 1025, 1025, FAKE, FAKE, FAKE, 1025, None) == dg.DET_ERR_UNSUPPORTED
+    assert L.det_topk_canonicalize(FAKE, FAKE, 4, 8, 4, FAKE, FAKE, FAKE, 8, None) == dg.DET_ERR_INVALID_ARG
+    assert L.det_topk_canonicalize(None, FAKE, 4, 8, 8, FAKE, FAKE, FAKE, 8, None) == dg.DET_ERR_INVALID_ARG
+    # an output overlapping an input, or two outputs overlapping
+    assert L.det_topk_canonicalize(P(0x600000), P(0x610000), 4, 8, 8, P(0x600010), Z, P(0x520000), 8, None) == \
+        dg.DET_ERR_OVERLAP
+    assert L.det_topk_canonicalize(P(0x600000), P(0x610000), 4, 8, 8, Z, P(0x500010), P(0x520000), 8, None) == \
+        dg.DET_ERR_OVERLAP
+    # empty problems: OK with nothing launched
+    assert L.det_topk_canonicalize(None, None, 0, 8, 8, None, None, None, 8, None) == dg.DET_OK
+
+
 def test_colsum_validation_and_selector():
     L = lib()
     # shape-only rule: block_h = 8; block_t the largest of 256/128 that still

@@ -1,0 +1,58 @@
+"""GPU parity of det_topk_canonicalize against the CPU oracle (bitwise): ids,
+permuted logits and probabilities; slot-order invariance on the GPU."""
+import numpy as np
+import pytest
+
+import deterministic_gradient_reductions_amd as dg
+import workloads as W
+from oracle import topk as ot
+from tests.gpu_util import assert_bitwise, dev_f32, dev_i32, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def run(ids, logits, out_pad=0):
+    import torch
+    Q, K = ids.shape
+    i, l = dev_i32(ids), dev_f32(logits)
+    io = torch.full((Q, K + out_pad), 7, dtype=torch.int32, device="cuda")[:, :K]
+    lo = torch.full((Q, K + out_pad), 7.0, dtype=torch.float32, device="cuda")[:, :K]
+    po = torch.full((Q, K + out_pad), 7.0, dtype=torch.float32, device="cuda")[:, :K]
+    torch.cuda.synchronize()
+    dg.det_topk_canonicalize(i, l, io, lo, po)
+    return host(io), host(lo), host(po)
+
+
+def check(ids, logits, what, out_pad=0):
+    got = run(ids, logits, out_pad)
+    want = ot.canonicalize(ids, logits)
+    assert np.array_equal(got[0], want[0]), what + " ids"
+    assert_bitwise(got[1], want[1], what + " logits")
+    assert_bitwise(got[2], want[2], what + " probs")
+
+
+@pytest.mark.parametrize("Q,K,n_keys,distinct,pad", [(64, 512, 8192, True, 0.05), (33, 1000, 4096, True, 0.1),
+                                                     (50, 64, 100, False, 0.3), (7, 1, 5, False, 0.5),
+                                                     (20, 129, 300, False, 0.0), (9, 1024, 2000, True, 0.02),
+                                                     (12, 37, 20, False, 0.2)])
+def test_parity(Q, K, n_keys, distinct, pad):
+    note("topk parity Q=%d K=%d distinct=%s pad=%.2f" % (Q, K, distinct, pad))
+    inp = W.topk_inputs(Q=Q, K=K, n_keys=n_keys, seed=K, distinct=distinct, pad_frac=pad)
+    ids = inp.ids.copy()
+    ids[0, :] = -1  # a row that is all padding
+    check(ids, inp.logits, "topk", out_pad=3 if K % 2 else 0)
+
+
+def test_full_size_and_slot_order_invariance():
+    inp = W.topk_inputs(seed=7)  # 4096 x 512
+    note("topk full size")
+    ref = run(inp.ids, inp.logits)
+    want = ot.canonicalize(inp.ids, inp.logits)
+    assert np.array_equal(ref[0], want[0])
+    assert_bitwise(ref[1], want[1], "topk full logits"); assert_bitwise(ref[2], want[2], "topk full probs")
+    perm = np.argsort(np.random.default_rng(1).random(inp.ids.shape), axis=1)
+    got = run(np.take_along_axis(inp.ids, perm, 1), np.take_along_axis(inp.logits, perm, 1))
+    valid = ref[0] >= 0
+    assert np.array_equal(got[0], ref[0])
+    assert_bitwise(got[2], ref[2], "probs after reshuffle")
+    assert np.array_equal(got[1].view(np.uint32)[valid], ref[1].view(np.uint32)[valid])
