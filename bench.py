@@ -137,7 +137,8 @@ def build_workloads():
 
 
 def build_extra_workloads():
-    """Entry points measured beside the step (not part of it): grouped dbias at the dprob shapes."""
+    """Entry points measured beside the step (not part of it): grouped dbias at the dprob shapes
+    and the canonical compact top-k."""
     import torch
     import deterministic_gradient_reductions_amd as dg
     import workloads as W
@@ -153,7 +154,24 @@ def build_extra_workloads():
         lambda: dg.det_grouped_dbias(d, dA, offs, atomic=True),
         lambda: d.copy_(d0),
         lambda: d.cpu().numpy(),
-        nbytes=db.M * db.N * 2 + 8 * db.N * 4 * 2)]
+        nbytes=db.M * db.N * 2 + 8 * db.N * 4 * 2),
+        topk_workload()]
+
+
+def topk_workload():
+    """Canonical compact top-k, 4096 rows x 512 slots (deterministic by construction: its
+    comparison arm is the same call)."""
+    import torch
+    import deterministic_gradient_reductions_amd as dg
+    import workloads as W
+    tk = W.topk_inputs(seed=7)
+    ids = torch.from_numpy(tk.ids).cuda()
+    lg = torch.from_numpy(tk.logits).cuda()
+    io, lo, po = torch.empty_like(ids), torch.empty_like(lg), torch.empty_like(lg)
+    call = lambda: dg.det_topk_canonicalize(ids, lg, io, lo, po)
+    return Workload("topk_canon", call, call, lambda: po.zero_(),
+                    lambda: torch.cat([io.view(torch.float32).flatten(), lo.flatten(), po.flatten()]).cpu().numpy(),
+                    nbytes=tk.ids.size * (4 + 4 + 4 + 4 + 4))
 
 
 # ------------------------------------------------------------------- timing

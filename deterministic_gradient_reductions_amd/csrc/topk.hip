@@ -10,16 +10,21 @@
 // One wave per row. Each of the K slots becomes a 64-bit key (id << 32 | slot
 // for a valid id, 2^31 << 32 | slot for padding, all ones for the positions
 // that round K up to a power of two): the keys are distinct, so the sorted
-// order is unique and equals the stable order with padding last. The keys are
-// sorted with a bitonic network held in registers: element i = lane * EPL + r
-// (EPL elements per lane), partners within a lane are swapped in registers,
-// partners across lanes are exchanged with one shuffle per 32-bit half. The
+// order is unique and equals the stable order with padding last. When every
+// id of the row is below 2^21 - 1 the same order is carried by a 32-bit key
+// (id << 10 | slot, padding as id 2^21 - 1), which halves the cross-lane
+// traffic. The keys are sorted with a bitonic network held in registers:
+// element i = r * 64 + lane (EPL elements per lane, so loads and stores are
+// coalesced); partners at a distance below 64 are exchanged across lanes with
+// shuffles, partners further apart are swapped between registers. The
 // sorted keys give each output position its source slot, from which the id
 // and the logit are gathered. The softmax: the exact maximum of the valid
 // logits (a wave reduction), e = exp32(logit - max) (the gate's fixed
-// sequence), the left-to-right sum of the e's in the sorted order (readlane
-// feeds one dependent add per slot), and one correctly rounded division per
-// slot. Padding slots get +0.0.
+// sequence), the left-to-right sum of the e's in the sorted order, and one
+// correctly rounded division per slot. For the sums the four waves of a
+// workgroup leave their e's in LDS and lanes 0..3 of the first wave add one
+// row each, so four dependent-add chains share one instruction stream.
+// Padding slots get +0.0.
 #include "common.hpp"
 #include "detmath.hpp"
 
@@ -35,22 +40,86 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   return static_cast<uint64_t>(b) << 32 | a;
 }
 
+__device__ __forceinline__ uint32_t shfl_xor_k(uint32_t v, int m) {
+  return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m));
+}
+__device__ __forceinline__ uint64_t shfl_xor_k(uint64_t v, int m) { return shfl_xor64(v, m); }
+
+// Ascending bitonic sort of the wave's 64 * EPL keys, element i = r * 64 +
+// lane: partners closer than 64 are in other lanes (shuffles), partners
+// further apart in other registers.
+template <int EPL, typename T>
+__device__ __forceinline__ void bitonic(T (&key)[EPL], int lane) {
+  constexpr int N = 64 * EPL;
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int d = k >> 1; d > 0; d >>= 1) {
+      if (d >= 64) {
+        const int dr = d / 64;
+#pragma unroll
+        for (int r = 0; r < EPL; ++r) {
+          const int rp = r ^ dr;
+          if (rp > r) {
+            const int i = r * 64 + lane;
+            const bool up = (i & k) == 0;
+            const T a = key[r], b = key[rp];
+            const bool swap = up ? (a > b) : (a < b);
+            key[r] = swap ? b : a;
+            key[rp] = swap ? a : b;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < EPL; ++r) {
+          const int i = r * 64 + lane;
+          const T o = shfl_xor_k(key[r], d);
+          const bool up = (i & k) == 0;
+          const bool lower = (i & d) == 0;  // this element is the lower index of the pair
+          // an ascending pair keeps the smaller key at its lower index
+          const bool keep_min = (up == lower);
+          const T mn = key[r] < o ? key[r] : o, mx = key[r] < o ? o : key[r];
+          key[r] = keep_min ? mn : mx;
+        }
+      }
+    }
+  }
+}
+
+// True when every valid id of the row is below 2^21 - 1 (so id << 10 | slot
+// is a 32-bit key).
+template <int EPL>
+__device__ __forceinline__ bool wave_ids_narrow(const uint64_t (&key)[EPL]) {
+  bool wide = false;
+#pragma unroll
+  for (int r = 0; r < EPL; ++r) {
+    const uint32_t hi = static_cast<uint32_t>(key[r] >> 32);
+    wide = wide || (key[r] != ~0ull && hi != 0x80000000u && hi >= 0x1FFFFFu);
+  }
+  return __ballot(wide) == 0;
+}
+
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restrict__ ids, const float* __restrict__ logits,
                                                          int64_t Q, int K, int64_t ld, int32_t* __restrict__ ids_out,
                                                          float* __restrict__ logits_out, float* __restrict__ probs,
                                                          int64_t ld_out) {
   constexpr int N = 64 * EPL;  // padded row length, a power of two
-  const int lane = threadIdx.x & 63;
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (q >= Q) return;  // wave-uniform
-  const int32_t* const ir = ids + q * ld;
-  const float* const lr = logits + q * ld;
+  __shared__ float es[4][N];   // each wave's e values, in sorted order, for the sums
+  __shared__ float sums[4];
+  __shared__ int nvs[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const bool row = q < Q;  // wave-uniform; every wave reaches the barrier
+  const int32_t* const ir = ids + (row ? q : 0) * ld;
+  const float* const lr = logits + (row ? q : 0) * ld;
+  // element i = r * 64 + lane: partners at distance d < 64 sit in another
+  // lane (one shuffle per 32-bit half), at d >= 64 in another register
   uint64_t key[EPL];
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
-    const int i = lane * EPL + r;
-    if (i < K) {
+    const int i = r * 64 + lane;
+    if (row && i < K) {
       const int32_t id = ir[i];
       const uint32_t hi = id >= 0 ? static_cast<uint32_t>(id) : 0x80000000u;
       key[r] = static_cast<uint64_t>(hi) << 32 | static_cast<uint32_t>(i);
@@ -58,39 +127,26 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
       key[r] = ~0ull;
     }
   }
-  // bitonic sort, ascending
+  // keys of 32 bits (id << 10 | slot) when every id of the row is below
+  // 2^21 - 1 (K <= 1024 slots), else of 64 bits: the same order, half the
+  // cross-lane traffic
+  const bool narrow = wave_ids_narrow<EPL>(key);
+  if (narrow) {
+    uint32_t k32[EPL];
 #pragma unroll
-  for (int k = 2; k <= N; k <<= 1) {
-#pragma unroll
-    for (int d = k >> 1; d > 0; d >>= 1) {
-      if (d < EPL) {
-#pragma unroll
-        for (int r = 0; r < EPL; ++r) {
-          const int rp = r ^ d;
-          if (rp > r) {
-            const int i = lane * EPL + r;
-            const bool up = (i & k) == 0;
-            const uint64_t a = key[r], b = key[rp];
-            const bool swap = up ? (a > b) : (a < b);
-            key[r] = swap ? b : a;
-            key[rp] = swap ? a : b;
-          }
-        }
-      } else {
-        const int m = d / EPL;  // partner lane = lane ^ m
-#pragma unroll
-        for (int r = 0; r < EPL; ++r) {
-          const int i = lane * EPL + r;
-          const uint64_t o = shfl_xor64(key[r], m);
-          const bool up = (i & k) == 0;
-          const bool lower = (i & d) == 0;  // this element is the lower index of the pair
-          // ascending pair: the lower index keeps the smaller key
-          const bool keep_min = (up == lower);
-          const uint64_t mn = key[r] < o ? key[r] : o, mx = key[r] < o ? o : key[r];
-          key[r] = keep_min ? mn : mx;
-        }
-      }
+    for (int r = 0; r < EPL; ++r) {
+      const uint32_t hi = static_cast<uint32_t>(key[r] >> 32), lo = static_cast<uint32_t>(key[r]);
+      k32[r] = key[r] == ~0ull ? ~0u : ((hi == 0x80000000u ? 0x1FFFFFu : hi) << 10 | lo);
     }
+    bitonic<EPL>(k32, lane);
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+      const uint32_t hi = k32[r] >> 10, lo = k32[r] & 0x3FFu;
+      key[r] = k32[r] == ~0u ? ~0ull
+                             : (static_cast<uint64_t>(hi == 0x1FFFFFu ? 0x80000000u : hi) << 32 | lo);
+    }
+  } else {
+    bitonic<EPL>(key, lane);
   }
   // gather ids and logits by source slot; the valid slots come first
   int32_t idv[EPL];
@@ -99,16 +155,16 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
   float mx = -__builtin_inff();
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
-    const int i = lane * EPL + r;
+    const int i = r * 64 + lane;
     const uint32_t slot = static_cast<uint32_t>(key[r]);
-    const bool in = i < K;
+    const bool in = row && i < K;
     idv[r] = in ? ir[slot] : 0;
     lg[r] = in ? lr[slot] : 0.0f;
     const bool valid = in && (key[r] >> 32) < 0x80000000ull;
     nv_lane += valid ? 1 : 0;
     if (valid) mx = mx > lg[r] ? mx : lg[r];
   }
-  // exact maximum over the wave
+  // exact maximum and valid count over the wave
 #pragma unroll
   for (int m = 32; m > 0; m >>= 1) {
     const float o = __shfl_xor(mx, m);
@@ -120,23 +176,35 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
   float e[EPL];
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
-    const int i = lane * EPL + r;
+    const int i = r * 64 + lane;
     e[r] = i < nv ? dm::exp32(lg[r] - mx) : 0.0f;
+    es[wave][i] = e[r];
   }
-  // left-to-right sum in the sorted order: element i = lane * EPL + r
-  float S = -0.0f;
-  for (int l = 0; l < 64; ++l) {
-    if (l * EPL >= nv) break;  // uniform
-#pragma unroll
-    for (int r = 0; r < EPL; ++r)
-      if (l * EPL + r < nv) S = S + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e[r]), l));
+  if (lane == 0) nvs[wave] = row ? nv : 0;
+  __syncthreads();
+  // the left-to-right sums: lane w of wave 0 adds row w's values in order
+  // (four independent dependent-add chains in one instruction stream)
+  if (wave == 0 && lane < 4) {
+    const int nvw = nvs[lane];  // valid values of row `lane` (0 past Q): the prefix of its es row
+    const float* const ew = es[lane];
+    float S = -0.0f;
+    int i = 0;
+    for (; i + 4 <= nvw; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(ew + i);
+      S = S + v.x; S = S + v.y; S = S + v.z; S = S + v.w;
+    }
+    for (; i < nvw; ++i) S = S + ew[i];
+    sums[lane] = S;
   }
+  __syncthreads();
+  if (!row) return;
+  const float S = sums[wave];
   int32_t* const io = ids_out + q * ld_out;
   float* const lo = logits_out + q * ld_out;
   float* const po = probs + q * ld_out;
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
-    const int i = lane * EPL + r;
+    const int i = r * 64 + lane;
     if (i < K) {
       io[i] = idv[r];
       lo[i] = lg[r];

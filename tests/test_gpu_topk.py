@@ -43,6 +43,19 @@ def test_parity(Q, K, n_keys, distinct, pad):
     check(ids, inp.logits, "topk", out_pad=3 if K % 2 else 0)
 
 
+@pytest.mark.parametrize("top", [(1 << 21) - 2, (1 << 21) - 1, 2**31 - 1])
+def test_id_range(top):
+    """Ids up to the largest one the 32-bit sort key holds, and past it (the
+    64-bit key); rows of both kinds share workgroups."""
+    note("topk id range top=%d" % top)
+    inp = W.topk_inputs(Q=41, K=300, n_keys=64, seed=3, distinct=False, pad_frac=0.1)
+    ids = inp.ids.copy()
+    ids[ids >= 0] += top - 63
+    ids[1::3] = np.where(ids[1::3] >= 0, ids[1::3] - (top - 63), -1)  # small ids on every third row
+    ids[2, :] = -1
+    check(ids, inp.logits, "topk ids to %d" % top)
+
+
 def test_full_size_and_slot_order_invariance():
     inp = W.topk_inputs(seed=7)  # 4096 x 512
     note("topk full size")
