@@ -21,13 +21,19 @@ Per-element operation order (binary32, no fused multiply-add):
     x  = f32(a) + dt_bias[h];  nA = -exp32(A_log[h]);  e = exp32(-|x|)
     sp = softplus32(x);        sg = sigmoid32(x)      (both from the same e)
     t1 = f32(dg) * (nA * sp);  t2 = f32(dg) * (nA * sg)
+
+The elementwise gradient of the gate input (the scope table's gate-variants
+row; the page itself names only the two parameter gradients): x depends on
+a[t,h] and dt_bias[h] alike, so da[t,h] = dg * dg/da is the same term t2,
+kept per element and stored in the input precision (bf16 round to nearest
+even for bf16 inputs, float32 as is).
 """
 from __future__ import annotations
 
 import numpy as np
 
 from . import detmath
-from .primitives import accumulate, pairwise, sequential, tiles, widen_bf16
+from .primitives import accumulate, narrow_bf16, pairwise, sequential, tiles, widen_bf16
 
 
 def gate_input(x) -> np.ndarray:
@@ -52,6 +58,13 @@ def gate_terms(a_bits, dg_bits, A_log, dt_bias):
     t1 = dg * g
     t2 = dg * (nA[None, :] * sg)
     return t1.astype(np.float32), t2.astype(np.float32)
+
+
+def gate_da(a_bits, dg_bits, A_log, dt_bias) -> np.ndarray:
+    """da [T, H]: t2 per element, as bf16 bits (uint16) for bf16 inputs and
+    float32 for float32 inputs."""
+    _, t2 = gate_terms(a_bits, dg_bits, A_log, dt_bias)
+    return t2 if np.asarray(a_bits).dtype == np.float32 else narrow_bf16(t2)
 
 
 def gate_slots(a_bits, dg_bits, A_log, dt_bias, block_t: int):

@@ -33,6 +33,19 @@ def widen_bf16(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def narrow_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to
+    the even significand; NaN stays NaN (quiet), infinities and signed zeros
+    are kept. Written on the bit pattern: adding 0x7FFF plus the lowest kept
+    bit carries into the kept part exactly when the dropped half-word is above
+    the midpoint, or at it with an odd kept part."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    r = np.where(nan, (u >> 16) | 0x0040, r)
+    return (r & 0xFFFF).astype(np.uint16)
+
+
 def tiles(x: np.ndarray, block: int, axis: int) -> np.ndarray:
     """Split ``axis`` into consecutive tiles of ``block`` elements.
 

@@ -5,7 +5,7 @@ import pytest
 
 import workloads as W
 from oracle import brute, colsum as oc, dbias as odb, dprob as od, fp64, index_add as oi, wgrad as ow
-from oracle.primitives import widen_bf16
+from oracle.primitives import narrow_bf16, widen_bf16
 
 U = 2.0 ** -24
 
@@ -261,6 +261,87 @@ def test_colsum_invariants():
 
 
 # -------------------------------------------------------------------- index_add
+def _nearest_bf16_brute(x):
+    """Scalar restatement: the two bf16 values around x (as float64), the
+    nearer one, ties to the one with the even last significand bit."""
+    out = []
+    for v in np.asarray(x, np.float32):
+        if np.isnan(v):
+            out.append("nan")
+            continue
+        if np.isinf(v) or v == 0:
+            out.append(float(v))
+            continue
+        lo = (int(np.float32(v).view(np.uint32)) >> 16) << 16
+        cand = [lo, lo + 0x10000]
+        # a candidate past the largest finite value stands for 2^128 in the
+        # distance (IEEE overflow rounding) and is the infinity itself
+        vals = [float(np.uint32(c).view(np.float32)) for c in cand]
+        dist = [float(np.sign(v)) * 2.0 ** 128 if np.isinf(w) else w for w in vals]
+        d = [abs(float(v) - w) for w in dist]
+        if d[0] != d[1]:
+            out.append(vals[0] if d[0] < d[1] else vals[1])
+        else:
+            out.append(vals[0] if ((cand[0] >> 16) & 1) == 0 else vals[1])
+    return out
+
+
+def test_narrow_bf16_round_to_nearest_even():
+    rng = np.random.default_rng(3)
+    u = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32)
+    ties = (u & np.uint32(0xFFFF0000)) | np.uint32(0x8000)   # exactly halfway
+    special = np.array([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001, 0x00000001, 0x007FFFFF,
+                        0x7F7FFFFF, 0x7F7F8000, 0x3F808000, 0x3F818000], np.uint32)
+    x = np.concatenate([u, ties, special]).view(np.float32)
+    got = narrow_bf16(x)
+    # the library conversion (round to nearest even) on the same values
+    import torch
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(widen_bf16(got[nan])))
+    # brute nearest-value choice on a sample (float64 distances), incl. ties and overflow to inf
+    idx = np.r_[0:400, 20000:20400, 40000:40000 + len(special)]
+    br = _nearest_bf16_brute(x[idx])
+    w = widen_bf16(got[idx])
+    for g, b in zip(w, br):
+        assert (b == "nan" and np.isnan(g)) or (g == b and np.signbit(g) == np.signbit(b))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gate_da_is_the_derivative(dtype):
+    """da against a float64 central difference of the gate in a (independent
+    of the closed form), scaled by dg: within fp32 evaluation error plus the
+    output rounding."""
+    g = W.gate_inputs(T=300, H=6, seed=4, dtype=dtype)
+    da = oc.gate_da(g.a, g.dg, g.A_log, g.dt_bias)
+    daf = widen_bf16(da) if dtype == "bf16" else da
+    a64 = g.a.astype(np.float64) if dtype == "f32" else widen_bf16(g.a).astype(np.float64)
+    dg64 = g.dg.astype(np.float64) if dtype == "f32" else widen_bf16(g.dg).astype(np.float64)
+    nA = -np.exp(g.A_log.astype(np.float64))
+
+    def gate(a):
+        return nA[None, :] * np.logaddexp(0.0, a + g.dt_bias.astype(np.float64)[None, :])
+    h = 1e-5
+    fd = dg64 * (gate(a64 + h) - gate(a64 - h)) / (2 * h)
+    out_rel = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -23
+    err = np.abs(daf - fd)
+    assert np.all(err <= np.abs(fd) * (out_rel + 1e-5) + 1e-9), float((err / (np.abs(fd) + 1e-30)).max())
+    # da is never of the opposite sign to -dg (the gate falls with a)
+    assert np.all(daf * dg64 <= 0)
+
+
+def test_gate_da_sums_to_ddt_bias_order():
+    """With float32 inputs da is the unrounded ddt_bias term: its column sums in
+    the canonical order give ddt_bias bit for bit."""
+    g = W.gate_inputs(T=700, H=5, seed=8, dtype="f32")
+    da = oc.gate_da(g.a, g.dg, g.A_log, g.dt_bias)
+    _, ddt = oc.colsum(g.a, g.dg, g.A_log, g.dt_bias, np.zeros(5, np.float32), np.zeros(5, np.float32), 128)
+    from oracle.primitives import pairwise, sequential, tiles
+    s = sequential(pairwise(tiles(da, 128, axis=0)), axis=0)
+    assert np.array_equal(bits(np.float32(0) + s), bits(ddt))
+
+
 def small_index_inputs(seed=1, P=3000, n_rows=64, dim=16, pad=0.05, out_init="normal", dtype="bf16"):
     ids = W.zipf_ids(P, n_rows, 1.1, pad, seed)
     rng = np.random.default_rng(seed)
