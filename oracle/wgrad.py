@@ -20,12 +20,17 @@ Canonical order (the reading taken here):
 * main_grad[e][i, j] <- RN32(main_grad[e][i, j] + fold(Q_0 .. Q_{S_e - 1}))
   with fold the left-to-right sum starting at -0.0. An expert with no rows
   leaves its main_grad slice bitwise unchanged.
+* A bf16 main_grad (#8924, "Design and numerics": for bf16 out the bf16 dW is
+  added in bf16, bitwise the AccumulateGrad of the deterministic dW): the same
+  fold gives the float32 dW, which is rounded to bf16 (nearest even); the two
+  bf16 values are added in float32 (RN32) and the sum rounded to bf16, as a
+  bf16 tensor add does.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .primitives import NEG_ZERO, accumulate, widen_bf16
+from .primitives import NEG_ZERO, accumulate, narrow_bf16, widen_bf16
 
 K_TILE = 512
 
@@ -44,12 +49,24 @@ def split_ranges(offs, k_tile: int = K_TILE, ktiles_per_split: int = 0):
     return out
 
 
-def fold_partials(main_grad0: np.ndarray, partials) -> np.ndarray:
-    """RN32(main_grad0 + left-to-right fold of the partial list)."""
-    total = np.full(main_grad0.shape, NEG_ZERO, np.float32)
+def fold_total(partials, shape) -> np.ndarray:
+    """Left-to-right fold of the partial list, from -0.0."""
+    total = np.full(shape, NEG_ZERO, np.float32)
     for q in partials:
         total = np.add(total, np.asarray(q, np.float32), dtype=np.float32)
-    return accumulate(main_grad0, total)
+    return total
+
+
+def fold_partials(main_grad0: np.ndarray, partials) -> np.ndarray:
+    """RN32(main_grad0 + left-to-right fold of the partial list)."""
+    return accumulate(main_grad0, fold_total(partials, main_grad0.shape))
+
+
+def accumulate_bf16(main_grad_bits: np.ndarray, dW: np.ndarray) -> np.ndarray:
+    """bf16 main_grad (uint16 bits) plus the float32 dW, added in bf16:
+    RN_bf16(RN32(main_grad + RN_bf16(dW)))."""
+    d16 = widen_bf16(narrow_bf16(dW))
+    return narrow_bf16(np.add(widen_bf16(main_grad_bits), d16, dtype=np.float32))
 
 
 def chain_exact_rounded(g_f32: np.ndarray, x_f32: np.ndarray) -> np.ndarray:
@@ -73,4 +90,18 @@ def grouped_wgrad_acc(main_grad0, G_bits, X_bits, offs, k_tile: int = K_TILE, kt
             continue
         parts = [chain(widen_bf16(G_bits[b:t]), widen_bf16(X_bits[b:t])) for b, t in sp]
         mg[e] = fold_partials(mg[e], parts)
+    return mg
+
+
+def grouped_wgrad_acc_bf16(main_grad0_bits, G_bits, X_bits, offs, k_tile: int = K_TILE, ktiles_per_split: int = 0,
+                           chain=chain_exact_rounded, experts=None) -> np.ndarray:
+    """bf16 main_grad [E, M, N] (uint16 bits) after the bf16 accumulate of the
+    deterministic dW; experts with no rows keep their bits."""
+    mg = np.array(main_grad0_bits, np.uint16, copy=True)
+    splits = split_ranges(offs, k_tile, ktiles_per_split)
+    for e, sp in enumerate(splits):
+        if (experts is not None and e not in experts) or not sp:
+            continue
+        parts = [chain(widen_bf16(G_bits[b:t]), widen_bf16(X_bits[b:t])) for b, t in sp]
+        mg[e] = accumulate_bf16(mg[e], fold_total(parts, mg[e].shape))
     return mg

@@ -439,3 +439,38 @@ def test_wgrad_fp64_rel_l2():
     got = ow.grouped_wgrad_acc(inp.main_grad0, inp.G, inp.X, inp.offs, 512, 1)
     ex = fp64.wgrad64(inp.main_grad0, inp.G, inp.X, inp.offs)
     assert rel_l2(got, ex) <= 1e-5
+
+
+def test_wgrad_bf16_accumulate_is_the_bf16_tensor_add():
+    """The bf16 accumulate equals a bf16 tensor add of the bf16-rounded dW (the
+    library's AccumulateGrad for a bf16 gradient), including exponent gaps,
+    ties, signed zeros and overflow."""
+    import torch
+    rng = np.random.default_rng(11)
+    n = 50000
+    mg = narrow_bf16((rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32))
+    dW = (rng.standard_normal(n) * np.exp2(rng.integers(-40, 40, n))).astype(np.float32)
+    mg[:4] = narrow_bf16(np.array([0.0, -0.0, 3.0e38, -0.0], np.float32))
+    dW[:4] = np.array([-0.0, -0.0, 3.0e38, 0.0], np.float32)
+    got = ow.accumulate_bf16(mg, dW)
+    t = torch.from_numpy(mg.view(np.int16).copy()).view(torch.bfloat16)
+    t.add_(torch.from_numpy(dW).to(torch.bfloat16))
+    assert np.array_equal(got, t.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_wgrad_bf16_exact_integers_and_empty_expert():
+    """Small integer inputs: dW and main_grad + dW are integers bf16 holds
+    exactly, so the bf16 result is the exact sum; an empty expert keeps its bits."""
+    inp = W.wgrad_inputs(E=3, M=16, N=24, tokens=[40, 0, 700], integer=True, seed=2)
+    mg0 = narrow_bf16(np.random.default_rng(4).integers(-8, 9, size=(3, 16, 24)).astype(np.float32))
+    for C in (0, 1):
+        got = ow.grouped_wgrad_acc_bf16(mg0, inp.G, inp.X, inp.offs, ktiles_per_split=C)
+        Gf, Xf = widen_bf16(inp.G).astype(np.float64), widen_bf16(inp.X).astype(np.float64)
+        o = inp.offs
+        for e in range(3):
+            exact = widen_bf16(mg0[e]).astype(np.float64) + Gf[o[e]:o[e + 1]].T @ Xf[o[e]:o[e + 1]]
+            assert np.all(np.abs(exact) <= 256)
+            if o[e + 1] == o[e]:
+                assert np.array_equal(got[e], mg0[e])
+            else:
+                assert np.array_equal(widen_bf16(got[e]).astype(np.float64), exact)
