@@ -26,9 +26,10 @@ import threading
 
 __all__ = [
     "lib", "library_path", "DetError", "ColsumCfg", "IndexAddCfg", "DprobCfg", "WgradCfg", "Workspace",
-    "det_abi_version", "det_colsum", "det_colsum_select_cfg", "det_colsum_workspace_size", "det_index_add",
+    "det_abi_version", "det_colsum", "det_colsum_da", "det_colsum_select_cfg", "det_colsum_workspace_size", "det_index_add",
     "det_index_add_workspace_size", "det_index_add_bad_ids", "det_grouped_dprob", "det_grouped_dprob_workspace_size",
-    "det_grouped_wgrad_acc", "det_grouped_wgrad_acc_workspace_size", "det_grouped_dbias",
+    "det_grouped_wgrad_acc", "det_grouped_wgrad_acc_workspace_size", "det_grouped_wgrad_acc_bf16",
+    "det_grouped_wgrad_acc_bf16_workspace_size", "det_grouped_dbias",
     "det_grouped_dbias_workspace_size", "det_topk_canonicalize", "det_workspace_init", "det_detmath_eval",
     "DET_OK", "DET_ERR_INVALID_ARG", "DET_ERR_UNSUPPORTED", "DET_ERR_WORKSPACE", "DET_ERR_OVERLAP", "DET_ERR_HIP",
 ]
@@ -81,6 +82,8 @@ _SIGS = {
     "det_colsum_workspace_size": ([_I64, _I64, ctypes.POINTER(ColsumCfg), _INT, ctypes.POINTER(_SZ)], _INT),
     "det_colsum": ([_P, _I64, _I64, _P, _I64, _I64, _INT, _P, _P, _I64, _I64, _P, _P, ctypes.POINTER(ColsumCfg),
                     _P, _SZ, _INT, _P], _INT),
+    "det_colsum_da": ([_P, _I64, _I64, _P, _I64, _I64, _INT, _P, _P, _I64, _I64, _P, _P, _P, _I64, _I64,
+                       ctypes.POINTER(ColsumCfg), _P, _SZ, _INT, _P], _INT),
     "det_index_add_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(IndexAddCfg), _INT, ctypes.POINTER(_SZ)], _INT),
     "det_index_add": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _INT, ctypes.POINTER(IndexAddCfg), _P, _SZ, _INT,
                        _P], _INT),
@@ -98,6 +101,10 @@ _SIGS = {
                           _INT),
     "det_grouped_wgrad_acc": ([_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I32, _I64, _I64, _I64,
                                ctypes.POINTER(WgradCfg), _P, _SZ, _INT, _P], _INT),
+    "det_grouped_wgrad_acc_bf16_workspace_size": ([_I64, _I32, _I64, _I64, ctypes.POINTER(WgradCfg),
+                                                   ctypes.POINTER(_SZ)], _INT),
+    "det_grouped_wgrad_acc_bf16": ([_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I32, _I64, _I64, _I64,
+                                    ctypes.POINTER(WgradCfg), _P, _SZ, _P], _INT),
 }
 
 _lib = None
@@ -216,14 +223,27 @@ def det_colsum_workspace_size(T: int, H: int, cfg: ColsumCfg | None = None, atom
 
 
 def det_colsum(a, dg, A_log, dt_bias, dA_log, ddt_bias, cfg: ColsumCfg | None = None, atomic=False, ws=None,
-               stream=None) -> None:
-    """dA_log[h] += sum_t dg*g, ddt_bias[h] += sum_t dg*(-exp(A_log))*sigmoid(a+dt_bias). a, dg: [T, H]."""
+               stream=None, da=None) -> None:
+    """dA_log[h] += sum_t dg*g, ddt_bias[h] += sum_t dg*(-exp(A_log))*sigmoid(a+dt_bias). a, dg: [T, H].
+    With ``da`` ([T, H], the dtype of ``a``), also da = dg*(-exp(A_log))*sigmoid(a+dt_bias) per element
+    (det_colsum_da)."""
     T, H = a.shape
     need = det_colsum_workspace_size(T, H, cfg, atomic) if atomic in (0, 1, False, True) else 0
     wp, wn = _workspace(need, ws, stream)
-    _check(lib().det_colsum(_ptr(a), a.stride(0), a.stride(1), _ptr(dg), dg.stride(0), dg.stride(1), _dtype_code(a),
-                            _ptr(A_log), _ptr(dt_bias), T, H, _ptr(dA_log), _ptr(ddt_bias),
-                            ctypes.byref(cfg) if cfg else None, wp, wn, _atomic_flag(atomic), _stream_handle(stream)))
+    head = (_ptr(a), a.stride(0), a.stride(1), _ptr(dg), dg.stride(0), dg.stride(1), _dtype_code(a),
+            _ptr(A_log), _ptr(dt_bias), T, H, _ptr(dA_log), _ptr(ddt_bias))
+    tail = (ctypes.byref(cfg) if cfg else None, wp, wn, _atomic_flag(atomic), _stream_handle(stream))
+    if da is None:
+        _check(lib().det_colsum(*head, *tail))
+        return
+    if da.dtype != a.dtype or tuple(da.shape) != (T, H):
+        raise ValueError("da must have the shape and dtype of a")
+    _check(lib().det_colsum_da(*head, _ptr(da), da.stride(0), da.stride(1), *tail))
+
+
+def det_colsum_da(a, dg, A_log, dt_bias, dA_log, ddt_bias, da, **kw) -> None:
+    """det_colsum plus the elementwise da [T, H] (dtype of ``a``), overwritten."""
+    det_colsum(a, dg, A_log, dt_bias, dA_log, ddt_bias, da=da, **kw)
 
 
 # ------------------------------------------------------------------ index_add
@@ -330,6 +350,29 @@ def det_grouped_wgrad_acc(main_grad, G, X, offs, cfg: WgradCfg | None = None, at
                                        _ptr(X), X.stride(0), _ptr(offs), E, T_total, M, N,
                                        ctypes.byref(cfg) if cfg else None, wp, wn, _atomic_flag(atomic),
                                        _stream_handle(stream)))
+
+
+def det_grouped_wgrad_acc_bf16_workspace_size(T_total: int, E: int, M: int, N: int,
+                                              cfg: WgradCfg | None = None) -> int:
+    n = _SZ()
+    _check(lib().det_grouped_wgrad_acc_bf16_workspace_size(T_total, E, M, N, ctypes.byref(cfg) if cfg else None,
+                                                           ctypes.byref(n)))
+    return n.value
+
+
+def det_grouped_wgrad_acc_bf16(main_grad, G, X, offs, cfg: WgradCfg | None = None, ws=None, stream=None) -> None:
+    """bf16 main_grad [E, M, N]: main_grad[e] <- bf16(main_grad[e] + bf16(G_e^T X_e)), deterministic only."""
+    import torch
+    if main_grad.dtype != torch.bfloat16:
+        raise TypeError("main_grad must be bfloat16")
+    E, M, N = main_grad.shape
+    T_total = G.shape[0]
+    if G.stride(1) != 1 or X.stride(1) != 1 or main_grad.stride(2) != 1:
+        raise ValueError("G, X and main_grad must have unit innermost stride")
+    wp, wn = _workspace(det_grouped_wgrad_acc_bf16_workspace_size(T_total, E, M, N, cfg), ws, stream)
+    _check(lib().det_grouped_wgrad_acc_bf16(_ptr(main_grad), main_grad.stride(0), main_grad.stride(1), _ptr(G),
+                                            G.stride(0), _ptr(X), X.stride(0), _ptr(offs), E, T_total, M, N,
+                                            ctypes.byref(cfg) if cfg else None, wp, wn, _stream_handle(stream)))
 
 
 # ---------------------------------------------------------------- diagnostics

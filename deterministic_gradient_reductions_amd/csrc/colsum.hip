@@ -37,6 +37,8 @@ struct ColsumArgs {
   float* ddt_bias;
   float* slot1;      // [S][H]
   float* slot2;      // [S][H]
+  void* da;          // [T, H] in the input type, or NULL
+  int64_t da_st, da_sh;
 };
 
 // Adjacent pairwise tree over v[0..n-1] in place (n a power of two <= 32).
@@ -53,6 +55,15 @@ __device__ __forceinline__ float tree_regs(float (&v)[N]) {
 // Gate inputs: bf16 (widened exactly) or float32.
 __device__ __forceinline__ float gate_in(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 __device__ __forceinline__ float gate_in(const float* p, int64_t i) { return p[i]; }
+
+// The elementwise da, stored in the input type: bf16 by round to nearest even
+// on the bit pattern (NaN kept quiet), float32 as is.
+__device__ __forceinline__ void gate_out(uint16_t* p, int64_t i, float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t r = (u & 0x7FFFFFFFu) > 0x7F800000u ? (u >> 16) | 0x40u : (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  p[i] = static_cast<uint16_t>(r);
+}
+__device__ __forceinline__ void gate_out(float* p, int64_t i, float v) { p[i] = v; }
 
 template <int R, int BH, bool ATOMIC, typename TIn>
 __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
@@ -85,6 +96,7 @@ __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
         const float sg = dm::sigmoid_e(x, e);
         v1[i] = d * (nA * sp);
         v2[i] = d * (nA * sg);
+        if (p.da) gate_out(static_cast<TIn*>(p.da), t * p.da_st + h * p.da_sh, v2[i]);  // da = the ddt_bias term
       } else {
         v1[i] = -0.0f;
         v2[i] = -0.0f;
@@ -254,10 +266,11 @@ extern "C" int det_colsum_workspace_size(int64_t T, int64_t H, const det_colsum_
   return ok();
 }
 
-extern "C" int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_t dg_st, int64_t dg_sh,
-                          int in_dtype, const float* A_log, const float* dt_bias, int64_t T, int64_t H, float* dA_log,
-                          float* ddt_bias, const det_colsum_cfg* cfg, void* ws, size_t ws_bytes, int atomic,
-                          void* stream) {
+namespace {
+int colsum_entry(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_t dg_st, int64_t dg_sh, int in_dtype,
+                 const float* A_log, const float* dt_bias, int64_t T, int64_t H, float* dA_log, float* ddt_bias,
+                 void* da, int64_t da_st, int64_t da_sh, bool with_da, const det_colsum_cfg* cfg, void* ws,
+                 size_t ws_bytes, int atomic, void* stream) {
   if (int s = check_atomic_flag(atomic)) return s;
   if (T < 0 || H < 0) return set_error(DET_ERR_INVALID_ARG, "colsum: T and H must be >= 0");
   if (in_dtype != DET_BF16 && in_dtype != DET_F32)
@@ -265,7 +278,7 @@ extern "C" int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void*
   det_colsum_cfg c;
   if (int s = resolve_cfg(T, H, cfg, &c)) return s;
   if (T == 0 || H == 0) return ok();
-  if (!a || !dg || !A_log || !dt_bias || !dA_log || !ddt_bias)
+  if (!a || !dg || !A_log || !dt_bias || !dA_log || !ddt_bias || (with_da && !da))
     return set_error(DET_ERR_INVALID_ARG, "colsum: NULL pointer");
   if (a_st < 1 || a_sh < 1 || dg_st < 1 || dg_sh < 1)
     return set_error(DET_ERR_INVALID_ARG, "colsum: element strides must be >= 1");
@@ -281,6 +294,17 @@ extern "C" int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void*
   for (const Range& r : ins)
     if (overlaps(o1, r) || overlaps(o2, r))
       return set_error(DET_ERR_OVERLAP, "colsum: an output overlaps an input or the workspace");
+  if (with_da) {
+    if (da_st < 1 || da_sh < 1) return set_error(DET_ERR_INVALID_ARG, "colsum: da strides must be >= 1");
+    // one of the two strides must step over the whole extent of the other, so
+    // that no two elements of da share an address
+    if (!(da_st >= H * da_sh || da_sh >= T * da_st))
+      return set_error(DET_ERR_INVALID_ARG, "colsum: da strides map two elements to one address");
+    const Range od = range_strided(da, T, H, da_st, da_sh, esz);
+    if (overlaps(od, o1) || overlaps(od, o2)) return set_error(DET_ERR_OVERLAP, "colsum: da overlaps another output");
+    for (const Range& r : ins)
+      if (overlaps(od, r)) return set_error(DET_ERR_OVERLAP, "colsum: da overlaps an input or the workspace");
+  }
   ColsumArgs p;
   p.a = a;
   p.a_st = a_st;
@@ -298,6 +322,26 @@ extern "C" int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void*
   const size_t slot_bytes = align_up(static_cast<size_t>(ceil_div(T, c.block_t) * H) * 4, 256);
   p.slot1 = atomic ? nullptr : reinterpret_cast<float*>(w + DET_WS_HEADER_BYTES);
   p.slot2 = atomic ? nullptr : reinterpret_cast<float*>(w + DET_WS_HEADER_BYTES + slot_bytes);
+  p.da = with_da ? da : nullptr;
+  p.da_st = da_st;
+  p.da_sh = da_sh;
   launch(p, c, atomic, in_dtype == DET_F32, as_stream(stream));
-  return check_launch("det_colsum");
+  return check_launch(with_da ? "det_colsum_da" : "det_colsum");
+}
+}  // namespace
+
+extern "C" int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_t dg_st, int64_t dg_sh,
+                          int in_dtype, const float* A_log, const float* dt_bias, int64_t T, int64_t H, float* dA_log,
+                          float* ddt_bias, const det_colsum_cfg* cfg, void* ws, size_t ws_bytes, int atomic,
+                          void* stream) {
+  return colsum_entry(a, a_st, a_sh, dg, dg_st, dg_sh, in_dtype, A_log, dt_bias, T, H, dA_log, ddt_bias, nullptr, 1, 1,
+                      false, cfg, ws, ws_bytes, atomic, stream);
+}
+
+extern "C" int det_colsum_da(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_t dg_st, int64_t dg_sh,
+                             int in_dtype, const float* A_log, const float* dt_bias, int64_t T, int64_t H,
+                             float* dA_log, float* ddt_bias, void* da, int64_t da_st, int64_t da_sh,
+                             const det_colsum_cfg* cfg, void* ws, size_t ws_bytes, int atomic, void* stream) {
+  return colsum_entry(a, a_st, a_sh, dg, dg_st, dg_sh, in_dtype, A_log, dt_bias, T, H, dA_log, ddt_bias, da, da_st,
+                      da_sh, true, cfg, ws, ws_bytes, atomic, stream);
 }

@@ -94,6 +94,7 @@ struct WgradArgs {
   int64_t n_units;
   float* scratch;   // [max_splits][M][N]
   int64_t max_splits;
+  uint16_t* mg16;   // bf16 main_grad (the route where every split's partial goes to scratch)
 };
 
 // One split of one expert. Expert boundaries come from device offsets and are
@@ -332,7 +333,9 @@ __host__ void plan_xcds(WgradArgs& p, int block_m, int block_n) {
 //   block 2s+1:  MFMAs, then X block 2s+7 into the freed slot
 // The LDS stage written at stage s was last read at stage s-3, before two
 // barriers, and every LDS read of a stage follows the barrier after its write.
-template <int W, bool ATOMIC>
+// ALLS: every split's partial goes to scratch, also a lone split (the bf16
+// main_grad route); a template flag, so the other instances are unchanged.
+template <int W, bool ATOMIC, bool ALLS = false>
 __global__ __launch_bounds__(64 * W) void wgrad_kernel(WgradArgs p) {
   __shared__ __attribute__((aligned(16))) StageA la[kAStages];
   int64_t uq;
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(64 * W) void wgrad_kernel(WgradArgs p) {
 
   // Epilogue: lane (r, kg), MFMA (i, j), accumulator q holds output
   // m = m0 + 4 * (8*(q/4) + 4*kg + q%4) + i,  n = n0 + 128*wave + 4*r + j.
-  const bool direct = sp.n_split == 1;
+  const bool direct = sp.n_split == 1 && !ALLS;
   float* dst_base;
   int64_t ld_m;
   if (ATOMIC || direct) {
@@ -604,7 +607,7 @@ __device__ __forceinline__ void t_sync() {
   __builtin_amdgcn_s_barrier();
 }
 
-template <bool ATOMIC>
+template <bool ATOMIC, bool ALLS = false>
 __global__ __launch_bounds__(256) void wgrad_tl_kernel(WgradArgs p) {
   // [stage buffer 2][operand 2]: A (G) of buffer b at 2b, B (X) at 2b + 1
   __shared__ __attribute__((aligned(16))) TStage lds[4];
@@ -745,7 +748,7 @@ __global__ __launch_bounds__(256) void wgrad_tl_kernel(WgradArgs p) {
   const int mw = m0 + 128 * wm, nw = n0 + 128 * wn;
   if (ATOMIC) {
     t_epilogue<2>(p.mg + sp.e * p.ld_e, p.ld_m, mw, nw, r, kg, acc);
-  } else if (sp.n_split == 1) {
+  } else if (sp.n_split == 1 && !ALLS) {
     t_epilogue<0>(p.mg + sp.e * p.ld_e, p.ld_m, mw, nw, r, kg, acc);
   } else {
     t_epilogue<1>(p.scratch + sp.g * static_cast<int64_t>(p.M) * p.N, p.N, mw, nw, r, kg, acc);
@@ -784,6 +787,50 @@ __global__ __launch_bounds__(256) void wgrad_fold_kernel(WgradArgs p) {
   *reinterpret_cast<float4*>(d) = o;
 }
 
+// bf16 main_grad: dW = ((Q0 + Q1) + ...) in float32, rounded to bf16 (nearest
+// even), added to main_grad in float32 and the sum rounded to bf16: the bf16
+// tensor add of the bf16 dW. Experts with no rows are left untouched.
+__device__ __forceinline__ uint32_t rne_bf16(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? ((u >> 16) | 0x40u) & 0xFFFFu : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ uint32_t add_bf16(uint32_t m, float dw) {
+  const float d16 = __uint_as_float(rne_bf16(dw) << 16);
+  return rne_bf16(__uint_as_float(m << 16) + d16);
+}
+
+__global__ __launch_bounds__(256) void wgrad_fold_bf16_kernel(WgradArgs p) {
+  const int64_t per_e = static_cast<int64_t>(p.M) * p.N / 4;  // 4 values per thread
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int e = static_cast<int>(blockIdx.y);
+  if (idx >= per_e) return;
+  int64_t prev = p.offs[0];
+  prev = prev < 0 ? 0 : (prev > p.T_total ? p.T_total : prev);
+  int64_t g0 = 0, se = 0;
+  for (int x = 0; x <= e; ++x) {
+    int64_t nb = p.offs[x + 1];
+    nb = nb < prev ? prev : (nb > p.T_total ? p.T_total : nb);
+    const int64_t te = nb - prev;
+    const int64_t s = te == 0 ? 0 : (p.split_rows == 0 ? 1 : (te + p.split_rows - 1) / p.split_rows);
+    if (x < e) g0 += s; else se = s;
+    prev = nb;
+  }
+  if (se == 0) return;
+  const int64_t m = (idx * 4) / p.N;
+  const int64_t n = (idx * 4) % p.N;
+  float4 tot = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
+  for (int64_t s = 0; s < se; ++s) {
+    const float4 q = *reinterpret_cast<const float4*>(p.scratch + (g0 + s) * static_cast<int64_t>(p.M) * p.N + m * p.N + n);
+    tot.x = tot.x + q.x; tot.y = tot.y + q.y; tot.z = tot.z + q.z; tot.w = tot.w + q.w;
+  }
+  uint2* const d = reinterpret_cast<uint2*>(p.mg16 + e * p.ld_e + m * p.ld_m + n);
+  const uint2 o = *d;
+  uint2 r;
+  r.x = add_bf16(o.x & 0xFFFFu, tot.x) | add_bf16(o.x >> 16, tot.y) << 16;
+  r.y = add_bf16(o.y & 0xFFFFu, tot.z) | add_bf16(o.y >> 16, tot.w) << 16;
+  *d = r;
+}
+
 int resolve(const det_wgrad_cfg* cfg, det_wgrad_cfg* out) {
   det_wgrad_cfg c{kTT, kTT, kKTile, 0};
   if (cfg) c = *cfg;
@@ -820,6 +867,12 @@ size_t scratch_bytes(int64_t T_total, int32_t E, int64_t M, int64_t N, const det
   return static_cast<size_t>(max_splits(T_total, E, c)) * static_cast<size_t>(M * N) * 4;
 }
 
+// Every split's partial in scratch (the bf16 main_grad route), also with one split per expert.
+size_t scratch_bytes_all(int64_t T_total, int32_t E, int64_t M, int64_t N, const det_wgrad_cfg& c) {
+  if (T_total == 0 || E == 0 || M == 0 || N == 0) return 0;
+  return static_cast<size_t>(max_splits(T_total, E, c)) * static_cast<size_t>(M * N) * 4;
+}
+
 }  // namespace
 }  // namespace detgrad
 
@@ -837,11 +890,14 @@ extern "C" int det_grouped_wgrad_acc_workspace_size(int64_t T_total, int32_t E, 
   return ok();
 }
 
-extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_m, const void* G, int64_t ldg,
-                                     const void* X, int64_t ldx, const int32_t* offs, int32_t E, int64_t T_total,
-                                     int64_t M, int64_t N, const det_wgrad_cfg* cfg, void* ws, size_t ws_bytes,
-                                     int atomic, void* stream) {
+namespace {
+// bf16: main_grad holds bf16 values; every split's partial goes to scratch and
+// wgrad_fold_bf16_kernel adds the folded dW in bf16 (deterministic arm only).
+int wgrad_entry(void* main_grad, bool bf16, int64_t ld_e, int64_t ld_m, const void* G, int64_t ldg, const void* X,
+                int64_t ldx, const int32_t* offs, int32_t E, int64_t T_total, int64_t M, int64_t N,
+                const det_wgrad_cfg* cfg, void* ws, size_t ws_bytes, int atomic, void* stream) {
   if (int s = check_atomic_flag(atomic)) return s;
+  if (bf16 && atomic) return set_error(DET_ERR_UNSUPPORTED, "wgrad: a bf16 main_grad has no atomic arm");
   det_wgrad_cfg c;
   if (int s = resolve(cfg, &c)) return s;
   if (int s = check_shape(T_total, E, M, N, c)) return s;
@@ -850,23 +906,25 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
   if (ld_m < N || ld_e < M * ld_m)
     return set_error(DET_ERR_INVALID_ARG, "wgrad: need ld_m >= N and ld_e >= M*ld_m (an expanded main_grad is rejected)");
   if (ldg < M || ldx < N) return set_error(DET_ERR_INVALID_ARG, "wgrad: need ldg >= M and ldx >= N");
-  if (ldg % 8 || ldx % 8 || !aligned(G, 16) || !aligned(X, 16) || ld_m % 4 || ld_e % 4 || !aligned(main_grad, 16))
-    return set_error(DET_ERR_UNSUPPORTED, "wgrad: rows of G, X and main_grad must be 16-byte aligned");
+  if (ldg % 8 || ldx % 8 || !aligned(G, 16) || !aligned(X, 16) || ld_m % 4 || ld_e % 4 ||
+      !aligned(main_grad, bf16 ? 8 : 16))
+    return set_error(DET_ERR_UNSUPPORTED, "wgrad: rows of G, X and main_grad must be 16-byte (bf16 main_grad: 8-byte) aligned");
   // buffer loads use 32-bit byte offsets inside one split, including the rows
   // read ahead past its end (fewer than 512)
   if ((T_total + 512) * (ldg > ldx ? ldg : ldx) * 2 >= (1LL << 31))
     return set_error(DET_ERR_UNSUPPORTED, "wgrad: T_total x max(ldg, ldx) too large for 32-bit offsets");
-  const size_t sb = scratch_bytes(T_total, E, M, N, c);
+  const size_t sb = bf16 ? scratch_bytes_all(T_total, E, M, N, c) : scratch_bytes(T_total, E, M, N, c);
   const size_t need = (atomic || sb == 0) ? 0 : DET_WS_HEADER_BYTES + align_up(sb, 256);
   if (int s = check_workspace(ws, ws_bytes, need)) return s;
   Range out_full;
   out_full.lo = reinterpret_cast<uintptr_t>(main_grad);
-  out_full.hi = out_full.lo + static_cast<uintptr_t>(((E - 1) * ld_e + (M - 1) * ld_m + N) * 4);
+  out_full.hi = out_full.lo + static_cast<uintptr_t>(((E - 1) * ld_e + (M - 1) * ld_m + N) * (bf16 ? 2 : 4));
   if (overlaps(out_full, range2d(G, T_total, M, ldg, 2)) || overlaps(out_full, range2d(X, T_total, N, ldx, 2)) ||
       overlaps(out_full, range1d(offs, (static_cast<size_t>(E) + 1) * 4)) || overlaps(out_full, range1d(ws, ws_bytes)))
     return set_error(DET_ERR_OVERLAP, "wgrad: main_grad overlaps an input or the workspace");
   WgradArgs p;
-  p.mg = main_grad;
+  p.mg = bf16 ? nullptr : static_cast<float*>(main_grad);
+  p.mg16 = bf16 ? static_cast<uint16_t*>(main_grad) : nullptr;
   p.ld_e = ld_e;
   p.ld_m = ld_m;
   p.G = static_cast<const uint16_t*>(G);
@@ -891,24 +949,53 @@ extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_
     if (atomic)
       hipLaunchKernelGGL((wgrad_tl_kernel<true>), grid, dim3(256), 0, st, p);
     else
-      hipLaunchKernelGGL((wgrad_tl_kernel<false>), grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL((bf16 ? wgrad_tl_kernel<false, true> : wgrad_tl_kernel<false>), grid, dim3(256), 0, st, p);
   } else if (c.block_n == 512) {
     if (atomic)
       hipLaunchKernelGGL((wgrad_kernel<4, true>), grid, dim3(256), 0, st, p);
     else
-      hipLaunchKernelGGL((wgrad_kernel<4, false>), grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL((bf16 ? wgrad_kernel<4, false, true> : wgrad_kernel<4, false>), grid, dim3(256), 0, st, p);
   } else {
     if (atomic)
       hipLaunchKernelGGL((wgrad_kernel<2, true>), grid, dim3(128), 0, st, p);
     else
-      hipLaunchKernelGGL((wgrad_kernel<2, false>), grid, dim3(128), 0, st, p);
+      hipLaunchKernelGGL((bf16 ? wgrad_kernel<2, false, true> : wgrad_kernel<2, false>), grid, dim3(128), 0, st, p);
   }
   if (!atomic) {
-    if (p.split_rows != 0) {
-      const int64_t per_e = M * N / 4;
-      hipLaunchKernelGGL(wgrad_fold_kernel, dim3(static_cast<uint32_t>(ceil_div(per_e, 256)), static_cast<uint32_t>(E)),
-                         dim3(256), 0, st, p);
-    }
+    const int64_t per_e = M * N / 4;
+    const dim3 fgrid(static_cast<uint32_t>(ceil_div(per_e, 256)), static_cast<uint32_t>(E));
+    if (bf16)
+      hipLaunchKernelGGL(wgrad_fold_bf16_kernel, fgrid, dim3(256), 0, st, p);
+    else if (p.split_rows != 0)
+      hipLaunchKernelGGL(wgrad_fold_kernel, fgrid, dim3(256), 0, st, p);
   }
-  return check_launch("det_grouped_wgrad_acc");
+  return check_launch(bf16 ? "det_grouped_wgrad_acc_bf16" : "det_grouped_wgrad_acc");
+}
+}  // namespace
+
+extern "C" int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_m, const void* G, int64_t ldg,
+                                     const void* X, int64_t ldx, const int32_t* offs, int32_t E, int64_t T_total,
+                                     int64_t M, int64_t N, const det_wgrad_cfg* cfg, void* ws, size_t ws_bytes,
+                                     int atomic, void* stream) {
+  return wgrad_entry(main_grad, false, ld_e, ld_m, G, ldg, X, ldx, offs, E, T_total, M, N, cfg, ws, ws_bytes, atomic,
+                     stream);
+}
+
+extern "C" int det_grouped_wgrad_acc_bf16_workspace_size(int64_t T_total, int32_t E, int64_t M, int64_t N,
+                                                         const det_wgrad_cfg* cfg, size_t* bytes) {
+  if (!bytes) return set_error(DET_ERR_INVALID_ARG, "wgrad: bytes is NULL");
+  det_wgrad_cfg c;
+  if (int s = resolve(cfg, &c)) return s;
+  if (int s = check_shape(T_total, E, M, N, c)) return s;
+  const size_t sb = scratch_bytes_all(T_total, E, M, N, c);
+  *bytes = sb == 0 ? 0 : DET_WS_HEADER_BYTES + align_up(sb, 256);
+  return ok();
+}
+
+extern "C" int det_grouped_wgrad_acc_bf16(uint16_t* main_grad, int64_t ld_e, int64_t ld_m, const void* G, int64_t ldg,
+                                          const void* X, int64_t ldx, const int32_t* offs, int32_t E, int64_t T_total,
+                                          int64_t M, int64_t N, const det_wgrad_cfg* cfg, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  return wgrad_entry(main_grad, true, ld_e, ld_m, G, ldg, X, ldx, offs, E, T_total, M, N, cfg, ws, ws_bytes, 0,
+                     stream);
 }

@@ -114,6 +114,26 @@ int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_
                int in_dtype, const float* A_log, const float* dt_bias, int64_t T, int64_t H, float* dA_log,
                float* ddt_bias, const det_colsum_cfg* cfg, void* ws, size_t ws_bytes, int atomic, void* stream);
 
+/* det_colsum_da: det_colsum that also writes the elementwise gradient of the
+ * gate input (the same x depends on a and on dt_bias, so the term summed into
+ * ddt_bias is da itself):
+ *
+ *   da[t,h] = dg[t,h] * (-exp(A_log[h])) * sigmoid(x)   (overwritten, not accumulated)
+ *
+ * computed in float32 exactly as the ddt_bias term and stored in in_dtype:
+ * bf16 by round to nearest even (NaN stays NaN), float32 unchanged. The GDN
+ * gate page names only the two parameter gradients; the elementwise output is
+ * the gate-variants extension of the same kernel. dA_log and ddt_bias are
+ * bitwise those of det_colsum, on both arms.
+ * da: [T, H] with element strides (da_st, da_sh) >= 1 such that no two
+ *     elements share an address (da_st >= H*da_sh or da_sh >= T*da_st); it
+ *     must not overlap a, dg, A_log, dt_bias, dA_log, ddt_bias or ws.
+ * Other arguments, errors and the workspace as for det_colsum. */
+int det_colsum_da(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_t dg_st, int64_t dg_sh,
+                  int in_dtype, const float* A_log, const float* dt_bias, int64_t T, int64_t H, float* dA_log,
+                  float* ddt_bias, void* da, int64_t da_st, int64_t da_sh, const det_colsum_cfg* cfg, void* ws,
+                  size_t ws_bytes, int atomic, void* stream);
+
 /* ------------------------------------------------------------------------
  * det_index_add: out[ids[p]] += src[p] without float atomics.
  * Megatron-LM PR #7441 (DSv4 deterministic mode), source 3: the sparse-
@@ -266,6 +286,29 @@ int det_grouped_wgrad_acc_workspace_size(int64_t T_total, int32_t E, int64_t M, 
 int det_grouped_wgrad_acc(float* main_grad, int64_t ld_e, int64_t ld_m, const void* G, int64_t ldg, const void* X,
                           int64_t ldx, const int32_t* offs, int32_t E, int64_t T_total, int64_t M, int64_t N,
                           const det_wgrad_cfg* cfg, void* ws, size_t ws_bytes, int atomic, void* stream);
+
+/* det_grouped_wgrad_acc_bf16: the same grouped weight gradient accumulated
+ * into a bf16 main_grad. FlashInfer PR #8924, "Design and numerics": for a
+ * bf16 output the bf16 dW is added in bf16, bitwise the AccumulateGrad of the
+ * deterministic dW. Here dW[e] is the float32 fold of the expert's split
+ * partials exactly as in det_grouped_wgrad_acc; then, per element,
+ *
+ *   main_grad <- RN_bf16( RN32( main_grad + RN_bf16(dW) ) )
+ *
+ * (RN_bf16: round to nearest even, NaN kept). Experts with no rows keep their
+ * bits. Every split's partial goes to the workspace (also with
+ * ktiles_per_split = 0, one split per expert) and one fold kernel adds.
+ * main_grad: [E, M, N] bf16 bits, strides (ld_e, ld_m, 1) in elements, both
+ * multiples of 4, 8-byte aligned. No atomic arm. Other arguments and errors
+ * as for det_grouped_wgrad_acc.
+ * ws: det_grouped_wgrad_acc_bf16_workspace_size() bytes (max_splits x M x N
+ *     float32: E x M x N with one split per expert). */
+int det_grouped_wgrad_acc_bf16_workspace_size(int64_t T_total, int32_t E, int64_t M, int64_t N,
+                                              const det_wgrad_cfg* cfg, size_t* bytes);
+int det_grouped_wgrad_acc_bf16(uint16_t* main_grad, int64_t ld_e, int64_t ld_m, const void* G, int64_t ldg,
+                               const void* X, int64_t ldx, const int32_t* offs, int32_t E, int64_t T_total,
+                               int64_t M, int64_t N, const det_wgrad_cfg* cfg, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* ------------------------------------------------------------------------
  * det_topk_canonicalize: canonical order of a compact indexer top-k.

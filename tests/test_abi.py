@@ -250,3 +250,34 @@ def test_wgrad_validation():
     # empty problems are OK and touch nothing
     assert L.det_grouped_wgrad_acc(None, 0, 0, None, 0, None, 0, None, 0, 0, 128, 512, None, None, 0, 0, None) == \
         dg.DET_OK
+
+
+def test_colsum_da_validation():
+    """det_colsum_da rejects a missing da, bad strides, strides that send two
+    elements to one address, and overlaps (no case reaches a launch)."""
+    L = lib()
+    o1, o2 = P(0x900000), P(0x900100)
+
+    def call(da, st, sh, T=16, H=16):
+        return L.det_colsum_da(FAKE, 16, 1, FAKE, 16, 1, 0, FAKE, FAKE, T, H, o1, o2, da, st, sh, None, None, 0, 1,
+                               None)
+    assert call(None, 16, 1) == dg.DET_ERR_INVALID_ARG
+    assert call(P(0xA00000), 0, 1) == dg.DET_ERR_INVALID_ARG
+    assert call(P(0xA00000), 1, 1) == dg.DET_ERR_INVALID_ARG and "address" in err()
+    assert call(P(0xA00000), 8, 1) == dg.DET_ERR_INVALID_ARG   # rows of 16 heads 8 elements apart
+    assert call(FAKE, 16, 1) == dg.DET_ERR_OVERLAP              # da over a
+    assert call(P(0x900000 - 64), 16, 1) == dg.DET_ERR_OVERLAP  # da over dA_log
+
+
+def test_wgrad_bf16_validation_and_workspace():
+    L = lib()
+    n = dg.det_grouped_wgrad_acc_bf16_workspace_size(38346, 8, 1408, 2048)
+    assert n >= 8 * 1408 * 2048 * 4  # every expert's partial, also with one split per expert
+    assert dg.det_grouped_wgrad_acc_bf16_workspace_size(0, 8, 1408, 2048) == 0
+    # missing workspace, misaligned main_grad, bad shape (no case reaches a launch)
+    assert L.det_grouped_wgrad_acc_bf16(P(0x900000), 512 * 256, 512, FAKE, 256, FAKE, 512, FAKE, 2, 1000, 256, 512,
+                                        None, None, 0, None) == dg.DET_ERR_WORKSPACE
+    assert L.det_grouped_wgrad_acc_bf16(P(0x900002), 512 * 256, 512, FAKE, 256, FAKE, 512, FAKE, 2, 1000, 256, 512,
+                                        None, None, 0, None) == dg.DET_ERR_UNSUPPORTED
+    assert L.det_grouped_wgrad_acc_bf16(P(0x900000), 512 * 256, 512, FAKE, 256, FAKE, 512, FAKE, 2, 1000, 200, 512,
+                                        None, None, 0, None) == dg.DET_ERR_UNSUPPORTED

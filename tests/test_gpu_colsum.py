@@ -165,3 +165,45 @@ def test_f32_inputs_transposed_and_atomic_arm():
     assert_bitwise(r1, w1, "dA_log f32 T"); assert_bitwise(r2, w2, "ddt_bias f32 T")
     a1, a2 = run(inp, cfg=dg.ColsumCfg(128, 16), atomic=True)
     assert rel_l2(a1 - inp.dA_log0, w1 - inp.dA_log0) <= 1e-5 and rel_l2(a2 - inp.ddt_bias0, w2 - inp.ddt_bias0) <= 1e-5
+
+
+def run_da(inp, cfg=None, atomic=False, da_layout="rows"):
+    """det_colsum_da: returns (dA_log, ddt_bias, da) with da as stored (bf16 bits or float32)."""
+    import torch
+    T, H = inp.a.shape
+    f32 = inp.a.dtype == np.float32
+    dev_in = dev_f32 if f32 else dev_bf16
+    a = dev_in(inp.a)
+    d = dev_in(inp.dg_base)[:, H:]
+    o1, o2 = dev_f32(inp.dA_log0), dev_f32(inp.ddt_bias0)
+    dt = torch.float32 if f32 else torch.bfloat16
+    if da_layout == "rows":
+        da = torch.full((T, H), float("nan"), dtype=dt, device="cuda")
+    elif da_layout == "cols":  # column-major: a transposed view
+        da = torch.full((H, T), float("nan"), dtype=dt, device="cuda").t()
+    else:  # a column slice of a wider tensor
+        da = torch.full((T, 3 * H), float("nan"), dtype=dt, device="cuda")[:, H:2 * H]
+    torch.cuda.synchronize()
+    dg.det_colsum_da(a, d, dev_f32(inp.A_log), dev_f32(inp.dt_bias), o1, o2, da, cfg=cfg, atomic=atomic)
+    out = da.contiguous().cpu()
+    out = out.numpy() if f32 else out.view(torch.int16).numpy().view(np.uint16)
+    return host(o1), host(o2), out
+
+
+@pytest.mark.parametrize("dtype,T,H,layout", [("bf16", 16384, 32, "rows"), ("bf16", 1000, 12, "cols"),
+                                              ("f32", 4096, 16, "slice"), ("f32", 333, 5, "rows")])
+def test_da_output(dtype, T, H, layout):
+    """da bitwise against the oracle (bf16 round to nearest even, or float32),
+    and dA_log / ddt_bias bitwise those of det_colsum, on both arms."""
+    note("colsum_da %s T=%d H=%d %s" % (dtype, T, H, layout))
+    inp = W.gate_inputs(T=T, H=H, seed=T + H, out_init="normal", dtype=dtype)
+    want_da = oc.gate_da(inp.a, inp.dg, inp.A_log, inp.dt_bias)
+    c = dg.det_colsum_select_cfg(T, H)
+    w1, w2 = oc.colsum(inp.a, inp.dg, inp.A_log, inp.dt_bias, inp.dA_log0, inp.ddt_bias0, c.block_t)
+    g1, g2, gda = run_da(inp, da_layout=layout)
+    assert np.array_equal(gda.view(np.uint16 if dtype == "bf16" else np.uint32),
+                          want_da.view(np.uint16 if dtype == "bf16" else np.uint32)), "da"
+    assert_bitwise(g1, w1, "dA_log"); assert_bitwise(g2, w2, "ddt_bias")
+    a1, a2, ada = run_da(inp, atomic=True, da_layout=layout)
+    assert np.array_equal(ada.view(np.uint8), gda.view(np.uint8)), "da on the atomic arm"
+    assert rel_l2(a1, w1) < 1e-5 and rel_l2(a2, w2) < 1e-5

@@ -163,3 +163,64 @@ def test_full_size_sampled():
         Gf = fp64.widen(inp.G[a:b]); Xf = fp64.widen(inp.X[a:b])
         ex = inp.main_grad0[e][rows].astype(np.float64) + Gf[:, rows].T @ Xf
         assert rel_l2(got[e][rows] - inp.main_grad0[e][rows], ex - inp.main_grad0[e][rows]) <= 1e-5
+
+
+def run_bf16(inp, mg16, C=0, block_m=128, block_n=512, offs=None):
+    """det_grouped_wgrad_acc_bf16 on bf16 main_grad bits; returns the bits after the call."""
+    import torch
+    Gd, Xd = dev_bf16(inp.G), dev_bf16(inp.X)
+    mg = torch.from_numpy(np.ascontiguousarray(mg16).view(np.int16)).cuda().view(torch.bfloat16)
+    o = dev_i32(inp.offs if offs is None else offs)
+    torch.cuda.synchronize()
+    dg.det_grouped_wgrad_acc_bf16(mg, Gd, Xd, o, cfg=cfg(C, block_n, block_m))
+    return mg.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_init(shape, seed, scale=1.0):
+    from oracle.primitives import narrow_bf16
+    return narrow_bf16((np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32))
+
+
+@pytest.mark.parametrize("C", [0, 1, 3])
+def test_bf16_main_grad_exact_integers(C):
+    """Integer inputs: bitwise the oracle's bf16 accumulate of the exact dW; the
+    empty expert keeps its bits."""
+    inp = W.wgrad_inputs(E=4, M=M_, N=N_, tokens=[700, 0, 1300, 17], seed=3, integer=True)
+    mg16 = bf16_init((4, M_, N_), 9, 4.0)
+    note("wgrad bf16 exact integers C=%d" % C)
+    got = run_bf16(inp, mg16, C)
+    want = ow.grouped_wgrad_acc_bf16(mg16, inp.G, inp.X, inp.offs, ktiles_per_split=C)
+    assert np.array_equal(got, want)
+    assert np.array_equal(got[1], mg16[1])
+
+
+@pytest.mark.parametrize("C,bm,bn", [(0, 128, 512), (2, 256, 256), (0, 256, 256)])
+def test_bf16_main_grad_is_bf16_add_of_the_fp32_dw(C, bm, bn):
+    """Realistic inputs: the bf16 result equals the oracle's bf16 accumulate of
+    the float32 dW that det_grouped_wgrad_acc produces with the same tiles and
+    splits (into a -0.0 main_grad, which returns dW itself), bit for bit."""
+    inp = W.wgrad_inputs(E=3, M=M_, N=N_, tokens=[1500, 900, 0], seed=12)
+    note("wgrad bf16 vs fp32 dW C=%d tile %dx%d" % (C, bm, bn))
+    dW = run(inp, C=C, mg0=np.full((3, M_, N_), -0.0, np.float32), block_m=bm, block_n=bn)
+    mg16 = bf16_init((3, M_, N_), 5, 0.01)
+    got = run_bf16(inp, mg16, C, block_m=bm, block_n=bn)
+    want = mg16.copy()
+    for e in range(2):
+        want[e] = ow.accumulate_bf16(mg16[e], dW[e])
+    assert np.array_equal(got, want)
+
+
+def test_bf16_main_grad_full_size_replay():
+    """The scale workload (E = 8, 1408 x 2048, tiles 256 x 256, one split per
+    expert): bitwise against the oracle's bf16 add of the fp32 path's dW, and
+    bitwise across two calls."""
+    inp = W.wgrad_inputs(seed=5)
+    E, M, N = 8, inp.M, inp.N
+    note("wgrad bf16 full size")
+    dW = run(inp, C=0, mg0=np.full((E, M, N), -0.0, np.float32), block_m=256, block_n=256)
+    mg16 = bf16_init((E, M, N), 6, 0.01)
+    a = run_bf16(inp, mg16, 0, block_m=256, block_n=256)
+    b = run_bf16(inp, mg16, 0, block_m=256, block_n=256)
+    assert np.array_equal(a, b)
+    for e in range(E):
+        assert np.array_equal(a[e], ow.accumulate_bf16(mg16[e], dW[e])), e
