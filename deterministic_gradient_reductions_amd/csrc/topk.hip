@@ -15,8 +15,10 @@
 // (id << 10 | slot, padding as id 2^21 - 1), which halves the cross-lane
 // traffic. The keys are sorted with a bitonic network held in registers:
 // element i = r * 64 + lane (EPL elements per lane, so loads and stores are
-// coalesced); partners at a distance below 64 are exchanged across lanes with
-// shuffles, partners further apart are swapped between registers. The
+// coalesced); partners at a distance below 64 are exchanged across lanes (DPP
+// quad permutations for distances 1 and 2, ds_bpermute beyond, all exchanges
+// of a step issued together), partners further apart are swapped between
+// registers. The
 // sorted keys give each output position its source slot, from which the id
 // and the logit are gathered. The softmax: the exact maximum of the valid
 // logits (a wave reduction), e = exp32(logit - max) (the gate's fixed
@@ -33,17 +35,19 @@ namespace {
 
 constexpr int kMaxK = 1024;
 
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-  const uint32_t a = static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), m));
-  const uint32_t b = static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), m));
-  return static_cast<uint64_t>(b) << 32 | a;
-}
-
+// The value of lane ^ m. m = 1 and m = 2 stay inside a group of four lanes
+// and move by a DPP quad permutation (a VALU operand modifier, no LDS-pipe
+// round trip); larger distances use ds_bpermute. Every lane of the wave is
+// active here.
 __device__ __forceinline__ uint32_t shfl_xor_k(uint32_t v, int m) {
+  if (m == 1) return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true));
+  if (m == 2) return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true));
   return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m));
 }
-__device__ __forceinline__ uint64_t shfl_xor_k(uint64_t v, int m) { return shfl_xor64(v, m); }
+__device__ __forceinline__ uint64_t shfl_xor_k(uint64_t v, int m) {
+  const uint32_t lo = shfl_xor_k(static_cast<uint32_t>(v), m), hi = shfl_xor_k(static_cast<uint32_t>(v >> 32), m);
+  return static_cast<uint64_t>(hi) << 32 | lo;
+}
 
 // Ascending bitonic sort of the wave's 64 * EPL keys, element i = r * 64 +
 // lane: partners closer than 64 are in other lanes (shuffles), partners
@@ -70,15 +74,18 @@ __device__ __forceinline__ void bitonic(T (&key)[EPL], int lane) {
           }
         }
       } else {
+        // all exchanges of the step first, so that they are in flight together
+        T o[EPL];
+#pragma unroll
+        for (int r = 0; r < EPL; ++r) o[r] = shfl_xor_k(key[r], d);
 #pragma unroll
         for (int r = 0; r < EPL; ++r) {
           const int i = r * 64 + lane;
-          const T o = shfl_xor_k(key[r], d);
           const bool up = (i & k) == 0;
           const bool lower = (i & d) == 0;  // this element is the lower index of the pair
           // an ascending pair keeps the smaller key at its lower index
           const bool keep_min = (up == lower);
-          const T mn = key[r] < o ? key[r] : o, mx = key[r] < o ? o : key[r];
+          const T mn = key[r] < o[r] ? key[r] : o[r], mx = key[r] < o[r] ? o[r] : key[r];
           key[r] = keep_min ? mn : mx;
         }
       }
