@@ -14,9 +14,12 @@ Canonical order (the reading taken here):
   counted from the expert's first row; ``ktiles_per_split`` consecutive K tiles
   form one split (0 means the whole expert is one split).
 * Each split s produces a float32 partial Q_s[i, j] by a chain of matrix-core
-  steps over its rows in ascending order, starting from +0.0. The steps' own
-  rounding is a property of the matrix-core instruction, which the pages do
-  not describe; ``chain`` is therefore a parameter of this oracle.
+  steps over its rows in ascending 16-row blocks, starting from +0.0. The
+  steps' own rounding is a property of the matrix-core instruction, which the
+  pages do not describe; ``chain_mfma`` takes it from the instruction model of
+  oracle/mfma.py (the default), and ``chain_exact_rounded`` is the exact
+  product rounded once, which every order gives when all partial sums are
+  exactly representable (small-integer inputs).
 * main_grad[e][i, j] <- RN32(main_grad[e][i, j] + fold(Q_0 .. Q_{S_e - 1}))
   with fold the left-to-right sum starting at -0.0. An expert with no rows
   leaves its main_grad slice bitwise unchanged.
@@ -30,6 +33,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import mfma
 from .primitives import NEG_ZERO, accumulate, narrow_bf16, widen_bf16
 
 K_TILE = 512
@@ -69,39 +73,54 @@ def accumulate_bf16(main_grad_bits: np.ndarray, dW: np.ndarray) -> np.ndarray:
     return narrow_bf16(np.add(widen_bf16(main_grad_bits), d16, dtype=np.float32))
 
 
-def chain_exact_rounded(g_f32: np.ndarray, x_f32: np.ndarray) -> np.ndarray:
-    """RN32 of the exact G^T X (float64 is exact for small-integer inputs).
+def chain_mfma(G_bits: np.ndarray, X_bits: np.ndarray, r0: int, r1: int, rows=None) -> np.ndarray:
+    """Q over token rows [r0, r1) of G [T, M] and X [T, N] (bf16 bits): per output (i, j) the chain of
+    the matrix-core step model from +0 over 16-row blocks counted from r0 (rows past r1 are zero), for
+    the output rows ``rows`` (all by default)."""
+    return mfma.wgrad_partial(G_bits, X_bits, r0, r1, rows)
+
+
+def chain_exact_rounded(G_bits: np.ndarray, X_bits: np.ndarray, r0: int, r1: int, rows=None) -> np.ndarray:
+    """RN32 of the exact G^T X over rows [r0, r1) (float64 is exact for small-integer inputs).
 
     Any summation order gives this result whenever every partial sum is an
     exactly representable integer, so it is the chain for exact-integer pins.
     """
-    return (g_f32.astype(np.float64).T @ x_f32.astype(np.float64)).astype(np.float32)
+    g = widen_bf16(G_bits[r0:r1]).astype(np.float64)
+    if rows is not None:
+        g = g[:, np.asarray(rows)]
+    return (g.T @ widen_bf16(X_bits[r0:r1]).astype(np.float64)).astype(np.float32)
 
 
 def grouped_wgrad_acc(main_grad0, G_bits, X_bits, offs, k_tile: int = K_TILE, ktiles_per_split: int = 0,
-                      chain=chain_exact_rounded, experts=None) -> np.ndarray:
-    """Return the updated main_grad [E, M, N] (main_grad0 is not modified)."""
-    mg = np.array(main_grad0, np.float32, copy=True)
+                      chain=chain_mfma, experts=None, rows=None) -> np.ndarray:
+    """Return the updated main_grad [E, M, N] (main_grad0 is not modified).
+
+    With ``rows`` (output row indices), only those rows are computed and the
+    result is [E, len(rows), N]; with ``experts``, other experts keep main_grad0."""
+    mg = np.array(main_grad0 if rows is None else np.asarray(main_grad0)[:, np.asarray(rows)], np.float32, copy=True)
     splits = split_ranges(offs, k_tile, ktiles_per_split)
     for e, sp in enumerate(splits):
         if experts is not None and e not in experts:
             continue
         if not sp:
             continue
-        parts = [chain(widen_bf16(G_bits[b:t]), widen_bf16(X_bits[b:t])) for b, t in sp]
+        parts = [chain(G_bits, X_bits, b, t, rows) for b, t in sp]
         mg[e] = fold_partials(mg[e], parts)
     return mg
 
 
 def grouped_wgrad_acc_bf16(main_grad0_bits, G_bits, X_bits, offs, k_tile: int = K_TILE, ktiles_per_split: int = 0,
-                           chain=chain_exact_rounded, experts=None) -> np.ndarray:
+                           chain=chain_mfma, experts=None, rows=None) -> np.ndarray:
     """bf16 main_grad [E, M, N] (uint16 bits) after the bf16 accumulate of the
-    deterministic dW; experts with no rows keep their bits."""
-    mg = np.array(main_grad0_bits, np.uint16, copy=True)
+    deterministic dW; experts with no rows keep their bits. ``rows`` as for
+    grouped_wgrad_acc."""
+    mg0 = np.asarray(main_grad0_bits)
+    mg = np.array(mg0 if rows is None else mg0[:, np.asarray(rows)], np.uint16, copy=True)
     splits = split_ranges(offs, k_tile, ktiles_per_split)
     for e, sp in enumerate(splits):
         if (experts is not None and e not in experts) or not sp:
             continue
-        parts = [chain(widen_bf16(G_bits[b:t]), widen_bf16(X_bits[b:t])) for b, t in sp]
+        parts = [chain(G_bits, X_bits, b, t, rows) for b, t in sp]
         mg[e] = accumulate_bf16(mg[e], fold_total(parts, mg[e].shape))
     return mg
