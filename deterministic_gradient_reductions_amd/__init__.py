@@ -30,7 +30,7 @@ __all__ = [
     "det_index_add_workspace_size", "det_index_add_bad_ids", "det_grouped_dprob", "det_grouped_dprob_workspace_size",
     "det_grouped_wgrad_acc", "det_grouped_wgrad_acc_workspace_size", "det_grouped_wgrad_acc_bf16",
     "det_grouped_wgrad_acc_bf16_workspace_size", "det_grouped_dbias",
-    "det_grouped_dbias_workspace_size", "det_topk_canonicalize", "det_workspace_init", "det_detmath_eval",
+    "det_grouped_dbias_workspace_size", "det_topk_canonicalize", "det_workspace_init", "det_detmath_eval", "det_mfma_eval",
     "DET_OK", "DET_ERR_INVALID_ARG", "DET_ERR_UNSUPPORTED", "DET_ERR_WORKSPACE", "DET_ERR_OVERLAP", "DET_ERR_HIP",
 ]
 
@@ -94,6 +94,7 @@ _SIGS = {
     "det_grouped_wgrad_acc_workspace_size": ([_I64, _I32, _I64, _I64, ctypes.POINTER(WgradCfg), _INT,
                                               ctypes.POINTER(_SZ)], _INT),
     "det_detmath_eval": ([_P, _P, _I64, _INT, _P], _INT),
+    "det_mfma_eval": ([_P, _P, _P, _P, _I64, _INT, _P], _INT),
     "det_topk_canonicalize": ([_P, _P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
     "det_grouped_dbias_workspace_size": ([_I64, _I64, _I32, ctypes.POINTER(DbiasCfg), _INT, ctypes.POINTER(_SZ)],
                                          _INT),
@@ -199,6 +200,18 @@ def det_workspace_init(ws, stream=None) -> None:
     _check(lib().det_workspace_init(p, n, _stream_handle(stream)))
 
 
+def _require(t, dtype, name: str, contiguous: bool = False, unit_col: bool = False) -> None:
+    """Raise TypeError/ValueError before any call when a tensor's dtype or layout does not match the C ABI."""
+    import torch
+    want = {"f32": torch.float32, "i32": torch.int32, "bf16": torch.bfloat16}[dtype]
+    if t.dtype != want:
+        raise TypeError("%s must be %s, got %s" % (name, want, t.dtype))
+    if contiguous and not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if unit_col and t.dim() >= 1 and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("%s must have unit innermost stride" % name)
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -228,6 +241,10 @@ def det_colsum(a, dg, A_log, dt_bias, dA_log, ddt_bias, cfg: ColsumCfg | None = 
     With ``da`` ([T, H], the dtype of ``a``), also da = dg*(-exp(A_log))*sigmoid(a+dt_bias) per element
     (det_colsum_da)."""
     T, H = a.shape
+    if dg.dtype != a.dtype or tuple(dg.shape) != (T, H):
+        raise TypeError("dg must have the shape and dtype of a")
+    for t, n in ((A_log, "A_log"), (dt_bias, "dt_bias"), (dA_log, "dA_log"), (ddt_bias, "ddt_bias")):
+        _require(t, "f32", n, contiguous=True)
     need = det_colsum_workspace_size(T, H, cfg, atomic) if atomic in (0, 1, False, True) else 0
     wp, wn = _workspace(need, ws, stream)
     head = (_ptr(a), a.stride(0), a.stride(1), _ptr(dg), dg.stride(0), dg.stride(1), _dtype_code(a),
@@ -258,12 +275,24 @@ def det_index_add_workspace_size(n_src: int, dim: int, n_rows: int, cfg: IndexAd
 def det_index_add(out, ids, src, cfg: IndexAddCfg | None = None, atomic=False, ws=None, stream=None) -> None:
     """out[ids[p]] += src[p] for 0 <= ids[p] < out.shape[0]; out float32 [R, D], src bf16 [P, D]."""
     n_rows, dim = out.shape
+    _require(out, "f32", "out", unit_col=True)
+    _require(ids, "i32", "ids", contiguous=True)
+    if src.dtype not in _src_dtypes():
+        raise TypeError("src must be bfloat16 or float32, got %s" % src.dtype)
+    _require(src, "bf16" if src.dtype == _src_dtypes()[0] else "f32", "src", unit_col=True)
     n_src = ids.numel()
+    if src.dim() != 2 or src.shape[0] != n_src or src.shape[1] != dim:
+        raise ValueError("src must be [ids.numel(), out.shape[1]]")
     need = det_index_add_workspace_size(n_src, dim, n_rows, cfg, atomic) if atomic in (0, 1, False, True) else 0
     wp, wn = _workspace(need, ws, stream)
     _check(lib().det_index_add(_ptr(out), n_rows, dim, out.stride(0), _ptr(ids), n_src, _ptr(src), src.stride(0),
                                _dtype_code(src), ctypes.byref(cfg) if cfg else None, wp, wn, _atomic_flag(atomic),
                                _stream_handle(stream)))
+
+
+def _src_dtypes():
+    import torch
+    return (torch.bfloat16, torch.float32)
 
 
 def det_index_add_bad_ids(ws=None, stream=None) -> int:
@@ -284,8 +313,12 @@ def det_grouped_dprob_workspace_size(M: int, N: int, cfg: DprobCfg | None = None
 def det_grouped_dprob(dprob, dY, C, offs, cfg: DprobCfg | None = None, atomic=False, ws=None, stream=None) -> None:
     """dprob[m] += sum_n dY[m,n]*relu(C[m,n])^2 for offs[0] <= m < offs[E]; dY, C bf16 [M, N]."""
     M, N = dY.shape
-    if dY.stride(1) != 1 or C.stride(1) != 1:
-        raise ValueError("dY and C must have unit column stride")
+    _require(dY, "bf16", "dY", unit_col=True)
+    _require(C, "bf16", "C", unit_col=True)
+    _require(dprob, "f32", "dprob", contiguous=True)
+    _require(offs, "i32", "offs", contiguous=True)
+    if tuple(C.shape) != (M, N) or dprob.numel() != M:
+        raise ValueError("C must be [M, N] like dY and dprob [M]")
     need = det_grouped_dprob_workspace_size(M, N, cfg, atomic) if atomic in (0, 1, False, True) else 0
     wp, wn = _workspace(need, ws, stream)
     _check(lib().det_grouped_dprob(_ptr(dprob), _ptr(dY), dY.stride(0), _ptr(C), C.stride(0), M, N, _ptr(offs),
@@ -305,8 +338,11 @@ def det_grouped_dbias(dbias, dA, offs, cfg: DbiasCfg | None = None, atomic=False
     """dbias[e] += column sums of dA[offs[e]:offs[e+1]]; dA bf16 [M, N], dbias fp32 [E, N]."""
     M, N = dA.shape
     E = offs.numel() - 1
-    if dA.stride(1) != 1 or dbias.stride(1) != 1:
-        raise ValueError("dA and dbias must have unit column stride")
+    _require(dA, "bf16", "dA", unit_col=True)
+    _require(dbias, "f32", "dbias", unit_col=True)
+    _require(offs, "i32", "offs", contiguous=True)
+    if tuple(dbias.shape) != (E, N):
+        raise ValueError("dbias must be [E, N] with E = offs.numel() - 1")
     need = det_grouped_dbias_workspace_size(M, N, E, cfg, atomic) if atomic in (0, 1, False, True) else 0
     wp, wn = _workspace(need, ws, stream)
     _check(lib().det_grouped_dbias(_ptr(dbias), dbias.stride(0), _ptr(dA), dA.stride(0), M, N, _ptr(offs), E,
@@ -319,6 +355,10 @@ def det_topk_canonicalize(ids, logits, ids_out, logits_out, probs, stream=None) 
     """Per row of the [Q, K] compact top-k: ids sorted (padding last), logits permuted alike,
     softmax recomputed in that order. ids int32, logits and outputs float32 (ids_out int32)."""
     Q, K = ids.shape
+    _require(ids, "i32", "ids")
+    _require(ids_out, "i32", "ids_out")
+    for t, n in ((logits, "logits"), (logits_out, "logits_out"), (probs, "probs")):
+        _require(t, "f32", n)
     if ids.stride(1) != 1 or logits.stride(1) != 1 or ids.stride(0) != logits.stride(0):
         raise ValueError("ids and logits need unit column stride and one row stride")
     if not (ids_out.stride(0) == logits_out.stride(0) == probs.stride(0)) or \
@@ -337,13 +377,23 @@ def det_grouped_wgrad_acc_workspace_size(T_total: int, E: int, M: int, N: int, c
     return n.value
 
 
+def _wgrad_operands(G, X, offs, E, M, N) -> None:
+    _require(G, "bf16", "G", unit_col=True)
+    _require(X, "bf16", "X", unit_col=True)
+    _require(offs, "i32", "offs", contiguous=True)
+    if G.dim() != 2 or X.dim() != 2 or G.shape[1] != M or X.shape[1] != N or X.shape[0] != G.shape[0]:
+        raise ValueError("G must be [T, M] and X [T, N] for main_grad [E, M, N]")
+    if offs.numel() != E + 1:
+        raise ValueError("offs must hold E + 1 offsets")
+
+
 def det_grouped_wgrad_acc(main_grad, G, X, offs, cfg: WgradCfg | None = None, atomic=False, ws=None,
                           stream=None) -> None:
     """main_grad[e] += G[offs[e]:offs[e+1]]^T X[offs[e]:offs[e+1]]; main_grad fp32 [E, M, N]."""
     E, M, N = main_grad.shape
     T_total = G.shape[0]
-    if G.stride(1) != 1 or X.stride(1) != 1 or main_grad.stride(2) != 1:
-        raise ValueError("G, X and main_grad must have unit innermost stride")
+    _require(main_grad, "f32", "main_grad", unit_col=True)
+    _wgrad_operands(G, X, offs, E, M, N)
     need = det_grouped_wgrad_acc_workspace_size(T_total, E, M, N, cfg, atomic) if atomic in (0, 1, False, True) else 0
     wp, wn = _workspace(need, ws, stream)
     _check(lib().det_grouped_wgrad_acc(_ptr(main_grad), main_grad.stride(0), main_grad.stride(1), _ptr(G), G.stride(0),
@@ -367,8 +417,8 @@ def det_grouped_wgrad_acc_bf16(main_grad, G, X, offs, cfg: WgradCfg | None = Non
         raise TypeError("main_grad must be bfloat16")
     E, M, N = main_grad.shape
     T_total = G.shape[0]
-    if G.stride(1) != 1 or X.stride(1) != 1 or main_grad.stride(2) != 1:
-        raise ValueError("G, X and main_grad must have unit innermost stride")
+    _require(main_grad, "bf16", "main_grad", unit_col=True)
+    _wgrad_operands(G, X, offs, E, M, N)
     wp, wn = _workspace(det_grouped_wgrad_acc_bf16_workspace_size(T_total, E, M, N, cfg), ws, stream)
     _check(lib().det_grouped_wgrad_acc_bf16(_ptr(main_grad), main_grad.stride(0), main_grad.stride(1), _ptr(G),
                                             G.stride(0), _ptr(X), X.stride(0), _ptr(offs), E, T_total, M, N,
@@ -382,3 +432,18 @@ DETMATH_FN = {"exp32": 0, "log1p32": 1, "softplus32": 2, "sigmoid32": 3}
 def det_detmath_eval(x, y, fn: str, stream=None) -> None:
     """y = fn(x) elementwise on the GPU with the gate's detmath sequences (tests only)."""
     _check(lib().det_detmath_eval(_ptr(x), _ptr(y), x.numel(), DETMATH_FN[fn], _stream_handle(stream)))
+
+
+def det_mfma_eval(A, B, C, D, stream=None) -> None:
+    """D[q] = chain of the weight gradient's matrix-core instruction over the 16-wide k blocks of
+    A[q] [32, K] and B[q] [K, 32] (bf16), starting from C[q] [32, 32] float32 (tests only)."""
+    import torch
+    n, m, K = A.shape
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16 or C.dtype != torch.float32 or D.dtype != torch.float32:
+        raise TypeError("A, B must be bfloat16 and C, D float32")
+    if m != 32 or K % 16 or tuple(B.shape) != (n, K, 32) or tuple(C.shape) != (n, 32, 32) or \
+            tuple(D.shape) != (n, 32, 32):
+        raise ValueError("shapes must be A [n,32,K], B [n,K,32], C and D [n,32,32] with K a multiple of 16")
+    if not (A.is_contiguous() and B.is_contiguous() and C.is_contiguous() and D.is_contiguous()):
+        raise ValueError("A, B, C and D must be contiguous")
+    _check(lib().det_mfma_eval(_ptr(A), _ptr(B), _ptr(C), _ptr(D), n, K // 16, _stream_handle(stream)))

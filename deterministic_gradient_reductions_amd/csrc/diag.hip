@@ -1,10 +1,46 @@
-// Diagnostic entry point: evaluates the device detmath functions elementwise,
-// so tests can compare the GPU's bits with the CPU oracle's.
+// Diagnostic entry points: the device detmath functions evaluated elementwise,
+// and chains of the matrix-core instruction of the weight gradient on plain
+// row-major operands, so tests can compare the GPU's bits with the CPU
+// oracle's.
 #include "common.hpp"
 #include "detmath.hpp"
 
 namespace detgrad {
 namespace {
+typedef __bf16 dbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float df32x16_t __attribute__((ext_vector_type(16)));
+
+// One wave per chain. Lane l = 32 kg + r holds A[r][16 b + 8 kg + e] and
+// B[16 b + 8 kg + e][r] (e = 0..7) of block b, and accumulator c holds
+// D[8 (c / 4) + 4 kg + c % 4][r]: the operand layout of the weight-gradient
+// kernel, where k = 8 kg + e is the token row inside a 16-row block.
+__global__ __launch_bounds__(256) void mfma_eval_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                                        const float* __restrict__ C, float* __restrict__ D, int64_t n,
+                                                        int kblocks) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (q >= n) return;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 31, kg = lane >> 5;
+  const int K = 16 * kblocks;
+  const uint16_t* a = A + q * 32 * K;
+  const uint16_t* b = B + q * K * 32;
+  df32x16_t acc;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) acc[c] = C[q * 1024 + (8 * (c / 4) + 4 * kg + c % 4) * 32 + r];
+  for (int blk = 0; blk < kblocks; ++blk) {
+    dbf16x8_t fa, fb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = 16 * blk + 8 * kg + e;
+      fa[e] = __builtin_bit_cast(__bf16, a[r * K + k]);
+      fb[e] = __builtin_bit_cast(__bf16, b[k * 32 + r]);
+    }
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < 16; ++c) D[q * 1024 + (8 * (c / 4) + 4 * kg + c % 4) * 32 + r] = acc[c];
+}
+
 __global__ void detmath_eval_kernel(const float* __restrict__ x, float* __restrict__ y, int64_t n, int fn) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -33,4 +69,19 @@ extern "C" int det_detmath_eval(const float* x, float* y, int64_t n, int fn, voi
   if (grid > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "detmath_eval: n too large");
   hipLaunchKernelGGL(detmath_eval_kernel, dim3(grid), dim3(256), 0, as_stream(stream), x, y, n, fn);
   return check_launch("det_detmath_eval");
+}
+
+extern "C" int det_mfma_eval(const uint16_t* A, const uint16_t* B, const float* C, float* D, int64_t n, int kblocks,
+                             void* stream) {
+  if (n < 0 || kblocks < 1 || kblocks > 4096) return set_error(DET_ERR_INVALID_ARG, "mfma_eval: bad n or kblocks");
+  if (n == 0) return ok();
+  if (!A || !B || !C || !D) return set_error(DET_ERR_INVALID_ARG, "mfma_eval: NULL pointer");
+  const size_t ab = static_cast<size_t>(n) * 32 * 16 * kblocks * 2;
+  const Range d = range1d(D, static_cast<size_t>(n) * 4096);
+  if (overlaps(d, range1d(A, ab)) || overlaps(d, range1d(B, ab)) || overlaps(d, range1d(C, static_cast<size_t>(n) * 4096)))
+    return set_error(DET_ERR_OVERLAP, "mfma_eval: D overlaps an input");
+  const int64_t grid = ceil_div(n, 4);
+  if (grid > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "mfma_eval: n too large");
+  hipLaunchKernelGGL(mfma_eval_kernel, dim3(grid), dim3(256), 0, as_stream(stream), A, B, C, D, n, kblocks);
+  return check_launch("det_mfma_eval");
 }

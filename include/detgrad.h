@@ -165,9 +165,9 @@ int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t out_ld, const
                   size_t ws_bytes, int atomic, void* stream);
 /* Number of ids dropped as out of range (not -1) by the last det_index_add
  * that used this workspace. Synchronises `stream`; for tests and debugging.
- * Returns DET_ERR_HIP if that call's offsets kernel gave up waiting for the
- * totals of one of its workgroups (a bounded wait that never times out when
- * the GPU schedules all of them; the result of such a call is not valid). */
+ * No kernel of det_index_add waits for another workgroup (each stage hands
+ * its results to the next through a kernel boundary), so a call cannot stall
+ * on a busy GPU. */
 int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* count, void* stream);
 
 /* ------------------------------------------------------------------------
@@ -342,6 +342,20 @@ int det_topk_canonicalize(const int32_t* ids, const float* logits, int64_t Q, in
  * device arrays that must not overlap. Lets a test compare the GPU's bits
  * with the CPU oracle's over any sample of inputs. */
 int det_detmath_eval(const float* x, float* y, int64_t n, int fn, void* stream);
+
+/* det_mfma_eval runs chains of the weight gradient's matrix-core instruction
+ * (v_mfma_f32_32x32x16_bf16) on plain operands, for the tests that pin the
+ * oracle's model of that instruction (the pages say nothing about matrix-core
+ * rounding; FlashInfer PR #8924 makes the deterministic dW's bits part of the
+ * contract). For q < n: acc = C[q]; for b = 0..kblocks-1,
+ * acc = mfma(A[q][:, 16b:16b+16], B[q][16b:16b+16, :], acc); D[q] = acc.
+ * k = 8 kg + e inside a block is the operand element e of lane group kg, which
+ * is token row 16b + k of a weight-gradient block.
+ * A: [n][32][16 kblocks] bf16 bits, B: [n][16 kblocks][32] bf16 bits,
+ * C, D: [n][32][32] float32; all row-major, contiguous, device memory; D must
+ * not overlap the inputs. kblocks in [1, 4096]. */
+int det_mfma_eval(const uint16_t* A, const uint16_t* B, const float* C, float* D, int64_t n, int kblocks,
+                  void* stream);
 
 #ifdef __cplusplus
 }

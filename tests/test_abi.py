@@ -281,3 +281,56 @@ def test_wgrad_bf16_validation_and_workspace():
                                         None, None, 0, None) == dg.DET_ERR_UNSUPPORTED
     assert L.det_grouped_wgrad_acc_bf16(P(0x900000), 512 * 256, 512, FAKE, 256, FAKE, 512, FAKE, 2, 1000, 200, 512,
                                         None, None, 0, None) == dg.DET_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_wrong_dtypes_and_layouts():
+    """The Python binding checks dtypes and layouts before any library call (CPU tensors suffice): an int64
+    ids or offs tensor, a float64 output or a column-strided operand would otherwise be read as other words."""
+    import torch
+    f32, bf, i32, i64 = torch.float32, torch.bfloat16, torch.int32, torch.int64
+    out = torch.zeros(8, 16, dtype=f32)
+    src = torch.zeros(10, 16, dtype=bf)
+    with pytest.raises(TypeError):
+        dg.det_index_add(out, torch.zeros(10, dtype=i64), src)
+    with pytest.raises(TypeError):
+        dg.det_index_add(out.double(), torch.zeros(10, dtype=i32), src)
+    with pytest.raises(ValueError):
+        dg.det_index_add(out, torch.zeros(10, dtype=i32), torch.zeros(10, 32, dtype=bf)[:, ::2])
+    with pytest.raises(ValueError):
+        dg.det_index_add(out, torch.zeros(20, dtype=i32)[::2], src)
+    dY = torch.zeros(4, 16, dtype=bf)
+    with pytest.raises(TypeError):
+        dg.det_grouped_dprob(torch.zeros(4, dtype=f32), dY, dY, torch.tensor([0, 4], dtype=i64))
+    with pytest.raises(TypeError):
+        dg.det_grouped_dprob(torch.zeros(4, dtype=torch.float64), dY, dY, torch.tensor([0, 4], dtype=i32))
+    with pytest.raises(ValueError):
+        dg.det_grouped_dprob(torch.zeros(4, dtype=f32), dY, torch.zeros(4, 32, dtype=bf)[:, ::2],
+                             torch.tensor([0, 4], dtype=i32))
+    with pytest.raises(TypeError):
+        dg.det_grouped_dbias(torch.zeros(1, 16, dtype=f32), dY, torch.tensor([0, 4], dtype=i64))
+    with pytest.raises(ValueError):
+        dg.det_grouped_dbias(torch.zeros(2, 16, dtype=f32), dY, torch.tensor([0, 4], dtype=i32))
+    G, X = torch.zeros(8, 128, dtype=bf), torch.zeros(8, 256, dtype=bf)
+    mg = torch.zeros(1, 128, 256, dtype=f32)
+    with pytest.raises(TypeError):
+        dg.det_grouped_wgrad_acc(mg, G, X, torch.tensor([0, 8], dtype=i64))
+    with pytest.raises(TypeError):
+        dg.det_grouped_wgrad_acc(mg, G.float(), X, torch.tensor([0, 8], dtype=i32))
+    with pytest.raises(TypeError):
+        dg.det_grouped_wgrad_acc(mg.double(), G, X, torch.tensor([0, 8], dtype=i32))
+    with pytest.raises(ValueError):
+        dg.det_grouped_wgrad_acc(mg, G, X, torch.tensor([0, 4, 8], dtype=i32))
+    with pytest.raises(TypeError):
+        dg.det_grouped_wgrad_acc_bf16(mg, G, X, torch.tensor([0, 8], dtype=i32))
+    a = torch.zeros(4, 2, dtype=bf)
+    p = torch.zeros(2, dtype=f32)
+    with pytest.raises(TypeError):
+        dg.det_colsum(a, a.float(), p, p, p.clone(), p.clone())
+    with pytest.raises(TypeError):
+        dg.det_colsum(a, a, p.double(), p, p.clone(), p.clone())
+    ids = torch.zeros(2, 4, dtype=i32)
+    lg = torch.zeros(2, 4, dtype=f32)
+    with pytest.raises(TypeError):
+        dg.det_topk_canonicalize(ids.long(), lg, ids.clone(), lg.clone(), lg.clone())
+    with pytest.raises(TypeError):
+        dg.det_topk_canonicalize(ids, lg, ids.clone(), lg.clone(), lg.double())
