@@ -9,8 +9,9 @@
 //              than -1 are counted as bad.
 //  2. prefix   per id, exclusive prefix of hist[*][id] over blocks (in place)
 //              and the id's total count.
-//  3. scan     one workgroup: exclusive scans of the counts (segment offsets of
-//              the sorted order) and of ceil(count / L) (chunk offsets).
+//  3. scan     per-workgroup totals of the counts, then exclusive scans of the
+//              counts (segment offsets of the sorted order) and of
+//              ceil(count / L) (chunk offsets), and the chunk descriptors.
 //  4. scatter  one wave per block walks its positions in order, 64 at a time;
 //              the lanes holding the same id find each other with one ballot
 //              per id bit, so each lane's rank among equal ids is its position
@@ -45,7 +46,7 @@ inline __host__ __device__ int hist_stride(int64_t n_rows) { return static_cast<
 constexpr int kMaxGroups = kMaxRows / 256;  // workgroups of the offsets kernel (one thread per id)
 
 struct Layout {
-  size_t hist, segtot, pub, seg_off, chunk_off, full_off, chunk_desc, perm, scratch, total;
+  size_t hist, segtot, wg_tot, seg_off, chunk_off, full_off, chunk_desc, perm, scratch, total;
   int64_t nblk, nseg, max_chunks;
 };
 
@@ -57,7 +58,7 @@ Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L) {
   size_t o = DET_WS_HEADER_BYTES;
   l.hist = o;      o = align_up(o + static_cast<size_t>(l.nblk * hist_stride(n_rows)) * 2, 256);
   l.segtot = o;    o = align_up(o + static_cast<size_t>(l.nseg * n_rows) * 4, 256);
-  l.pub = o;       o = align_up(o + static_cast<size_t>(3 * kMaxGroups) * 4, 256);
+  l.wg_tot = o;   o = align_up(o + static_cast<size_t>(3 * kMaxGroups) * 4, 256);
   l.seg_off = o;   o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
   l.chunk_off = o; o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
   l.full_off = o;  o = align_up(o + static_cast<size_t>(n_rows + 1) * 4, 256);
@@ -90,13 +91,8 @@ __device__ __forceinline__ uint64_t match_peers(int32_t id, bool valid) {
 // the LDS serialises; that is far cheaper than matching lanes first).
 __global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
                                                 int hist_ld, uint16_t* __restrict__ hist,
-                                                uint32_t* __restrict__ hdr, uint32_t* __restrict__ pub) {
+                                                uint32_t* __restrict__ hdr) {
   extern __shared__ uint32_t lds_hist[];
-  // the offsets kernel's exchange words start unpublished, its timeout flag clear
-  if (blockIdx.x == 0) {
-    if (threadIdx.x < 3 * kMaxGroups) pub[threadIdx.x] = 0u;
-    if (threadIdx.x == 0) hdr[2] = 0u;
-  }
   for (int k = threadIdx.x; k < hist_ld; k += 256) lds_hist[k] = 0u;
   __syncthreads();
   const int64_t b = blockIdx.x;
@@ -164,17 +160,16 @@ __device__ __forceinline__ uint32_t ceil_div_rcp(uint32_t n, uint32_t L, uint32_
 }
 
 // ---- 3. offsets and chunk descriptors, one thread per id and 256 ids per
-// workgroup. Thread k adds up id k's segment totals (leaving their exclusive
-// prefix in place) to its count c, with n = ceil(c / L) chunks of which
-// f = floor(c / L) are full. Then the exclusive scans over ids of c (segment
-// offsets), n (chunk offsets) and f (full chunks): a workgroup scans its own
-// ids, publishes its three totals in the workspace (the top bit marks a
-// published word: totals stay below 2^31; the count kernel of the same call
-// clears the words) and reads every workgroup's totals for its prefix and the
-// grand totals. Integer sums only: exact in any order. Every workgroup
-// publishes before it waits and there are at most 64 of them, so all of them
-// are resident together and the waits end; a wait is bounded all the same,
-// and a timeout is recorded in header word 2.
+// workgroup, in two kernels. ia_totals: thread k adds up id k's segment totals
+// (leaving their exclusive prefix in place) to its count c, parks c in its
+// seg_off entry, and with n = ceil(c / L) chunks of which f = floor(c / L) are
+// full, every workgroup stores its totals of c, n and f in the workspace.
+// ia_offsets: the exclusive scans over ids of c (segment offsets), n (chunk
+// offsets) and f (full chunks): a workgroup scans its own ids and adds the
+// totals of the workgroups before it, and takes the grand totals from all of
+// them. The kernel boundary orders every workgroup's totals before any read of
+// them, so no workgroup ever waits for another. Integer sums only: exact in
+// any order.
 //
 // Then the 16-byte descriptors {id, first sorted row, rows, scratch slot} of
 // every chunk, so a gather wave starts from one load. The gather takes them
@@ -213,22 +208,23 @@ __device__ __forceinline__ uint32_t row_incl_scan(uint32_t v) {
   return v;
 }
 
-constexpr uint32_t kPublished = 0x80000000u;
-constexpr int kSpinLimit = 1 << 20;
-
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_incl_scan(v)), 63));
 }
 
-__global__ __launch_bounds__(256) void ia_offsets(uint32_t* __restrict__ segtot, int64_t nseg, int n_rows, int L,
-                                                  uint32_t rcp, int64_t n_src, uint32_t* __restrict__ pub,
-                                                  uint32_t* __restrict__ seg_off, uint32_t* __restrict__ chunk_off,
-                                                  uint32_t* __restrict__ full_off, int4* __restrict__ desc,
-                                                  uint32_t* __restrict__ hdr) {
+// Count c of id k (its segment totals turned into their exclusive prefix in
+// place), its chunks n and its full chunks f.
+__device__ __forceinline__ void id_counts(uint32_t c, int L, uint32_t rcp, uint32_t& nc, uint32_t& fc) {
+  nc = ceil_div_rcp(c, L, rcp);
+  fc = nc - (nc * static_cast<uint32_t>(L) != c ? 1u : 0u);
+}
+
+__global__ __launch_bounds__(256) void ia_totals(uint32_t* __restrict__ segtot, int64_t nseg, int n_rows, int L,
+                                                 uint32_t rcp, uint32_t* __restrict__ wg_tot,
+                                                 uint32_t* __restrict__ counts) {
   __shared__ uint32_t w_tot[3][4];
-  __shared__ uint32_t g_tot[2][3];  // [0]: workgroups before this one, [1]: all
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x, ng = gridDim.x;
+  const int b = blockIdx.x;
   const int k = b * 256 + tid;
   uint32_t c = 0;
   if (k < n_rows) {
@@ -242,14 +238,50 @@ __global__ __launch_bounds__(256) void ia_offsets(uint32_t* __restrict__ segtot,
         c += v[j];
       }
     }
+    counts[k] = c;
   }
-  const uint32_t nc = ceil_div_rcp(c, L, rcp);
-  const uint32_t fc = nc - (nc * static_cast<uint32_t>(L) != c ? 1u : 0u);
+  uint32_t nc, fc;
+  id_counts(c, L, rcp, nc, fc);
+  const uint32_t t0 = wave_sum(c), t1 = wave_sum(nc), t2 = wave_sum(fc);
+  if (lane == 0) {
+    w_tot[0][wave] = t0;
+    w_tot[1][wave] = t1;
+    w_tot[2][wave] = t2;
+  }
+  __syncthreads();
+  if (tid < 3) wg_tot[tid * kMaxGroups + b] = w_tot[tid][0] + w_tot[tid][1] + w_tot[tid][2] + w_tot[tid][3];
+}
+
+__global__ __launch_bounds__(256) void ia_offsets(int n_rows, int L, uint32_t rcp, int64_t n_src,
+                                                  const uint32_t* __restrict__ wg_tot,
+                                                  uint32_t* __restrict__ seg_off, uint32_t* __restrict__ chunk_off,
+                                                  uint32_t* __restrict__ full_off, int4* __restrict__ desc,
+                                                  uint32_t* __restrict__ hdr) {
+  __shared__ uint32_t w_tot[3][4];
+  __shared__ uint32_t g_tot[2][3];  // [0]: workgroups before this one, [1]: all
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x, ng = gridDim.x;
+  const int k = b * 256 + tid;
+  const uint32_t c = k < n_rows ? seg_off[k] : 0u;  // the count ia_totals parked there
+  uint32_t nc, fc;
+  id_counts(c, L, rcp, nc, fc);
   const uint32_t i0 = wave_incl_scan(c), i1 = wave_incl_scan(nc), i2 = wave_incl_scan(fc);
   if (lane == 63) {
     w_tot[0][wave] = i0;
     w_tot[1][wave] = i1;
     w_tot[2][wave] = i2;
+  }
+  if (wave == 0) {
+    // lane j holds workgroup j's totals (written by ia_totals, a finished kernel)
+    const uint32_t v0 = lane < ng ? wg_tot[lane] : 0u, v1 = lane < ng ? wg_tot[kMaxGroups + lane] : 0u,
+                   v2 = lane < ng ? wg_tot[2 * kMaxGroups + lane] : 0u;
+    const uint32_t p0 = wave_sum(lane < b ? v0 : 0u), p1 = wave_sum(lane < b ? v1 : 0u),
+                   p2 = wave_sum(lane < b ? v2 : 0u);
+    const uint32_t a0 = wave_sum(v0), a1 = wave_sum(v1), a2 = wave_sum(v2);
+    if (lane == 0) {
+      g_tot[0][0] = p0; g_tot[0][1] = p1; g_tot[0][2] = p2;
+      g_tot[1][0] = a0; g_tot[1][1] = a1; g_tot[1][2] = a2;
+    }
   }
   __syncthreads();
   uint32_t e0 = i0 - c, e1 = i1 - nc, e2 = i2 - fc;  // exclusive prefix inside the workgroup
@@ -260,34 +292,6 @@ __global__ __launch_bounds__(256) void ia_offsets(uint32_t* __restrict__ segtot,
       e1 += w_tot[1][w];
       e2 += w_tot[2][w];
     }
-  if (wave == 0) {
-    if (lane < 3) {
-      const uint32_t t = w_tot[lane][0] + w_tot[lane][1] + w_tot[lane][2] + w_tot[lane][3];
-      __hip_atomic_store(pub + lane * kMaxGroups + b, t | kPublished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // lane j waits for workgroup j's three totals
-    uint32_t v0 = 0, v1 = 0, v2 = 0;
-    if (lane < ng) {
-      int spins = 0;
-      do {
-        v0 = __hip_atomic_load(pub + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v1 = __hip_atomic_load(pub + kMaxGroups + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v2 = __hip_atomic_load(pub + 2 * kMaxGroups + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } while ((v0 & v1 & v2 & kPublished) == 0u && ++spins < kSpinLimit);
-      if ((v0 & v1 & v2 & kPublished) == 0u) hdr[2] = 1u;
-      v0 &= ~kPublished;
-      v1 &= ~kPublished;
-      v2 &= ~kPublished;
-    }
-    const uint32_t p0 = wave_sum(lane < b ? v0 : 0u), p1 = wave_sum(lane < b ? v1 : 0u),
-                   p2 = wave_sum(lane < b ? v2 : 0u);
-    const uint32_t a0 = wave_sum(v0), a1 = wave_sum(v1), a2 = wave_sum(v2);
-    if (lane == 0) {
-      g_tot[0][0] = p0; g_tot[0][1] = p1; g_tot[0][2] = p2;
-      g_tot[1][0] = a0; g_tot[1][1] = a1; g_tot[1][2] = a2;
-    }
-  }
-  __syncthreads();
   const uint32_t seg = g_tot[0][0] + e0, chk = g_tot[0][1] + e1, ful = g_tot[0][2] + e2;
   const uint32_t n_full = g_tot[1][2];
   if (k < n_rows) {
@@ -1088,7 +1092,7 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   auto* hdr = reinterpret_cast<uint32_t*>(w);
   auto* hist = reinterpret_cast<uint16_t*>(w + l.hist);
   const int hist_ld = hist_stride(n_rows);
-  auto* pub = reinterpret_cast<uint32_t*>(w + l.pub);
+  auto* wg_tot = reinterpret_cast<uint32_t*>(w + l.wg_tot);
   auto* seg_off = reinterpret_cast<uint32_t*>(w + l.seg_off);
   auto* chunk_off = reinterpret_cast<uint32_t*>(w + l.chunk_off);
   auto* full_off = reinterpret_cast<uint32_t*>(w + l.full_off);
@@ -1097,12 +1101,14 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
   auto* scratch = reinterpret_cast<float*>(w + l.scratch);
   const size_t lds_count = static_cast<size_t>(hist_ld) * 4;
   auto* segtot = reinterpret_cast<uint32_t*>(w + l.segtot);
-  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, hist_ld, hist, hdr, pub);
+  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, hist_ld, hist, hdr);
   hipLaunchKernelGGL(ia_prefix_seg, dim3(ceil_div(n_rows, 256), l.nseg), dim3(256), 0, st, hist, hist_ld, l.nblk, nr,
                      segtot);
   const uint32_t rcp = static_cast<uint32_t>(0xFFFFFFFFull / static_cast<uint64_t>(L));
-  hipLaunchKernelGGL(ia_offsets, dim3(static_cast<uint32_t>(ceil_div(n_rows, 256))), dim3(256), 0, st, segtot, l.nseg,
-                     nr, L, rcp, n_src, pub, seg_off, chunk_off, full_off, chunk_desc, hdr);
+  const dim3 off_grid(static_cast<uint32_t>(ceil_div(n_rows, 256)));
+  hipLaunchKernelGGL(ia_totals, off_grid, dim3(256), 0, st, segtot, l.nseg, nr, L, rcp, wg_tot, seg_off);
+  hipLaunchKernelGGL(ia_offsets, off_grid, dim3(256), 0, st, nr, L, rcp, n_src, wg_tot, seg_off, chunk_off, full_off,
+                     chunk_desc, hdr);
   switch (scatter_waves(n_rows)) {
     case 4: launch_scatter<4>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
     case 2: launch_scatter<2>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
@@ -1156,12 +1162,11 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
 extern "C" int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* count, void* stream) {
   if (!count) return set_error(DET_ERR_INVALID_ARG, "index_add_bad_ids: count is NULL");
   if (int s = check_workspace(ws, ws_bytes, DET_WS_HEADER_BYTES)) return s;
-  uint32_t v[2] = {0u, 0u};  // header words 1 (bad ids of the last call) and 2 (exchange timeout)
+  uint32_t v = 0u;  // header word 1: bad ids of the last call
   const hipStream_t st = as_stream(stream);
-  hipError_t e = hipMemcpyAsync(v, static_cast<const char*>(ws) + 4, 8, hipMemcpyDeviceToHost, st);
+  hipError_t e = hipMemcpyAsync(&v, static_cast<const char*>(ws) + 4, 4, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return set_error(DET_ERR_HIP, "index_add_bad_ids: %s", hipGetErrorString(e));
-  if (v[1] != 0u) return set_error(DET_ERR_HIP, "index_add: the offsets kernel timed out waiting for a workgroup");
-  *count = v[0];
+  *count = v;
   return ok();
 }
