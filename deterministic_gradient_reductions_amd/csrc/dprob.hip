@@ -14,10 +14,11 @@
 // load (row-contiguous, fully coalesced), dprob is read and written once:
 // 4 bytes per (m, n) plus 8 bytes per row. The kernel is HBM-bound.
 //
-// The atomic arm keeps the same tile partials but gives each 512-column chunk
-// of a row to a different wave, which sums its tiles and adds the result into
-// dprob[m] with a hardware float atomic; the order of those adds follows the
-// scheduler, as on the page's default path.
+// The atomic arm keeps the same tile partials but adds every one of them into
+// dprob[m] with a hardware float atomic, as the page's default path does
+// across CTAs. The four 512-column chunks of a row go to the four waves of one
+// workgroup, which run side by side, so the order in which a row's sixteen
+// adds land follows the scheduler and the memory system.
 #include "common.hpp"
 
 namespace detgrad {
@@ -144,14 +145,11 @@ __global__ __launch_bounds__(kWG) void dprob_atomic_kernel(float* __restrict__ d
   const int64_t n_chunks = (N + kChunk - 1) / kChunk;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (rows <= 0 || w >= rows * n_chunks) return;
-  const int64_t ch = w / rows;  // chunk-major: the chunks of one row land in different workgroups
-  const int64_t m = lo + w % rows;
+  const int64_t m = lo + w / n_chunks;  // row-major: the chunks of one row run on neighbouring waves
+  const int64_t ch = w % n_chunks;
   const float s = chunk_slots<VEC>(dY + m * ldy, C + m * ldc, ch, N, lane);
-  float run = -0.0f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (ch * kChunk + q * kTileN < N) run = run + readlane(s, 16 * q);
-  if (lane == 0) unsafeAtomicAdd(dprob + m, run);
+  // lanes 16q hold the slot of tile 4 ch + q
+  if ((lane & 15) == 0 && ch * kChunk + (lane >> 4) * kTileN < N) unsafeAtomicAdd(dprob + m, s);
 }
 
 int check_cfg(const det_dprob_cfg* cfg, det_dprob_cfg* out) {

@@ -66,7 +66,7 @@ def test_full_size_parity_and_non_default_stream():
 
 def test_replay_under_load_and_atomic_arm():
     import torch
-    inp = W.dprob_inputs(M=4096, N=2048, E=8, min_tokens=64, seed=24, out_init="normal")
+    inp = W.dprob_inputs(M=16384, N=2048, E=8, min_tokens=64, seed=24, out_init="normal")
     ref = od.grouped_dprob(inp.dprob0, inp.dY, inp.C, inp.offs)
     dY, C, o = dev_bf16(inp.dY), dev_bf16(inp.C), dev_i32(inp.offs)
     d0 = dev_f32(inp.dprob0)
@@ -89,6 +89,7 @@ def test_replay_under_load_and_atomic_arm():
         assert rel_l2(a - inp.dprob0, ref - inp.dprob0) <= 1e-5
     distinct = len({a.tobytes() for a in atom})
     note("dprob atomic arm: %d distinct bit patterns in 20 runs" % distinct)
+    assert distinct > 1, "the atomic arm is bit-stable here, so the replay check could not fail"
 
 
 def test_exact_integer_inputs_match_integer_sum():
