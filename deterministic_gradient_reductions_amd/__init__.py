@@ -26,7 +26,7 @@ import threading
 
 __all__ = [
     "lib", "library_path", "DetError", "ColsumCfg", "IndexAddCfg", "DprobCfg", "WgradCfg", "Workspace",
-    "det_abi_version", "det_colsum", "det_colsum_da", "det_colsum_select_cfg", "det_colsum_workspace_size", "det_index_add",
+    "det_abi_version", "det_colsum", "det_colsum_da", "det_colsum_noalloc", "det_colsum_select_cfg", "det_colsum_workspace_size", "det_index_add",
     "det_index_add_workspace_size", "det_index_add_bad_ids", "det_grouped_dprob", "det_grouped_dprob_workspace_size",
     "det_grouped_wgrad_acc", "det_grouped_wgrad_acc_workspace_size", "det_grouped_wgrad_acc_bf16",
     "det_grouped_wgrad_acc_bf16_workspace_size", "det_grouped_dbias",
@@ -84,6 +84,8 @@ _SIGS = {
                     _P, _SZ, _INT, _P], _INT),
     "det_colsum_da": ([_P, _I64, _I64, _P, _I64, _I64, _INT, _P, _P, _I64, _I64, _P, _P, _P, _I64, _I64,
                        ctypes.POINTER(ColsumCfg), _P, _SZ, _INT, _P], _INT),
+    "det_colsum_noalloc": ([_P, _I64, _I64, _P, _I64, _I64, _INT, _P, _P, _I64, _I64, _P, _P,
+                            ctypes.POINTER(ColsumCfg), _INT, _P], _INT),
     "det_index_add_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(IndexAddCfg), _INT, ctypes.POINTER(_SZ)], _INT),
     "det_index_add": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _INT, ctypes.POINTER(IndexAddCfg), _P, _SZ, _INT,
                        _P], _INT),
@@ -261,6 +263,19 @@ def det_colsum(a, dg, A_log, dt_bias, dA_log, ddt_bias, cfg: ColsumCfg | None = 
 def det_colsum_da(a, dg, A_log, dt_bias, dA_log, ddt_bias, da, **kw) -> None:
     """det_colsum plus the elementwise da [T, H] (dtype of ``a``), overwritten."""
     det_colsum(a, dg, A_log, dt_bias, dA_log, ddt_bias, da=da, **kw)
+
+
+def det_colsum_noalloc(a, dg, A_log, dt_bias, dA_log, ddt_bias, cfg: ColsumCfg | None = None, atomic=False,
+                       stream=None) -> None:
+    """det_colsum with its slots in the library's static device scratch (no workspace, no allocation)."""
+    T, H = a.shape
+    if dg.dtype != a.dtype or tuple(dg.shape) != (T, H):
+        raise TypeError("dg must have the shape and dtype of a")
+    for t, n in ((A_log, "A_log"), (dt_bias, "dt_bias"), (dA_log, "dA_log"), (ddt_bias, "ddt_bias")):
+        _require(t, "f32", n, contiguous=True)
+    _check(lib().det_colsum_noalloc(_ptr(a), a.stride(0), a.stride(1), _ptr(dg), dg.stride(0), dg.stride(1),
+                                    _dtype_code(a), _ptr(A_log), _ptr(dt_bias), T, H, _ptr(dA_log), _ptr(ddt_bias),
+                                    ctypes.byref(cfg) if cfg else None, _atomic_flag(atomic), _stream_handle(stream)))
 
 
 # ------------------------------------------------------------------ index_add

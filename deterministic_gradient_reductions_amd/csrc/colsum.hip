@@ -17,6 +17,8 @@
 //
 // The per-element work is about 80 VALU operations (exp, log1p, two divisions),
 // so at large T the kernel is bound by vector ALU throughput, not HBM.
+#include <mutex>
+
 #include "common.hpp"
 #include "detmath.hpp"
 
@@ -266,11 +268,52 @@ extern "C" int det_colsum_workspace_size(int64_t T, int64_t H, const det_colsum_
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch of det_colsum_noalloc, for callers that cannot allocate. Each
+// GPU the library runs on holds its own copy of this array until the process
+// ends. Host code never passes the array's name to a kernel (on the host that
+// name is only a stand-in): the device address of each GPU's copy is looked up
+// once per device with hipGetSymbolAddress and kept here.
+namespace detgrad {
+namespace {
+constexpr size_t kNoAllocBytes = size_t(4) << 20;  // header + two slot arrays of up to 2 MiB - 128 B each
+}  // namespace
+}  // namespace detgrad
+
+static __device__ __align__(256) char scratch[detgrad::kNoAllocBytes];
+
+namespace detgrad {
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of this GPU's copy of `scratch` (the current device's).
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(DET_ERR_HIP, "colsum_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return set_error(DET_ERR_UNSUPPORTED, "colsum_noalloc: device %d", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return set_error(DET_ERR_HIP, "colsum_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(g_scratch_err[dev]));
+  *out = g_scratch_ptr[dev];
+  return DET_OK;
+}
+}  // namespace
+}  // namespace detgrad
+
+namespace detgrad {
 namespace {
 int colsum_entry(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_t dg_st, int64_t dg_sh, int in_dtype,
                  const float* A_log, const float* dt_bias, int64_t T, int64_t H, float* dA_log, float* ddt_bias,
                  void* da, int64_t da_st, int64_t da_sh, bool with_da, const det_colsum_cfg* cfg, void* ws,
-                 size_t ws_bytes, int atomic, void* stream) {
+                 size_t ws_bytes, int atomic, void* stream, bool noalloc = false) {
   if (int s = check_atomic_flag(atomic)) return s;
   if (T < 0 || H < 0) return set_error(DET_ERR_INVALID_ARG, "colsum: T and H must be >= 0");
   if (in_dtype != DET_BF16 && in_dtype != DET_F32)
@@ -285,7 +328,19 @@ int colsum_entry(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int6
   if (ceil_div(T, c.block_t) > 0x7FFFFFFF || ceil_div(H, c.block_h) > 65535)
     return set_error(DET_ERR_UNSUPPORTED, "colsum: problem too large for the launch grid");
   const size_t need = atomic ? 0 : ws_bytes_for(T, H, c);
-  if (int s = check_workspace(ws, ws_bytes, need)) return s;
+  if (noalloc) {
+    if (need > kNoAllocBytes)
+      return set_error(DET_ERR_WORKSPACE,
+                       "colsum_noalloc: the slots need %zu bytes, more than the %zu of the library's static scratch "
+                       "(use det_colsum with a workspace, or a larger block_t)",
+                       need, static_cast<size_t>(kNoAllocBytes));
+    if (need > 0) {
+      if (int s = noalloc_scratch(&ws)) return s;
+      ws_bytes = kNoAllocBytes;
+    }
+  } else if (int s = check_workspace(ws, ws_bytes, need)) {
+    return s;
+  }
   const Range o1 = range1d(dA_log, H * 4), o2 = range1d(ddt_bias, H * 4);
   const size_t esz = in_dtype == DET_F32 ? 4 : 2;
   const Range ins[] = {range_strided(a, T, H, a_st, a_sh, esz), range_strided(dg, T, H, dg_st, dg_sh, esz),
@@ -329,6 +384,7 @@ int colsum_entry(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int6
   return check_launch(with_da ? "det_colsum_da" : "det_colsum");
 }
 }  // namespace
+}  // namespace detgrad
 
 extern "C" int det_colsum(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_t dg_st, int64_t dg_sh,
                           int in_dtype, const float* A_log, const float* dt_bias, int64_t T, int64_t H, float* dA_log,
@@ -344,4 +400,15 @@ extern "C" int det_colsum_da(const void* a, int64_t a_st, int64_t a_sh, const vo
                              const det_colsum_cfg* cfg, void* ws, size_t ws_bytes, int atomic, void* stream) {
   return colsum_entry(a, a_st, a_sh, dg, dg_st, dg_sh, in_dtype, A_log, dt_bias, T, H, dA_log, ddt_bias, da, da_st,
                       da_sh, true, cfg, ws, ws_bytes, atomic, stream);
+}
+
+// For callers that cannot allocate: det_colsum with its slots in the library's
+// static scratch (see noalloc_scratch). Every call on a GPU shares that GPU's
+// scratch, so calls that can overlap on one GPU race.
+extern "C" int det_colsum_noalloc(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_t dg_st,
+                                  int64_t dg_sh, int in_dtype, const float* A_log, const float* dt_bias, int64_t T,
+                                  int64_t H, float* dA_log, float* ddt_bias, const det_colsum_cfg* cfg, int atomic,
+                                  void* stream) {
+  return colsum_entry(a, a_st, a_sh, dg, dg_st, dg_sh, in_dtype, A_log, dt_bias, T, H, dA_log, ddt_bias, nullptr, 1, 1,
+                      false, cfg, nullptr, 0, atomic, stream, true);
 }

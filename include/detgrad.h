@@ -134,6 +134,20 @@ int det_colsum_da(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int
                   float* ddt_bias, void* da, int64_t da_st, int64_t da_sh, const det_colsum_cfg* cfg, void* ws,
                   size_t ws_bytes, int atomic, void* stream);
 
+/* det_colsum_noalloc: det_colsum for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without a workspace, the same bits on
+ * both arms. The slots live in a static device array of the library, 4 MiB
+ * per GPU, held until the process ends. A problem whose slots need more
+ * (256 + 2 * ceil(T / block_t) * H * 4 bytes, rounded up to 256 per slot
+ * array) returns DET_ERR_WORKSPACE before any launch. The call allocates
+ * nothing. Every call on one GPU shares that GPU's array, so two calls that
+ * can run at the same time on one GPU (two streams, two threads) race and
+ * must be ordered by the caller. */
+int det_colsum_noalloc(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int64_t dg_st, int64_t dg_sh,
+                       int in_dtype, const float* A_log, const float* dt_bias, int64_t T, int64_t H, float* dA_log,
+                       float* ddt_bias, const det_colsum_cfg* cfg, int atomic, void* stream);
+
 /* ------------------------------------------------------------------------
  * det_index_add: out[ids[p]] += src[p] without float atomics.
  * Megatron-LM PR #7441 (DSv4 deterministic mode), source 3: the sparse-
