@@ -12,9 +12,14 @@ workload with inputs resident in HBM:
 The timed region is exactly K steps between two device synchronisations;
 ``value`` is the step's algorithmic bytes divided by the step time (GB/s).
 Per-kernel figures (absolute GB/s or TFLOP/s, fraction of peak, deterministic
-over atomic time ratio with a bootstrap 95% CI, 20-replay bit identity) are
-measured after the step loop. One JSON line goes to stdout; progress goes to
-stderr.
+over atomic time ratio with a bootstrap 95% CI, 20-replay bit identity and the
+atomic arm's count of distinct results) are measured after the step loop, and
+beside the step: grouped dbias, the canonical top-k, the gate backward at
+T = 4096 x H = 16 and at T = 4,194,304 x H = 32 (a bandwidth-sized companion)
+and every gate tile configuration. One JSON line goes to stdout; progress goes
+to stderr.
+
+    python bench.py --only wgrad --steps 20   # one entry point, K timed calls (for profilers)
 """
 from __future__ import annotations
 
@@ -50,6 +55,8 @@ def parse():
                     help="after the measurements, copy a 256 MiB buffer three times (a kernel of known traffic, "
                          "against which hardware byte counters are scaled)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--only", default="", help="comma-separated entry points: run only their deterministic calls "
+                    "(warmup + steps), print their mean times and exit (for profiler runs)")
     return ap.parse_args()
 
 
@@ -57,10 +64,14 @@ def parse():
 class Workload:
     """Device inputs and algorithmic cost of one entry point."""
 
-    def __init__(self, name, call_det, call_atomic, reset, read_out, nbytes, flops=0.0, bound="hbm"):
+    def __init__(self, name, call_det, call_atomic, reset, read_out, nbytes, flops=0.0, bound="hbm", note="",
+                 extra_arms=None, valu_ops=0.0):
         self.name, self.call_det, self.call_atomic = name, call_det, call_atomic
         self.reset, self.read_out = reset, read_out
         self.nbytes, self.flops, self.bound = nbytes, flops, bound
+        self.note = note                    # what the atomic arm is
+        self.extra_arms = extra_arms or {}  # label -> (det call, atomic call) timed the same way
+        self.valu_ops = valu_ops            # VALU lane-operations per call (ALU-bound kernels)
 
 
 def build_workloads():
@@ -125,20 +136,28 @@ def build_workloads():
     G, X, woffs, mg = bf(wg.G), bf(wg.X), i32(wg.offs), f32(wg.main_grad0)
     mg0 = mg.clone()
     wws = dg.Workspace(dg.det_grouped_wgrad_acc_workspace_size(T_total, 8, 1408, 2048))
+    # The comparison arm is split-K with float atomics, 4 K tiles (2048 rows) per split: with one split per
+    # expert every element receives a single atomic add per call and the arm is bit-stable, so the smallest
+    # splits whose results vary from run to run (1, 2 or 4 K tiles; 4 is the fastest) are the honest arm.
+    split4 = dg.WgradCfg(256, 256, 512, 4)
+    ws4 = dg.Workspace(dg.det_grouped_wgrad_acc_workspace_size(T_total, 8, 1408, 2048, split4))
     out.append(Workload(
         "wgrad",
         lambda: dg.det_grouped_wgrad_acc(mg, G, X, woffs, ws=wws),
-        lambda: dg.det_grouped_wgrad_acc(mg, G, X, woffs, atomic=True),
+        lambda: dg.det_grouped_wgrad_acc(mg, G, X, woffs, cfg=split4, atomic=True),
         lambda: mg.copy_(mg0),
         lambda: mg.cpu().numpy(),
         nbytes=T_total * (1408 + 2048) * 2 + 8 * 1408 * 2048 * 4 * 2,
-        flops=2.0 * 1408 * 2048 * T_total, bound="mfma"))
+        flops=2.0 * 1408 * 2048 * T_total, bound="mfma",
+        note="deterministic: default call (one split per expert); atomic: split-K with 4 K tiles per split",
+        extra_arms={"same_split_4": (lambda: dg.det_grouped_wgrad_acc(mg, G, X, woffs, cfg=split4, ws=ws4),
+                                     lambda: dg.det_grouped_wgrad_acc(mg, G, X, woffs, cfg=split4, atomic=True))}))
     return out
 
 
 def build_extra_workloads():
-    """Entry points measured beside the step (not part of it): grouped dbias at the dprob shapes
-    and the canonical compact top-k."""
+    """Entry points measured beside the step (not part of it): grouped dbias at the dprob shapes, the
+    canonical compact top-k, and the gate backward at the small size and at the bandwidth companion."""
     import torch
     import deterministic_gradient_reductions_amd as dg
     import workloads as W
@@ -155,7 +174,48 @@ def build_extra_workloads():
         lambda: d.copy_(d0),
         lambda: d.cpu().numpy(),
         nbytes=db.M * db.N * 2 + 8 * db.N * 4 * 2),
-        topk_workload()]
+        topk_workload(), colsum_workload(4096, 16, "colsum_tiny"),
+        colsum_workload(4 * 1024 * 1024, 32, "colsum_companion", device_inputs=True)]
+
+
+# VALU lane-operations per (t, h) element of the gate backward: the VALU instructions the colsum kernel
+# executes per element (the detmath sequences of exp, log1p and two divisions, the two products and the
+# pairwise tree), measured with the SQ_INSTS_VALU counter at the bandwidth-sized companion: 238,354,432 wave
+# instructions x 64 lanes / (4,194,304 x 32) elements.
+COLSUM_VALU_OPS_PER_ELEM = 113.7
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # non-packed fp32 lane-operations: 39.3 T/s
+
+
+def colsum_workload(T, H, name, device_inputs=False, cfg=None):
+    """The gate backward at another size (beside the step). ``device_inputs`` draws a and dg on the GPU
+    (the bandwidth companion has 512 MiB of inputs; its results are timed, not compared)."""
+    import torch
+    import deterministic_gradient_reductions_amd as dg
+    import workloads as W
+    if device_inputs:
+        gen = torch.Generator(device="cuda").manual_seed(11)
+        a = torch.randn((T, H), generator=gen, device="cuda").to(torch.bfloat16)
+        dgv = torch.randn((T, 2 * H), generator=gen, device="cuda").to(torch.bfloat16)[:, H:]
+        Al = torch.empty(H, device="cuda").uniform_(-2.0, 1.0, generator=gen)
+        db = torch.empty(H, device="cuda").uniform_(-1.0, 1.0, generator=gen)
+        o1, o2 = torch.zeros(H, device="cuda"), torch.zeros(H, device="cuda")
+    else:
+        g = W.gate_inputs(T, H, seed=1, out_init="normal")
+        bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).cuda().view(torch.bfloat16)
+        a, dgv = bf(g.a), bf(g.dg_base)[:, H:]
+        Al, db = torch.from_numpy(g.A_log).cuda(), torch.from_numpy(g.dt_bias).cuda()
+        o1, o2 = torch.from_numpy(g.dA_log0).cuda(), torch.from_numpy(g.ddt_bias0).cuda()
+    o10, o20 = o1.clone(), o2.clone()
+    c = cfg or dg.det_colsum_select_cfg(T, H)
+    ws = dg.Workspace(dg.det_colsum_workspace_size(T, H, c))
+    return Workload(
+        name,
+        lambda: dg.det_colsum(a, dgv, Al, db, o1, o2, cfg=c, ws=ws),
+        lambda: dg.det_colsum(a, dgv, Al, db, o1, o2, cfg=c, atomic=True),
+        lambda: (o1.copy_(o10), o2.copy_(o20)),
+        lambda: torch.cat([o1, o2]).cpu().numpy(),
+        nbytes=T * H * 4 + H * 4 * 6, bound="alu", note="tile %dx%d" % (c.block_t, c.block_h),
+        valu_ops=COLSUM_VALU_OPS_PER_ELEM * T * H)
 
 
 def topk_workload():
@@ -169,7 +229,7 @@ def topk_workload():
     lg = torch.from_numpy(tk.logits).cuda()
     io, lo, po = torch.empty_like(ids), torch.empty_like(lg), torch.empty_like(lg)
     call = lambda: dg.det_topk_canonicalize(ids, lg, io, lo, po)
-    return Workload("topk_canon", call, call, lambda: po.zero_(),
+    return Workload("topk_canon", call, None, lambda: po.zero_(),
                     lambda: torch.cat([io.view(torch.float32).flatten(), lo.flatten(), po.flatten()]).cpu().numpy(),
                     nbytes=tk.ids.size * (4 + 4 + 4 + 4 + 4))
 
@@ -183,26 +243,32 @@ def bootstrap_ratio_ci(det, atom, n=2000, seed=0):
     return float(np.percentile(r, 2.5)), float(np.percentile(r, 97.5))
 
 
-def per_kernel(wl, reps, flush):
+def time_pairs(call_det, call_atomic, reps, flush):
+    """HIP-event times (us) of both arms, interleaved in pairs; call_atomic may be None."""
     import torch
     det_t, atom_t = [], []
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for _ in range(3):
-        wl.call_det(); wl.call_atomic()
+        call_det()
+        if call_atomic:
+            call_atomic()
     torch.cuda.synchronize()
     for r in range(reps):
         flush()
-        ev[0].record(); wl.call_det(); ev[1].record()
-        flush()
-        ev[2].record(); wl.call_atomic(); ev[3].record()
+        ev[0].record(); call_det(); ev[1].record()
+        if call_atomic:
+            flush()
+            ev[2].record(); call_atomic(); ev[3].record()
         torch.cuda.synchronize()
         det_t.append(ev[0].elapsed_time(ev[1]) * 1e3)
-        atom_t.append(ev[2].elapsed_time(ev[3]) * 1e3)
+        if call_atomic:
+            atom_t.append(ev[2].elapsed_time(ev[3]) * 1e3)
     return np.array(det_t), np.array(atom_t)
 
 
 def replay_check(wl, n=20):
-    """n deterministic replays from the same start state under side-stream load: all bit patterns equal?"""
+    """n deterministic replays from the same start state under side-stream load: all bit patterns equal?
+    Also the number of distinct results of the atomic arm over n runs (None without an atomic arm)."""
     import torch
     side = torch.cuda.Stream()
     a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
@@ -214,6 +280,8 @@ def replay_check(wl, n=20):
         wl.reset(); wl.call_det()
         torch.cuda.synchronize()
         pats.add(hashlib.sha1(wl.read_out().view(np.uint32).tobytes()).hexdigest())
+        if wl.call_atomic is None:
+            continue
         with torch.cuda.stream(side):
             for _ in range(4):
                 a.mul_(1.0000001)
@@ -221,60 +289,139 @@ def replay_check(wl, n=20):
         torch.cuda.synchronize()
         apats.add(hashlib.sha1(wl.read_out().view(np.uint32).tobytes()).hexdigest())
     wl.reset()
-    return len(pats) == 1, len(apats)
+    return len(pats) == 1, (len(apats) if wl.call_atomic is not None else None)
+
+
+def kernel_record(w, reps, flush, in_step_us=None):
+    det_cold, atom_cold = time_pairs(w.call_det, w.call_atomic, reps, flush)
+    det_warm, atom_warm = time_pairs(w.call_det, w.call_atomic, reps, lambda: None)
+    same, apats = replay_check(w)
+    med = float(np.median(det_cold))
+    k = {
+        "us_in_step": round(float(in_step_us), 3) if in_step_us is not None else None,
+        "us_det_cold_median": round(med, 3),
+        "us_det_cold_p10_p90": [round(float(np.percentile(det_cold, 10)), 3),
+                                round(float(np.percentile(det_cold, 90)), 3)],
+        "us_det_warm_median": round(float(np.median(det_warm)), 3),
+        "GB_per_s_cold": round(w.nbytes / med / 1e3, 2),
+        "frac_hbm_peak_cold": round(w.nbytes / med / 1e3 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": int(w.nbytes),
+        "replay_bit_identical_20": bool(same),
+    }
+    if w.call_atomic is not None:
+        lo, hi = bootstrap_ratio_ci(det_cold, atom_cold)
+        k.update({
+            "us_atomic_cold_median": round(float(np.median(atom_cold)), 3),
+            "us_atomic_warm_median": round(float(np.median(atom_warm)), 3),
+            "det_over_atomic": round(med / float(np.median(atom_cold)), 4),
+            "det_over_atomic_ci95": [round(lo, 4), round(hi, 4)],
+            "atomic_distinct_patterns_20": int(apats),
+        })
+    else:
+        k["atomic_arm"] = None  # deterministic by construction, nothing is accumulated
+    if w.note:
+        k["note"] = w.note
+    if w.flops:
+        k["TFLOP_per_s_cold"] = round(w.flops / med / 1e6, 2)
+        k["frac_mfma_peak_cold"] = round(w.flops / med / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4)
+    if w.valu_ops:
+        k["valu_Tops_cold"] = round(w.valu_ops / med / 1e6, 2)
+        k["frac_valu_peak_cold"] = round(w.valu_ops / med / 1e6 / VALU_PEAK_TOPS, 4)
+    for label, (cd, ca) in w.extra_arms.items():
+        d2, a2 = time_pairs(cd, ca, reps, flush)
+        lo, hi = bootstrap_ratio_ci(d2, a2)
+        k[label] = {"us_det_cold_median": round(float(np.median(d2)), 3),
+                    "us_atomic_cold_median": round(float(np.median(a2)), 3),
+                    "det_over_atomic": round(float(np.median(d2) / np.median(a2)), 4),
+                    "det_over_atomic_ci95": [round(lo, 4), round(hi, 4)]}
+    return k
+
+
+def colsum_tile_sweep(reps, flush):
+    """Cold median (us) of the deterministic gate backward at T = 16384, H = 32 (strided dg) for every tile
+    configuration block_t x block_h in {64, 128, 256} x {8, 16, 32}."""
+    import deterministic_gradient_reductions_amd as dg
+    out = {}
+    for bt in (64, 128, 256):
+        for bh in (8, 16, 32):
+            w = colsum_workload(16384, 32, "sweep", cfg=dg.ColsumCfg(bt, bh))
+            d, _ = time_pairs(w.call_det, None, reps, flush)
+            out["%dx%d" % (bt, bh)] = round(float(np.median(d)), 3)
+    return out
 
 
 # ------------------------------------------------------------- CPU baseline
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(target_s):
-    """Time the CPU oracle, single-threaded, on bounded samples of the same workloads."""
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
+    """Time the CPU oracle on the host's cores, on bounded samples of the step's workloads.
+
+    The oracle is run as it stands; independent parts go to a thread pool (numpy releases the GIL): gate
+    heads and dprob rows are independent, index_add is one call (its stable sort spans all ids), and the
+    matrix-core chains of the weight gradient run in the oracle's C file on OpenMP threads. The weight gradient is sampled (output rows of
+    every expert) and scaled to the full problem by the sampled fraction of its chains."""
+    import concurrent.futures as cf
     import workloads as W
-    from oracle import colsum as oc, dprob as od, index_add as oi, wgrad as ow
-    samples = []
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    try:
-        t0 = time.perf_counter()
-        spent = 0.0
-        g = W.gate_inputs(16384, 32, seed=2)
-        t = time.perf_counter(); oc.colsum(g.a, g.dg, g.A_log, g.dt_bias, g.dA_log0, g.ddt_bias0, 64)
-        samples.append(("colsum T=16384 H=32 (full)", 16384 * 32 * 4, time.perf_counter() - t))
-        dp = W.dprob_inputs(seed=4)
-        t = time.perf_counter(); od.grouped_dprob(dp.dprob0, dp.dY, dp.C, dp.offs)
-        samples.append(("dprob 16384x2048 (full)", 16384 * 2048 * 4 + 16384 * 8, time.perf_counter() - t))
-        del dp
-        ia = W.index_add_inputs(seed=3)
-        nv = int(np.count_nonzero(ia.ids >= 0))
-        t = time.perf_counter(); oi.index_add(ia.out0, ia.ids, ia.src, 256)
-        samples.append(("index_add 4096x512 -> 8192x128 (full)", ia.ids.size * 4 + nv * 256 + 8192 * 128 * 8,
-                        time.perf_counter() - t))
-        del ia
-        spent = sum(x[2] for x in samples)
-        # wgrad: as many experts of the full workload as fit in the remaining compute budget
-        wg = W.wgrad_inputs(seed=5)
-        done_e, done_tok, t_w = 0, 0, 0.0
-        for e in range(8):
-            if spent + t_w > target_s:
-                break
-            t = time.perf_counter()
-            ow.grouped_wgrad_acc(wg.main_grad0, wg.G, wg.X, wg.offs, experts=[e])
-            t_w += time.perf_counter() - t
-            done_e += 1
-            done_tok += int(wg.offs[e + 1] - wg.offs[e])
-        if done_e:
-            samples.append(("wgrad %d of 8 experts, %d tokens (float64 matrix-product chain)" % (done_e, done_tok),
-                            done_tok * 3456 * 2 + done_e * 1408 * 2048 * 8, t_w))
-        log("cpu oracle: %.1f s of compute, %.1f s with input generation" % (
-            sum(x[2] for x in samples), time.perf_counter() - t0))
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
+    from oracle import _cmodel, colsum as oc, dprob as od, index_add as oi, wgrad as ow
+    n = _cmodel.threads()
+    pool = cf.ThreadPoolExecutor(n)
+    samples = []   # (label, algorithmic bytes of the full problem, CPU seconds for the full problem)
+
+    def split(k):
+        return [(i * k // n, (i + 1) * k // n) for i in range(n) if (i + 1) * k // n > i * k // n]
+
+    t0 = time.perf_counter()
+    g = W.gate_inputs(16384, 32, seed=2)
+    t = time.perf_counter()
+    list(pool.map(lambda r: oc.colsum(g.a[:, r[0]:r[1]], g.dg[:, r[0]:r[1]], g.A_log[r[0]:r[1]],
+                                      g.dt_bias[r[0]:r[1]], g.dA_log0[r[0]:r[1]], g.ddt_bias0[r[0]:r[1]], 64),
+                  split(32)))
+    samples.append(("colsum T=16384 H=32 (full, heads split)", 16384 * 32 * 4 + 32 * 4 * 6, time.perf_counter() - t))
+    dp = W.dprob_inputs(seed=4)
+    t = time.perf_counter()
+    list(pool.map(lambda r: od.grouped_dprob(dp.dprob0[r[0]:r[1]], dp.dY[r[0]:r[1]], dp.C[r[0]:r[1]],
+                                             np.array([0, r[1] - r[0]], np.int32)), split(16384)))
+    samples.append(("dprob 16384x2048 (full, rows split)", 16384 * 2048 * 4 + 16384 * 8, time.perf_counter() - t))
+    del dp
+    ia = W.index_add_inputs(seed=3)
+    nv = int(np.count_nonzero(ia.ids >= 0))
+    nt = int(np.count_nonzero(np.bincount(ia.ids[ia.ids >= 0], minlength=8192)))
+    t = time.perf_counter()
+    oi.index_add(ia.out0, ia.ids, ia.src, 256)   # one call: its stable sort is over all ids
+    samples.append(("index_add 4096x512 -> 8192x128 (full, one thread)", ia.ids.size * 4 + nv * 256 + nt * 128 * 8,
+                    time.perf_counter() - t))
+    del ia
+    spent = sum(x[2] for x in samples)
+    wg = W.wgrad_inputs(seed=5)
+    T_total = int(wg.offs[-1])
+    rows = 8
+    t = time.perf_counter()
+    ow.grouped_wgrad_acc(wg.main_grad0, wg.G, wg.X, wg.offs, rows=np.arange(rows))
+    tw = time.perf_counter() - t
+    if spent + tw < target_s:   # a larger sample while the budget allows
+        rows = int(min(1408, max(rows, rows * (target_s - spent) / max(tw, 1e-3) * 0.8)))
+        t = time.perf_counter()
+        ow.grouped_wgrad_acc(wg.main_grad0, wg.G, wg.X, wg.offs, rows=np.arange(rows))
+        tw = time.perf_counter() - t
+    samples.append(("wgrad E=8 %d tokens: %d of 1408 output rows of every expert (matrix-core model chains), "
+                    "scaled x%.1f" % (T_total, rows, 1408 / rows),
+                    T_total * (1408 + 2048) * 2 + 8 * 1408 * 2048 * 8, tw * 1408 / rows))
+    pool.shutdown()
+    log("cpu oracle: %.1f s of compute, %.1f s with input generation, %d threads" % (
+        spent + tw, time.perf_counter() - t0, n))
     nbytes = sum(s[1] for s in samples)
     secs = sum(s[2] for s in samples)
-    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "; ".join("%s: %.2f s" % (s[0], s[2]) for s in samples)}
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": "%s; threads %d on %s" % ("; ".join("%s: %.2f s" % (s[0], s[2]) for s in samples), n,
+                                               _cpu_model())}
 
 
 def traffic_for(kernel_name):
@@ -292,6 +439,18 @@ def traffic_for(kernel_name):
         return None
 
 
+def copy_calibration():
+    """A plain copy of known size (reads and writes exactly COPY_BYTES each), three times: the kernel against
+    which hardware byte counters are scaled."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 copies of %d bytes" % COPY_BYTES)
+
+
 # --------------------------------------------------------------------- main
 def main():
     args = parse()
@@ -301,7 +460,16 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.init()
+    only = set(x for x in args.only.split(",") if x)
     wls = build_workloads()
+    if only:
+        pool = wls + (build_extra_workloads() if only - {w.name for w in wls} else [])
+        unknown = only - {w.name for w in pool}
+        if unknown:
+            print("--only: unknown entry points %s" % sorted(unknown), file=sys.stderr)
+            sys.exit(2)
+        wls = [w for w in pool if w.name in only]
+        del pool
     # Cold cache: read a 1 GiB buffer (4x the 256 MB last-level cache) between
     # timed runs. A read leaves only clean lines behind, so the timed kernel
     # pays no write-back of someone else's dirty data.
@@ -334,36 +502,23 @@ def main():
         in_step[wls[k % len(wls)].name].append(evs[k][0].elapsed_time(evs[k][1]) * 1e3)
     step_bytes = sum(w.nbytes for w in wls)
     log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
+    if only:
+        print(json.dumps({"only": sorted(only), "steps": args.steps, "ms_per_step": round(ms_per_step, 4),
+                          "us_per_call": {k: round(float(np.mean(v)), 3) for k, v in in_step.items()}}), flush=True)
+        if args.copy_calibration:
+            copy_calibration()
+        return
 
     kernels, outside = {}, {}
-    extra = build_extra_workloads()
-    for w in wls + extra:
-        det_cold, atom_cold = per_kernel(w, args.reps, flush)
-        det_warm, atom_warm = per_kernel(w, args.reps, lambda: None)
-        same, apats = replay_check(w)
-        lo, hi = bootstrap_ratio_ci(det_cold, atom_cold)
-        med = float(np.median(det_cold))
-        k = {
-            "us_in_step": round(float(np.mean(in_step[w.name])), 3) if w.name in in_step else None,
-            "us_det_cold_median": round(med, 3),
-            "us_det_cold_p10_p90": [round(float(np.percentile(det_cold, 10)), 3),
-                                    round(float(np.percentile(det_cold, 90)), 3)],
-            "us_atomic_cold_median": round(float(np.median(atom_cold)), 3),
-            "us_det_warm_median": round(float(np.median(det_warm)), 3),
-            "us_atomic_warm_median": round(float(np.median(atom_warm)), 3),
-            "det_over_atomic": round(med / float(np.median(atom_cold)), 4),
-            "det_over_atomic_ci95": [round(lo, 4), round(hi, 4)],
-            "GB_per_s_cold": round(w.nbytes / med / 1e3, 2),
-            "frac_hbm_peak_cold": round(w.nbytes / med / 1e3 / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": int(w.nbytes),
-            "replay_bit_identical_20": bool(same),
-            "atomic_distinct_patterns_20": int(apats),
-        }
-        if w.flops:
-            k["TFLOP_per_s_cold"] = round(w.flops / med / 1e6, 2)
-            k["frac_mfma_peak_cold"] = round(w.flops / med / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4)
-        (kernels if w.name in in_step else outside)[w.name] = k
-        log("%-9s %s" % (w.name, json.dumps(k)))
+    for w in wls:
+        kernels[w.name] = kernel_record(w, args.reps, flush, float(np.mean(in_step[w.name])))
+        log("%-9s %s" % (w.name, json.dumps(kernels[w.name])))
+    for w in build_extra_workloads():
+        outside[w.name] = kernel_record(w, args.reps, flush)
+        log("%-9s %s" % (w.name, json.dumps(outside[w.name])))
+        del w
+    outside["colsum_tile_sweep_us"] = colsum_tile_sweep(args.reps, flush)
+    log("colsum sweep %s" % json.dumps(outside["colsum_tile_sweep_us"]))
 
     # roofline of the dominant kernel: the entry point with the largest share of the step
     dom = max(wls, key=lambda w: np.mean(in_step[w.name]))
@@ -396,13 +551,7 @@ def main():
         "kernels_outside_step": outside,
     }
     if args.copy_calibration:
-        # a plain copy of known size: reads and writes exactly COPY_BYTES each
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 copies of %d bytes" % COPY_BYTES)
+        copy_calibration()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(res), flush=True)
