@@ -109,6 +109,25 @@ def literal_sequential_index_add(out0, ids, src):
     return out
 
 
+def indexer_dk(dk0, ids, predict, target, q, scale, chunk_rows):
+    """Fused indexer dK, one slot at a time: kept targets clamped below at the float32 nearest e^-100 on
+    valid slots, the row sum left to right, the slot coefficient, its source row c * q, then the chunked
+    index_add above (ids, predict, target [Q][K]; q [Q][D] bf16 bits or float32 values)."""
+    n_rows = len(dk0)
+    e100 = np.array([27], np.uint32).view(np.float32)[0]
+    Q, K = len(ids), len(ids[0])
+    flat_ids, src = [], []
+    for r in range(Q):
+        valid = [0 <= int(ids[r][j]) < n_rows for j in range(K)]
+        kept = [(F(target[r][j]) if F(target[r][j]) > e100 else e100) if valid[j] else F(0.0) for j in range(K)]
+        S = fold(kept)
+        for j in range(K):
+            c = F(F(F(F(predict[r][j]) * S) - kept[j]) * F(scale)) if valid[j] else F(0.0)
+            flat_ids.append(int(ids[r][j]))
+            src.append([F(c * _gate(v)) for v in q[r]])
+    return index_add(dk0, flat_ids, src, chunk_rows)
+
+
 def wgrad_exact_integer(main_grad0, G, X, offs):
     """For small-integer inputs: main_grad0 + exact integer G_e^T X_e, per element."""
     E, M, N = np.shape(main_grad0)

@@ -130,6 +130,62 @@ def index_add_inputs(Q: int = 4096, K: int = 512, n_rows: int = 8192, dim: int =
     return IndexAddInputs(n_rows, dim, ids, src, out0)
 
 
+# --------------------------------------------------------- fused indexer dK source
+@dataclass
+class IndexerDkInputs:
+    """Sparse-indexer dK with its source rows made from the score gradient:
+    per query row r and top-k slot j an id (-1 = padding), the indexer's
+    softmax ``predict`` over the row's valid slots, the attention ``target``
+    (rows summing to 0.5, a few entries below e^-100 or zero), the indexer
+    query rows ``q`` and the float32 normalisation ``scale``."""
+    n_rows: int
+    dim: int
+    ids: np.ndarray      # int32 [Q, K]
+    predict: np.ndarray  # float32 [Q, K]
+    target: np.ndarray   # float32 [Q, K]
+    q: np.ndarray        # uint16 [Q, D] bf16 bits
+    scale: np.float32
+    dk0: np.ndarray      # float32 [n_rows, D]
+
+
+def indexer_dk_inputs(Q: int = 4096, K: int = 512, n_rows: int = 8192, dim: int = 128, seed: int = 8,
+                      zipf_s: float = 1.1, pad_frac: float = 0.05, out_init: str = "zero",
+                      loss_coeff: float = 0.1, batch: int = 1, sm_scale=None, grad_loss: float = 1.0,
+                      integer: bool = False) -> IndexerDkInputs:
+    """Ids as for the index_add workload (Zipf over keys, duplicates, 5% padding); predict = softmax of
+    N(0,1) logits over the valid slots (float64, rounded once); target = U(0,1) weights normalised to 0.5
+    per row with 2% of slots replaced by 0, -0, subnormals or values below e^-100; q ~ N(0,1) bf16.
+    ``integer`` draws small dyadic predict, target and q and a power-of-two scale instead, so that every
+    step is exact."""
+    ids = zipf_ids(Q * K, n_rows, zipf_s, pad_frac, seed, 0).reshape(Q, K)
+    valid = (ids >= 0) & (ids < n_rows)
+    rng = _rng(seed, 1)
+    if integer:
+        predict = (rng.integers(0, 9, (Q, K)) / 8.0).astype(np.float32)
+        target = (rng.integers(1, 17, (Q, K)) / 16.0).astype(np.float32)
+        q = bf16_bits(rng.integers(-2, 3, (Q, dim)).astype(np.float32))
+        scale = np.float32(0.25)
+    else:
+        lg = rng.standard_normal((Q, K))
+        lg = np.where(valid, lg, -np.inf)
+        m = np.max(np.where(valid, lg, -1e300), axis=1, keepdims=True)
+        e = np.where(valid, np.exp(lg - m), 0.0)
+        predict = (e / np.maximum(e.sum(1, keepdims=True), 1e-300)).astype(np.float32)
+        w = rng.random((Q, K))
+        target = (0.5 * w / w.sum(1, keepdims=True)).astype(np.float32)
+        tiny = rng.random((Q, K)) < 0.02
+        tiny_vals = np.array([0.0, -0.0, 1e-45, 2.8e-45, 3.0e-44, 4.0e-44, 1e-40, 1e-30], np.float32)
+        target[tiny] = tiny_vals[rng.integers(0, len(tiny_vals), int(tiny.sum()))]
+        q = bf16_bits(_rng(seed, 2).standard_normal((Q, dim), dtype=np.float32))
+        sm = 1.0 / np.sqrt(dim) if sm_scale is None else sm_scale
+        scale = np.float32(loss_coeff / (batch * Q) * sm * grad_loss)
+    if out_init == "zero":
+        dk0 = np.zeros((n_rows, dim), np.float32)
+    else:
+        dk0 = _rng(seed, 3).standard_normal((n_rows, dim), dtype=np.float32)
+    return IndexerDkInputs(n_rows, dim, ids.astype(np.int32), predict, target, q, scale, dk0)
+
+
 # -------------------------------------------------------------------------- dprob
 @dataclass
 class DprobInputs:
