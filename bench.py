@@ -174,7 +174,7 @@ def build_extra_workloads():
         lambda: d.copy_(d0),
         lambda: d.cpu().numpy(),
         nbytes=db.M * db.N * 2 + 8 * db.N * 4 * 2),
-        topk_workload(), colsum_workload(4096, 16, "colsum_tiny"),
+        topk_workload(), indexer_dk_workload(), colsum_workload(4096, 16, "colsum_tiny"),
         colsum_workload(4 * 1024 * 1024, 32, "colsum_companion", device_inputs=True)]
 
 
@@ -216,6 +216,32 @@ def colsum_workload(T, H, name, device_inputs=False, cfg=None):
         lambda: torch.cat([o1, o2]).cpu().numpy(),
         nbytes=T * H * 4 + H * 4 * 6, bound="alu", note="tile %dx%d" % (c.block_t, c.block_h),
         valu_ops=COLSUM_VALU_OPS_PER_ELEM * T * H)
+
+
+def indexer_dk_workload():
+    """The fused sparse-indexer dK: 4096 query rows x top-k 512 Zipf ids into 8192 x 128, source rows made
+    from the clipped-KL score gradient and the bf16 query rows (no stored source rows)."""
+    import torch
+    import deterministic_gradient_reductions_amd as dg
+    import workloads as W
+    x = W.indexer_dk_inputs(seed=8, out_init="normal")
+    ids = torch.from_numpy(x.ids).cuda()
+    p, t = torch.from_numpy(x.predict).cuda(), torch.from_numpy(x.target).cuda()
+    q = torch.from_numpy(np.ascontiguousarray(x.q).view(np.int16)).cuda().view(torch.bfloat16)
+    dk = torch.from_numpy(x.dk0).cuda()
+    dk0 = dk.clone()
+    cfg = dg.IndexAddCfg(256)
+    ws = dg.Workspace(dg.det_indexer_dk_workspace_size(4096, 512, 128, 8192, cfg))
+    wsa = dg.Workspace(dg.det_indexer_dk_workspace_size(4096, 512, 128, 8192, cfg, atomic=True))
+    n_touched = int(np.count_nonzero(np.bincount(x.ids[x.ids >= 0], minlength=8192)))
+    return Workload(
+        "indexer_dk",
+        lambda: dg.det_indexer_dk(dk, ids, p, t, q, x.scale, cfg=cfg, ws=ws),
+        lambda: dg.det_indexer_dk(dk, ids, p, t, q, x.scale, cfg=cfg, atomic=True, ws=wsa),
+        lambda: dk.copy_(dk0),
+        lambda: dk.cpu().numpy(),
+        nbytes=x.ids.size * 12 + 4096 * 128 * 2 + n_touched * 128 * 8,
+        note="ids, predict, target per slot + the query rows once + touched dK rows read and written")
 
 
 def topk_workload():

@@ -10,6 +10,7 @@ every call raises.
 Functions (same names as the C ABI):
     det_colsum(a, dg, A_log, dt_bias, dA_log, ddt_bias, cfg=None, atomic=False)
     det_index_add(out, ids, src, cfg=None, atomic=False)
+    det_indexer_dk(dk, ids, predict, target, q, scale, cfg=None, atomic=False)
     det_grouped_dprob(dprob, dY, C, offs, cfg=None, atomic=False)
     det_grouped_wgrad_acc(main_grad, G, X, offs, cfg=None, atomic=False)
     det_grouped_dbias(dbias, dA, offs, cfg=None, atomic=False)
@@ -27,7 +28,7 @@ import threading
 __all__ = [
     "lib", "library_path", "DetError", "ColsumCfg", "IndexAddCfg", "DprobCfg", "WgradCfg", "Workspace",
     "det_abi_version", "det_colsum", "det_colsum_da", "det_colsum_noalloc", "det_colsum_select_cfg", "det_colsum_workspace_size", "det_index_add",
-    "det_index_add_workspace_size", "det_index_add_bad_ids", "det_grouped_dprob", "det_grouped_dprob_workspace_size",
+    "det_index_add_workspace_size", "det_index_add_bad_ids", "det_indexer_dk", "det_indexer_dk_workspace_size", "det_grouped_dprob", "det_grouped_dprob_workspace_size",
     "det_grouped_wgrad_acc", "det_grouped_wgrad_acc_workspace_size", "det_grouped_wgrad_acc_bf16",
     "det_grouped_wgrad_acc_bf16_workspace_size", "det_grouped_dbias",
     "det_grouped_dbias_workspace_size", "det_topk_canonicalize", "det_workspace_init", "det_detmath_eval", "det_mfma_eval",
@@ -90,6 +91,10 @@ _SIGS = {
     "det_index_add": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _INT, ctypes.POINTER(IndexAddCfg), _P, _SZ, _INT,
                        _P], _INT),
     "det_index_add_bad_ids": ([_P, _SZ, ctypes.POINTER(_I64), _P], _INT),
+    "det_indexer_dk_workspace_size": ([_I64, _I64, _I64, _I64, ctypes.POINTER(IndexAddCfg), _INT, ctypes.POINTER(_SZ)],
+                                      _INT),
+    "det_indexer_dk": ([_P, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _I64, _INT, ctypes.c_float,
+                        ctypes.POINTER(IndexAddCfg), _P, _SZ, _INT, _P], _INT),
     "det_grouped_dprob_workspace_size": ([_I64, _I64, ctypes.POINTER(DprobCfg), _INT, ctypes.POINTER(_SZ)], _INT),
     "det_grouped_dprob": ([_P, _P, _I64, _P, _I64, _I64, _I64, _P, _I32, ctypes.POINTER(DprobCfg), _P, _SZ, _INT,
                            _P], _INT),
@@ -315,6 +320,37 @@ def det_index_add_bad_ids(ws=None, stream=None) -> int:
     c = _I64()
     _check(lib().det_index_add_bad_ids(wp, wn, ctypes.byref(c), _stream_handle(stream)))
     return c.value
+
+
+# --------------------------------------------------------- fused indexer dK
+def det_indexer_dk_workspace_size(Q: int, K: int, dim: int, n_rows: int, cfg: IndexAddCfg | None = None,
+                                  atomic=False) -> int:
+    n = _SZ()
+    _check(lib().det_indexer_dk_workspace_size(Q, K, dim, n_rows, ctypes.byref(cfg) if cfg else None,
+                                               _atomic_flag(atomic), ctypes.byref(n)))
+    return n.value
+
+
+def det_indexer_dk(dk, ids, predict, target, q, scale: float, cfg: IndexAddCfg | None = None, atomic=False,
+                   ws=None, stream=None) -> None:
+    """dk[ids] += the clipped-KL score gradient times the query rows, in det_index_add's canonical order.
+    ids int32 [Q, K], predict and target float32 [Q, K] (contiguous), q bf16 [Q, D], dk float32 [R, D]."""
+    n_rows, dim = dk.shape
+    _require(dk, "f32", "dk", unit_col=True)
+    _require(ids, "i32", "ids", contiguous=True)
+    _require(predict, "f32", "predict", contiguous=True)
+    _require(target, "f32", "target", contiguous=True)
+    _require(q, "bf16", "q", unit_col=True)
+    Q, K = ids.shape
+    if tuple(predict.shape) != (Q, K) or tuple(target.shape) != (Q, K) or q.dim() != 2 or q.shape[0] != Q or \
+            q.shape[1] != dim:
+        raise ValueError("need ids, predict, target [Q, K], q [Q, D] and dk [R, D]")
+    need = det_indexer_dk_workspace_size(Q, K, dim, n_rows, cfg, atomic) if atomic in (0, 1, False, True) else 0
+    wp, wn = _workspace(need, ws, stream)
+    _check(lib().det_indexer_dk(_ptr(dk), n_rows, dim, dk.stride(0), _ptr(ids), _ptr(predict), _ptr(target), Q, K,
+                                _ptr(q), q.stride(0), DET_BF16, ctypes.c_float(float(scale)),
+                                ctypes.byref(cfg) if cfg else None, wp, wn, _atomic_flag(atomic),
+                                _stream_handle(stream)))
 
 
 # ---------------------------------------------------------------------- dprob

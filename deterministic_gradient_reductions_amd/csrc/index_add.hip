@@ -46,11 +46,12 @@ inline __host__ __device__ int hist_stride(int64_t n_rows) { return static_cast<
 constexpr int kMaxGroups = kMaxRows / 256;  // workgroups of the offsets kernel (one thread per id)
 
 struct Layout {
-  size_t hist, segtot, wg_tot, seg_off, chunk_off, full_off, chunk_desc, perm, scratch, total;
+  size_t hist, segtot, wg_tot, seg_off, chunk_off, full_off, chunk_desc, perm, scratch, coef, total;
   int64_t nblk, nseg, max_chunks;
 };
 
-Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L) {
+// coef: the fused indexer dK's per-slot coefficients [n_src] float32 follow.
+Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L, bool coef = false) {
   Layout l;
   l.nblk = ceil_div(n_src, kBlockPos);
   l.nseg = ceil_div(l.nblk, kSegBlocks);
@@ -65,6 +66,7 @@ Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L) {
   l.chunk_desc = o; o = align_up(o + static_cast<size_t>(l.max_chunks) * 16, 256);
   l.perm = o;      o = align_up(o + static_cast<size_t>(n_src) * 4, 256);
   l.scratch = o;   o = align_up(o + static_cast<size_t>(l.max_chunks * dim) * 4, 256);
+  l.coef = o;      o = coef ? align_up(o + static_cast<size_t>(n_src) * 4, 256) : o;
   l.total = o;
   return l;
 }
@@ -156,6 +158,17 @@ __device__ __forceinline__ uint32_t ceil_div_rcp(uint32_t n, uint32_t L, uint32_
   q += c1;
   r -= c1 * L;
   q += r >= L ? 1u : 0u;
+  return q;
+}
+
+// floor(n / K) for n < 2^31, with rcp = floor((2^32 - 1) / K) as above.
+__device__ __forceinline__ uint32_t floor_div_rcp(uint32_t n, uint32_t K, uint32_t rcp) {
+  uint32_t q = __umulhi(n, rcp);
+  uint32_t r = n - q * K;
+  const uint32_t c1 = r >= K ? 1u : 0u;
+  q += c1;
+  r -= c1 * K;
+  q += r >= K ? 1u : 0u;
   return q;
 }
 
@@ -663,14 +676,37 @@ __device__ __forceinline__ uint32_t zero_vec(uint32_t) { return 0u; }
 __device__ __forceinline__ uint2 zero_vec(uint2) { return make_uint2(0u, 0u); }
 __device__ __forceinline__ uint4 zero_vec(uint4) { return make_uint4(0u, 0u, 0u, 0u); }
 
-template <int DPL, int NPOS>
+// Source rows made on the fly (the fused indexer dK): source row p is
+// RN32(coef[p] * q[p / K]), q being the bf16 query rows (row stride q_ld).
+struct FusedSrc {
+  const float* coef;
+  uint32_t K, krcp;
+};
+
+__device__ __forceinline__ void add_scaled_bf16(float (&acc)[2], uint32_t v, float c) {
+  acc[0] = acc[0] + c * bf16_lo(v); acc[1] = acc[1] + c * bf16_hi(v);
+}
+__device__ __forceinline__ void add_scaled_bf16(float (&acc)[4], uint2 v, float c) {
+  acc[0] = acc[0] + c * bf16_lo(v.x); acc[1] = acc[1] + c * bf16_hi(v.x);
+  acc[2] = acc[2] + c * bf16_lo(v.y); acc[3] = acc[3] + c * bf16_hi(v.y);
+}
+__device__ __forceinline__ void add_scaled_bf16(float (&acc)[8], uint4 v, float c) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    acc[2 * k] = acc[2 * k] + c * bf16_lo(w[k]);
+    acc[2 * k + 1] = acc[2 * k + 1] + c * bf16_hi(w[k]);
+  }
+}
+
+template <int DPL, int NPOS, bool FUSED = false>
 __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict__ src, int64_t src_ld, int dim,
                                                       const int32_t* __restrict__ perm,
                                                       const uint32_t* __restrict__ chunk_off,
                                                       const int4* __restrict__ desc, int n_rows,
                                                       float* __restrict__ out, int64_t out_ld,
                                                       float* __restrict__ scratch, int64_t n_src,
-                                                      int64_t max_chunks) {
+                                                      int64_t max_chunks, FusedSrc fz) {
   typedef typename RowVec<DPL>::T V;
   const int lane = threadIdx.x & 63;
   const uint32_t w = static_cast<uint32_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -696,6 +732,19 @@ __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict
     const int32_t x = perm[ok ? r0 + 64 * i + lane : r0];
     pos[i] = ok ? x : 0;
   }
+  // fused source: each lane turns its positions into query rows and loads
+  // their coefficients once (rows past the chunk end take 1.0, see below)
+  int32_t qrow[NPOS];
+  float cf[NPOS];
+  if (FUSED) {
+#pragma unroll
+    for (int i = 0; i < NPOS; ++i) {
+      const bool ok = 64 * i + lane < len && pos[i] >= 0 && pos[i] < n_src;
+      const uint32_t pp = ok ? static_cast<uint32_t>(pos[i]) : 0u;
+      qrow[i] = static_cast<int32_t>(floor_div_rcp(pp, fz.K, fz.krcp));
+      cf[i] = ok ? fz.coef[pp] : 1.0f;
+    }
+  }
   // a single-chunk id adds into out directly: its out row is fetched now,
   // while the row loads are in flight
   float* const dst = slot < 0 ? out + static_cast<int64_t>(k) * out_ld + d0 : scratch + static_cast<int64_t>(slot) * dim + d0;
@@ -717,12 +766,25 @@ __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict
       V v[kB];
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        int64_t p = __builtin_amdgcn_readlane(pos[i], h + u);
-        p = (p >= 0 && p < n_src) ? p : 0;  // always a valid row
+        int64_t p;
+        if (FUSED) {
+          p = __builtin_amdgcn_readlane(qrow[i], h + u);  // a query row below Q
+        } else {
+          p = __builtin_amdgcn_readlane(pos[i], h + u);
+          p = (p >= 0 && p < n_src) ? p : 0;  // always a valid row
+        }
         v[u] = *reinterpret_cast<const V*>(src + p * src_ld + d0);
       }
+      if (FUSED) {
+        // past the chunk end: bf16 -0.0 times 1.0 is -0.0, which leaves every sum unchanged
 #pragma unroll
-      for (int u = 0; u < kB; ++u) add_bf16(acc, 64 * i + h + u < len ? v[u] : neg_zero_vec(v[u]));
+        for (int u = 0; u < kB; ++u)
+          add_scaled_bf16(acc, 64 * i + h + u < len ? v[u] : neg_zero_vec(v[u]),
+                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cf[i]), h + u)));
+      } else {
+#pragma unroll
+        for (int u = 0; u < kB; ++u) add_bf16(acc, 64 * i + h + u < len ? v[u] : neg_zero_vec(v[u]));
+      }
     }
   }
 #pragma unroll
@@ -1005,6 +1067,117 @@ __global__ __launch_bounds__(256) void ia_atomic(const int32_t* __restrict__ ids
   for (int i = 0; i < 8; ++i) unsafeAtomicAdd(o + i, v.get(i));
 }
 
+// ---- fused indexer dK: per-slot coefficients of the clipped-KL score gradient
+// (DSv4 page, source 3 fix). One wave per query row, four rows per workgroup.
+// Lane l holds slots 8 l .. 8 l + 7 of each 512-slot piece of the row (16-byte
+// loads of ids, target and predict, all issued at once) and turns its targets
+// into kept targets (max(target, e^-100) on a slot whose id lies in
+// [0, n_rows), +0 elsewhere and past K). The row sum S is then the ordered
+// chain over the slots, each value fetched from its lane with readlane (an
+// appended +0 never changes a non-empty sum); finally every slot gets
+// c = RN32(RN32(RN32(predict * S) - kept) * scale), and 0 on a dropped slot.
+constexpr uint32_t kEps100Bits = 0x0000001Bu;  // the float32 nearest e^-100 (27 * 2^-149)
+constexpr int kCoefPiece = 512;                // slots per piece: 64 lanes x 8
+constexpr int kCoefMaxPieces = 2;              // K <= 1024
+
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const int32_t* p, int32_t (&v)[8]) {
+  const int4 a = *reinterpret_cast<const int4*>(p), b = *reinterpret_cast<const int4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <int PIECES, bool VEC>
+__global__ __launch_bounds__(256) void ia_coef(const int32_t* __restrict__ ids, const float* __restrict__ predict,
+                                               const float* __restrict__ target, int64_t Q, int K, int n_rows,
+                                               float scale, float* __restrict__ coef) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= Q) return;  // wave-uniform
+  const int64_t base = r * K;
+  const float eps = __uint_as_float(kEps100Bits);
+  int32_t id[PIECES][8];
+  float tg[PIECES][8], pr[PIECES][8];
+#pragma unroll
+  for (int c = 0; c < PIECES; ++c) {
+    const int j0 = c * kCoefPiece + 8 * lane;
+    if (VEC && j0 + 8 <= K) {  // K % 8 == 0 here, so a piece's lane is all in or all out
+      load8(ids + base + j0, id[c]);
+      load8(target + base + j0, tg[c]);
+      load8(predict + base + j0, pr[c]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool in = j0 + e < K;
+        id[c][e] = in ? ids[base + j0 + e] : -1;
+        tg[c][e] = in ? target[base + j0 + e] : 0.0f;
+        pr[c][e] = in ? predict[base + j0 + e] : 0.0f;
+      }
+    }
+  }
+  float kept[PIECES][8];
+#pragma unroll
+  for (int c = 0; c < PIECES; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool valid = id[c][e] >= 0 && id[c][e] < n_rows;  // slots past K carry id -1
+      // max(target, eps) that keeps a NaN target, as numpy's maximum does
+      kept[c][e] = valid ? (!(tg[c][e] <= eps) ? tg[c][e] : eps) : 0.0f;
+    }
+  // S = ((-0 + kept_0) + kept_1) + ... in slot order; slot 512 c + 8 l + e sits in lane l, register (c, e)
+  float S = -0.0f;
+#pragma unroll
+  for (int c = 0; c < PIECES; ++c)
+#pragma unroll
+    for (int l = 0; l < 64; ++l)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) S = S + readlane(kept[c][e], l);
+#pragma unroll
+  for (int c = 0; c < PIECES; ++c) {
+    const int j0 = c * kCoefPiece + 8 * lane;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool valid = id[c][e] >= 0 && id[c][e] < n_rows;
+      const float g = pr[c][e] * S - kept[c][e];
+      o[e] = valid ? g * scale : 0.0f;
+    }
+    if (VEC && j0 + 8 <= K) {
+      *reinterpret_cast<float4*>(coef + base + j0) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(coef + base + j0 + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (j0 + e < K) coef[base + j0 + e] = o[e];
+    }
+  }
+}
+
+// Comparison arm of the fused indexer dK: every element of every valid slot's
+// source row RN32(c * q) added into dk with a hardware float atomic, no sort.
+template <int GS>
+__global__ __launch_bounds__(256) void ia_atomic_fused(const int32_t* __restrict__ ids, int64_t n_src,
+                                                       const uint16_t* __restrict__ q, int64_t q_ld, int dim,
+                                                       int n_rows, float* __restrict__ out, int64_t out_ld,
+                                                       FusedSrc fz) {
+  const int g = threadIdx.x / GS;
+  const int lg = threadIdx.x % GS;
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * (256 / GS) + g;
+  if (p >= n_src || 8 * lg >= dim) return;
+  const int32_t id = ids[p];
+  if (id < 0 || id >= n_rows) return;
+  const int d0 = 8 * lg;
+  const uint32_t row = floor_div_rcp(static_cast<uint32_t>(p), fz.K, fz.krcp);
+  const float c = fz.coef[p];
+  Row8<uint16_t> v;
+  v.load(q + static_cast<int64_t>(row) * q_ld + d0);
+  float* o = out + static_cast<int64_t>(id) * out_ld + d0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) unsafeAtomicAdd(o + i, c * v.get(i));
+}
+
 int group_size(int64_t dim) {
   const int64_t d8 = dim / 8;
   int gs = 1;
@@ -1029,6 +1202,90 @@ int check_shape(int64_t n_src, int64_t dim, int64_t n_rows) {
                      static_cast<long long>(n_rows));
   if (n_src > 0x7FFFFFFFLL) return set_error(DET_ERR_UNSUPPORTED, "index_add: n_src must be < 2^31");
   return DET_OK;
+}
+
+// Stages 1-6 on `stream` (the caller has validated every argument). With fz,
+// source row p is RN32(fz->coef[p] * src[p / fz->K]) (bf16 query rows, the
+// one-wave-per-chunk gather only: dim in {128, 256, 512}, L <= 1024).
+int pipeline(const Layout& l, void* ws, float* out, int64_t n_rows, int64_t dim, int64_t out_ld,
+             const int32_t* ids, int64_t n_src, const void* src, int64_t src_ld, bool f32, int L, hipStream_t st,
+             const FusedSrc* fz, const char* what) {
+  const auto* s16 = static_cast<const uint16_t*>(src);
+  const auto* s32 = static_cast<const float*>(src);
+  const int gs = group_size(dim);
+  const int nr = static_cast<int>(n_rows);
+  char* w = static_cast<char*>(ws);
+  auto* hdr = reinterpret_cast<uint32_t*>(w);
+  auto* hist = reinterpret_cast<uint16_t*>(w + l.hist);
+  const int hist_ld = hist_stride(n_rows);
+  auto* wg_tot = reinterpret_cast<uint32_t*>(w + l.wg_tot);
+  auto* seg_off = reinterpret_cast<uint32_t*>(w + l.seg_off);
+  auto* chunk_off = reinterpret_cast<uint32_t*>(w + l.chunk_off);
+  auto* full_off = reinterpret_cast<uint32_t*>(w + l.full_off);
+  auto* chunk_desc = reinterpret_cast<int4*>(w + l.chunk_desc);
+  auto* perm = reinterpret_cast<int32_t*>(w + l.perm);
+  auto* scratch = reinterpret_cast<float*>(w + l.scratch);
+  const size_t lds_count = static_cast<size_t>(hist_ld) * 4;
+  auto* segtot = reinterpret_cast<uint32_t*>(w + l.segtot);
+  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, hist_ld, hist, hdr);
+  hipLaunchKernelGGL(ia_prefix_seg, dim3(ceil_div(n_rows, 256), l.nseg), dim3(256), 0, st, hist, hist_ld, l.nblk, nr,
+                     segtot);
+  const uint32_t rcp = static_cast<uint32_t>(0xFFFFFFFFull / static_cast<uint64_t>(L));
+  const dim3 off_grid(static_cast<uint32_t>(ceil_div(n_rows, 256)));
+  hipLaunchKernelGGL(ia_totals, off_grid, dim3(256), 0, st, segtot, l.nseg, nr, L, rcp, wg_tot, seg_off);
+  hipLaunchKernelGGL(ia_offsets, off_grid, dim3(256), 0, st, nr, L, rcp, n_src, wg_tot, seg_off, chunk_off, full_off,
+                     chunk_desc, hdr);
+  switch (scatter_waves(n_rows)) {
+    case 4: launch_scatter<4>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
+    case 2: launch_scatter<2>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
+    default: launch_scatter<1>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
+  }
+  const int64_t grid_g = ceil_div(l.max_chunks, 256 / gs);
+#define DET_IA_TAIL_T(G, E, S)                                                                                  \
+  if (gs == G) {                                                                                                 \
+    if (L <= G * kPosPerLane)                                                                                    \
+      hipLaunchKernelGGL((ia_gather<G, E>), dim3(grid_g), dim3(256), 0, st, S, src_ld, (int)dim, perm, seg_off,  \
+                         chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);                           \
+    else                                                                                                         \
+      hipLaunchKernelGGL((ia_gather_long<G, E>), dim3(grid_g), dim3(256), 0, st, S, src_ld, (int)dim, perm,      \
+                         seg_off, chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);                  \
+  }
+#define DET_IA_TAIL(G)                   \
+  if (f32) {                             \
+    DET_IA_TAIL_T(G, float, s32)         \
+  } else {                               \
+    DET_IA_TAIL_T(G, uint16_t, s16)      \
+  }
+  const int dpl = (dim % 64 == 0) ? static_cast<int>(dim / 64) : 0;
+  // the one-wave-per-chunk gather is for bf16 rows; float32 rows take the lane-group gather
+  if (fz || (!f32 && (dpl == 2 || dpl == 4 || dpl == 8) && L <= 64 * kPosPerLane)) {
+    const int64_t grid_w = ceil_div(l.max_chunks, 4);
+    // position registers per lane sized to the chunk length (fewer registers, more waves per SIMD)
+#define DET_IA_WAVE(D, NP)                                                                                      \
+  if (!fz && dpl == D && L <= 64 * NP && (NP == 4 || L > 64 * (NP / 2)))                                        \
+    hipLaunchKernelGGL((ia_gather_wave<D, NP>), dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim, perm,     \
+                       chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks, FusedSrc{});     \
+  if (fz && dpl == D && L <= 64 * NP && (NP == 4 || L > 64 * (NP / 2)))                                         \
+    hipLaunchKernelGGL((ia_gather_wave<D, NP, true>), dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim,      \
+                       perm, chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks, *fz);
+    DET_IA_WAVE(2, 4) DET_IA_WAVE(2, 8) DET_IA_WAVE(2, 16)
+    DET_IA_WAVE(4, 4) DET_IA_WAVE(4, 8) DET_IA_WAVE(4, 16)
+    DET_IA_WAVE(8, 4) DET_IA_WAVE(8, 8) DET_IA_WAVE(8, 16)
+#undef DET_IA_WAVE
+  } else {
+    DET_IA_TAIL(1) DET_IA_TAIL(2) DET_IA_TAIL(4) DET_IA_TAIL(8) DET_IA_TAIL(16) DET_IA_TAIL(32) DET_IA_TAIL(64)
+  }
+#undef DET_IA_TAIL
+#undef DET_IA_TAIL_T
+  const int ds = fold_slice(dim);
+  const dim3 fold_grid(static_cast<uint32_t>((n_rows < kFoldGroups ? n_rows : kFoldGroups) * (dim / ds)));
+  if (ds == 32)
+    hipLaunchKernelGGL(ia_fold<32>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
+  else if (ds == 16)
+    hipLaunchKernelGGL(ia_fold<16>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
+  else
+    hipLaunchKernelGGL(ia_fold<8>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
+  return check_launch(what);
 }
 
 }  // namespace
@@ -1088,75 +1345,7 @@ extern "C" int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t ou
 #undef DET_IA_ATOMIC
     return check_launch("det_index_add (atomic)");
   }
-  char* w = static_cast<char*>(ws);
-  auto* hdr = reinterpret_cast<uint32_t*>(w);
-  auto* hist = reinterpret_cast<uint16_t*>(w + l.hist);
-  const int hist_ld = hist_stride(n_rows);
-  auto* wg_tot = reinterpret_cast<uint32_t*>(w + l.wg_tot);
-  auto* seg_off = reinterpret_cast<uint32_t*>(w + l.seg_off);
-  auto* chunk_off = reinterpret_cast<uint32_t*>(w + l.chunk_off);
-  auto* full_off = reinterpret_cast<uint32_t*>(w + l.full_off);
-  auto* chunk_desc = reinterpret_cast<int4*>(w + l.chunk_desc);
-  auto* perm = reinterpret_cast<int32_t*>(w + l.perm);
-  auto* scratch = reinterpret_cast<float*>(w + l.scratch);
-  const size_t lds_count = static_cast<size_t>(hist_ld) * 4;
-  auto* segtot = reinterpret_cast<uint32_t*>(w + l.segtot);
-  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, hist_ld, hist, hdr);
-  hipLaunchKernelGGL(ia_prefix_seg, dim3(ceil_div(n_rows, 256), l.nseg), dim3(256), 0, st, hist, hist_ld, l.nblk, nr,
-                     segtot);
-  const uint32_t rcp = static_cast<uint32_t>(0xFFFFFFFFull / static_cast<uint64_t>(L));
-  const dim3 off_grid(static_cast<uint32_t>(ceil_div(n_rows, 256)));
-  hipLaunchKernelGGL(ia_totals, off_grid, dim3(256), 0, st, segtot, l.nseg, nr, L, rcp, wg_tot, seg_off);
-  hipLaunchKernelGGL(ia_offsets, off_grid, dim3(256), 0, st, nr, L, rcp, n_src, wg_tot, seg_off, chunk_off, full_off,
-                     chunk_desc, hdr);
-  switch (scatter_waves(n_rows)) {
-    case 4: launch_scatter<4>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
-    case 2: launch_scatter<2>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
-    default: launch_scatter<1>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
-  }
-  const int64_t grid_g = ceil_div(l.max_chunks, 256 / gs);
-#define DET_IA_TAIL_T(G, E, S)                                                                                  \
-  if (gs == G) {                                                                                                 \
-    if (L <= G * kPosPerLane)                                                                                    \
-      hipLaunchKernelGGL((ia_gather<G, E>), dim3(grid_g), dim3(256), 0, st, S, src_ld, (int)dim, perm, seg_off,  \
-                         chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);                           \
-    else                                                                                                         \
-      hipLaunchKernelGGL((ia_gather_long<G, E>), dim3(grid_g), dim3(256), 0, st, S, src_ld, (int)dim, perm,      \
-                         seg_off, chunk_off, nr, L, out, out_ld, scratch, n_src, l.max_chunks);                  \
-  }
-#define DET_IA_TAIL(G)                   \
-  if (f32) {                             \
-    DET_IA_TAIL_T(G, float, s32)         \
-  } else {                               \
-    DET_IA_TAIL_T(G, uint16_t, s16)      \
-  }
-  const int dpl = (dim % 64 == 0) ? static_cast<int>(dim / 64) : 0;
-  // the one-wave-per-chunk gather is for bf16 rows; float32 rows take the lane-group gather
-  if (!f32 && (dpl == 2 || dpl == 4 || dpl == 8) && L <= 64 * kPosPerLane) {
-    const int64_t grid_w = ceil_div(l.max_chunks, 4);
-    // position registers per lane sized to the chunk length (fewer registers, more waves per SIMD)
-#define DET_IA_WAVE(D, NP)                                                                                      \
-  if (dpl == D && L <= 64 * NP && (NP == 4 || L > 64 * (NP / 2)))                                               \
-    hipLaunchKernelGGL((ia_gather_wave<D, NP>), dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim, perm,     \
-                       chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks);
-    DET_IA_WAVE(2, 4) DET_IA_WAVE(2, 8) DET_IA_WAVE(2, 16)
-    DET_IA_WAVE(4, 4) DET_IA_WAVE(4, 8) DET_IA_WAVE(4, 16)
-    DET_IA_WAVE(8, 4) DET_IA_WAVE(8, 8) DET_IA_WAVE(8, 16)
-#undef DET_IA_WAVE
-  } else {
-    DET_IA_TAIL(1) DET_IA_TAIL(2) DET_IA_TAIL(4) DET_IA_TAIL(8) DET_IA_TAIL(16) DET_IA_TAIL(32) DET_IA_TAIL(64)
-  }
-#undef DET_IA_TAIL
-#undef DET_IA_TAIL_T
-  const int ds = fold_slice(dim);
-  const dim3 fold_grid(static_cast<uint32_t>((n_rows < kFoldGroups ? n_rows : kFoldGroups) * (dim / ds)));
-  if (ds == 32)
-    hipLaunchKernelGGL(ia_fold<32>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
-  else if (ds == 16)
-    hipLaunchKernelGGL(ia_fold<16>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
-  else
-    hipLaunchKernelGGL(ia_fold<8>, fold_grid, dim3(256), 0, st, chunk_off, nr, (int)dim, scratch, out, out_ld);
-  return check_launch("det_index_add");
+  return pipeline(l, ws, out, n_rows, dim, out_ld, ids, n_src, src, src_ld, f32, L, st, nullptr, "det_index_add");
 }
 
 extern "C" int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* count, void* stream) {
@@ -1169,4 +1358,103 @@ extern "C" int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* c
   if (e != hipSuccess) return set_error(DET_ERR_HIP, "index_add_bad_ids: %s", hipGetErrorString(e));
   *count = v;
   return ok();
+}
+
+// ---------------------------------------------------------------------------
+// det_indexer_dk: the fused sparse-indexer dK (DSv4 page, source 3 fix). The
+// coefficient kernel turns (ids, predict, target) into one float32 per slot;
+// the index_add pipeline then gathers RN32(c * q[row]) instead of stored
+// source rows. The comparison arm adds the same products with float atomics.
+namespace {
+int indexer_dk_check(int64_t Q, int64_t K, int64_t dim, int64_t n_rows, const det_index_add_cfg* cfg, int* L) {
+  if (Q < 0 || K < 0) return set_error(DET_ERR_INVALID_ARG, "indexer_dk: Q and K must be >= 0");
+  if (K > 1024) return set_error(DET_ERR_UNSUPPORTED, "indexer_dk: K must be <= 1024, got %lld", static_cast<long long>(K));
+  if (Q * K > 0x7FFFFFFFLL) return set_error(DET_ERR_UNSUPPORTED, "indexer_dk: Q * K must be < 2^31");
+  if (int s = check_shape(Q * K, dim, n_rows)) return s;
+  if (int s = resolve(cfg, L)) return s;
+  if (dim != 0 && dim != 128 && dim != 256 && dim != 512)
+    return set_error(DET_ERR_UNSUPPORTED, "indexer_dk: dim must be 128, 256 or 512, got %lld", static_cast<long long>(dim));
+  if (*L > 1024) return set_error(DET_ERR_UNSUPPORTED, "indexer_dk: chunk_rows must be <= 1024, got %d", *L);
+  return DET_OK;
+}
+
+size_t indexer_dk_ws(int64_t Q, int64_t K, int64_t dim, int64_t n_rows, int L, int atomic) {
+  const int64_t n_src = Q * K;
+  if (n_src == 0 || n_rows == 0 || dim == 0) return 0;
+  if (atomic) return DET_WS_HEADER_BYTES + align_up(static_cast<size_t>(n_src) * 4, 256);
+  return layout(n_src, dim, n_rows, L, true).total;
+}
+}  // namespace
+
+extern "C" int det_indexer_dk_workspace_size(int64_t Q, int64_t K, int64_t dim, int64_t n_rows,
+                                            const det_index_add_cfg* cfg, int atomic, size_t* bytes) {
+  if (int s = check_atomic_flag(atomic)) return s;
+  if (!bytes) return set_error(DET_ERR_INVALID_ARG, "indexer_dk: bytes is NULL");
+  int L;
+  if (int s = indexer_dk_check(Q, K, dim, n_rows, cfg, &L)) return s;
+  *bytes = indexer_dk_ws(Q, K, dim, n_rows, L, atomic);
+  return ok();
+}
+
+extern "C" int det_indexer_dk(float* dk, int64_t n_rows, int64_t dim, int64_t dk_ld, const int32_t* ids,
+                              const float* predict, const float* target, int64_t Q, int64_t K, const void* q,
+                              int64_t q_ld, int q_dtype, float scale, const det_index_add_cfg* cfg, void* ws,
+                              size_t ws_bytes, int atomic, void* stream) {
+  if (int s = check_atomic_flag(atomic)) return s;
+  int L;
+  if (int s = indexer_dk_check(Q, K, dim, n_rows, cfg, &L)) return s;
+  if (q_dtype != DET_BF16)
+    return set_error(q_dtype == DET_F32 ? DET_ERR_UNSUPPORTED : DET_ERR_INVALID_ARG,
+                     "indexer_dk: q must be bf16 (dtype %d)", q_dtype);
+  const int64_t n_src = Q * K;
+  if (n_src == 0 || n_rows == 0 || dim == 0) return ok();
+  if (!dk || !ids || !predict || !target || !q) return set_error(DET_ERR_INVALID_ARG, "indexer_dk: NULL pointer");
+  if (dk_ld < dim || q_ld < dim) return set_error(DET_ERR_INVALID_ARG, "indexer_dk: dk_ld and q_ld must be >= dim");
+  if (dk_ld % 4 || q_ld % 8 || !aligned(dk, 16) || !aligned(q, 16))
+    return set_error(DET_ERR_UNSUPPORTED, "indexer_dk: dk and q rows must be 16-byte aligned");
+  const size_t need = indexer_dk_ws(Q, K, dim, n_rows, L, atomic);
+  if (int s = check_workspace(ws, ws_bytes, need)) return s;
+  const Range o = range2d(dk, n_rows, dim, dk_ld, 4);
+  const size_t slot_bytes = static_cast<size_t>(n_src) * 4;
+  if (overlaps(o, range1d(ids, slot_bytes)) || overlaps(o, range1d(predict, slot_bytes)) ||
+      overlaps(o, range1d(target, slot_bytes)) || overlaps(o, range2d(q, Q, dim, q_ld, 2)) ||
+      overlaps(o, range1d(ws, ws_bytes)))
+    return set_error(DET_ERR_OVERLAP, "indexer_dk: dk overlaps an input or the workspace");
+  const hipStream_t st = as_stream(stream);
+  char* w = static_cast<char*>(ws);
+  const Layout l = layout(n_src, dim, n_rows, L, true);
+  float* coef = reinterpret_cast<float*>(w + (atomic ? DET_WS_HEADER_BYTES : l.coef));
+  // one wave per query row; 16-byte loads when every row starts 32-byte aligned
+  const dim3 coef_grid(static_cast<uint32_t>(ceil_div(Q, 4)));
+  const bool vec = K % 8 == 0 && aligned(ids, 32) && aligned(predict, 32) && aligned(target, 32) && aligned(ws, 32);
+  const int Ki = static_cast<int>(K), nr = static_cast<int>(n_rows);
+#define DET_IA_COEF(P, V)                                                                                         \
+  hipLaunchKernelGGL((ia_coef<P, V>), coef_grid, dim3(256), 0, st, ids, predict, target, Q, Ki, nr, scale, coef);
+  if (K <= kCoefPiece) {
+    if (vec) { DET_IA_COEF(1, true) } else { DET_IA_COEF(1, false) }
+  } else {
+    if (vec) { DET_IA_COEF(2, true) } else { DET_IA_COEF(2, false) }
+  }
+#undef DET_IA_COEF
+  FusedSrc fz;
+  fz.coef = coef;
+  fz.K = static_cast<uint32_t>(K);
+  fz.krcp = static_cast<uint32_t>(0xFFFFFFFFull / static_cast<uint64_t>(K));
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  if (atomic) {
+    const int gs = group_size(dim);
+    const int64_t grid = ceil_div(n_src, 256 / gs);
+    const int nr = static_cast<int>(n_rows);
+    if (gs == 16)
+      hipLaunchKernelGGL(ia_atomic_fused<16>, dim3(grid), dim3(256), 0, st, ids, n_src, q16, q_ld, (int)dim, nr, dk,
+                         dk_ld, fz);
+    else if (gs == 32)
+      hipLaunchKernelGGL(ia_atomic_fused<32>, dim3(grid), dim3(256), 0, st, ids, n_src, q16, q_ld, (int)dim, nr, dk,
+                         dk_ld, fz);
+    else
+      hipLaunchKernelGGL(ia_atomic_fused<64>, dim3(grid), dim3(256), 0, st, ids, n_src, q16, q_ld, (int)dim, nr, dk,
+                         dk_ld, fz);
+    return check_launch("det_indexer_dk (atomic)");
+  }
+  return pipeline(l, ws, dk, n_rows, dim, dk_ld, ids, n_src, q, q_ld, false, L, st, &fz, "det_indexer_dk");
 }

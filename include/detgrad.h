@@ -185,6 +185,45 @@ int det_index_add(float* out, int64_t n_rows, int64_t dim, int64_t out_ld, const
 int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* count, void* stream);
 
 /* ------------------------------------------------------------------------
+ * det_indexer_dk: the sparse-indexer dK with its source rows made on the fly.
+ * Megatron-LM PR #7441 (DSv4 deterministic mode), source 3 and its fix: the
+ * deterministic indexer backward computes the clipped-log KL gradient of the
+ * indexer scores, predict * sum(kept_target) - kept_target with the targets
+ * clamped at e^-100 and a valid-slot mask, normalised by
+ * loss_coeff / (B * S_q) * sm_scale * grad_loss, and accumulates dK over the
+ * key ids without atomics. Per query row r and top-k slot j:
+ *
+ *   valid   = 0 <= ids[r][j] < n_rows
+ *   kept    = valid ? max(target[r][j], EPS) : 0    EPS = 27 * 2^-149, the float32 nearest e^-100
+ *   S_r     = ((-0 + kept[r][0]) + kept[r][1]) + ...  (slot order)
+ *   c       = RN32(RN32(RN32(predict[r][j] * S_r) - kept) * scale)
+ *   src     = RN32(c * q[r][d])                       (source row of slot (r, j))
+ *   dk[id] += the det_index_add canonical order over the src rows of valid slots
+ *
+ * (chunks of chunk_rows rows in stable id order, folded left to right, one
+ * add into dk[id]). scale is the caller's float32 product of loss_coeff /
+ * (B * S_q), sm_scale and grad_loss (the score being sm_scale * q . k). The
+ * bits equal det_index_add on the explicit float32 source rows.
+ *
+ * ids: [Q, K] int32, predict, target: [Q, K] float32, all contiguous (row
+ *      stride K); K <= 1024. q: [Q, dim] bf16 (q_dtype DET_BF16; DET_F32 is
+ *      DET_ERR_UNSUPPORTED), row stride q_ld >= dim, a multiple of 8, 16-byte
+ *      aligned. dk: [n_rows, dim] float32, row stride dk_ld >= dim (multiple
+ *      of 4, 16-byte aligned), accumulated. dim in {128, 256, 512},
+ *      n_rows <= 16384.
+ * cfg: NULL = {chunk_rows = 256}; chunk_rows in [1, 1024].
+ * ws:  det_indexer_dk_workspace_size() bytes: the det_index_add workspace
+ *      plus one float32 coefficient per slot; the atomic arm (per-element
+ *      float atomics of the same products, no sort) needs the coefficients
+ *      only. Bad ids are counted as for det_index_add (det_index_add_bad_ids
+ *      reads the count from this workspace). */
+int det_indexer_dk_workspace_size(int64_t Q, int64_t K, int64_t dim, int64_t n_rows, const det_index_add_cfg* cfg,
+                                  int atomic, size_t* bytes);
+int det_indexer_dk(float* dk, int64_t n_rows, int64_t dim, int64_t dk_ld, const int32_t* ids, const float* predict,
+                   const float* target, int64_t Q, int64_t K, const void* q, int64_t q_ld, int q_dtype, float scale,
+                   const det_index_add_cfg* cfg, void* ws, size_t ws_bytes, int atomic, void* stream);
+
+/* ------------------------------------------------------------------------
  * det_grouped_dprob: dprob of a grouped-GEMM dsReLU backward.
  * cudnn-frontend PR #521 (deterministic dprob): each N tile of a token gets
  * its own slot with a single writer, each subtile's partial is stored by its

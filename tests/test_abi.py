@@ -334,3 +334,36 @@ def test_binding_rejects_wrong_dtypes_and_layouts():
         dg.det_topk_canonicalize(ids.long(), lg, ids.clone(), lg.clone(), lg.clone())
     with pytest.raises(TypeError):
         dg.det_topk_canonicalize(ids, lg, ids.clone(), lg.clone(), lg.double())
+
+
+def test_indexer_dk_validation():
+    import ctypes
+    L = lib()
+    P = ctypes.c_void_p
+    n = ctypes.c_size_t()
+    f = ctypes.c_float(0.1)
+    assert L.det_indexer_dk_workspace_size(64, 2048, 128, 100, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
+    assert L.det_indexer_dk_workspace_size(64, 512, 96, 100, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
+    c = dg.IndexAddCfg(2048)
+    assert L.det_indexer_dk_workspace_size(64, 512, 128, 100, ctypes.byref(c), 0, ctypes.byref(n)) == \
+        dg.DET_ERR_UNSUPPORTED
+    assert L.det_indexer_dk_workspace_size(64, 512, 128, 100, None, 2, ctypes.byref(n)) == dg.DET_ERR_INVALID_ARG
+    assert L.det_indexer_dk_workspace_size(64, 512, 128, 100, None, 1, ctypes.byref(n)) == 0
+    assert n.value == 256 + 64 * 512 * 4
+    assert L.det_indexer_dk_workspace_size(64, 512, 128, 100, None, 0, ctypes.byref(n)) == 0
+    full = n.value
+    assert L.det_index_add_workspace_size(64 * 512, 128, 100, None, 0, ctypes.byref(n)) == 0
+    assert full == n.value + 64 * 512 * 4
+    dk, ids, pr, tg, q = P(0x10000000), P(0x20000000), P(0x30000000), P(0x40000000), P(0x50000000)
+    ws = P(0x60000000)
+    # float32 q, a NULL pointer, a short workspace, dk overlapping q: all refused before any launch
+    assert L.det_indexer_dk(dk, 100, 128, 128, ids, pr, tg, 64, 512, q, 128, 1, f, None, ws, full, 0, None) == \
+        dg.DET_ERR_UNSUPPORTED
+    assert L.det_indexer_dk(dk, 100, 128, 128, None, pr, tg, 64, 512, q, 128, 0, f, None, ws, full, 0, None) == \
+        dg.DET_ERR_INVALID_ARG
+    assert L.det_indexer_dk(dk, 100, 128, 128, ids, pr, tg, 64, 512, q, 128, 0, f, None, ws, full - 256, 0, None) == \
+        dg.DET_ERR_WORKSPACE
+    assert L.det_indexer_dk(P(0x50000100), 100, 128, 128, ids, pr, tg, 64, 512, q, 128, 0, f, None, ws, full, 0,
+                            None) == dg.DET_ERR_OVERLAP
+    # empty problems are legal and launch nothing
+    assert L.det_indexer_dk(None, 100, 128, 128, None, None, None, 0, 512, None, 128, 0, f, None, None, 0, 0, None) == 0
