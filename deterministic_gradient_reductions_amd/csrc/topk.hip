@@ -1,11 +1,11 @@
 // det_topk_canonicalize: canonical order of a compact indexer top-k.
 //
-// Megatron-LM PR #7441 (DSv4 deterministic mode), source 1: the compact
-// indexer top-k returns a row's selected ids in a run-dependent slot order,
-// and its compact softmax is accumulated in that order. The fix sorts each
-// row's ids with the padding last, permutes the logits the same way,
-// recomputes the softmax in that order, and gives all-padding rows zero
-// probabilities instead of NaN.
+// Megatron-LM PR #7441 (DSv4 deterministic mode), source 1 and its fix: the
+// slot order of a row's selected ids, and so the order of its softmax sum,
+// changed between runs. Here every row is put in one canonical order (ids
+// ascending, padding after them), its logits follow the same permutation, the
+// softmax is summed again in that order, and a row without any valid id gets
+// probabilities of zero.
 //
 // One wave per row. Each of the K slots becomes a 64-bit key (id << 32 | slot
 // for a valid id, 2^31 << 32 | slot for padding, all ones for the positions

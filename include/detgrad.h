@@ -365,11 +365,11 @@ int det_grouped_wgrad_acc_bf16(uint16_t* main_grad, int64_t ld_e, int64_t ld_m, 
 
 /* ------------------------------------------------------------------------
  * det_topk_canonicalize: canonical order of a compact indexer top-k.
- * Megatron-LM PR #7441 (DSv4 deterministic mode), source 1: the compact
- * indexer top-k returns each row's ids in a run-dependent slot order and
- * accumulates its softmax in that order; the fix sorts the ids of every row
- * with the padding last, permutes the logits with the same permutation,
- * recomputes the softmax in that order, and makes all-padding rows zero.
+ * Megatron-LM PR #7441 (DSv4 deterministic mode), source 1 and its fix: a
+ * row's selected ids, and so the terms of its softmax sum, came out in an
+ * order that varied between runs; every row is put in one canonical order
+ * (padding at the end, logits moved alongside), its softmax is summed again
+ * in that order, and a row without a valid id gets probabilities of zero.
  *
  * Canonical order per row: slots with a valid id (>= 0) by ascending id,
  * equal ids by ascending slot, then the padding slots (negative ids) by slot.

@@ -1,9 +1,10 @@
 """Gate-backward column sums, ordered (test infrastructure only).
 
 Megatron-LM PR #8244 (ordered A_log/dt_bias reduction in the fused pre-GDR
-gate backward), description: when determinism is requested each program writes
-independent FP32 partial sums and the caller reduces them on the same stream;
-the tile comes from a shape-only selector and the same tile sizes the scratch.
+gate backward), description: in deterministic mode the per-program FP32
+partials are kept apart and summed afterwards, in a fixed order, on the stream
+the backward runs on; a rule on the shape alone picks the tile, which also
+fixes the scratch size.
 The page names only the two gradients; the gate itself is the Gated-DeltaNet
 one, g = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h]), whose parameter
 gradients are

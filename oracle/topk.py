@@ -1,12 +1,11 @@
 """Canonical compact top-k: per-row id order and the softmax recomputed in it
 (test infrastructure only).
 
-Megatron-LM PR #7441 (DSv4 deterministic mode), source 1: the compact indexer
-top-k returns each row's selected ids in a slot order that changes from run to
-run, and its compact softmax is accumulated in that order. The fix sorts the
-ids of every row with the padding last, permutes the logits with the same
-permutation, recomputes the softmax in the new order, and gives rows that are
-all padding zero probabilities rather than NaN.
+Megatron-LM PR #7441 (DSv4 deterministic mode), source 1 and its fix: the
+order in which a row's selected ids (and the terms of its softmax sum) come
+out varied between runs; the fix puts every row in one canonical order, with
+the padding at the end and the logits moved alongside, sums the softmax again
+in that order, and leaves rows without a valid id at probability zero.
 
 Canonical definition (the reading taken here), per row q of K slots:
 * order: the slots with a valid id (>= 0) by ascending id, equal ids by

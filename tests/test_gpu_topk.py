@@ -69,3 +69,20 @@ def test_full_size_and_slot_order_invariance():
     assert np.array_equal(got[0], ref[0])
     assert_bitwise(got[2], ref[2], "probs after reshuffle")
     assert np.array_equal(got[1].view(np.uint32)[valid], ref[1].view(np.uint32)[valid])
+
+
+def test_replay_under_load():
+    """20 calls at 4096 x 512 while a side stream streams HBM: identical bits every time."""
+    import torch
+    from tests.gpu_util import SideLoad
+    inp = W.topk_inputs(seed=7)
+    i, l = dev_i32(inp.ids), dev_f32(inp.logits)
+    io, lo, po = torch.empty_like(i), torch.empty_like(l), torch.empty_like(l)
+    load = SideLoad()
+    pats = set()
+    for r in range(20):
+        load.kick()
+        dg.det_topk_canonicalize(i, l, io, lo, po)
+        pats.add(host(io).tobytes() + host(lo).tobytes() + host(po).tobytes())
+    load.wait()
+    assert len(pats) == 1
