@@ -17,10 +17,12 @@
 //              per id bit, so each lane's rank among equal ids is its position
 //              order inside the batch plus the id's running LDS count: a stable
 //              counting sort. perm[seg_off[id] + prefix + rank] = p.
-//  5. gather   one lane group per chunk of L sorted rows of one id: each lane
-//              owns 8 consecutive dims (one 16-byte bf16 load per row) and
-//              folds the chunk's rows left to right. A single-chunk id is added
-//              into out directly; otherwise the partial goes to scratch.
+//  5. gather   one wave (or lane group) per chunk of L sorted rows of one id:
+//              each lane owns consecutive dims of the row and folds the
+//              chunk's rows left to right. Stored bf16 rows below 2^31 bytes
+//              are read through a buffer resource with a rolling window of
+//              row loads in flight. A single-chunk id is added into out
+//              directly; otherwise the partial goes to scratch.
 //  6. fold     ids with several chunks fold their chunk partials left to right
 //              and add the total into out once.
 // Traffic: the src rows of valid ids (256 B per row at dim 128) dominate;
@@ -791,6 +793,98 @@ __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict
   for (int i = 0; i < DPL; ++i) dst[i] = (slot < 0 ? o[i] + acc[i] : acc[i]);
 }
 
+// The same gather with the rows loaded through a buffer resource (source
+// tensors below 2^31 bytes): every lane holds the 32-bit byte offsets of its
+// positions' rows, computed once, so a row costs one readlane and one load,
+// and a rolling window keeps kB row loads in flight across the chunk (the row
+// that leaves the window is added, the next one is issued into its place).
+// Rows past the chunk end are not loaded: their offset is out of the resource
+// range (the load returns zeros without a memory access) and -0.0 is added in
+// their place, which leaves every sum bitwise unchanged. Same fold order as
+// ia_gather_wave: rows left to right from -0.0.
+template <typename V>
+__device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff);
+template <>
+__device__ __forceinline__ uint32_t buf_load<uint32_t>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+template <>
+__device__ __forceinline__ uint2 buf_load<uint2>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+  return make_uint2(v[0], v[1]);
+}
+template <>
+__device__ __forceinline__ uint4 buf_load<uint4>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const u4 v = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int DPL, int NPOS>
+__global__ __launch_bounds__(256) void ia_gather_buf(const uint16_t* __restrict__ src, int64_t src_ld, int dim,
+                                                     uint32_t src_bytes, const int32_t* __restrict__ perm,
+                                                     const uint32_t* __restrict__ chunk_off,
+                                                     const int4* __restrict__ desc, int n_rows,
+                                                     float* __restrict__ out, int64_t out_ld,
+                                                     float* __restrict__ scratch, int64_t n_src,
+                                                     int64_t max_chunks) {
+  typedef typename RowVec<DPL>::T V;
+  const int lane = threadIdx.x & 63;
+  const uint32_t w = static_cast<uint32_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (w >= max_chunks) return;  // wave-uniform
+  const uint32_t n_chunks = chunk_off[n_rows];
+  const int4 dsc = desc[w];
+  if (w >= n_chunks) return;  // wave-uniform
+  // the descriptor is the same in every lane: keep it in scalar registers
+  const int k = __builtin_amdgcn_readfirstlane(dsc.x);
+  const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(dsc.y));
+  const int len = __builtin_amdgcn_readfirstlane(dsc.z);
+  const int slot = __builtin_amdgcn_readfirstlane(dsc.w);
+  const int d0 = DPL * lane;
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = -0.0f;
+  const uint32_t row_bytes = static_cast<uint32_t>(src_ld) * 2u;
+  uint32_t off[NPOS];
+#pragma unroll
+  for (int i = 0; i < NPOS; ++i) {
+    const bool in = 64 * i + lane < len;
+    const int32_t x = perm[in ? r0 + 64 * i + lane : r0];
+    const bool ok = in && x >= 0 && x < n_src;  // always a valid row
+    off[i] = (ok ? static_cast<uint32_t>(x) : 0u) * row_bytes;
+  }
+  float* const dst = slot < 0 ? out + static_cast<int64_t>(k) * out_ld + d0 : scratch + static_cast<int64_t>(slot) * dim + d0;
+  float o[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) o[i] = slot < 0 ? dst[i] : 0.0f;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0,
+                                                                      static_cast<int>(src_bytes), 0x00020000);
+  const int32_t voff = d0 * 2;
+  constexpr int kB = 64 / DPL;           // loads in flight
+  constexpr int kRows = 64 * NPOS;
+  // soffset of row r: its byte offset, or past the resource (no load) beyond the chunk
+#define DET_IA_SOFF(r) ((r) < len ? static_cast<int32_t>(__builtin_amdgcn_readlane(off[(r) / 64], (r) % 64)) \
+                                  : static_cast<int32_t>(0x80000000u))
+  V buf[kB];
+#pragma unroll
+  for (int u = 0; u < kB; ++u) buf[u] = buf_load<V>(rs, voff, DET_IA_SOFF(u));
+#pragma unroll
+  for (int b = 0; b < kRows / kB; ++b) {
+    if (b * kB >= len) break;  // wave-uniform
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int r = b * kB + u;
+      const V x = buf[u];
+      if (r + kB < kRows) buf[u] = buf_load<V>(rs, voff, DET_IA_SOFF(r + kB));
+      add_bf16(acc, r < len ? x : neg_zero_vec(x));
+    }
+  }
+#undef DET_IA_SOFF
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) dst[i] = (slot < 0 ? o[i] + acc[i] : acc[i]);
+}
+
 // Chunks longer than GS * 16 rows (a large chunk_rows setting): one lane group
 // walks the rows with the permutation read as it goes.
 template <int GS, typename E>
@@ -1261,10 +1355,18 @@ int pipeline(const Layout& l, void* ws, float* out, int64_t n_rows, int64_t dim,
   if (fz || (!f32 && (dpl == 2 || dpl == 4 || dpl == 8) && L <= 64 * kPosPerLane)) {
     const int64_t grid_w = ceil_div(l.max_chunks, 4);
     // position registers per lane sized to the chunk length (fewer registers, more waves per SIMD)
+    // stored source rows below 2^31 bytes: the buffer-resource gather
+    const bool bufok = !fz && n_src * src_ld * 2 < (static_cast<int64_t>(1) << 31);
+    const uint32_t src_bytes = bufok ? static_cast<uint32_t>(n_src * src_ld * 2) : 0u;
 #define DET_IA_WAVE(D, NP)                                                                                      \
-  if (!fz && dpl == D && L <= 64 * NP && (NP == 4 || L > 64 * (NP / 2)))                                        \
-    hipLaunchKernelGGL((ia_gather_wave<D, NP>), dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim, perm,     \
-                       chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks, FusedSrc{});     \
+  if (!fz && dpl == D && L <= 64 * NP && (NP == 4 || L > 64 * (NP / 2))) {                                      \
+    if (bufok)                                                                                                  \
+      hipLaunchKernelGGL((ia_gather_buf<D, NP>), dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim,         \
+                         src_bytes, perm, chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks);  \
+    else                                                                                                        \
+      hipLaunchKernelGGL((ia_gather_wave<D, NP>), dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim, perm,   \
+                         chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks, FusedSrc{});   \
+  }                                                                                                             \
   if (fz && dpl == D && L <= 64 * NP && (NP == 4 || L > 64 * (NP / 2)))                                         \
     hipLaunchKernelGGL((ia_gather_wave<D, NP, true>), dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim,      \
                        perm, chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks, *fz);
