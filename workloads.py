@@ -148,6 +148,12 @@ class IndexerDkInputs:
     dk0: np.ndarray      # float32 [n_rows, D]
 
 
+def indexer_dk_ids(Q: int = 4096, K: int = 512, n_rows: int = 8192, seed: int = 8, zipf_s: float = 1.1,
+                   pad_frac: float = 0.05) -> np.ndarray:
+    """The [Q, K] key ids of the fused indexer-dK workload (the index_add id recipe, one row per query)."""
+    return zipf_ids(Q * K, n_rows, zipf_s, pad_frac, seed, 0).reshape(Q, K)
+
+
 def indexer_dk_inputs(Q: int = 4096, K: int = 512, n_rows: int = 8192, dim: int = 128, seed: int = 8,
                       zipf_s: float = 1.1, pad_frac: float = 0.05, out_init: str = "zero",
                       loss_coeff: float = 0.1, batch: int = 1, sm_scale=None, grad_loss: float = 1.0,
@@ -157,7 +163,7 @@ def indexer_dk_inputs(Q: int = 4096, K: int = 512, n_rows: int = 8192, dim: int 
     per row with 2% of slots replaced by 0, -0, subnormals or values below e^-100; q ~ N(0,1) bf16.
     ``integer`` draws small dyadic predict, target and q and a power-of-two scale instead, so that every
     step is exact."""
-    ids = zipf_ids(Q * K, n_rows, zipf_s, pad_frac, seed, 0).reshape(Q, K)
+    ids = indexer_dk_ids(Q, K, n_rows, seed, zipf_s, pad_frac)
     valid = (ids >= 0) & (ids < n_rows)
     rng = _rng(seed, 1)
     if integer:
@@ -285,10 +291,15 @@ class WgradInputs:
     tokens: np.ndarray = field(default=None)
 
 
+def wgrad_tokens(E: int = 8, t_lo: int = 1024, t_hi: int = 8192, seed: int = 5) -> np.ndarray:
+    """Token rows per expert of the grouped weight-gradient workload, U{t_lo..t_hi}."""
+    return _rng(seed, 0).integers(t_lo, t_hi + 1, size=E)
+
+
 def wgrad_inputs(E: int = 8, M: int = 1408, N: int = 2048, tokens=None, t_lo: int = 1024, t_hi: int = 8192,
                  seed: int = 5, std: float = 0.02, out_init: str = "zero", integer: bool = False) -> WgradInputs:
     if tokens is None:
-        tokens = _rng(seed, 0).integers(t_lo, t_hi + 1, size=E)
+        tokens = wgrad_tokens(E, t_lo, t_hi, seed)
     tokens = np.asarray(tokens, np.int64)
     offs = np.concatenate([[0], np.cumsum(tokens)]).astype(np.int32)
     T = int(offs[-1])
