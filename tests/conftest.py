@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped (not failed) when no GPU is present; on a GPU machine a
+    # GPU tests are skipped (not failed) when no GPU is present; with a GPU, a
     # missing library is a hard failure inside the tests themselves.
     try:
         import torch
