@@ -219,8 +219,8 @@ def test_wgrad_validation():
         dg.DET_ERR_UNSUPPORTED
     assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 100, 512, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
     assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 384, None, 0, ctypes.byref(n)) == dg.DET_ERR_UNSUPPORTED
-    # the default 128 x 256 workgroup tile takes N in multiples of 256, the 128 x 512 tile in multiples of
-    # 512; other widths are refused
+    # the default 256 x 256 workgroup tile (like 128 x 256) takes N in multiples of 256, the 128 x 512 tile
+    # in multiples of 512; other widths are refused
     wide = dg.WgradCfg(128, 512, 512, 0)
     assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 768, None, 0, ctypes.byref(n)) == dg.DET_OK
     assert L.det_grouped_wgrad_acc_workspace_size(100, 1, 128, 768, ctypes.byref(wide), 0, ctypes.byref(n)) == \
