@@ -92,24 +92,28 @@ __device__ __forceinline__ uint64_t match_peers(int32_t id, bool valid) {
 
 // ---- 1. count. Integer LDS atomics: the counts are exact in any order (the
 // hot Zipf key makes a few lanes of an instruction share an address, which
-// the LDS serialises; that is far cheaper than matching lanes first).
-__global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                int hist_ld, uint16_t* __restrict__ hist,
-                                                uint32_t* __restrict__ hdr) {
+// the LDS serialises; that is far cheaper than matching lanes first). A block
+// of positions is one workgroup of kSortThreads threads (16 waves, so that
+// the two blocks a compute unit holds keep its SIMDs busy).
+constexpr int kSortThreads = 1024;
+
+__global__ __launch_bounds__(kSortThreads) void ia_count(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
+                                                         int hist_ld, uint16_t* __restrict__ hist,
+                                                         uint32_t* __restrict__ hdr) {
   extern __shared__ uint32_t lds_hist[];
-  for (int k = threadIdx.x; k < hist_ld; k += 256) lds_hist[k] = 0u;
-  __syncthreads();
+  for (int k = threadIdx.x; k < hist_ld; k += kSortThreads) lds_hist[k] = 0u;
   const int64_t b = blockIdx.x;
   const int64_t p0 = b * kBlockPos;
   const int64_t p1 = p0 + kBlockPos < n_src ? p0 + kBlockPos : n_src;
-  uint32_t bad = 0;
-  constexpr int kPer = kBlockPos / 256;
+  constexpr int kPer = kBlockPos / kSortThreads;
   int32_t idv[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int64_t p = p0 + threadIdx.x + u * 256;
+    const int64_t p = p0 + threadIdx.x + u * kSortThreads;
     idv[u] = p < p1 ? ids[p] : -1;
   }
+  __syncthreads();
+  uint32_t bad = 0;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int32_t id = idv[u];
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(256) void ia_count(const int32_t* __restrict__ ids,
   __syncthreads();
   // counts are at most kBlockPos: eight 16-bit entries per 16-byte store
   uint4* row = reinterpret_cast<uint4*>(hist + b * hist_ld);
-  for (int k8 = threadIdx.x; k8 < hist_ld / 8; k8 += 256) {
+  for (int k8 = threadIdx.x; k8 < hist_ld / 8; k8 += kSortThreads) {
     const uint32_t* c = lds_hist + 8 * k8;
     row[k8] = make_uint4(c[0] | c[1] << 16, c[2] | c[3] << 16, c[4] | c[5] << 16, c[6] | c[7] << 16);
   }
@@ -349,65 +353,62 @@ __global__ __launch_bounds__(256) void ia_offsets(int n_rows, int L, uint32_t rc
   }
 }
 
-// ---- 4. stable scatter. The block's 4096 positions are cut into NW
-// sub-blocks, one per walking wave.
-//   match:  all four waves take the block's 64-position batches in turn; the
+// ---- 4. stable scatter. One workgroup of 16 waves per block of 4096
+// positions, cut into NW sub-blocks (one walking wave each).
+//   match:  wave w takes the block's 64-position batches w, w + 16, ...; the
 //           lanes holding the same id find each other with one ballot per id
 //           bit, which gives each lane its rank among equal ids of the batch
-//           and the group size; (id, rank, group size at the lowest lane of
-//           the group) is packed in place of the id.
-//   count:  each walking wave adds the group sizes of its sub-block into its
-//           own LDS table (one add per distinct id and batch: exact in any
-//           order).
+//           and the group size. The group's lowest lane adds the size into
+//           the count table of the batch's sub-block (one LDS add per
+//           distinct id and batch: exact in any order), and (id, rank, group
+//           size at the lowest lane) is packed into the block's LDS list.
 //   bases:  for every id present in the block, the first destination of each
 //           sub-block = segment offset + earlier segments + earlier blocks +
 //           the counts of the earlier sub-blocks (global loads for present
 //           ids, issued without branches).
 //   chain:  each walking wave walks its sub-block in order, batch by batch:
-//           perm[base + rank] = p, then the group's lowest lane advances the
-//           id's running count: a stable counting sort. Within one wave the
-//           LDS read of an id's running count precedes its leader's update in
-//           program order, so no barrier is needed.
+//           destination = the id's running count + rank, written over the
+//           packed entry, then the group's lowest lane advances the running
+//           count: a stable counting sort. Within one wave the LDS read of an
+//           id's running count precedes its leader's update in program order,
+//           so no barrier is needed, and the chain touches only LDS.
+//   store:  all waves write perm[destination] = p for the block's positions.
 // Packed match result: id (14 bits) | rank << 14 (6 bits) | size << 20 (7
 // bits, 0 except at the group's lowest lane); -1 for ids out of range.
 constexpr uint32_t kPackRank = 14, kPackSize = 20;
 
 template <int NW>
-__global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                  int tab_ld, int hist_ld, const uint16_t* __restrict__ prefix,
-                                                  const uint32_t* __restrict__ segbase,
-                                                  const uint32_t* __restrict__ seg_off, int32_t* __restrict__ perm) {
+__global__ __launch_bounds__(kSortThreads) void ia_scatter(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
+                                                           int tab_ld, int hist_ld, const uint16_t* __restrict__ prefix,
+                                                           const uint32_t* __restrict__ segbase,
+                                                           const uint32_t* __restrict__ seg_off,
+                                                           int32_t* __restrict__ perm) {
   extern __shared__ uint32_t lds[];
   uint32_t* tab = lds;                                           // [NW][tab_ld], tab_ld = n_rows rounded up to 4
   int32_t* lid = reinterpret_cast<int32_t*>(lds + NW * tab_ld);  // [kBlockPos]
+  constexpr int kWaves = kSortThreads / 64;
   constexpr int kSub = kBlockPos / NW;
   constexpr int kBatches = kBlockPos / 64;
+  constexpr int kBpS = kBatches / NW;       // batches per sub-block
+  constexpr int kMine = kBatches / kWaves;  // batches per wave
+  static_assert(kMine * kWaves == kBatches && kBpS * NW == kBatches, "whole batches per wave and sub-block");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t b = blockIdx.x;
   const int64_t p0 = b * kBlockPos;
   const int64_t p1 = p0 + kBlockPos < n_src ? p0 + kBlockPos : n_src;
-  {
-    uint4* t4 = reinterpret_cast<uint4*>(tab);
-    for (int k = tid; k < NW * tab_ld / 4; k += 256) t4[k] = make_uint4(0u, 0u, 0u, 0u);
+  int32_t x[kMine];
+#pragma unroll
+  for (int q = 0; q < kMine; ++q) {
+    const int64_t p = p0 + 64 * (wave + kWaves * q) + lane;
+    x[q] = p < p1 ? ids[p] : -1;
   }
   {
-    constexpr int kPer = kBlockPos / 256;
-    int32_t v[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int64_t p = p0 + tid + 256 * u;
-      v[u] = p < p1 ? ids[p] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) lid[tid + 256 * u] = v[u];
+    uint4* t4 = reinterpret_cast<uint4*>(tab);
+    for (int k = tid; k < NW * tab_ld / 4; k += kSortThreads) t4[k] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
   {
     const uint64_t lt = __lanemask_lt();
-    constexpr int kMine = kBatches / 4;  // batches per wave
-    int32_t x[kMine];
-#pragma unroll
-    for (int q = 0; q < kMine; ++q) x[q] = lid[(wave + 4 * q) * 64 + lane];
 #pragma unroll
     for (int q = 0; q < kMine; ++q) {
       const int32_t id = x[q];
@@ -415,19 +416,10 @@ __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ id
       const uint64_t peers = match_peers(id, valid);
       const uint32_t rank = static_cast<uint32_t>(__popcll(peers & lt));
       const uint32_t size = (valid && rank == 0) ? static_cast<uint32_t>(__popcll(peers)) : 0u;
-      x[q] = valid ? static_cast<int32_t>(static_cast<uint32_t>(id) | (rank << kPackRank) | (size << kPackSize)) : -1;
-    }
-#pragma unroll
-    for (int q = 0; q < kMine; ++q) lid[(wave + 4 * q) * 64 + lane] = x[q];
-  }
-  __syncthreads();
-  if (wave < NW) {
-    uint32_t* t = tab + wave * tab_ld;
-#pragma unroll 4
-    for (int off = wave * kSub; off < (wave + 1) * kSub; off += 64) {
-      const int32_t xv = lid[off + lane];
-      const uint32_t size = (static_cast<uint32_t>(xv) >> kPackSize) & 0x7Fu;
-      if (xv >= 0 && size != 0) atomicAdd(&t[xv & 0x3FFF], size);
+      const int batch = wave + kWaves * q;
+      if (size != 0) atomicAdd(&tab[(batch / kBpS) * tab_ld + id], size);
+      lid[64 * batch + lane] =
+          valid ? static_cast<int32_t>(static_cast<uint32_t>(id) | (rank << kPackRank) | (size << kPackSize)) : -1;
     }
   }
   __syncthreads();
@@ -435,12 +427,13 @@ __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ id
   const uint32_t* sb = segbase + (b / kSegBlocks) * n_rows;
   // only ids present in the block need a base (absent ids are never read in
   // the walk); absent ids load entry 0 instead, so the loads need no branches
-  for (int k0 = 0; k0 < n_rows; k0 += 256 * 16) {
-    uint32_t c[16][NW];
-    bool present[16];
+  constexpr int kU = 8;
+  for (int k0 = 0; k0 < n_rows; k0 += kSortThreads * kU) {
+    uint32_t c[kU][NW];
+    bool present[kU];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int k = k0 + tid + 256 * u;
+    for (int u = 0; u < kU; ++u) {
+      const int k = k0 + tid + kSortThreads * u;
       uint32_t any = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
@@ -449,15 +442,15 @@ __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ id
       }
       present[u] = any != 0;
     }
-    uint32_t base[16];
+    uint32_t base[kU];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int kk = present[u] ? k0 + tid + 256 * u : 0;
+    for (int u = 0; u < kU; ++u) {
+      const int kk = present[u] ? k0 + tid + kSortThreads * u : 0;
       base[u] = seg_off[kk] + sb[kk] + pre[kk];
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int k = k0 + tid + 256 * u;
+    for (int u = 0; u < kU; ++u) {
+      const int k = k0 + tid + kSortThreads * u;
       if (present[u]) {
         uint32_t run = base[u];
 #pragma unroll
@@ -469,24 +462,32 @@ __global__ __launch_bounds__(256) void ia_scatter(const int32_t* __restrict__ id
     }
   }
   __syncthreads();
-  if (wave >= NW) return;
-  uint32_t* t = tab + wave * tab_ld;
-  constexpr int kSteps = kSub / 64;
-#pragma unroll
-  for (int q = 0; q < kSteps; ++q) {
-    const int32_t xv = lid[wave * kSub + 64 * q + lane];
-    if (xv >= 0) {
-      const int32_t id = xv & 0x3FFF;
-      const uint32_t rank = (static_cast<uint32_t>(xv) >> kPackRank) & 0x3Fu;
-      const uint32_t size = (static_cast<uint32_t>(xv) >> kPackSize) & 0x7Fu;
-      const uint32_t old = t[id];
-      const uint64_t dest = static_cast<uint64_t>(old) + rank;
-      if (dest < static_cast<uint64_t>(n_src))
-        perm[dest] = static_cast<int32_t>(p0 + wave * kSub + 64 * q + lane);
+  if (wave < NW) {
+    uint32_t* t = tab + wave * tab_ld;
+    int32_t* mine = lid + wave * kSub;
+    constexpr int kSteps = kSub / 64;
+#pragma unroll 8
+    for (int q = 0; q < kSteps; ++q) {
+      const int32_t xv = mine[64 * q + lane];
+      if (xv >= 0) {
+        const int32_t id = xv & 0x3FFF;
+        const uint32_t rank = (static_cast<uint32_t>(xv) >> kPackRank) & 0x3Fu;
+        const uint32_t size = (static_cast<uint32_t>(xv) >> kPackSize) & 0x7Fu;
+        const uint32_t old = t[id];
+        const uint64_t dest = static_cast<uint64_t>(old) + rank;
+        mine[64 * q + lane] = dest < static_cast<uint64_t>(n_src) ? static_cast<int32_t>(dest) : -1;
+        __builtin_amdgcn_wave_barrier();
+        if (size != 0) t[id] = old + size;
+      }
       __builtin_amdgcn_wave_barrier();
-      if (size != 0) t[id] = old + size;
     }
-    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kBlockPos / kSortThreads; ++u) {
+    const int pos = tid + kSortThreads * u;
+    const int32_t d = lid[pos];
+    if (d >= 0) perm[d] = static_cast<int32_t>(p0 + pos);
   }
 }
 
@@ -513,7 +514,7 @@ void launch_scatter(int64_t nblk, int n_rows, hipStream_t st, const int32_t* ids
       raised = true;
     }
   }
-  hipLaunchKernelGGL(ia_scatter<NW>, dim3(static_cast<uint32_t>(nblk)), dim3(256), lds, st, ids, n_src, n_rows,
+  hipLaunchKernelGGL(ia_scatter<NW>, dim3(static_cast<uint32_t>(nblk)), dim3(kSortThreads), lds, st, ids, n_src, n_rows,
                      pad_rows, hist_stride(n_rows), hist, segtot, seg_off, perm);
 }
 
@@ -1321,7 +1322,7 @@ int pipeline(const Layout& l, void* ws, float* out, int64_t n_rows, int64_t dim,
   auto* scratch = reinterpret_cast<float*>(w + l.scratch);
   const size_t lds_count = static_cast<size_t>(hist_ld) * 4;
   auto* segtot = reinterpret_cast<uint32_t*>(w + l.segtot);
-  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(256), lds_count, st, ids, n_src, nr, hist_ld, hist, hdr);
+  hipLaunchKernelGGL(ia_count, dim3(l.nblk), dim3(kSortThreads), lds_count, st, ids, n_src, nr, hist_ld, hist, hdr);
   hipLaunchKernelGGL(ia_prefix_seg, dim3(ceil_div(n_rows, 256), l.nseg), dim3(256), 0, st, hist, hist_ld, l.nblk, nr,
                      segtot);
   const uint32_t rcp = static_cast<uint32_t>(0xFFFFFFFFull / static_cast<uint64_t>(L));

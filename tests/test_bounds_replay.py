@@ -369,6 +369,80 @@ def replay_index_add(ids, n_rows, dim, L, Q=None, K=None):
                                             [np.zeros(0, np.int64)]), max_chunks)
 
 
+def replay_sort(ids, n_rows):
+    """LDS and global indices of the count and scatter kernels (blocks of 4096 positions, 1024 threads,
+    NW walking sub-blocks), and the destination each position gets from the kernel's decomposition
+    (segment offset + earlier segments + earlier blocks + earlier sub-blocks + running count + rank),
+    which must be the position's place in the stable order."""
+    ids = np.asarray(ids, np.int64).ravel()
+    n_src = ids.size
+    B, T, SEG = 4096, 1024, 16
+    nblk = cdiv(n_src, B)
+    nseg = cdiv(nblk, SEG)
+    hist_ld = cdiv(n_rows, 8) * 8
+    pad = cdiv(n_rows, 4) * 4
+    nw = next((w for w in (4, 2) if w * pad * 4 + B * 4 <= 80 * 1024), 1)
+    bps = (B // 64) // nw
+    assert nw * pad * 4 + B * 4 <= 160 * 1024
+    # count: positions p0 + tid + 1024 u, u < 4; LDS histogram entries [0, hist_ld); row stores hist_ld / 8 vectors
+    p = np.arange(n_src)
+    valid = (ids >= 0) & (ids < n_rows)
+    inside("count lds", ids[valid], hist_ld)
+    inside("count hist row", np.array([0, nblk * hist_ld - 1]), nblk * hist_ld)
+    # scatter: wave w takes batches w + 16 q; the batch's sub-block table is batch // bps
+    b = p // B
+    batch = (p - b * B) // 64
+    lane = p % 64
+    wave, q = batch % 16, batch // 16
+    assert (64 * (wave + 16 * q) + lane == p - b * B).all()
+    sub = batch // bps
+    inside("scatter tab", (sub * pad + ids)[valid], nw * pad)
+    inside("scatter lid", 64 * batch + lane, B)
+    # bases: ids k0 + tid + 1024 u, u < 8; global loads at present ids only
+    inside("scatter segtot", (b // SEG) * n_rows + np.where(valid, ids, 0), nseg * n_rows)
+    inside("scatter prefix", b * hist_ld + np.where(valid, ids, 0), nblk * hist_ld)
+    # destinations from the decomposition
+    v = np.nonzero(valid)[0]
+    iv = ids[v]
+    cnt = np.bincount(iv, minlength=n_rows)
+    seg_off = np.concatenate([[0], np.cumsum(cnt)])[:-1]
+    def before(group):  # positions of the same id earlier inside the same group
+        key = group * n_rows + iv
+        order = np.argsort(key, kind="stable")
+        ks = key[order]
+        first = np.searchsorted(ks, ks, side="left")
+        r = np.empty(v.size, np.int64)
+        r[order] = np.arange(v.size) - first
+        return r
+    seg = b[v] // SEG
+    blk = b[v]
+    sb = before(np.zeros_like(seg)) - before(seg)                            # earlier segments
+    pre = before(seg) - before(blk)                                          # earlier blocks of the segment
+    subpre = before(blk) - before(blk * nw + sub[v])                          # earlier sub-blocks of the block
+    bat = blk * (B // 64) + batch[v]
+    run = before(blk * nw + sub[v]) - before(bat)                             # earlier batches of the sub-block
+    rank = before(bat)                                                        # rank in the batch
+    assert (rank < 64).all()
+    dest = seg_off[iv] + sb + pre + subpre + run + rank
+    inside("scatter perm", dest, n_src)
+    perm, _ = oi.stable_order(ids, n_rows)
+    inv = np.empty(n_src, np.int64)
+    inv[perm] = np.arange(perm.size)
+    assert (dest == inv[v]).all()
+
+
+def test_sort_full():
+    replay_sort(W.zipf_ids(4096 * 512, 8192, 1.1, 0.05, 3, 0), 8192)
+
+
+@pytest.mark.parametrize("n_rows", [300, 4000, 16384])
+def test_sort_ragged(n_rows):
+    rng = np.random.default_rng(n_rows)
+    ids = rng.integers(-3, n_rows + 50, 70001)
+    ids[100:3000] = n_rows // 2                  # one hot id
+    replay_sort(ids, n_rows)
+
+
 @pytest.mark.parametrize("L", [1, 7, 64, 256, 512, 1024, 65536])
 def test_index_add_full(L):
     ids = W.zipf_ids(4096 * 512, 8192, 1.1, 0.05, 3, 0)
