@@ -376,6 +376,41 @@ def colsum_tile_sweep(reps, flush):
     return out
 
 
+def library_reference(reps, flush):
+    """Context for the weight-gradient fraction (not a comparison arm): the library GEMM (torch.mm, which
+    runs hipBLASLt) in bf16 on the same expert products one expert at a time (G_e^T made contiguous
+    beforehand; a bf16 result and no accumulate, so it does less work than the entry point), and on a
+    square 8192 x 8192 x 8192 product, with operands of the workload's magnitude (N(0, 0.02) bf16)."""
+    import torch
+    import workloads as W
+    wg = W.wgrad_inputs(seed=5)
+    offs = [int(v) for v in wg.offs]
+    G = torch.from_numpy(np.ascontiguousarray(wg.G).view(np.int16)).cuda().view(torch.bfloat16)
+    X = torch.from_numpy(np.ascontiguousarray(wg.X).view(np.int16)).cuda().view(torch.bfloat16)
+    E = len(offs) - 1
+    Gt = [G[offs[e]:offs[e + 1]].t().contiguous() for e in range(E)]
+    Xe = [X[offs[e]:offs[e + 1]] for e in range(E)]
+    outs = [torch.empty((wg.M, wg.N), dtype=torch.bfloat16, device="cuda") for _ in range(E)]
+
+    def experts():
+        for e in range(E):
+            torch.mm(Gt[e], Xe[e], out=outs[e])
+    d, _ = time_pairs(experts, None, reps, flush)
+    f = 2.0 * wg.M * wg.N * offs[-1]
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    A = (torch.randn((8192, 8192), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    B = (torch.randn((8192, 8192), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    C = torch.empty((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    d2, _ = time_pairs(lambda: torch.mm(A, B, out=C), None, max(5, reps // 5), flush)
+    f2 = 2.0 * 8192 ** 3
+    m, m2 = float(np.median(d)), float(np.median(d2))
+    return {"library": "torch.mm (hipBLASLt), bf16 operands N(0, 0.02), bf16 result",
+            "wgrad_experts_one_at_a_time_us": round(m, 3),
+            "wgrad_experts_frac_mfma_peak": round(f / m / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "square_8192_us": round(m2, 3),
+            "square_8192_frac_mfma_peak": round(f2 / m2 / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4)}
+
+
 # ------------------------------------------------------------- CPU baseline
 def _cpu_model():
     try:
@@ -545,6 +580,8 @@ def main():
         del w
     outside["colsum_tile_sweep_us"] = colsum_tile_sweep(args.reps, flush)
     log("colsum sweep %s" % json.dumps(outside["colsum_tile_sweep_us"]))
+    libref = library_reference(args.reps, flush)
+    log("library reference %s" % json.dumps(libref))
 
     # roofline of the dominant kernel: the entry point with the largest share of the step
     dom = max(wls, key=lambda w: np.mean(in_step[w.name]))
@@ -575,6 +612,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "kernels_outside_step": outside,
+        "library_reference": libref,
     }
     if args.copy_calibration:
         copy_calibration()
