@@ -27,8 +27,8 @@ def test_every_listed_test_exists():
             tree = ast.parse(open(os.path.join(HERE, f)).read())
             defs[f] = {n.name for n in tree.body if isinstance(n, ast.FunctionDef)}
     for name, e in MANIFEST.items():
-        assert e["cite"]
-        for kind in ("replay", "parity", "atomic"):
+        assert e["cite"] and e["graph"]
+        for kind in ("replay", "parity", "atomic", "graph"):
             for t in e[kind] or []:
                 f, fn = t.split("::")
                 assert fn in defs.get(f, set()), "%s: %s missing" % (name, t)
