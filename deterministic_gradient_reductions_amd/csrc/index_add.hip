@@ -97,9 +97,11 @@ __device__ __forceinline__ uint64_t match_peers(int32_t id, bool valid) {
 // the two blocks a compute unit holds keep its SIMDs busy).
 constexpr int kSortThreads = 1024;
 
-__global__ __launch_bounds__(kSortThreads) void ia_count(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                         int hist_ld, uint16_t* __restrict__ hist,
-                                                         uint32_t* __restrict__ hdr) {
+// (launch bounds: 16 waves per block and two blocks per compute unit, so at
+// most 64 registers per lane)
+__global__ __launch_bounds__(kSortThreads, 8) void ia_count(const int32_t* __restrict__ ids, int64_t n_src,
+                                                            int n_rows, int hist_ld, uint16_t* __restrict__ hist,
+                                                            uint32_t* __restrict__ hdr) {
   extern __shared__ uint32_t lds_hist[];
   for (int k = threadIdx.x; k < hist_ld; k += kSortThreads) lds_hist[k] = 0u;
   const int64_t b = blockIdx.x;
@@ -378,11 +380,12 @@ __global__ __launch_bounds__(256) void ia_offsets(int n_rows, int L, uint32_t rc
 constexpr uint32_t kPackRank = 14, kPackSize = 20;
 
 template <int NW>
-__global__ __launch_bounds__(kSortThreads) void ia_scatter(const int32_t* __restrict__ ids, int64_t n_src, int n_rows,
-                                                           int tab_ld, int hist_ld, const uint16_t* __restrict__ prefix,
-                                                           const uint32_t* __restrict__ segbase,
-                                                           const uint32_t* __restrict__ seg_off,
-                                                           int32_t* __restrict__ perm) {
+__global__ __launch_bounds__(kSortThreads, 8) void ia_scatter(const int32_t* __restrict__ ids, int64_t n_src,
+                                                              int n_rows, int tab_ld, int hist_ld,
+                                                              const uint16_t* __restrict__ prefix,
+                                                              const uint32_t* __restrict__ segbase,
+                                                              const uint32_t* __restrict__ seg_off,
+                                                              int32_t* __restrict__ perm) {
   extern __shared__ uint32_t lds[];
   uint32_t* tab = lds;                                           // [NW][tab_ld], tab_ld = n_rows rounded up to 4
   int32_t* lid = reinterpret_cast<int32_t*>(lds + NW * tab_ld);  // [kBlockPos]
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(kSortThreads) void ia_scatter(const int32_t* __rest
   const uint32_t* sb = segbase + (b / kSegBlocks) * n_rows;
   // only ids present in the block need a base (absent ids are never read in
   // the walk); absent ids load entry 0 instead, so the loads need no branches
-  constexpr int kU = 8;
+  constexpr int kU = 16 / NW;  // ids per thread: one round for every n_rows the LDS tables allow
   for (int k0 = 0; k0 < n_rows; k0 += kSortThreads * kU) {
     uint32_t c[kU][NW];
     bool present[kU];
