@@ -411,6 +411,40 @@ def library_reference(reps, flush):
             "square_8192_frac_mfma_peak": round(f2 / m2 / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4)}
 
 
+def measured_ceilings(flush, reps=5):
+    """What this machine delivers, measured beside the kernels (context for the fractions of the published
+    peaks): the matrix cores alone (det_mfma_rate: the weight gradient's 4 x 4 MFMA pattern from registers,
+    one workgroup per compute unit, about 5 ms per launch) on operands of the workload's magnitude
+    (N(0, 0.02) bf16) and on constant operands (every value 1.0); and a plain device copy (cold) of the
+    dprob workload's size (134 MB) and of 1 GiB, counting the bytes read and written."""
+    import torch
+    import deterministic_gradient_reductions_amd as dg
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 16384
+    flops = float(blocks) * 4 * iters * 16 * 32768
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    n_ops = 64 * 64 * 64
+    res = {}
+    for name, ops in (("mfma_random_bf16", (torch.randn(n_ops, generator=gen, device="cuda") * 0.02).to(torch.bfloat16)),
+                      ("mfma_constant_bf16", torch.ones(n_ops, dtype=torch.bfloat16, device="cuda"))):
+        d, _ = time_pairs(lambda: dg.det_mfma_rate(ops, out, blocks, iters), None, reps, lambda: None)
+        med = float(np.median(d))
+        res[name] = {"TFLOP_per_s": round(flops / med / 1e6, 1),
+                     "frac_mfma_peak": round(flops / med / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4)}
+    for name, n in (("hbm_copy_134MB", 16384 * 2048), ("hbm_copy_1GiB", 256 * 1024 * 1024)):
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        d, _ = time_pairs(lambda: y.copy_(x), None, max(reps, 10), flush)
+        med = float(np.median(d))
+        res[name] = {"GB_per_s": round(2 * n * 4 / med / 1e3, 1),
+                     "frac_hbm_peak": round(2 * n * 4 / med / 1e3 / HBM_PEAK_GBS, 4)}
+        del x, y
+    res["note"] = ("matrix cores: the weight gradient's MFMA pattern from registers with no memory traffic; "
+                   "copies: a cold float32 device copy, read plus written bytes")
+    return res
+
+
 # ------------------------------------------------------------- CPU baseline
 def _cpu_model():
     try:
@@ -582,6 +616,8 @@ def main():
     log("colsum sweep %s" % json.dumps(outside["colsum_tile_sweep_us"]))
     libref = library_reference(args.reps, flush)
     log("library reference %s" % json.dumps(libref))
+    ceil = measured_ceilings(flush)
+    log("measured ceilings %s" % json.dumps(ceil))
 
     # roofline of the dominant kernel: the entry point with the largest share of the step
     dom = max(wls, key=lambda w: np.mean(in_step[w.name]))
@@ -613,6 +649,7 @@ def main():
         "kernels": kernels,
         "kernels_outside_step": outside,
         "library_reference": libref,
+        "measured_ceilings": ceil,
     }
     if args.copy_calibration:
         copy_calibration()

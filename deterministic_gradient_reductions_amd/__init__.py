@@ -32,7 +32,7 @@ __all__ = [
     "det_grouped_wgrad_acc", "det_grouped_wgrad_acc_workspace_size", "det_grouped_wgrad_acc_bf16",
     "det_grouped_wgrad_acc_bf16_workspace_size", "det_grouped_dbias",
     "det_grouped_dbias_workspace_size", "det_topk_canonicalize", "det_workspace_init", "det_detmath_eval", "det_mfma_eval",
-    "DET_OK", "DET_ERR_INVALID_ARG", "DET_ERR_UNSUPPORTED", "DET_ERR_WORKSPACE", "DET_ERR_OVERLAP", "DET_ERR_HIP",
+    "det_mfma_rate", "DET_OK", "DET_ERR_INVALID_ARG", "DET_ERR_UNSUPPORTED", "DET_ERR_WORKSPACE", "DET_ERR_OVERLAP", "DET_ERR_HIP",
 ]
 
 DET_OK, DET_ERR_INVALID_ARG, DET_ERR_UNSUPPORTED, DET_ERR_WORKSPACE, DET_ERR_OVERLAP, DET_ERR_HIP = 0, -1, -2, -3, -4, -5
@@ -102,6 +102,7 @@ _SIGS = {
                                               ctypes.POINTER(_SZ)], _INT),
     "det_detmath_eval": ([_P, _P, _I64, _INT, _P], _INT),
     "det_mfma_eval": ([_P, _P, _P, _P, _I64, _INT, _P], _INT),
+    "det_mfma_rate": ([_P, _I64, _P, _I64, _INT, _INT, _P], _INT),
     "det_topk_canonicalize": ([_P, _P, _I64, _I64, _I64, _P, _P, _P, _I64, _P], _INT),
     "det_grouped_dbias_workspace_size": ([_I64, _I64, _I32, ctypes.POINTER(DbiasCfg), _INT, ctypes.POINTER(_SZ)],
                                          _INT),
@@ -498,3 +499,15 @@ def det_mfma_eval(A, B, C, D, stream=None) -> None:
     if not (A.is_contiguous() and B.is_contiguous() and C.is_contiguous() and D.is_contiguous()):
         raise ValueError("A, B, C and D must be contiguous")
     _check(lib().det_mfma_eval(_ptr(A), _ptr(B), _ptr(C), _ptr(D), n, K // 16, _stream_handle(stream)))
+
+
+def det_mfma_rate(ops, out, blocks: int, iters: int, stream=None) -> None:
+    """Measurement aid: `blocks` workgroups run `iters` rounds of the weight gradient's 4 x 4 MFMA pattern on
+    operand values taken from ops (bf16, >= 64*64*64 values), 16 * 32768 flops per wave and round; out
+    (float32, >= 256 * blocks) receives each lane's accumulator sum."""
+    import torch
+    if ops.dtype != torch.bfloat16 or out.dtype != torch.float32:
+        raise TypeError("ops must be bfloat16 and out float32")
+    if not (ops.is_contiguous() and out.is_contiguous()):
+        raise ValueError("ops and out must be contiguous")
+    _check(lib().det_mfma_rate(_ptr(ops), ops.numel(), _ptr(out), out.numel(), blocks, iters, _stream_handle(stream)))

@@ -41,6 +41,52 @@ __global__ __launch_bounds__(256) void mfma_eval_kernel(const uint16_t* __restri
   for (int c = 0; c < 16; ++c) D[q * 1024 + (8 * (c / 4) + 4 * kg + c % 4) * 32 + r] = acc[c];
 }
 
+// The weight gradient's accumulator pattern alone: every wave holds four A and
+// four B fragments (lane layout as above) read once from `ops`, then runs
+// `iters` rounds of the 4 x 4 MFMAs into sixteen accumulators, with no memory
+// traffic in the loop. Lane l of wave w takes its 64 operand values from set
+// (global wave index mod kRateSets). Each lane writes the sum of its
+// accumulators once, so no MFMA can be dropped. A measurement aid: how fast
+// the matrix cores run on the caller's operand values.
+constexpr int kRateSets = 64;
+constexpr int64_t kRateOps = static_cast<int64_t>(kRateSets) * 64 * 64;  // bf16 values the kernel reads
+
+__global__ __launch_bounds__(256) void mfma_rate_kernel(const uint16_t* __restrict__ ops, float* __restrict__ out,
+                                                        int iters) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const uint16_t* src = ops + ((gw % kRateSets) * 64 + lane) * 64;
+  dbf16x8_t a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[i][e] = __builtin_bit_cast(__bf16, src[8 * i + e]);
+      b[i][e] = __builtin_bit_cast(__bf16, src[32 + 8 * i + e]);
+    }
+  df32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[i][j][c] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < 16; ++c) s = s + acc[i][j][c];
+  out[gw * 64 + lane] = s;
+}
+
 __global__ void detmath_eval_kernel(const float* __restrict__ x, float* __restrict__ y, int64_t n, int fn) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -84,4 +130,19 @@ extern "C" int det_mfma_eval(const uint16_t* A, const uint16_t* B, const float* 
   if (grid > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "mfma_eval: n too large");
   hipLaunchKernelGGL(mfma_eval_kernel, dim3(grid), dim3(256), 0, as_stream(stream), A, B, C, D, n, kblocks);
   return check_launch("det_mfma_eval");
+}
+
+extern "C" int det_mfma_rate(const uint16_t* ops, int64_t n_ops, float* out, int64_t n_out, int blocks, int iters,
+                             void* stream) {
+  if (blocks < 1 || blocks > (1 << 20) || iters < 0 || iters > (1 << 24))
+    return set_error(DET_ERR_INVALID_ARG, "mfma_rate: blocks must be in [1, 2^20] and iters in [0, 2^24]");
+  if (!ops || !out) return set_error(DET_ERR_INVALID_ARG, "mfma_rate: NULL pointer");
+  if (n_ops < kRateOps)
+    return set_error(DET_ERR_INVALID_ARG, "mfma_rate: ops must hold %lld bf16 values", static_cast<long long>(kRateOps));
+  if (n_out < static_cast<int64_t>(blocks) * 256)
+    return set_error(DET_ERR_INVALID_ARG, "mfma_rate: out must hold 256 floats per block");
+  if (overlaps(range1d(out, static_cast<size_t>(n_out) * 4), range1d(ops, static_cast<size_t>(n_ops) * 2)))
+    return set_error(DET_ERR_OVERLAP, "mfma_rate: out overlaps ops");
+  hipLaunchKernelGGL(mfma_rate_kernel, dim3(blocks), dim3(256), 0, as_stream(stream), ops, out, iters);
+  return check_launch("det_mfma_rate");
 }

@@ -410,6 +410,18 @@ int det_detmath_eval(const float* x, float* y, int64_t n, int fn, void* stream);
 int det_mfma_eval(const uint16_t* A, const uint16_t* B, const float* C, float* D, int64_t n, int kblocks,
                   void* stream);
 
+/* det_mfma_rate is a measurement aid, not part of any reduction: `blocks`
+ * workgroups of four waves, each wave holding four A and four B fragments of
+ * the weight gradient's instruction (bf16 values from `ops`, read once) and
+ * running `iters` rounds of the 4 x 4 pattern of MFMAs into sixteen
+ * accumulators, with no memory traffic in the loop: 16 * 32768 flops per wave
+ * and round. It times the matrix cores on the caller's operand values (their
+ * power, and so the clock they allow, depends on those values). out[w*64 + l]
+ * receives lane l of wave w's accumulator sum.
+ * ops: >= 64*64*64 bf16 values, device memory; out: >= 256 * blocks floats,
+ * not overlapping ops. blocks in [1, 2^20], iters in [0, 2^24]. */
+int det_mfma_rate(const uint16_t* ops, int64_t n_ops, float* out, int64_t n_out, int blocks, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,4 +92,4 @@ MANIFEST = {
 
 # declared functions that are sizes, set-up or diagnostics rather than accumulating entry points
 NOT_ENTRY_POINTS = {"det_abi_version", "det_last_error", "det_workspace_init", "det_index_add_bad_ids",
-                    "det_colsum_select_cfg", "det_detmath_eval", "det_mfma_eval"}
+                    "det_colsum_select_cfg", "det_detmath_eval", "det_mfma_eval", "det_mfma_rate"}

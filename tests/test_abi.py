@@ -367,3 +367,14 @@ def test_indexer_dk_validation():
                             None) == dg.DET_ERR_OVERLAP
     # empty problems are legal and launch nothing
     assert L.det_indexer_dk(None, 100, 128, 128, None, None, None, 0, 512, None, 128, 0, f, None, None, 0, 0, None) == 0
+
+
+def test_mfma_rate_validation():
+    L = lib()
+    ops = 64 * 64 * 64
+    assert L.det_mfma_rate(FAKE, ops, P(0x900000), 256, 0, 1, None) == dg.DET_ERR_INVALID_ARG    # no blocks
+    assert L.det_mfma_rate(FAKE, ops, P(0x900000), 256, 1, -1, None) == dg.DET_ERR_INVALID_ARG   # negative iters
+    assert L.det_mfma_rate(None, ops, P(0x900000), 256, 1, 1, None) == dg.DET_ERR_INVALID_ARG    # NULL ops
+    assert L.det_mfma_rate(FAKE, ops - 1, P(0x900000), 256, 1, 1, None) == dg.DET_ERR_INVALID_ARG  # ops too short
+    assert L.det_mfma_rate(FAKE, ops, P(0x900000), 511, 2, 1, None) == dg.DET_ERR_INVALID_ARG    # out too short
+    assert L.det_mfma_rate(P(0x800000), ops, P(0x800100), 256, 1, 1, None) == dg.DET_ERR_OVERLAP  # out inside ops

@@ -126,3 +126,16 @@ def test_chains_match_the_model(kind, K):
     want = mfma.eval_c(A, B, C).view(np.uint32)
     note("mfma chains %s K=%d: %d differ of %d" % (kind, K, int((got != want).sum()), got.size))
     assert np.array_equal(got, want)
+
+
+def test_rate_probe_runs_the_pattern():
+    """det_mfma_rate (the measurement aid for the matrix-core ceiling) runs every MFMA it is asked for:
+    with every operand 1.0, each of the 16 accumulators of a wave gains 16 per element and round, so a
+    lane's sum after `iters` rounds is 16 x 16 x 16 x iters (exact in float32)."""
+    import torch
+    ops = torch.ones(64 * 64 * 64, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((3 * 256,), -1.0, dtype=torch.float32, device="cuda")
+    for iters in (0, 1, 7):
+        dg.det_mfma_rate(ops, out, 3, iters)
+        torch.cuda.synchronize()
+        assert (out == float(4096 * iters)).all(), (iters, out.unique())
