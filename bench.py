@@ -631,6 +631,11 @@ def main():
     roof["traffic"] = traffic_for(dom.name)
     roof["kernel"] = dom.name
     roof["avg_launch_us"] = round(avg_us, 3)
+    # the same kernel against what this box measured beside it (measured_ceilings): the matrix cores on
+    # operands of the workload's magnitude, or a device copy
+    c = ceil["mfma_random_bf16"]["TFLOP_per_s"] if dom.bound == "mfma" else ceil["hbm_copy_1GiB"]["GB_per_s"]
+    roof["measured_ceiling"] = c
+    roof["frac_of_measured_ceiling"] = round(roof["achieved"] / c, 4)
 
     res = {
         "metric": "GB/s (%HBM peak) per det_* kernel; det/atomic time ratio; bitwise replay",
