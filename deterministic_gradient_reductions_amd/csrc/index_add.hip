@@ -48,11 +48,12 @@ inline __host__ __device__ int hist_stride(int64_t n_rows) { return static_cast<
 constexpr int kMaxGroups = kMaxRows / 256;  // workgroups of the offsets kernel (one thread per id)
 
 struct Layout {
-  size_t hist, segtot, wg_tot, seg_off, chunk_off, full_off, chunk_desc, perm, scratch, coef, total;
+  size_t hist, segtot, wg_tot, seg_off, chunk_off, full_off, chunk_desc, perm, scratch, coef, pairs, total;
   int64_t nblk, nseg, max_chunks;
 };
 
-// coef: the fused indexer dK's per-slot coefficients [n_src] float32 follow.
+// coef: the fused indexer dK's per-slot coefficients [n_src] float32 follow,
+// then its sorted order as (slot, coefficient) pairs [n_src] (in place of perm).
 Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L, bool coef = false) {
   Layout l;
   l.nblk = ceil_div(n_src, kBlockPos);
@@ -69,6 +70,7 @@ Layout layout(int64_t n_src, int64_t dim, int64_t n_rows, int64_t L, bool coef =
   l.perm = o;      o = align_up(o + static_cast<size_t>(n_src) * 4, 256);
   l.scratch = o;   o = align_up(o + static_cast<size_t>(l.max_chunks * dim) * 4, 256);
   l.coef = o;      o = coef ? align_up(o + static_cast<size_t>(n_src) * 4, 256) : o;
+  l.pairs = o;     o = coef ? align_up(o + static_cast<size_t>(n_src) * 8, 256) : o;
   l.total = o;
   return l;
 }
@@ -374,7 +376,11 @@ __global__ __launch_bounds__(256) void ia_offsets(int n_rows, int L, uint32_t rc
 //           count: a stable counting sort. Within one wave the LDS read of an
 //           id's running count precedes its leader's update in program order,
 //           so no barrier is needed, and the chain touches only LDS.
-//   store:  all waves write perm[destination] = p for the block's positions.
+//   store:  all waves write perm[destination] = p for the block's positions
+//           (for the fused indexer dK the pair (p, coefficient of slot p)
+//           instead: one 8-byte store, and the gather then reads every
+//           coefficient in the sorted order instead of one random 4-byte
+//           read per row).
 // Packed match result: id (14 bits) | rank << 14 (6 bits) | size << 20 (7
 // bits, 0 except at the group's lowest lane); -1 for ids out of range.
 constexpr uint32_t kPackRank = 14, kPackSize = 20;
@@ -385,7 +391,9 @@ __global__ __launch_bounds__(kSortThreads, 8) void ia_scatter(const int32_t* __r
                                                               const uint16_t* __restrict__ prefix,
                                                               const uint32_t* __restrict__ segbase,
                                                               const uint32_t* __restrict__ seg_off,
-                                                              int32_t* __restrict__ perm) {
+                                                              int32_t* __restrict__ perm,
+                                                              const float* __restrict__ coef_in,
+                                                              int2* __restrict__ pairs) {
   extern __shared__ uint32_t lds[];
   uint32_t* tab = lds;                                           // [NW][tab_ld], tab_ld = n_rows rounded up to 4
   int32_t* lid = reinterpret_cast<int32_t*>(lds + NW * tab_ld);  // [kBlockPos]
@@ -486,11 +494,25 @@ __global__ __launch_bounds__(kSortThreads, 8) void ia_scatter(const int32_t* __r
     }
   }
   __syncthreads();
+  constexpr int kPerT = kBlockPos / kSortThreads;
+  float cv[kPerT];
+  if (coef_in) {
 #pragma unroll
-  for (int u = 0; u < kBlockPos / kSortThreads; ++u) {
+    for (int u = 0; u < kPerT; ++u) {
+      const int64_t p = p0 + tid + kSortThreads * u;
+      cv[u] = p < p1 ? coef_in[p] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPerT; ++u) {
     const int pos = tid + kSortThreads * u;
     const int32_t d = lid[pos];
-    if (d >= 0) perm[d] = static_cast<int32_t>(p0 + pos);
+    if (d >= 0) {
+      if (coef_in)
+        pairs[d] = make_int2(static_cast<int32_t>(p0 + pos), __float_as_int(cv[u]));
+      else
+        perm[d] = static_cast<int32_t>(p0 + pos);
+    }
   }
 }
 
@@ -506,7 +528,8 @@ int scatter_waves(int64_t n_rows) {
 
 template <int NW>
 void launch_scatter(int64_t nblk, int n_rows, hipStream_t st, const int32_t* ids, int64_t n_src,
-                    const uint16_t* hist, const uint32_t* segtot, const uint32_t* seg_off, int32_t* perm) {
+                    const uint16_t* hist, const uint32_t* segtot, const uint32_t* seg_off, int32_t* perm,
+                    const float* coef_in, int2* pairs) {
   const int pad_rows = (n_rows + 3) / 4 * 4;  // table rows padded for 16-byte zeroing
   const size_t lds = static_cast<size_t>(NW) * pad_rows * 4 + kBlockPos * 4;
   if (lds > 64 * 1024) {
@@ -518,7 +541,7 @@ void launch_scatter(int64_t nblk, int n_rows, hipStream_t st, const int32_t* ids
     }
   }
   hipLaunchKernelGGL(ia_scatter<NW>, dim3(static_cast<uint32_t>(nblk)), dim3(kSortThreads), lds, st, ids, n_src, n_rows,
-                     pad_rows, hist_stride(n_rows), hist, segtot, seg_off, perm);
+                     pad_rows, hist_stride(n_rows), hist, segtot, seg_off, perm, coef_in, pairs);
 }
 
 // Binary search: the id whose chunk range [chunk_off[k], chunk_off[k+1]) holds c.
@@ -685,7 +708,8 @@ __device__ __forceinline__ uint4 zero_vec(uint4) { return make_uint4(0u, 0u, 0u,
 // Source rows made on the fly (the fused indexer dK): source row p is
 // RN32(coef[p] * q[p / K]), q being the bf16 query rows (row stride q_ld).
 struct FusedSrc {
-  const float* coef;
+  const float* coef;         // by slot p (the atomic arm)
+  const int2* pairs;         // by sorted row r: (slot, coefficient bits) (the gather)
   uint32_t K, krcp;
 };
 
@@ -732,23 +756,29 @@ __global__ __launch_bounds__(256) void ia_gather_wave(const uint16_t* __restrict
   for (int i = 0; i < DPL; ++i) acc[i] = -0.0f;
   // NPOS * 64 >= the chunk length: positions beyond len are never read
   int32_t pos[NPOS];
-#pragma unroll
-  for (int i = 0; i < NPOS; ++i) {
-    const bool ok = 64 * i + lane < len;
-    const int32_t x = perm[ok ? r0 + 64 * i + lane : r0];
-    pos[i] = ok ? x : 0;
-  }
-  // fused source: each lane turns its positions into query rows and loads
-  // their coefficients once (rows past the chunk end take 1.0, see below)
+  // fused source: the sorted (slot, coefficient) pairs; each lane turns its
+  // slots into query rows once (rows past the chunk end take 1.0, see below)
   int32_t qrow[NPOS];
   float cf[NPOS];
+#pragma unroll
+  for (int i = 0; i < NPOS; ++i) {
+    const bool in = 64 * i + lane < len;
+    if (FUSED) {
+      const int2 pr = fz.pairs[in ? r0 + 64 * i + lane : r0];
+      pos[i] = in ? pr.x : 0;
+      cf[i] = in ? __int_as_float(pr.y) : 1.0f;
+    } else {
+      const int32_t x = perm[in ? r0 + 64 * i + lane : r0];
+      pos[i] = in ? x : 0;
+    }
+  }
   if (FUSED) {
 #pragma unroll
     for (int i = 0; i < NPOS; ++i) {
       const bool ok = 64 * i + lane < len && pos[i] >= 0 && pos[i] < n_src;
       const uint32_t pp = ok ? static_cast<uint32_t>(pos[i]) : 0u;
       qrow[i] = static_cast<int32_t>(floor_div_rcp(pp, fz.K, fz.krcp));
-      cf[i] = ok ? fz.coef[pp] : 1.0f;
+      if (!ok) cf[i] = 1.0f;
     }
   }
   // a single-chunk id adds into out directly: its out row is fetched now,
@@ -1333,10 +1363,13 @@ int pipeline(const Layout& l, void* ws, float* out, int64_t n_rows, int64_t dim,
   hipLaunchKernelGGL(ia_totals, off_grid, dim3(256), 0, st, segtot, l.nseg, nr, L, rcp, wg_tot, seg_off);
   hipLaunchKernelGGL(ia_offsets, off_grid, dim3(256), 0, st, nr, L, rcp, n_src, wg_tot, seg_off, chunk_off, full_off,
                      chunk_desc, hdr);
+  // the fused indexer dK's coefficients follow the positions into the sorted order
+  const float* coef_in = fz ? fz->coef : nullptr;
+  int2* pairs = fz ? reinterpret_cast<int2*>(w + l.pairs) : nullptr;
   switch (scatter_waves(n_rows)) {
-    case 4: launch_scatter<4>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
-    case 2: launch_scatter<2>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
-    default: launch_scatter<1>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm); break;
+    case 4: launch_scatter<4>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm, coef_in, pairs); break;
+    case 2: launch_scatter<2>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm, coef_in, pairs); break;
+    default: launch_scatter<1>(l.nblk, nr, st, ids, n_src, hist, segtot, seg_off, perm, coef_in, pairs); break;
   }
   const int64_t grid_g = ceil_div(l.max_chunks, 256 / gs);
 #define DET_IA_TAIL_T(G, E, S)                                                                                  \
@@ -1544,6 +1577,7 @@ extern "C" int det_indexer_dk(float* dk, int64_t n_rows, int64_t dim, int64_t dk
 #undef DET_IA_COEF
   FusedSrc fz;
   fz.coef = coef;
+  fz.pairs = atomic ? nullptr : reinterpret_cast<const int2*>(w + l.pairs);
   fz.K = static_cast<uint32_t>(K);
   fz.krcp = static_cast<uint32_t>(0xFFFFFFFFull / static_cast<uint64_t>(K));
   const auto* q16 = static_cast<const uint16_t*>(q);

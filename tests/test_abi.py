@@ -353,7 +353,7 @@ def test_indexer_dk_validation():
     assert L.det_indexer_dk_workspace_size(64, 512, 128, 100, None, 0, ctypes.byref(n)) == 0
     full = n.value
     assert L.det_index_add_workspace_size(64 * 512, 128, 100, None, 0, ctypes.byref(n)) == 0
-    assert full == n.value + 64 * 512 * 4
+    assert full == n.value + 3 * 64 * 512 * 4  # the coefficients by slot, then (slot, coefficient) pairs in sorted order
     dk, ids, pr, tg, q = P(0x10000000), P(0x20000000), P(0x30000000), P(0x40000000), P(0x50000000)
     ws = P(0x60000000)
     # float32 q, a NULL pointer, a short workspace, dk overlapping q: all refused before any launch

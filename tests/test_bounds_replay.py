@@ -361,7 +361,9 @@ def replay_index_add(ids, n_rows, dim, L, Q=None, K=None):
         inside("index_add src rows", pos, n_src)
     else:
         inside("indexer_dk query rows", pos // K, Q)
-        inside("indexer_dk coef slots", pos, n_src)
+        inside("indexer_dk coef slots (scatter, by slot)", pos, n_src)
+        # the gather reads (slot, coefficient) pairs in the sorted order: entries r0 .. r0 + len - 1
+        inside("indexer_dk sorted pairs", np.concatenate([r0, r0 + ln - 1]), n_src)
     inside("index_add out rows", k[slot < 0], n_rows)
     # fold: the chunk partials of every id with more than one chunk
     multi = nc > 1
