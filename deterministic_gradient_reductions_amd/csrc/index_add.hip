@@ -30,6 +30,8 @@
 //
 // The atomic arm adds each src row into out[id] with per-element hardware float
 // atomics and no sort, as a non-deterministic index_add does.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace detgrad {
@@ -919,6 +921,134 @@ __global__ __launch_bounds__(256) void ia_gather_buf(const uint16_t* __restrict_
   for (int i = 0; i < DPL; ++i) dst[i] = (slot < 0 ? o[i] + acc[i] : acc[i]);
 }
 
+// The fused gather at dim 128: four chunks per wave, a 16-lane group per chunk
+// and 8 dims per lane, so a query row is one 16-byte load per lane and a wave
+// instruction reads four rows (a quarter of the load instructions of the
+// one-wave-per-chunk form, whose 4-byte loads of L2-resident query rows are
+// limited by the address units). Lane lg of a group holds the (slot,
+// coefficient) pairs of rows lg, lg + 16, ...; row r's query-row offset and
+// coefficient reach the group by a DPP row broadcast from lane r % 16. Each
+// group folds its own chunk left to right from -0.0; rows past a group's
+// chunk end load nothing (offset outside the resource) and add -0.0 times
+// 1.0, which leaves its sum bitwise unchanged. A wave runs as many rows as
+// its longest chunk (the descriptor list gives the full chunks first, so most
+// waves hold four chunks of equal length).
+constexpr int kQuadInFlight = 4;  // rows of each group in flight (fewer registers, more waves per SIMD)
+
+template <int R>
+__device__ __forceinline__ uint32_t row_bcast16(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x150 + R, 0xF, 0xF, false));
+}
+
+// Steps U.. of block B (rows B * KB + U): add the row that leaves the window,
+// load the row KB ahead into its place.
+template <bool UNI, int KB, int B, int U>
+__device__ __forceinline__ void quad_steps(__amdgpu_buffer_rsrc_t rs, int32_t lgoff, const uint32_t (&off)[16],
+                                           const uint32_t (&cf)[16], int len, float (&acc)[8], uint4 (&buf)[KB]) {
+  if constexpr (U < KB) {
+    constexpr int r = B * KB + U;
+    const uint4 x = buf[U];
+    if constexpr (r + KB < 256)
+      buf[U] = buf_load<uint4>(rs, static_cast<int32_t>(row_bcast16<(r + KB) % 16>(off[(r + KB) / 16])) + lgoff, 0);
+    const uint4 v = (UNI || r < len) ? x : make_uint4(0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u);
+    add_scaled_bf16(acc, v, __uint_as_float(row_bcast16<r % 16>(cf[r / 16])));
+    quad_steps<UNI, KB, B, U + 1>(rs, lgoff, off, cf, len, acc, buf);
+  }
+}
+
+template <bool UNI, int KB, int B>
+__device__ __forceinline__ void quad_blocks(__amdgpu_buffer_rsrc_t rs, int32_t lgoff, const uint32_t (&off)[16],
+                                            const uint32_t (&cf)[16], int len, int lmax, float (&acc)[8],
+                                            uint4 (&buf)[KB]) {
+  if constexpr (B * KB < 256) {
+    if (B * KB >= lmax) return;  // wave-uniform
+    quad_steps<UNI, KB, B, 0>(rs, lgoff, off, cf, len, acc, buf);
+    quad_blocks<UNI, KB, B + 1>(rs, lgoff, off, cf, len, lmax, acc, buf);
+  }
+}
+
+template <int KB, int U>
+__device__ __forceinline__ void quad_prologue(__amdgpu_buffer_rsrc_t rs, int32_t lgoff, const uint32_t (&off)[16],
+                                              uint4 (&buf)[KB]) {
+  if constexpr (U < KB) {
+    buf[U] = buf_load<uint4>(rs, static_cast<int32_t>(row_bcast16<U % 16>(off[U / 16])) + lgoff, 0);
+    quad_prologue<KB, U + 1>(rs, lgoff, off, buf);
+  }
+}
+
+// UNI: all four chunks have the wave's length (a multiple of KB): no per-row select.
+template <bool UNI, int KB>
+__device__ __forceinline__ void quad_run(std::integral_constant<bool, UNI>, __amdgpu_buffer_rsrc_t rs, int32_t lgoff,
+                                         const uint32_t (&off)[16], const uint32_t (&cf)[16], int len, int lmax,
+                                         float (&acc)[8]) {
+  uint4 buf[KB];
+  quad_prologue<KB, 0>(rs, lgoff, off, buf);
+  quad_blocks<UNI, KB, 0>(rs, lgoff, off, cf, len, lmax, acc, buf);
+}
+
+__global__ __launch_bounds__(256) void ia_gather_quad(const uint16_t* __restrict__ q, int64_t q_ld, uint32_t q_bytes,
+                                                      const uint32_t* __restrict__ chunk_off,
+                                                      const int4* __restrict__ desc, int n_rows,
+                                                      float* __restrict__ out, int64_t out_ld,
+                                                      float* __restrict__ scratch, int64_t n_src, int64_t max_chunks,
+                                                      FusedSrc fz) {
+  constexpr int KB = kQuadInFlight;
+  const int lane = threadIdx.x & 63, lg = lane & 15;
+  const uint32_t c0 = 4 * (static_cast<uint32_t>(blockIdx.x) * 4 + (threadIdx.x >> 6));
+  if (c0 >= max_chunks) return;  // wave-uniform
+  const uint32_t n_chunks = chunk_off[n_rows];
+  if (c0 >= n_chunks) return;  // wave-uniform
+  const uint32_t c = c0 + (lane >> 4);
+  const bool live = c < n_chunks && c < max_chunks;
+  const int4 dsc = desc[live ? c : c0];
+  const int k = dsc.x;
+  const uint32_t r0 = static_cast<uint32_t>(dsc.y);
+  const int len = live ? dsc.z : 0;
+  const int slot = dsc.w;
+  const int l0 = __builtin_amdgcn_readlane(len, 0), l1 = __builtin_amdgcn_readlane(len, 16);
+  const int l2 = __builtin_amdgcn_readlane(len, 32), l3 = __builtin_amdgcn_readlane(len, 48);
+  const int lmax = max(max(l0, l1), max(l2, l3));
+  const bool uni = l0 == lmax && l1 == lmax && l2 == lmax && l3 == lmax && lmax % KB == 0;
+  const uint32_t row_bytes = static_cast<uint32_t>(q_ld) * 2u;
+  uint32_t off[16], cf[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = lg + 16 * i;
+    const bool in = t < len;
+    const int2 pr = fz.pairs[in ? r0 + t : r0];
+    const bool ok = in && pr.x >= 0 && pr.x < n_src;  // always a valid slot
+    const uint32_t pp = ok ? static_cast<uint32_t>(pr.x) : 0u;
+    off[i] = in ? floor_div_rcp(pp, fz.K, fz.krcp) * row_bytes : 0x80000000u;
+    cf[i] = in ? static_cast<uint32_t>(pr.y) : __float_as_uint(1.0f);
+  }
+  const int d0 = 8 * lg;
+  float* const dst = slot < 0 ? out + static_cast<int64_t>(k) * out_ld + d0 : scratch + static_cast<int64_t>(slot) * 128 + d0;
+  float4 oa = make_float4(0.0f, 0.0f, 0.0f, 0.0f), ob = oa;
+  if (live && slot < 0) {
+    oa = *reinterpret_cast<const float4*>(dst);
+    ob = *reinterpret_cast<const float4*>(dst + 4);
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = -0.0f;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(q), 0,
+                                                                      static_cast<int>(q_bytes), 0x00020000);
+  if (uni)
+    quad_run<true, KB>(std::integral_constant<bool, true>(), rs, d0 * 2, off, cf, len, lmax, acc);
+  else
+    quad_run<false, KB>(std::integral_constant<bool, false>(), rs, d0 * 2, off, cf, len, lmax, acc);
+  if (!live) return;
+  if (slot < 0) {
+    oa.x = oa.x + acc[0]; oa.y = oa.y + acc[1]; oa.z = oa.z + acc[2]; oa.w = oa.w + acc[3];
+    ob.x = ob.x + acc[4]; ob.y = ob.y + acc[5]; ob.z = ob.z + acc[6]; ob.w = ob.w + acc[7];
+  } else {
+    oa = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    ob = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+  *reinterpret_cast<float4*>(dst) = oa;
+  *reinterpret_cast<float4*>(dst + 4) = ob;
+}
+
 // Chunks longer than GS * 16 rows (a large chunk_rows setting): one lane group
 // walks the rows with the permutation read as it goes.
 template <int GS, typename E>
@@ -1395,6 +1525,13 @@ int pipeline(const Layout& l, void* ws, float* out, int64_t n_rows, int64_t dim,
     // stored source rows below 2^31 bytes: the buffer-resource gather
     const bool bufok = !fz && n_src * src_ld * 2 < (static_cast<int64_t>(1) << 31);
     const uint32_t src_bytes = bufok ? static_cast<uint32_t>(n_src * src_ld * 2) : 0u;
+    // fused at dim 128 with chunks of at most 256 rows and query rows below 2^31 bytes: four chunks per wave
+    const int64_t q_bytes = fz ? n_src / fz->K * src_ld * 2 : 0;
+    const bool quad = fz && dim == 128 && L <= 256 && q_bytes < (static_cast<int64_t>(1) << 31);
+    if (quad)
+      hipLaunchKernelGGL(ia_gather_quad, dim3(ceil_div(l.max_chunks, 16)), dim3(256), 0, st, s16, src_ld,
+                         static_cast<uint32_t>(q_bytes), chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src,
+                         l.max_chunks, *fz);
 #define DET_IA_WAVE(D, NP)                                                                                      \
   if (!fz && dpl == D && L <= 64 * NP && (NP == 4 || L > 64 * (NP / 2))) {                                      \
     if (bufok)                                                                                                  \
@@ -1404,7 +1541,7 @@ int pipeline(const Layout& l, void* ws, float* out, int64_t n_rows, int64_t dim,
       hipLaunchKernelGGL((ia_gather_wave<D, NP>), dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim, perm,   \
                          chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks, FusedSrc{});   \
   }                                                                                                             \
-  if (fz && dpl == D && L <= 64 * NP && (NP == 4 || L > 64 * (NP / 2)))                                         \
+  if (!quad && fz && dpl == D && L <= 64 * NP && (NP == 4 || L > 64 * (NP / 2)))                                \
     hipLaunchKernelGGL((ia_gather_wave<D, NP, true>), dim3(grid_w), dim3(256), 0, st, s16, src_ld, (int)dim,      \
                        perm, chunk_off, chunk_desc, nr, out, out_ld, scratch, n_src, l.max_chunks, *fz);
     DET_IA_WAVE(2, 4) DET_IA_WAVE(2, 8) DET_IA_WAVE(2, 16)
