@@ -12,17 +12,20 @@
 //  3. scan     per-workgroup totals of the counts, then exclusive scans of the
 //              counts (segment offsets of the sorted order) and of
 //              ceil(count / L) (chunk offsets), and the chunk descriptors.
-//  4. scatter  one wave per block walks its positions in order, 64 at a time;
-//              the lanes holding the same id find each other with one ballot
-//              per id bit, so each lane's rank among equal ids is its position
-//              order inside the batch plus the id's running LDS count: a stable
-//              counting sort. perm[seg_off[id] + prefix + rank] = p.
+//  4. scatter  per block, the lanes holding the same id in a batch of 64
+//              positions find each other with one ballot per id bit, so each
+//              lane's rank among equal ids is its position order inside the
+//              batch plus the id's running LDS count, walked batch by batch: a
+//              stable counting sort. perm[seg_off[id] + prefix + rank] = p (the
+//              fused indexer dK stores the pair (p, coefficient of p) there).
 //  5. gather   one wave (or lane group) per chunk of L sorted rows of one id:
 //              each lane owns consecutive dims of the row and folds the
 //              chunk's rows left to right. Stored bf16 rows below 2^31 bytes
 //              are read through a buffer resource with a rolling window of
-//              row loads in flight. A single-chunk id is added into out
-//              directly; otherwise the partial goes to scratch.
+//              row loads in flight; the fused indexer dK at dim 128 takes four
+//              chunks per wave with 16-byte loads of its query rows. A
+//              single-chunk id is added into out directly; otherwise the
+//              partial goes to scratch.
 //  6. fold     ids with several chunks fold their chunk partials left to right
 //              and add the total into out once.
 // Traffic: the src rows of valid ids (256 B per row at dim 128) dominate;
