@@ -1647,7 +1647,9 @@ extern "C" int det_index_add_bad_ids(const void* ws, size_t ws_bytes, int64_t* c
 namespace {
 int indexer_dk_check(int64_t Q, int64_t K, int64_t dim, int64_t n_rows, const det_index_add_cfg* cfg, int* L) {
   if (Q < 0 || K < 0) return set_error(DET_ERR_INVALID_ARG, "indexer_dk: Q and K must be >= 0");
-  if (K > 1024) return set_error(DET_ERR_UNSUPPORTED, "indexer_dk: K must be <= 1024, got %lld", static_cast<long long>(K));
+  if (K > kCoefMaxPieces * kCoefPiece)
+    return set_error(DET_ERR_UNSUPPORTED, "indexer_dk: K must be <= %d, got %lld", kCoefMaxPieces * kCoefPiece,
+                     static_cast<long long>(K));
   if (Q * K > 0x7FFFFFFFLL) return set_error(DET_ERR_UNSUPPORTED, "indexer_dk: Q * K must be < 2^31");
   if (int s = check_shape(Q * K, dim, n_rows)) return s;
   if (int s = resolve(cfg, L)) return s;
