@@ -39,6 +39,8 @@ struct ColsumArgs {
   float* ddt_bias;
   float* slot1;      // [S][H]
   float* slot2;      // [S][H]
+  int64_t n_tiles;   // S
+  int n_hg;          // head groups: ceil(H / block_h)
   void* da;          // [T, H] in the input type, or NULL
   int64_t da_st, da_sh;
 };
@@ -76,39 +78,64 @@ __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
   __shared__ float red1[kWG];
   __shared__ float red2[kWG];
 
+  // XCD-aware order. Workgroups are dispatched to the 8 XCDs round-robin
+  // (workgroup u runs on XCD u % 8) and each XCD has its own L2. Workgroup
+  // u = 8 * n_hg * c + 8 * j + x takes tile 8c + x and head group j, so the
+  // head groups of one tile run back to back on one XCD: a head group reads
+  // block_h of a row's H elements, and the row's other head groups then find
+  // its cache lines in that XCD's L2 instead of fetching them again.
+  const uint32_t u = blockIdx.x;
+  const uint32_t per = 8u * static_cast<uint32_t>(p.n_hg);
+  const uint32_t r = u % per;
+  const int64_t tile = static_cast<int64_t>(u / per) * 8 + (r & 7u);
+  if (tile >= p.n_tiles) return;  // the last group of 8 tiles may be short
   const int tid = threadIdx.x;
   const int hl = tid % BH;
   const int rb = tid / BH;
-  const int64_t h = static_cast<int64_t>(blockIdx.y) * BH + hl;
-  const int64_t tile = blockIdx.x;
+  const int64_t h = static_cast<int64_t>(r >> 3) * BH + hl;
   const int64_t r0 = tile * kBT + static_cast<int64_t>(rb) * R;
 
   float v1[R], v2[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    v1[i] = -0.0f;
+    v2[i] = -0.0f;
+  }
   if (h < p.H) {
     const float nA = -dm::exp32(p.A_log[h]);
     const float bias = p.dt_bias[h];
+    // row r0 of head h; row r0 + i is i row strides further (the strides are
+    // uniform, so each row costs one 64-bit address add)
+    const TIn* const ra = pa + r0 * p.a_st + h * p.a_sh;
+    const TIn* const rd = pdg + r0 * p.dg_st + h * p.dg_sh;
+    // All of the thread's loads are issued before any math, so their latencies
+    // overlap (da, when it is written, overlaps no input: the host checks that).
+    float xa[R], xd[R];
+    auto term = [&](int i) {
+      float sp, sg;
+      dm::softplus_sigmoid(xa[i], sp, sg);
+      v1[i] = xd[i] * (nA * sp);
+      v2[i] = xd[i] * (nA * sg);
+      if (p.da) gate_out(static_cast<TIn*>(p.da), (r0 + i) * p.da_st + h * p.da_sh, v2[i]);  // da = the ddt_bias term
+    };
+    if ((tile + 1) * kBT <= p.T) {  // every row of the tile exists (all tiles but a tail)
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int64_t t = r0 + i;
-      if (t < p.T) {
-        const float x = gate_in(pa, t * p.a_st + h * p.a_sh) + bias;
-        const float d = gate_in(pdg, t * p.dg_st + h * p.dg_sh);
-        const float e = dm::exp32(dm::neg_abs(x));
-        const float sp = dm::softplus_e(x, e);
-        const float sg = dm::sigmoid_e(x, e);
-        v1[i] = d * (nA * sp);
-        v2[i] = d * (nA * sg);
-        if (p.da) gate_out(static_cast<TIn*>(p.da), t * p.da_st + h * p.da_sh, v2[i]);  // da = the ddt_bias term
-      } else {
-        v1[i] = -0.0f;
-        v2[i] = -0.0f;
+      for (int i = 0; i < R; ++i) {
+        xa[i] = gate_in(ra, i * p.a_st) + bias;
+        xd[i] = gate_in(rd, i * p.dg_st);
       }
-    }
-  } else {
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      v1[i] = -0.0f;
-      v2[i] = -0.0f;
+      for (int i = 0; i < R; ++i) term(i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const bool in = r0 + i < p.T;
+        xa[i] = in ? gate_in(ra, i * p.a_st) + bias : 0.0f;
+        xd[i] = in ? gate_in(rd, i * p.dg_st) : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        if (r0 + i < p.T) term(i);
     }
   }
   red1[rb * BH + hl] = tree_regs<R>(v1);
@@ -137,46 +164,71 @@ __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
 }
 
 // Phase 2: fold the tile slots of every head left to right and add the totals.
-// One wave per (head, gradient). Lane j loads tiles j, j + 64, j + 128 and
-// j + 192 of a round of 256 tiles (the next round's loads are in flight while
-// a round is added; tiles past S read as -0.0, which leaves the sum bitwise
-// unchanged). The values are then added in tile order through readlane: one
-// dependent add per tile, the same in every lane.
-constexpr int kFoldRound = 256;
-
-__device__ __forceinline__ void fold_load(float (&v)[4], const float* s, int64_t i0, int64_t S, int64_t H,
-                                          int lane) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t i = i0 + lane + 64 * q;
-    v[q] = i < S ? s[i * H] : -0.0f;
-  }
-}
-
-__device__ __forceinline__ float fold_add(const float (&v)[4], float tot) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int j = 0; j < 64; ++j) tot = tot + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[q]), j));
-  return tot;
-}
+// One wave per (head, gradient); the fold is one chain of dependent adds, so
+// its time is the chain's length times the add's issue latency. Rounds of 1024
+// tiles: lane j loads tiles 16j .. 16j + 15 of the round (the next round's
+// loads are in flight while a round is added) and parks them in LDS; the chain
+// then reads four consecutive tiles at a time with one LDS read that every
+// lane makes at the same address, so each tile costs one add with a register
+// operand. Tiles past S read as -0.0, which leaves the sum bitwise unchanged.
+constexpr int kFoldRound = 1024;
+constexpr int kFoldPerLane = kFoldRound / 64;
+constexpr int kFoldAhead = 8;  // LDS reads in flight ahead of the chain
 
 __global__ __launch_bounds__(64) void colsum_fold_kernel(const float* __restrict__ slot1,
                                                          const float* __restrict__ slot2, int64_t S, int64_t H,
                                                          float* __restrict__ dA_log, float* __restrict__ ddt_bias) {
+  __shared__ float4 park[kFoldRound / 4];
   const int lane = threadIdx.x;
   const int64_t h = blockIdx.x;
   const bool second = blockIdx.y != 0;
   const float* const s = (second ? slot2 : slot1) + h;
+  float v[kFoldPerLane];
+  auto load = [&](int64_t i0) {
+#pragma unroll
+    for (int k = 0; k < kFoldPerLane; ++k) {
+      const int64_t i = i0 + kFoldPerLane * lane + k;
+      v[k] = i < S ? s[i * H] : -0.0f;
+    }
+  };
   float tot = -0.0f;
-  float va[4], vb[4];
-  fold_load(va, s, 0, S, H, lane);
-  for (int64_t i0 = 0; i0 < S; i0 += 2 * kFoldRound) {
-    if (i0 + kFoldRound < S) fold_load(vb, s, i0 + kFoldRound, S, H, lane);
-    tot = fold_add(va, tot);
-    if (i0 + kFoldRound >= S) break;
-    if (i0 + 2 * kFoldRound < S) fold_load(va, s, i0 + 2 * kFoldRound, S, H, lane);
-    tot = fold_add(vb, tot);
+  load(0);
+  for (int64_t i0 = 0; i0 < S; i0 += kFoldRound) {
+    // the previous round's LDS reads precede these writes in the wave's order
+#pragma unroll
+    for (int q = 0; q < kFoldPerLane / 4; ++q)
+      park[(kFoldPerLane / 4) * lane + q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    if (i0 + kFoldRound < S) load(i0 + kFoldRound);
+    const int64_t left = S - i0;
+    if (left >= kFoldRound) {
+      // a whole round, unrolled, with each LDS read issued kFoldAhead steps
+      // before the adds that use it (the scheduling barriers keep that order)
+      float4 w[kFoldAhead];
+#pragma unroll
+      for (int q = 0; q < kFoldAhead; ++q) w[q] = park[q];
+#pragma unroll
+      for (int q = 0; q < kFoldRound / 4; ++q) {
+        const float4 x = w[q % kFoldAhead];
+        if (q + kFoldAhead < kFoldRound / 4) w[q % kFoldAhead] = park[q + kFoldAhead];
+        tot = tot + x.x;
+        tot = tot + x.y;
+        tot = tot + x.z;
+        tot = tot + x.w;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      const int n16 = static_cast<int>((left + 15) / 16);
+      for (int g = 0; g < n16; ++g) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 w = park[4 * g + q];
+          tot = tot + w.x;
+          tot = tot + w.y;
+          tot = tot + w.z;
+          tot = tot + w.w;
+        }
+      }
+    }
   }
   if (lane == 0) {
     float* const o = (second ? ddt_bias : dA_log) + h;
@@ -204,12 +256,13 @@ void launch_one(const ColsumArgs& p, int atomic, dim3 grid, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((colsum_kernel<R, BH, false, TIn>), grid, dim3(kWG), 0, st, p);
     hipLaunchKernelGGL(colsum_fold_kernel, dim3(static_cast<uint32_t>(p.H), 2), dim3(64), 0, st, p.slot1, p.slot2,
-                       static_cast<int64_t>(grid.x), p.H, p.dA_log, p.ddt_bias);
+                       p.n_tiles, p.H, p.dA_log, p.ddt_bias);
   }
 }
 
 void launch(const ColsumArgs& p, const det_colsum_cfg& c, int atomic, bool f32_in, hipStream_t st) {
-  const dim3 grid(static_cast<uint32_t>(ceil_div(p.T, c.block_t)), static_cast<uint32_t>(ceil_div(p.H, c.block_h)));
+  // groups of 8 tiles times the head groups (see colsum_kernel's order)
+  const dim3 grid(static_cast<uint32_t>(ceil_div(p.n_tiles, 8) * 8 * p.n_hg));
 #define DET_COLSUM_CASE(bt, bh) \
   if (c.block_t == bt && c.block_h == bh)                                                                 \
     return f32_in ? launch_one<bt, bh, float>(p, atomic, grid, st) : launch_one<bt, bh, uint16_t>(p, atomic, grid, st);
@@ -325,7 +378,7 @@ int colsum_entry(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int6
     return set_error(DET_ERR_INVALID_ARG, "colsum: NULL pointer");
   if (a_st < 1 || a_sh < 1 || dg_st < 1 || dg_sh < 1)
     return set_error(DET_ERR_INVALID_ARG, "colsum: element strides must be >= 1");
-  if (ceil_div(T, c.block_t) > 0x7FFFFFFF || ceil_div(H, c.block_h) > 65535)
+  if (ceil_div(H, c.block_h) > 65535 || ceil_div(ceil_div(T, c.block_t), 8) * 8 * ceil_div(H, c.block_h) > 0x7FFFFFFF)
     return set_error(DET_ERR_UNSUPPORTED, "colsum: problem too large for the launch grid");
   const size_t need = atomic ? 0 : ws_bytes_for(T, H, c);
   if (noalloc) {
@@ -377,6 +430,8 @@ int colsum_entry(const void* a, int64_t a_st, int64_t a_sh, const void* dg, int6
   const size_t slot_bytes = align_up(static_cast<size_t>(ceil_div(T, c.block_t) * H) * 4, 256);
   p.slot1 = atomic ? nullptr : reinterpret_cast<float*>(w + DET_WS_HEADER_BYTES);
   p.slot2 = atomic ? nullptr : reinterpret_cast<float*>(w + DET_WS_HEADER_BYTES + slot_bytes);
+  p.n_tiles = ceil_div(T, c.block_t);
+  p.n_hg = static_cast<int>(ceil_div(H, c.block_h));
   p.da = with_da ? da : nullptr;
   p.da_st = da_st;
   p.da_sh = da_sh;

@@ -19,6 +19,23 @@
 // softplus32(x) = x for x > 20 (PyTorch's default threshold), else
 //   max(x, +0) + log1p32(exp32(-|x|)).
 // sigmoid32(x) = (x >= 0 ? 1 : e) / (1 + e) with e = exp32(-|x|).
+//
+// The device evaluates these definitions with fewer instructions and the same
+// bits:
+// - exp32's scaling is one ldexp(p, k): p lies in [0.70, 1.42] and
+//   floor(k/2) >= -75 wherever the result is used, so p * 2^floor(k/2) is
+//   exact and the two multiplies round once, as ldexp does. The range cases
+//   are selects, not branches; a NaN input gives a NaN (its payload may differ).
+// - The gate's two quotients, y / (2 + y) and (1 or y) / (1 + y) with
+//   y = exp32(-|x|) in [0, 1], use the correctly rounded division sequence
+//   (a reciprocal, one Newton step, a quotient and two remainder corrections
+//   with fused multiply-adds) without its operand scaling and special-case
+//   fixup. The denominator lies in [1, 3], so the scaling never applies for
+//   y >= 2^-24. Below that the denominator rounds to exactly 1 or 2, every
+//   remainder is exact in the subnormal range, and the corrections land on
+//   the correctly rounded quotient.
+// Every float32 input of exp32, softplus32 and sigmoid32 has been compared
+// with the CPU sequences.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,12 +49,9 @@ constexpr float kInvLn2 = 0x1.715476p+0f;  // bits 0x3FB8AA3B
 constexpr float kLn2Hi = 0x1.62e4p-1f;     // bits 0x3F317200
 constexpr float kLn2Lo = 0x1.7f7d1cp-20f;  // bits 0x35BFBE8E
 
-__device__ __forceinline__ float pow2i(int n) { return __uint_as_float(static_cast<uint32_t>(n + 127) << 23); }
-
-__device__ __forceinline__ float exp32(float x) {
-  if (x != x) return x;
-  if (x > 89.0f) return __builtin_inff();
-  if (x < -104.0f) return 0.0f;
+// Polynomial and scaling of exp32 for a finite x in [-104, 89] (other x give
+// a value the callers replace).
+__device__ __forceinline__ float exp32_core(float x) {
   const float kf = __builtin_rintf(x * kInvLn2);
   const float r = (x - kf * kLn2Hi) - kf * kLn2Lo;
   float p = 1.0f / 5040.0f;
@@ -48,14 +62,29 @@ __device__ __forceinline__ float exp32(float x) {
   p = p * r; p = p + 1.0f / 2.0f;
   p = p * r; p = p + 1.0f;
   p = p * r; p = p + 1.0f;
-  const int k = static_cast<int>(kf);
-  const int k1 = k >> 1;  // arithmetic shift: floor(k / 2)
-  const int k2 = k - k1;
-  return (p * pow2i(k1)) * pow2i(k2);
+  return __builtin_amdgcn_ldexpf(p, static_cast<int>(kf));
 }
 
-__device__ __forceinline__ float log1p32(float y) {
-  const float s = y / (2.0f + y);
+// (a NaN x fails both range tests and keeps the core's NaN)
+__device__ __forceinline__ float exp32(float x) {
+  const float y = exp32_core(x);
+  return x > 89.0f ? __builtin_inff() : (x < -104.0f ? 0.0f : y);
+}
+
+// exp32 of x <= 0 (or NaN), as the gate calls it: e = exp32(-|x|).
+__device__ __forceinline__ float exp32_nonpos(float x) { return x < -104.0f ? 0.0f : exp32_core(x); }
+
+// n / d, correctly rounded, for d in [1, 3] and n in [0, 1] (NaN propagates).
+__device__ __forceinline__ float div_unit(float n, float d) {
+  const float r0 = __builtin_amdgcn_rcpf(d);
+  const float r = __builtin_fmaf(__builtin_fmaf(-d, r0, 1.0f), r0, r0);
+  const float q0 = n * r;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-d, q0, n), r, q0);
+  return __builtin_fmaf(__builtin_fmaf(-d, q1, n), r, q1);
+}
+
+// 2 atanh(s) to the s^13 term, given s = y / (2 + y)
+__device__ __forceinline__ float log1p32_series(float s) {
   const float z = s * s;
   float q = 1.0f / 13.0f;
   q = q * z; q = q + 1.0f / 11.0f;
@@ -68,20 +97,16 @@ __device__ __forceinline__ float log1p32(float y) {
   return t + t * q;
 }
 
-// softplus32(x) given e = exp32(-|x|)
-__device__ __forceinline__ float softplus_e(float x, float e) {
+__device__ __forceinline__ float log1p32(float y) { return log1p32_series(y / (2.0f + y)); }
+
+// softplus32(x) and sigmoid32(x) from one e = exp32(-|x|) (e in [0, 1]).
+__device__ __forceinline__ void softplus_sigmoid(float x, float& sp, float& sg) {
+  const float e = exp32_nonpos(__uint_as_float(__float_as_uint(x) | 0x80000000u));
   const float m = x > 0.0f ? x : 0.0f;
-  const float small = m + log1p32(e);
-  return x > 20.0f ? x : small;
+  const float small = m + log1p32_series(div_unit(e, 2.0f + e));
+  sp = x > 20.0f ? x : small;
+  sg = div_unit(x >= 0.0f ? 1.0f : e, 1.0f + e);
 }
-
-// sigmoid32(x) given e = exp32(-|x|)
-__device__ __forceinline__ float sigmoid_e(float x, float e) {
-  const float num = x >= 0.0f ? 1.0f : e;
-  return num / (1.0f + e);
-}
-
-__device__ __forceinline__ float neg_abs(float x) { return __uint_as_float(__float_as_uint(x) | 0x80000000u); }
 
 }  // namespace dm
 }  // namespace detgrad

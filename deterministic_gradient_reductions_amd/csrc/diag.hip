@@ -91,12 +91,12 @@ __global__ void detmath_eval_kernel(const float* __restrict__ x, float* __restri
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const float v = x[i];
-  float r;
+  float r, sp, sg;
   switch (fn) {
     case 0: r = dm::exp32(v); break;
     case 1: r = dm::log1p32(v); break;
-    case 2: r = dm::softplus_e(v, dm::exp32(dm::neg_abs(v))); break;
-    default: r = dm::sigmoid_e(v, dm::exp32(dm::neg_abs(v))); break;
+    case 2: dm::softplus_sigmoid(v, sp, sg); r = sp; break;   // the gate's own evaluation
+    default: dm::softplus_sigmoid(v, sp, sg); r = sg; break;
   }
   y[i] = r;
 }

@@ -32,9 +32,39 @@ def cdiv(a, b):
 
 
 # ------------------------------------------------------------------ colsum
+def colsum_order(T, H, BT, BH):
+    """colsum_kernel's workgroup order: a 1-D grid of groups of 8 tiles times the head
+    groups; workgroup u = 8 * HG * c + 8 * j + x takes tile 8c + x and head group j and
+    exits when that tile is past the end. Returns (tile, head group) per workgroup, -1
+    for the exiting ones."""
+    S, HG = cdiv(T, BT), cdiv(H, BH)
+    u = np.arange(cdiv(S, 8) * 8 * HG, dtype=np.int64)
+    per = 8 * HG
+    r = u % per
+    tile = (u // per) * 8 + (r & 7)
+    hg = r >> 3
+    live = tile < S
+    return np.where(live, tile, -1), np.where(live, hg, -1)
+
+
+def test_colsum_order_covers_every_tile_once():
+    for T, H, BT, BH in [(16384, 32, 64, 8), (16323, 32, 256, 32), (4133, 17, 128, 16), (100, 5, 64, 8),
+                         (4194304, 32, 256, 8), (64 * 9, 40, 64, 8)]:
+        tile, hg = colsum_order(T, H, BT, BH)
+        S, HG = cdiv(T, BT), cdiv(H, BH)
+        live = tile >= 0
+        pairs = tile[live] * HG + hg[live]
+        assert np.array_equal(np.sort(pairs), np.arange(S * HG)), (T, H, BT, BH)
+        # the head groups of one tile sit on one XCD (u % 8) and run back to back
+        u = np.nonzero(live)[0]
+        assert np.all((u % 8) == (tile[live] % 8))
+
+
 def replay_colsum(T, H, BT, BH, tiles=None, dg_view=True):
     """colsum_kernel<R, BH> and colsum_fold_kernel; a is [T, H] contiguous, dg the
-    [T, 2H] base tensor viewed from column H (the gate backward's layout)."""
+    [T, 2H] base tensor viewed from column H (the gate backward's layout). The
+    workgroup order is colsum_order's (checked to cover every (tile, head group)
+    once), so the replay walks tiles and head groups directly."""
     R = BT * BH // WG
     kBT, S = R * WG // BH, cdiv(T, BT)
     assert kBT == BT
