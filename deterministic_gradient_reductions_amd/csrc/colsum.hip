@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kWG) void colsum_kernel(ColsumArgs p) {
 // operand. Tiles past S read as -0.0, which leaves the sum bitwise unchanged.
 constexpr int kFoldRound = 1024;
 constexpr int kFoldPerLane = kFoldRound / 64;
-constexpr int kFoldAhead = 8;  // LDS reads in flight ahead of the chain
+constexpr int kFoldAhead = 16;  // LDS reads in flight ahead of the chain
 
 __global__ __launch_bounds__(64) void colsum_fold_kernel(const float* __restrict__ slot1,
                                                          const float* __restrict__ slot2, int64_t S, int64_t H,

@@ -27,15 +27,14 @@
 //   exact and the two multiplies round once, as ldexp does. The range cases
 //   are selects, not branches; a NaN input gives a NaN (its payload may differ).
 // - The gate's two quotients, y / (2 + y) and (1 or y) / (1 + y) with
-//   y = exp32(-|x|) in [0, 1], use the correctly rounded division sequence
-//   (a reciprocal, one Newton step, a quotient and two remainder corrections
-//   with fused multiply-adds) without its operand scaling and special-case
-//   fixup. The denominator lies in [1, 3], so the scaling never applies for
-//   y >= 2^-24. Below that the denominator rounds to exactly 1 or 2, every
-//   remainder is exact in the subnormal range, and the corrections land on
-//   the correctly rounded quotient.
-// Every float32 input of exp32, softplus32 and sigmoid32 has been compared
-// with the CPU sequences.
+//   y = exp32(-|x|) in [0, 1], take a reciprocal, one Newton step, the
+//   quotient and one remainder correction with fused multiply-adds (Markstein's
+//   form: correctly rounded when the refined reciprocal is within half an ulp),
+//   with no operand scaling or special-case fixup: the denominator lies in
+//   [1, 3], and below y = 2^-24 it rounds to exactly 1 or 2, where every step is
+//   exact. That these quotients equal the correctly rounded ones for every x is
+//   established by comparing every float32 input of softplus32 and sigmoid32
+//   (and of exp32) with the CPU sequences, which divide with IEEE division.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -74,13 +73,13 @@ __device__ __forceinline__ float exp32(float x) {
 // exp32 of x <= 0 (or NaN), as the gate calls it: e = exp32(-|x|).
 __device__ __forceinline__ float exp32_nonpos(float x) { return x < -104.0f ? 0.0f : exp32_core(x); }
 
-// n / d, correctly rounded, for d in [1, 3] and n in [0, 1] (NaN propagates).
+// n / d for d in [1, 3] and n in [0, 1] (NaN propagates): correctly rounded for
+// the gate's operands (see above).
 __device__ __forceinline__ float div_unit(float n, float d) {
   const float r0 = __builtin_amdgcn_rcpf(d);
   const float r = __builtin_fmaf(__builtin_fmaf(-d, r0, 1.0f), r0, r0);
   const float q0 = n * r;
-  const float q1 = __builtin_fmaf(__builtin_fmaf(-d, q0, n), r, q0);
-  return __builtin_fmaf(__builtin_fmaf(-d, q1, n), r, q1);
+  return __builtin_fmaf(__builtin_fmaf(-d, q0, n), r, q0);
 }
 
 // 2 atanh(s) to the s^13 term, given s = y / (2 + y)
@@ -102,7 +101,7 @@ __device__ __forceinline__ float log1p32(float y) { return log1p32_series(y / (2
 // softplus32(x) and sigmoid32(x) from one e = exp32(-|x|) (e in [0, 1]).
 __device__ __forceinline__ void softplus_sigmoid(float x, float& sp, float& sg) {
   const float e = exp32_nonpos(__uint_as_float(__float_as_uint(x) | 0x80000000u));
-  const float m = x > 0.0f ? x : 0.0f;
+  const float m = __builtin_fmaxf(x, 0.0f);
   const float small = m + log1p32_series(div_unit(e, 2.0f + e));
   sp = x > 20.0f ? x : small;
   sg = div_unit(x >= 0.0f ? 1.0f : e, 1.0f + e);
