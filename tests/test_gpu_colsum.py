@@ -84,7 +84,10 @@ def test_tiny_shape_default_cfg_and_selector():
     assert_bitwise(r1, w1, "dA_log"); assert_bitwise(r2, w2, "ddt_bias")
 
 
-@pytest.mark.parametrize("T,H", [(1, 1), (63, 5), (1000, 40), (2049, 3), (300, 33), (33000, 2), (70001, 3)])
+# (700, 300): 38 head groups of 8 over tile groups of 8 with a short last group;
+# (300000, 3): a fold of several full 1024-tile rounds and a partial one at block_t 64
+@pytest.mark.parametrize("T,H", [(1, 1), (63, 5), (1000, 40), (2049, 3), (300, 33), (33000, 2), (70001, 3),
+                                 (700, 300), (300000, 3)])
 def test_ragged_heads_and_rows(T, H):
     inp = W.gate_inputs(T, H, seed=7, out_init="normal")
     for bt, bh in ((64, 8), (256, 32), (128, 16)):
