@@ -1340,6 +1340,7 @@ __global__ __launch_bounds__(256) void ia_atomic(const int32_t* __restrict__ ids
 constexpr uint32_t kEps100Bits = 0x0000001Bu;  // the float32 nearest e^-100 (27 * 2^-149)
 constexpr int kCoefPiece = 512;                // slots per piece: 64 lanes x 8
 constexpr int kCoefMaxPieces = 2;              // K <= 1024
+constexpr int kCoefAhead = 16;                 // LDS loads in flight ahead of the S chain
 
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
@@ -1387,14 +1388,35 @@ __global__ __launch_bounds__(256) void ia_coef(const int32_t* __restrict__ ids, 
       // max(target, eps) that keeps a NaN target, as numpy's maximum does
       kept[c][e] = valid ? (!(tg[c][e] <= eps) ? tg[c][e] : eps) : 0.0f;
     }
-  // S = ((-0 + kept_0) + kept_1) + ... in slot order; slot 512 c + 8 l + e sits in lane l, register (c, e)
+  // S = ((-0 + kept_0) + kept_1) + ... in slot order. Slot 512 c + 8 l + e sits
+  // in lane l, register (c, e); the wave parks the row's kept values in LDS in
+  // slot order and the chain reads four consecutive slots with one LDS load
+  // that every lane makes at the same address, each load issued kCoefAhead
+  // steps before its adds (so each slot costs one dependent add with a
+  // register operand). The wave reads only what it wrote itself, and a wave's
+  // LDS accesses complete in order.
+  __shared__ float4 park[4][PIECES * kCoefPiece / 4];
+  float4* const kw = park[threadIdx.x >> 6];
+#pragma unroll
+  for (int c = 0; c < PIECES; ++c) {
+    kw[c * (kCoefPiece / 4) + 2 * lane] = make_float4(kept[c][0], kept[c][1], kept[c][2], kept[c][3]);
+    kw[c * (kCoefPiece / 4) + 2 * lane + 1] = make_float4(kept[c][4], kept[c][5], kept[c][6], kept[c][7]);
+  }
+  constexpr int kN4 = PIECES * kCoefPiece / 4;
   float S = -0.0f;
+  float4 w[kCoefAhead];
 #pragma unroll
-  for (int c = 0; c < PIECES; ++c)
+  for (int q = 0; q < kCoefAhead; ++q) w[q] = kw[q];
 #pragma unroll
-    for (int l = 0; l < 64; ++l)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) S = S + readlane(kept[c][e], l);
+  for (int q = 0; q < kN4; ++q) {
+    const float4 x = w[q % kCoefAhead];
+    if (q + kCoefAhead < kN4) w[q % kCoefAhead] = kw[q + kCoefAhead];
+    S = S + x.x;
+    S = S + x.y;
+    S = S + x.z;
+    S = S + x.w;
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int c = 0; c < PIECES; ++c) {
     const int j0 = c * kCoefPiece + 8 * lane;
