@@ -10,10 +10,12 @@
 // these are the absolute M blocks), and the segment sum is a left-to-right fold
 // of the expert's slots, added once into dbias.
 //
-// Tile kernel: a workgroup owns one tile (block_m rows of one expert) and 512
-// columns; consecutive workgroups take the column blocks of one tile. Lane l
-// of each wave holds 8 consecutive columns (one 16-byte load per row, fully
-// coalesced); wave w takes the w-th quarter of the tile's rows and reduces it
+// Tile kernel: a workgroup owns one tile (block_m rows of one expert) and
+// block_n columns (512, 256 or 128: columns are independent, so the width
+// never changes a bit; narrower blocks give more workgroups, which evens out
+// the work per compute unit); consecutive workgroups take the column blocks of
+// one tile. Lane l of each wave holds block_n / 64 consecutive columns (one
+// 16-, 8- or 4-byte load per row, coalesced); wave w takes the w-th quarter of the tile's rows and reduces it
 // with the adjacent pairwise tree, fed row by row into a stack of partial
 // sums while the next 16 rows' loads are in flight (rows past the expert's
 // end are -0.0); the four quarter values meet in LDS as
@@ -30,7 +32,8 @@
 namespace detgrad {
 namespace {
 
-constexpr int kCols = 512;  // columns per workgroup: 64 lanes x 8
+// Columns per workgroup: 64 lanes x CPL (8, 4 or 2 columns per lane, one
+// 16-, 8- or 4-byte load per row), the configuration's block_n.
 
 // Inclusive scans over the 64 lanes on DPP (row shifts by 1, 2, 4, 8, then
 // the last lane of row 0 into rows 1 and 3 and of row 1 into rows 2 and 3);
@@ -97,16 +100,30 @@ __device__ bool tile_of(const int32_t* __restrict__ offs, int E, uint32_t M, int
   return false;
 }
 
-// Rows of one piece: 16-byte loads of 8 columns; a row at or past the
-// tile's end r1 loads row `safe` (< r1; a whole piece can lie past r1) and is
-// replaced by -0.0 when it is added.
-template <int P>
-__device__ __forceinline__ void load_piece(uint4 (&v)[P], const uint16_t* __restrict__ dA, int64_t lda, int64_t a,
-                                           int64_t r1, int64_t safe, int64_t col) {
+// One row of a lane's CPL columns as CPL / 2 words (two bf16 each).
+template <int CPL>
+__device__ __forceinline__ void load_row(uint32_t (&w)[CPL / 2], const uint16_t* p) {
+  if constexpr (CPL == 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (CPL == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+// Rows of one piece: a row at or past the tile's end r1 loads row `safe`
+// (< r1; a whole piece can lie past r1) and is replaced by -0.0 when it is
+// added.
+template <int P, int CPL>
+__device__ __forceinline__ void load_piece(uint32_t (&v)[P][CPL / 2], const uint16_t* __restrict__ dA, int64_t lda,
+                                           int64_t a, int64_t r1, int64_t safe, int64_t col) {
 #pragma unroll
   for (int i = 0; i < P; ++i) {
     const int64_t r = a + i < r1 ? a + i : safe;
-    v[i] = *reinterpret_cast<const uint4*>(dA + r * lda + col);
+    load_row<CPL>(v[i], dA + r * lda + col);
   }
 }
 
@@ -114,30 +131,31 @@ __device__ __forceinline__ void load_piece(uint4 (&v)[P], const uint16_t* __rest
 // the adjacent pairwise tree kept as a stack of partial sums: row i goes in
 // as the right operand of every completed level (i's trailing one bits), so
 // the stack ends holding exactly the tree of all Q rows.
-template <int P, int LQ>
-__device__ __forceinline__ void push_piece(float (&stk)[LQ + 1][8], const uint4 (&v)[P], int p, int64_t a,
-                                           int64_t r1) {
+template <int P, int LQ, int CPL>
+__device__ __forceinline__ void push_piece(float (&stk)[LQ + 1][CPL], const uint32_t (&v)[P][CPL / 2], int p,
+                                           int64_t a, int64_t r1) {
 #pragma unroll
   for (int i = 0; i < P; ++i) {
     const int idx = p * P + i;
     const bool in = a + i < r1;  // wave-uniform
-    float c[8];
-    c[0] = in ? bf16_lo(v[i].x) : -0.0f; c[1] = in ? bf16_hi(v[i].x) : -0.0f;
-    c[2] = in ? bf16_lo(v[i].y) : -0.0f; c[3] = in ? bf16_hi(v[i].y) : -0.0f;
-    c[4] = in ? bf16_lo(v[i].z) : -0.0f; c[5] = in ? bf16_hi(v[i].z) : -0.0f;
-    c[6] = in ? bf16_lo(v[i].w) : -0.0f; c[7] = in ? bf16_hi(v[i].w) : -0.0f;
+    float c[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL / 2; ++k) {
+      c[2 * k] = in ? bf16_lo(v[i][k]) : -0.0f;
+      c[2 * k + 1] = in ? bf16_hi(v[i][k]) : -0.0f;
+    }
     int l = 0;
 #pragma unroll
     for (; l < LQ && ((idx >> l) & 1); ++l)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) c[k] = stk[l][k] + c[k];
+      for (int k = 0; k < CPL; ++k) c[k] = stk[l][k] + c[k];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) stk[l][k] = c[k];
+    for (int k = 0; k < CPL; ++k) stk[l][k] = c[k];
   }
 }
 
 // Q rows per wave (block_m / 4), loaded and reduced in pieces of at most 32 rows.
-template <int Q, bool ATOMIC>
+template <int Q, int CPL, bool ATOMIC>
 __global__ __launch_bounds__(256) void dbias_tile_kernel(const uint16_t* __restrict__ dA, int64_t lda, int64_t M,
                                                          int64_t N, const int32_t* __restrict__ offs, int E,
                                                          float* __restrict__ slots, int32_t* __restrict__ tstart,
@@ -149,6 +167,7 @@ __global__ __launch_bounds__(256) void dbias_tile_kernel(const uint16_t* __restr
   constexpr int NP = Q / P;
   constexpr int LQ = Q == 16 ? 4 : (Q == 32 ? 5 : 6);
   static_assert((1 << LQ) == Q && Q % P == 0, "Q is 16, 32 or 64");
+  constexpr int kCols = 64 * CPL;
   const uint32_t Mu = static_cast<uint32_t>(M);
   __shared__ float part[4][kCols + 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -174,30 +193,30 @@ __global__ __launch_bounds__(256) void dbias_tile_kernel(const uint16_t* __restr
   int e;
   uint32_t r0, r1;
   if (!tile_of(offs, E, Mu, LOG_BM, t, e, r0, r1)) return;  // past the last tile (the grid covers the worst case)
-  const int64_t col = static_cast<int64_t>(cb) * kCols + 8 * lane;
-  const bool live = col < N;  // N % 8 == 0: a lane's 8 columns are all inside or all outside
-  float q[8];
+  const int64_t col = static_cast<int64_t>(cb) * kCols + CPL * lane;
+  const bool live = col < N;  // N % 8 == 0: a lane's CPL columns are all inside or all outside
+  float q[CPL];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) q[c] = -0.0f;
+  for (int c = 0; c < CPL; ++c) q[c] = -0.0f;
   const int64_t a0 = r0 + static_cast<int64_t>(wave) * Q;
   if (live && a0 < r1) {
-    float stk[LQ + 1][8];
-    uint4 va[P], vb[P];
-    load_piece<P>(va, dA, lda, a0, r1, a0, col);
+    float stk[LQ + 1][CPL];
+    uint32_t va[P][CPL / 2], vb[P][CPL / 2];
+    load_piece<P, CPL>(va, dA, lda, a0, r1, a0, col);
 #pragma unroll
     for (int p = 0; p < NP; p += 2) {
-      if (p + 1 < NP) load_piece<P>(vb, dA, lda, a0 + (p + 1) * P, r1, a0, col);
-      push_piece<P, LQ>(stk, va, p, a0 + p * P, r1);
+      if (p + 1 < NP) load_piece<P, CPL>(vb, dA, lda, a0 + (p + 1) * P, r1, a0, col);
+      push_piece<P, LQ, CPL>(stk, va, p, a0 + p * P, r1);
       if (p + 1 < NP) {
-        if (p + 2 < NP) load_piece<P>(va, dA, lda, a0 + (p + 2) * P, r1, a0, col);
-        push_piece<P, LQ>(stk, vb, p + 1, a0 + (p + 1) * P, r1);
+        if (p + 2 < NP) load_piece<P, CPL>(va, dA, lda, a0 + (p + 2) * P, r1, a0, col);
+        push_piece<P, LQ, CPL>(stk, vb, p + 1, a0 + (p + 1) * P, r1);
       }
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) q[c] = stk[LQ][c];
+    for (int c = 0; c < CPL; ++c) q[c] = stk[LQ][c];
   }
 #pragma unroll
-  for (int c = 0; c < 8; ++c) part[wave][8 * lane + c] = q[c];
+  for (int c = 0; c < CPL; ++c) part[wave][CPL * lane + c] = q[c];
   __syncthreads();
   // the top two tree levels: thread i combines column i of the four quarters
   for (int i = threadIdx.x; i < kCols; i += 256) {
@@ -234,12 +253,24 @@ __global__ __launch_bounds__(256) void dbias_fold_kernel(const float* __restrict
   *o = *o + tot;
 }
 
-int check_cfg(const det_dbias_cfg* cfg, det_dbias_cfg* out) {
-  det_dbias_cfg c{128, 512};
+int64_t max_tiles(int64_t M, int64_t E, int bm);
+
+// block_n of the default configuration: the widest of 512, 256, 128 columns
+// per workgroup that still gives 2048 workgroups (eight per compute unit), so
+// that no compute unit holds a third more work than the average; 128 below.
+int default_block_n(int64_t M, int64_t N, int64_t E) {
+  for (int bn : {512, 256})
+    if (max_tiles(M, E, 128) * ceil_div(N, bn) >= 2048) return bn;
+  return 128;
+}
+
+int check_cfg(const det_dbias_cfg* cfg, det_dbias_cfg* out, int64_t M = 0, int64_t N = 0, int64_t E = 0) {
+  det_dbias_cfg c{128, default_block_n(M, N, E)};
   if (cfg) c = *cfg;
   if (c.block_m != 64 && c.block_m != 128 && c.block_m != 256)
     return set_error(DET_ERR_INVALID_ARG, "dbias: block_m must be 64, 128 or 256, got %d", c.block_m);
-  if (c.block_n != 512) return set_error(DET_ERR_INVALID_ARG, "dbias: block_n must be 512, got %d", c.block_n);
+  if (c.block_n != 128 && c.block_n != 256 && c.block_n != 512)
+    return set_error(DET_ERR_INVALID_ARG, "dbias: block_n must be 128, 256 or 512, got %d", c.block_n);
   *out = c;
   return DET_OK;
 }
@@ -262,7 +293,7 @@ extern "C" int det_grouped_dbias_workspace_size(int64_t M, int64_t N, int32_t E,
   if (!bytes) return set_error(DET_ERR_INVALID_ARG, "dbias: bytes is NULL");
   if (M < 0 || N < 0 || E < 0) return set_error(DET_ERR_INVALID_ARG, "dbias: M, N and E must be >= 0");
   det_dbias_cfg c;
-  if (int s = check_cfg(cfg, &c)) return s;
+  if (int s = check_cfg(cfg, &c, M, N, E)) return s;
   *bytes = (atomic || M == 0 || N == 0 || E == 0) ? 0 : ws_bytes_for(M, N, E, c.block_m);
   return ok();
 }
@@ -273,7 +304,7 @@ extern "C" int det_grouped_dbias(float* dbias, int64_t ld_e, const void* dA, int
   if (int s = check_atomic_flag(atomic)) return s;
   if (M < 0 || N < 0 || E < 0) return set_error(DET_ERR_INVALID_ARG, "dbias: M, N and E must be >= 0");
   det_dbias_cfg c;
-  if (int s = check_cfg(cfg, &c)) return s;
+  if (int s = check_cfg(cfg, &c, M, N, E)) return s;
   if (M == 0 || N == 0 || E == 0) return ok();  // no rows or no columns: dbias unchanged
   if (!dbias || !dA || !offs) return set_error(DET_ERR_INVALID_ARG, "dbias: NULL pointer");
   if (M > 0x7FFFFFFF) return set_error(DET_ERR_UNSUPPORTED, "dbias: M must be < 2^31");
@@ -282,7 +313,7 @@ extern "C" int det_grouped_dbias(float* dbias, int64_t ld_e, const void* dA, int
     return set_error(DET_ERR_UNSUPPORTED, "dbias: N and lda must be multiples of 8 and dA 16-byte aligned");
   if (E > 65535) return set_error(DET_ERR_UNSUPPORTED, "dbias: E must be <= 65535");
   const int64_t nt = max_tiles(M, E, c.block_m);
-  if (nt * ceil_div(N, kCols) > 0x7FFFFFFF || nt * N > (int64_t(1) << 40))
+  if (nt * ceil_div(N, c.block_n) > 0x7FFFFFFF || nt * N > (int64_t(1) << 40))
     return set_error(DET_ERR_UNSUPPORTED, "dbias: problem too large");
   const size_t need = atomic ? 0 : ws_bytes_for(M, N, E, c.block_m);
   if (int s = check_workspace(ws, ws_bytes, need)) return s;
@@ -296,18 +327,20 @@ extern "C" int det_grouped_dbias(float* dbias, int64_t ld_e, const void* dA, int
   auto* tstart = atomic ? nullptr : reinterpret_cast<int32_t*>(w + DET_WS_HEADER_BYTES);
   auto* slots = atomic ? nullptr
                        : reinterpret_cast<float*>(w + DET_WS_HEADER_BYTES + align_up(static_cast<size_t>(E + 1) * 4, 256));
-  const int ncb = static_cast<int>(ceil_div(N, kCols));
+  const int ncb = static_cast<int>(ceil_div(N, c.block_n));
   const dim3 grid(static_cast<uint32_t>(nt * ncb));
-#define DET_DBIAS_LAUNCH(Q)                                                                                       \
-  if (c.block_m == 4 * Q) {                                                                                       \
+#define DET_DBIAS_LAUNCH(Q, CPL)                                                                                  \
+  if (c.block_m == 4 * Q && c.block_n == 64 * CPL) {                                                              \
     if (atomic)                                                                                                   \
-      hipLaunchKernelGGL((dbias_tile_kernel<Q, true>), grid, dim3(256), 0, st, a, lda, M, N, offs, E, slots,      \
+      hipLaunchKernelGGL((dbias_tile_kernel<Q, CPL, true>), grid, dim3(256), 0, st, a, lda, M, N, offs, E, slots, \
                          tstart, dbias, ld_e, ncb);                                                               \
     else                                                                                                          \
-      hipLaunchKernelGGL((dbias_tile_kernel<Q, false>), grid, dim3(256), 0, st, a, lda, M, N, offs, E, slots,     \
-                         tstart, dbias, ld_e, ncb);                                                               \
+      hipLaunchKernelGGL((dbias_tile_kernel<Q, CPL, false>), grid, dim3(256), 0, st, a, lda, M, N, offs, E,       \
+                         slots, tstart, dbias, ld_e, ncb);                                                        \
   }
-  DET_DBIAS_LAUNCH(16) DET_DBIAS_LAUNCH(32) DET_DBIAS_LAUNCH(64)
+  DET_DBIAS_LAUNCH(16, 8) DET_DBIAS_LAUNCH(32, 8) DET_DBIAS_LAUNCH(64, 8)
+  DET_DBIAS_LAUNCH(16, 4) DET_DBIAS_LAUNCH(32, 4) DET_DBIAS_LAUNCH(64, 4)
+  DET_DBIAS_LAUNCH(16, 2) DET_DBIAS_LAUNCH(32, 2) DET_DBIAS_LAUNCH(64, 2)
 #undef DET_DBIAS_LAUNCH
   if (!atomic)
     hipLaunchKernelGGL(dbias_fold_kernel, dim3(static_cast<uint32_t>(ceil_div(N, 256)), static_cast<uint32_t>(E)),

@@ -278,8 +278,11 @@ int det_grouped_dprob(float* dprob, const void* dY, int64_t ldy, const void* C, 
  *        16-byte aligned (DET_ERR_UNSUPPORTED otherwise).
  * dbias: [E, N] float32, row stride ld_e >= N, accumulated.
  * offs:  [E+1] int32 device array; E <= 65535.
- * cfg:   NULL = {block_m = 128, block_n = 512}; block_m in {64, 128, 256},
- *        block_n must be 512.
+ * cfg:   block_m in {64, 128, 256}; block_n (columns per workgroup) in
+ *        {128, 256, 512}. NULL = block_m 128 and the widest block_n that
+ *        still gives (ceil(M / 128) + E) x ceil(N / block_n) >= 2048
+ *        workgroups, else 128 (a shape-only rule; block_n never changes a
+ *        bit).
  * ws:    the deterministic route needs det_grouped_dbias_workspace_size()
  *        bytes: the header, the per-expert tile starts and one float32 slot
  *        per possible tile and column, (ceil(M / block_m) + E) x N.

@@ -94,7 +94,7 @@ def test_dbias_validation():
     assert n.value == 256 + 256 + (128 + 8) * 2048 * 4
     assert L.det_grouped_dbias_workspace_size(16384, 2048, 8, None, 1, ctypes.byref(n)) == dg.DET_OK and n.value == 0
     assert L.det_grouped_dbias_workspace_size(16384, 2048, 8, None, 2, ctypes.byref(n)) == dg.DET_ERR_INVALID_ARG
-    for cfg in (dg.DbiasCfg(96, 512), dg.DbiasCfg(128, 256)):
+    for cfg in (dg.DbiasCfg(96, 512), dg.DbiasCfg(128, 384), dg.DbiasCfg(128, 64)):
         assert L.det_grouped_dbias_workspace_size(64, 64, 2, ctypes.byref(cfg), 0, ctypes.byref(n)) == \
             dg.DET_ERR_INVALID_ARG
     big = 1 << 22

@@ -160,14 +160,16 @@ def expert_table(offs, M, bm):
     return b, nt, first
 
 
-def replay_dbias(M, N, offs, bm, lda=None, past_end_row="quarter"):
+def replay_dbias(M, N, offs, bm, lda=None, past_end_row="quarter", bn=512):
     """past_end_row: the row a load takes once it lies past the tile end; "quarter" is the
-    kernel's rule (the quarter's first row), "piece" the piece's own first row."""
+    kernel's rule (the quarter's first row), "piece" the piece's own first row. bn: columns
+    per workgroup, bn / 64 per lane."""
     lda = N if lda is None else lda
     E = len(offs) - 1
     Q, P = bm // 4, 16
     NP = Q // P
-    ncb = cdiv(N, 512)
+    cpl = bn // 64
+    ncb = cdiv(N, bn)
     max_tiles = cdiv(M, bm) + E
     b, nt, first = expert_table(offs, M, bm)
     lane, wave = np.arange(64), np.arange(4)
@@ -186,9 +188,9 @@ def replay_dbias(M, N, offs, bm, lda=None, past_end_row="quarter"):
             r = np.where(a < r1, a, safe)
             inside("dbias dA rows (tile %d)" % t, r, M)
         for cb in range(ncb):
-            col = cb * 512 + 8 * lane
+            col = cb * bn + cpl * lane
             col = col[col < N]
-            assert (col + 7 < N).all()
+            assert (col + cpl - 1 < N).all()
             inside("dbias slot", t * N + col, max_tiles * N)
     # fold: slots of an expert's tiles, tstart has E + 1 entries
     inside("dbias fold tiles", np.arange(int(first[-1])), max_tiles)
@@ -196,13 +198,14 @@ def replay_dbias(M, N, offs, bm, lda=None, past_end_row="quarter"):
         inside("dbias dA extent", np.array([(M - 1) * lda + N - 1]), M * lda)
 
 
+@pytest.mark.parametrize("bn", [512, 256, 128])
 @pytest.mark.parametrize("bm", [64, 128, 256])
-def test_dbias(bm):
+def test_dbias(bm, bn):
     counts = W.expert_counts(16384, 8, 256, 6, 0)
     offs = np.concatenate([[0], np.cumsum(counts)])
-    replay_dbias(16384, 2048, offs, bm)
+    replay_dbias(16384, 2048, offs, bm, bn=bn)
     # ragged: tiles that end inside a quarter, an empty expert, offsets past M
-    replay_dbias(3001, 520, np.array([0, 10, 10, 1000, 2999, 3500]), bm, lda=528)
+    replay_dbias(3001, 520, np.array([0, 10, 10, 1000, 2999, 3500]), bm, lda=528, bn=bn)
 
 
 def test_dbias_replay_catches_a_piece_row_past_m():

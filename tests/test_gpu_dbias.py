@@ -11,7 +11,7 @@ from tests.gpu_util import SideLoad, assert_bitwise, dev_bf16, dev_f32, dev_i32,
 pytestmark = pytest.mark.gpu
 
 
-def run(inp, offs=None, block_m=128, atomic=False, ld_pad=0, out_pad=0, stream=None):
+def run(inp, offs=None, block_m=128, atomic=False, ld_pad=0, out_pad=0, stream=None, block_n=512):
     import torch
     M, N = inp.dA.shape
     if ld_pad:
@@ -26,7 +26,8 @@ def run(inp, offs=None, block_m=128, atomic=False, ld_pad=0, out_pad=0, stream=N
         d = dev_f32(inp.dbias0)
     o = dev_i32(inp.offs if offs is None else offs)
     torch.cuda.synchronize()
-    dg.det_grouped_dbias(d, dA, o, cfg=dg.DbiasCfg(block_m, 512), atomic=atomic, stream=stream)
+    cfg = None if block_n is None else dg.DbiasCfg(block_m, block_n)
+    dg.det_grouped_dbias(d, dA, o, cfg=cfg, atomic=atomic, stream=stream)
     if stream is not None:
         stream.synchronize()
     return host(d)
@@ -40,6 +41,17 @@ def test_parity_small(M, N, E, ld_pad, BM):
     inp = W.dbias_inputs(M=M, N=N, E=E, min_tokens=1, seed=41, out_init="normal")
     got = run(inp, block_m=BM, ld_pad=ld_pad, out_pad=4 if ld_pad else 0)
     assert_bitwise(got, odb.grouped_dbias(inp.dbias0, inp.dA, inp.offs, BM), "dbias")
+
+
+@pytest.mark.parametrize("BN", [256, 128, None])
+@pytest.mark.parametrize("M,N,E,ld_pad", [(1000, 520, 5, 0), (2500, 1032, 70, 16), (16384, 2048, 8, 0)])
+def test_block_n_never_changes_bits(M, N, E, ld_pad, BN):
+    """block_n (columns per workgroup) only shapes the launch: 256, 128 and the default (NULL)
+    give the oracle's bits at block_m 128, including the full-size workload."""
+    note("dbias block_n=%s M=%d N=%d E=%d" % (BN, M, N, E))
+    inp = W.dbias_inputs(M=M, N=N, E=E, min_tokens=1, seed=43, out_init="normal")
+    got = run(inp, block_m=128, ld_pad=ld_pad, out_pad=4 if ld_pad else 0, block_n=BN)
+    assert_bitwise(got, odb.grouped_dbias(inp.dbias0, inp.dA, inp.offs, 128), "dbias block_n")
 
 
 def test_offsets_clamped_and_empty_experts():
