@@ -15,8 +15,10 @@
 // The atomic arm computes the same tile slots and adds them into the outputs
 // with hardware float atomics, in whatever order the tiles finish.
 //
-// The per-element work is about 80 VALU operations (exp, log1p, two divisions),
-// so at large T the kernel is bound by vector ALU throughput, not HBM.
+// The per-element work is about 80 VALU lane-operations (exp, log1p, two
+// divisions), so at large T the tile kernel is bound by vector ALU
+// throughput; its workgroup order (below) keeps the HBM traffic at one read
+// of each input line.
 #include <mutex>
 
 #include "common.hpp"
