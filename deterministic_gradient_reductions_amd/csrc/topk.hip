@@ -15,18 +15,16 @@
 // (id << 10 | slot, padding as id 2^21 - 1), which halves the cross-lane
 // traffic. The keys are sorted with a bitonic network held in registers:
 // element i = r * 64 + lane (EPL elements per lane, so loads and stores are
-// coalesced); partners at a distance below 64 are exchanged across lanes (DPP
-// quad permutations for distances 1 and 2, ds_bpermute beyond, all exchanges
-// of a step issued together), partners further apart are swapped between
-// registers. The
+// coalesced); partners at a distance below 64 are exchanged across lanes on
+// the VALU (DPP for distances 1 to 8, the gfx950 lane swaps for 16 and 32),
+// partners further apart are swapped between registers. The
 // sorted keys give each output position its source slot, from which the id
 // and the logit are gathered. The softmax: the exact maximum of the valid
 // logits (a wave reduction), e = exp32(logit - max) (the gate's fixed
 // sequence), the left-to-right sum of the e's in the sorted order, and one
-// correctly rounded division per slot. For the sums the four waves of a
-// workgroup leave their e's in LDS and lanes 0..3 of the first wave add one
-// row each, so four dependent-add chains share one instruction stream.
-// Padding slots get +0.0.
+// correctly rounded division per slot. For the sum each wave leaves its e's
+// in LDS and runs the chain from uniform LDS reads issued ahead of the adds,
+// one dependent add per value. Padding slots get +0.0.
 #include "common.hpp"
 #include "detmath.hpp"
 
@@ -34,63 +32,92 @@ namespace detgrad {
 namespace {
 
 constexpr int kMaxK = 1024;
+constexpr int kSumAhead = 16;  // LDS reads in flight ahead of the softmax sum chain
 
-// The value of lane ^ m. m = 1 and m = 2 stay inside a group of four lanes
-// and move by a DPP quad permutation (a VALU operand modifier, no LDS-pipe
-// round trip); larger distances use ds_bpermute. Every lane of the wave is
-// active here.
-__device__ __forceinline__ uint32_t shfl_xor_k(uint32_t v, int m) {
-  if (m == 1) return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true));
-  if (m == 2) return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true));
-  return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m));
+// The value of lane ^ m, on the VALU (no LDS round trip): m = 1 and m = 2 by
+// a DPP quad permutation; m = 4 and m = 8 stay inside a row of 16 lanes, so
+// the partner is lane + m (row_shl) or lane - m (row_shr), whichever the
+// lane's bit m selects; m = 16 and m = 32 cross rows, and the gfx950 lane
+// swaps (v_permlane16_swap, v_permlane32_swap) of the value with itself give
+// each lane the other half's copy in one of their two results. Every lane of
+// the wave is active here (the DPP shifts' missing sources are never
+// selected).
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+  const int x = static_cast<int>(v);
+  if constexpr (M == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+  } else if constexpr (M == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+  } else if constexpr (M == 4 || M == 8) {
+    const uint32_t dn = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0x110 + M, 0xF, 0xF, false));  // row_shr
+    const uint32_t up = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0x100 + M, 0xF, 0xF, false));  // row_shl
+    return (lane & M) ? dn : up;
+  } else if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    static_assert(M == 32, "lane distances 1 .. 32");
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? p[0] : p[1];
+  }
 }
-__device__ __forceinline__ uint64_t shfl_xor_k(uint64_t v, int m) {
-  const uint32_t lo = shfl_xor_k(static_cast<uint32_t>(v), m), hi = shfl_xor_k(static_cast<uint32_t>(v >> 32), m);
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane(uint64_t v, int lane) {
+  const uint32_t lo = xor_lane<M>(static_cast<uint32_t>(v), lane), hi = xor_lane<M>(static_cast<uint32_t>(v >> 32), lane);
   return static_cast<uint64_t>(hi) << 32 | lo;
 }
 
 // Ascending bitonic sort of the wave's 64 * EPL keys, element i = r * 64 +
 // lane: partners closer than 64 are in other lanes (shuffles), partners
 // further apart in other registers.
-template <int EPL, typename T>
-__device__ __forceinline__ void bitonic(T (&key)[EPL], int lane) {
-  constexpr int N = 64 * EPL;
+// One step of phase K at distance D, then the phase's remaining steps. The
+// phase and distance are template arguments, so every exchange is a fixed
+// instruction sequence.
+template <int EPL, int K, int D, typename T>
+__device__ __forceinline__ void bitonic_step(T (&key)[EPL], int lane) {
+  if constexpr (D >= 64) {
+    constexpr int dr = D / 64;
 #pragma unroll
-  for (int k = 2; k <= N; k <<= 1) {
-#pragma unroll
-    for (int d = k >> 1; d > 0; d >>= 1) {
-      if (d >= 64) {
-        const int dr = d / 64;
-#pragma unroll
-        for (int r = 0; r < EPL; ++r) {
-          const int rp = r ^ dr;
-          if (rp > r) {
-            const int i = r * 64 + lane;
-            const bool up = (i & k) == 0;
-            const T a = key[r], b = key[rp];
-            const bool swap = up ? (a > b) : (a < b);
-            key[r] = swap ? b : a;
-            key[rp] = swap ? a : b;
-          }
-        }
-      } else {
-        // all exchanges of the step first, so that they are in flight together
-        T o[EPL];
-#pragma unroll
-        for (int r = 0; r < EPL; ++r) o[r] = shfl_xor_k(key[r], d);
-#pragma unroll
-        for (int r = 0; r < EPL; ++r) {
-          const int i = r * 64 + lane;
-          const bool up = (i & k) == 0;
-          const bool lower = (i & d) == 0;  // this element is the lower index of the pair
-          // an ascending pair keeps the smaller key at its lower index
-          const bool keep_min = (up == lower);
-          const T mn = key[r] < o[r] ? key[r] : o[r], mx = key[r] < o[r] ? o[r] : key[r];
-          key[r] = keep_min ? mn : mx;
-        }
+    for (int r = 0; r < EPL; ++r) {
+      const int rp = r ^ dr;
+      if (rp > r) {
+        const int i = r * 64 + lane;
+        const bool up = (i & K) == 0;
+        const T a = key[r], b = key[rp];
+        const bool swap = up ? (a > b) : (a < b);
+        key[r] = swap ? b : a;
+        key[rp] = swap ? a : b;
       }
     }
+  } else {
+    // all exchanges of the step first, so that they are in flight together
+    T o[EPL];
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) o[r] = xor_lane<D>(key[r], lane);
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+      const int i = r * 64 + lane;
+      const bool up = (i & K) == 0;
+      const bool lower = (i & D) == 0;  // this element is the lower index of the pair
+      // an ascending pair keeps the smaller key at its lower index
+      const bool keep_min = (up == lower);
+      const T mn = key[r] < o[r] ? key[r] : o[r], mx = key[r] < o[r] ? o[r] : key[r];
+      key[r] = keep_min ? mn : mx;
+    }
   }
+  if constexpr (D > 1) bitonic_step<EPL, K, D / 2>(key, lane);
+}
+
+template <int EPL, int K, typename T>
+__device__ __forceinline__ void bitonic_phase(T (&key)[EPL], int lane) {
+  bitonic_step<EPL, K, K / 2>(key, lane);
+  if constexpr (K < 64 * EPL) bitonic_phase<EPL, 2 * K>(key, lane);
+}
+
+template <int EPL, typename T>
+__device__ __forceinline__ void bitonic(T (&key)[EPL], int lane) {
+  bitonic_phase<EPL, 2>(key, lane);
 }
 
 // True when every valid id of the row is below 2^21 - 1 (so id << 10 | slot
@@ -112,12 +139,10 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
                                                          float* __restrict__ logits_out, float* __restrict__ probs,
                                                          int64_t ld_out) {
   constexpr int N = 64 * EPL;  // padded row length, a power of two
-  __shared__ float es[4][N];   // each wave's e values, in sorted order, for the sums
-  __shared__ float sums[4];
-  __shared__ int nvs[4];
+  __shared__ __attribute__((aligned(16))) float es[4][N];  // each wave's e values, in sorted order, for its sum
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  const bool row = q < Q;  // wave-uniform; every wave reaches the barrier
+  const bool row = q < Q;  // wave-uniform
   const int32_t* const ir = ids + (row ? q : 0) * ld;
   const float* const lr = logits + (row ? q : 0) * ld;
   // element i = r * 64 + lane: partners at distance d < 64 sit in another
@@ -172,40 +197,54 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
     if (valid) mx = mx > lg[r] ? mx : lg[r];
   }
   // exact maximum and valid count over the wave
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) {
-    const float o = __shfl_xor(mx, m);
-    mx = mx > o ? mx : o;
-  }
-  int nv = nv_lane;
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) nv += __shfl_xor(nv, m);
+  // (butterflies over lane distances 32, 16, .., 1, the same in every lane)
+  auto max_step = [&](float o) { mx = mx > o ? mx : o; };
+  max_step(__uint_as_float(xor_lane<32>(__float_as_uint(mx), lane)));
+  max_step(__uint_as_float(xor_lane<16>(__float_as_uint(mx), lane)));
+  max_step(__uint_as_float(xor_lane<8>(__float_as_uint(mx), lane)));
+  max_step(__uint_as_float(xor_lane<4>(__float_as_uint(mx), lane)));
+  max_step(__uint_as_float(xor_lane<2>(__float_as_uint(mx), lane)));
+  max_step(__uint_as_float(xor_lane<1>(__float_as_uint(mx), lane)));
+  uint32_t nvu = static_cast<uint32_t>(nv_lane);
+  nvu += xor_lane<32>(nvu, lane);
+  nvu += xor_lane<16>(nvu, lane);
+  nvu += xor_lane<8>(nvu, lane);
+  nvu += xor_lane<4>(nvu, lane);
+  nvu += xor_lane<2>(nvu, lane);
+  nvu += xor_lane<1>(nvu, lane);
+  const int nv = static_cast<int>(nvu);
+  // e values in sorted order: each wave parks its row in LDS, then every lane
+  // runs the row's left-to-right sum from the same uniform-address LDS reads
+  // (four values per read, the reads issued ahead of their adds), so
+  // the wave needs no barrier and every lane ends with the sum. Positions
+  // past nv hold +0.0: once a valid value has been added the sum is not -0.0,
+  // so adding +0.0 leaves its bits unchanged, and the chain can run over the
+  // whole padded row; a row without valid values uses no sum.
   float e[EPL];
+  float4* const ew = reinterpret_cast<float4*>(es[wave]);
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
     const int i = r * 64 + lane;
     e[r] = i < nv ? dm::exp32(lg[r] - mx) : 0.0f;
     es[wave][i] = e[r];
   }
-  if (lane == 0) nvs[wave] = row ? nv : 0;
-  __syncthreads();
-  // the left-to-right sums: lane w of wave 0 adds row w's values in order
-  // (four independent dependent-add chains in one instruction stream)
-  if (wave == 0 && lane < 4) {
-    const int nvw = nvs[lane];  // valid values of row `lane` (0 past Q): the prefix of its es row
-    const float* const ew = es[lane];
-    float S = -0.0f;
-    int i = 0;
-    for (; i + 4 <= nvw; i += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(ew + i);
-      S = S + v.x; S = S + v.y; S = S + v.z; S = S + v.w;
-    }
-    for (; i < nvw; ++i) S = S + ew[i];
-    sums[lane] = S;
+  constexpr int kN4 = N / 4;
+  float S = -0.0f;
+  float4 w[kSumAhead];
+#pragma unroll
+  for (int t = 0; t < kSumAhead; ++t) w[t] = ew[t];
+  // (no scheduling barriers here: the compiler keeps the reads ahead by
+  // itself, and barriers in this fully unrolled loop made it spill)
+#pragma unroll
+  for (int t = 0; t < kN4; ++t) {
+    const float4 x = w[t % kSumAhead];
+    if (t + kSumAhead < kN4) w[t % kSumAhead] = ew[t + kSumAhead];
+    S = S + x.x;
+    S = S + x.y;
+    S = S + x.z;
+    S = S + x.w;
   }
-  __syncthreads();
   if (!row) return;
-  const float S = sums[wave];
   int32_t* const io = ids_out + q * ld_out;
   float* const lo = logits_out + q * ld_out;
   float* const po = probs + q * ld_out;
