@@ -100,10 +100,13 @@ __device__ __forceinline__ void bitonic_step(T (&key)[EPL], int lane) {
       const int i = r * 64 + lane;
       const bool up = (i & K) == 0;
       const bool lower = (i & D) == 0;  // this element is the lower index of the pair
-      // an ascending pair keeps the smaller key at its lower index
+      // an ascending pair keeps the smaller key at its lower index. The
+      // element takes its partner's key when that one belongs here: the
+      // smaller one where the minimum stays, the larger one where the maximum
+      // does. Keys are distinct except the all-ones padding, and for equal
+      // keys either choice keeps the same value, so one compare decides.
       const bool keep_min = (up == lower);
-      const T mn = key[r] < o[r] ? key[r] : o[r], mx = key[r] < o[r] ? o[r] : key[r];
-      key[r] = keep_min ? mn : mx;
+      key[r] = ((o[r] > key[r]) != keep_min) ? o[r] : key[r];
     }
   }
   if constexpr (D > 1) bitonic_step<EPL, K, D / 2>(key, lane);
@@ -139,7 +142,8 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
                                                          float* __restrict__ logits_out, float* __restrict__ probs,
                                                          int64_t ld_out) {
   constexpr int N = 64 * EPL;  // padded row length, a power of two
-  __shared__ __attribute__((aligned(16))) float es[4][N];  // each wave's e values, in sorted order, for its sum
+  __shared__ __attribute__((aligned(16))) float es[4][N];  // each wave's logits by slot, then its e values in sorted order
+  __shared__ int32_t is[4][N];                             // each wave's ids by slot
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   const bool row = q < Q;  // wave-uniform
@@ -148,6 +152,8 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
   // element i = r * 64 + lane: partners at distance d < 64 sit in another
   // lane (one shuffle per 32-bit half), at d >= 64 in another register
   uint64_t key[EPL];
+  float lg_in[EPL];    // the row's logits and ids in slot order, kept from these loads
+  int32_t id_in[EPL];  // (their latency hides behind the sort)
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
     const int i = r * 64 + lane;
@@ -155,8 +161,12 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
       const int32_t id = ir[i];
       const uint32_t hi = id >= 0 ? static_cast<uint32_t>(id) : 0x80000000u;
       key[r] = static_cast<uint64_t>(hi) << 32 | static_cast<uint32_t>(i);
+      lg_in[r] = lr[i];
+      id_in[r] = id;
     } else {
       key[r] = ~0ull;
+      lg_in[r] = 0.0f;
+      id_in[r] = 0;
     }
   }
   // keys of 32 bits (id << 10 | slot) when every id of the row is below
@@ -180,7 +190,13 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
   } else {
     bitonic<EPL>(key, lane);
   }
-  // gather ids and logits by source slot; the valid slots come first
+  // ids and logits by source slot from the wave's LDS rows (parked there in
+  // slot order; padding keeps its own negative id); the valid slots come first
+#pragma unroll
+  for (int r = 0; r < EPL; ++r) {
+    es[wave][r * 64 + lane] = lg_in[r];
+    is[wave][r * 64 + lane] = id_in[r];
+  }
   int32_t idv[EPL];
   float lg[EPL];
   int nv_lane = 0;
@@ -190,8 +206,8 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
     const int i = r * 64 + lane;
     const uint32_t slot = static_cast<uint32_t>(key[r]);
     const bool in = row && i < K;
-    idv[r] = in ? ir[slot] : 0;
-    lg[r] = in ? lr[slot] : 0.0f;
+    idv[r] = in ? is[wave][slot] : 0;
+    lg[r] = in ? es[wave][slot] : 0.0f;
     const bool valid = in && (key[r] >> 32) < 0x80000000ull;
     nv_lane += valid ? 1 : 0;
     if (valid) mx = mx > lg[r] ? mx : lg[r];

@@ -56,6 +56,21 @@ def test_id_range(top):
     check(ids, inp.logits, "topk ids to %d" % top)
 
 
+def test_padding_keeps_its_own_negative_id():
+    """Every negative id is padding and comes out unchanged, in slot order after the valid ids:
+    -1, -2, -1000 and INT32_MIN mixed in one row, rows of 32- and 64-bit keys."""
+    inp = W.topk_inputs(Q=24, K=200, n_keys=3000, seed=11, distinct=True, pad_frac=0.0)
+    ids = inp.ids.copy()
+    rng = np.random.default_rng(5)
+    neg = np.array([-1, -2, -1000, np.iinfo(np.int32).min], np.int32)
+    mask = rng.random(ids.shape) < 0.15
+    ids[mask] = neg[rng.integers(0, 4, size=int(mask.sum()))]
+    ids[3, ::2] = np.where(ids[3, ::2] >= 0, ids[3, ::2] + (1 << 22), ids[3, ::2])  # a row with 64-bit keys
+    ids[4, :] = neg[rng.integers(0, 4, size=200)]                                 # a row of padding only
+    note("topk negative padding ids")
+    check(ids, inp.logits, "topk negative padding")
+
+
 def test_full_size_and_slot_order_invariance():
     inp = W.topk_inputs(seed=7)  # 4096 x 512
     note("topk full size")
