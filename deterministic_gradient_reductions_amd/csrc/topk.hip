@@ -136,37 +136,49 @@ __device__ __forceinline__ bool wave_ids_narrow(const uint64_t (&key)[EPL]) {
   return __ballot(wide) == 0;
 }
 
+// A row's ids and logits in slot order (position i = r * 64 + lane; past K
+// or past Q: id 0, logit 0, never used).
 template <int EPL>
-__global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restrict__ ids, const float* __restrict__ logits,
-                                                         int64_t Q, int K, int64_t ld, int32_t* __restrict__ ids_out,
-                                                         float* __restrict__ logits_out, float* __restrict__ probs,
-                                                         int64_t ld_out) {
-  constexpr int N = 64 * EPL;  // padded row length, a power of two
-  __shared__ __attribute__((aligned(16))) float es[4][N];  // each wave's logits by slot, then its e values in sorted order
-  __shared__ int32_t is[4][N];                             // each wave's ids by slot
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  const bool row = q < Q;  // wave-uniform
+struct TopkRow {
+  int32_t id[EPL];
+  float lg[EPL];
+};
+
+template <int EPL>
+__device__ __forceinline__ void topk_load(TopkRow<EPL>& in, const int32_t* __restrict__ ids,
+                                          const float* __restrict__ logits, int64_t q, bool row, int K, int64_t ld,
+                                          int lane) {
   const int32_t* const ir = ids + (row ? q : 0) * ld;
   const float* const lr = logits + (row ? q : 0) * ld;
+#pragma unroll
+  for (int r = 0; r < EPL; ++r) {
+    const int i = r * 64 + lane;
+    const bool in_row = row && i < K;
+    in.id[r] = in_row ? ir[i] : 0;
+    in.lg[r] = in_row ? lr[i] : 0.0f;
+  }
+}
+
+// One row, by one wave, from its loaded ids and logits; es and is are the
+// wave's LDS rows.
+template <int EPL>
+__device__ __forceinline__ void topk_row(const TopkRow<EPL>& in, int64_t q, bool row, int K, int lane, float* es,
+                                         int32_t* is, int32_t* __restrict__ ids_out,
+                                         float* __restrict__ logits_out, float* __restrict__ probs,
+                                         int64_t ld_out) {
+  constexpr int N = 64 * EPL;  // padded row length, a power of two
   // element i = r * 64 + lane: partners at distance d < 64 sit in another
-  // lane (one shuffle per 32-bit half), at d >= 64 in another register
+  // lane, at d >= 64 in another register
   uint64_t key[EPL];
-  float lg_in[EPL];    // the row's logits and ids in slot order, kept from these loads
-  int32_t id_in[EPL];  // (their latency hides behind the sort)
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
     const int i = r * 64 + lane;
     if (row && i < K) {
-      const int32_t id = ir[i];
+      const int32_t id = in.id[r];
       const uint32_t hi = id >= 0 ? static_cast<uint32_t>(id) : 0x80000000u;
       key[r] = static_cast<uint64_t>(hi) << 32 | static_cast<uint32_t>(i);
-      lg_in[r] = lr[i];
-      id_in[r] = id;
     } else {
       key[r] = ~0ull;
-      lg_in[r] = 0.0f;
-      id_in[r] = 0;
     }
   }
   // keys of 32 bits (id << 10 | slot) when every id of the row is below
@@ -191,11 +203,13 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
     bitonic<EPL>(key, lane);
   }
   // ids and logits by source slot from the wave's LDS rows (parked there in
-  // slot order; padding keeps its own negative id); the valid slots come first
+  // slot order; padding keeps its own negative id); the valid slots come
+  // first. (The previous row's reads of these rows precede these writes in
+  // the wave's order.)
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
-    es[wave][r * 64 + lane] = lg_in[r];
-    is[wave][r * 64 + lane] = id_in[r];
+    es[r * 64 + lane] = in.lg[r];
+    is[r * 64 + lane] = in.id[r];
   }
   int32_t idv[EPL];
   float lg[EPL];
@@ -205,10 +219,10 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
   for (int r = 0; r < EPL; ++r) {
     const int i = r * 64 + lane;
     const uint32_t slot = static_cast<uint32_t>(key[r]);
-    const bool in = row && i < K;
-    idv[r] = in ? is[wave][slot] : 0;
-    lg[r] = in ? es[wave][slot] : 0.0f;
-    const bool valid = in && (key[r] >> 32) < 0x80000000ull;
+    const bool in_row = row && i < K;
+    idv[r] = in_row ? is[slot] : 0;
+    lg[r] = in_row ? es[slot] : 0.0f;
+    const bool valid = in_row && (key[r] >> 32) < 0x80000000ull;
     nv_lane += valid ? 1 : 0;
     if (valid) mx = mx > lg[r] ? mx : lg[r];
   }
@@ -231,18 +245,18 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
   const int nv = static_cast<int>(nvu);
   // e values in sorted order: each wave parks its row in LDS, then every lane
   // runs the row's left-to-right sum from the same uniform-address LDS reads
-  // (four values per read, the reads issued ahead of their adds), so
-  // the wave needs no barrier and every lane ends with the sum. Positions
-  // past nv hold +0.0: once a valid value has been added the sum is not -0.0,
-  // so adding +0.0 leaves its bits unchanged, and the chain can run over the
-  // whole padded row; a row without valid values uses no sum.
+  // (four values per read, the reads issued ahead of their adds), so the wave
+  // needs no barrier and every lane ends with the sum. Positions past nv hold
+  // +0.0: once a valid value has been added the sum is not -0.0, so adding
+  // +0.0 leaves its bits unchanged, and the chain can run over the whole
+  // padded row; a row without valid values uses no sum.
   float e[EPL];
-  float4* const ew = reinterpret_cast<float4*>(es[wave]);
+  const float4* const ew = reinterpret_cast<const float4*>(es);
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
     const int i = r * 64 + lane;
     e[r] = i < nv ? dm::exp32(lg[r] - mx) : 0.0f;
-    es[wave][i] = e[r];
+    es[i] = e[r];
   }
   constexpr int kN4 = N / 4;
   float S = -0.0f;
@@ -260,7 +274,7 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
     S = S + x.z;
     S = S + x.w;
   }
-  if (!row) return;
+  if (!row) return;  // (wave-uniform)
   int32_t* const io = ids_out + q * ld_out;
   float* const lo = logits_out + q * ld_out;
   float* const po = probs + q * ld_out;
@@ -273,6 +287,24 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
       po[i] = i < nv ? e[r] / S : 0.0f;
     }
   }
+}
+
+// One wave per row, four rows per workgroup. (Two rows per wave, the second
+// row's loads in flight during the first row's sort, was slower: half as
+// many waves hide less latency.)
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restrict__ ids, const float* __restrict__ logits,
+                                                         int64_t Q, int K, int64_t ld, int32_t* __restrict__ ids_out,
+                                                         float* __restrict__ logits_out, float* __restrict__ probs,
+                                                         int64_t ld_out) {
+  constexpr int N = 64 * EPL;
+  __shared__ __attribute__((aligned(16))) float es[4][N];  // each wave's logits by slot, then its e values in sorted order
+  __shared__ int32_t is[4][N];                             // each wave's ids by slot
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  TopkRow<EPL> in;
+  topk_load<EPL>(in, ids, logits, q, q < Q, K, ld, lane);
+  topk_row<EPL>(in, q, q < Q, K, lane, es[wave], is[wave], ids_out, logits_out, probs, ld_out);
 }
 
 }  // namespace

@@ -349,8 +349,12 @@ def test_topk():
     inside("topk slot gather", slot, K)
     # narrow keys (id << 10 | slot) need ids below 2^21 - 1 and K <= 1024
     assert K <= 1024
-    q = np.arange(cdiv(Q, 4) * 4)
-    inside("topk rows", q[q < Q], Q)
+    # wave w of workgroup b takes row 4 b + w; rows past Q load row 0 and store nothing
+    for QQ in (Q, 1, 7, 8, 9, 4097):
+        b, w = np.meshgrid(np.arange(cdiv(QQ, 4)), np.arange(4), indexing="ij")
+        rows = (4 * b + w).ravel()
+        assert np.array_equal(np.sort(rows[rows < QQ]), np.arange(QQ))  # every row exactly once
+        inside("topk rows", np.where(rows < QQ, rows, 0), QQ)
 
 
 # ------------------------------------------------------------------ index_add / indexer dK
