@@ -418,6 +418,19 @@ __global__ __launch_bounds__(kSortThreads, 8) void ia_scatter(const int32_t* __r
     const int64_t p = p0 + 64 * (wave + kWaves * q) + lane;
     x[q] = p < p1 ? ids[p] : -1;
   }
+  // The global part of every id's base (segment offset + earlier segments +
+  // earlier blocks of the segment), loaded now for all ids k = tid + 1024 u
+  // (one round covers every n_rows the LDS tables allow), so that the loads'
+  // latency hides behind the match; absent ids' values are never used.
+  constexpr int kU = 16 / NW;
+  const uint16_t* pre = prefix + b * hist_ld;
+  const uint32_t* sb = segbase + (b / kSegBlocks) * n_rows;
+  uint32_t gbase[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int k = tid + kSortThreads * u;
+    gbase[u] = k < n_rows ? seg_off[k] + sb[k] + pre[k] : 0u;
+  }
   {
     uint4* t4 = reinterpret_cast<uint4*>(tab);
     for (int k = tid; k < NW * tab_ld / 4; k += kSortThreads) t4[k] = make_uint4(0u, 0u, 0u, 0u);
@@ -439,41 +452,25 @@ __global__ __launch_bounds__(kSortThreads, 8) void ia_scatter(const int32_t* __r
     }
   }
   __syncthreads();
-  const uint16_t* pre = prefix + b * hist_ld;
-  const uint32_t* sb = segbase + (b / kSegBlocks) * n_rows;
-  // only ids present in the block need a base (absent ids are never read in
-  // the walk); absent ids load entry 0 instead, so the loads need no branches
-  constexpr int kU = 16 / NW;  // ids per thread: one round for every n_rows the LDS tables allow
-  for (int k0 = 0; k0 < n_rows; k0 += kSortThreads * kU) {
-    uint32_t c[kU][NW];
-    bool present[kU];
+  // bases: only ids present in the block need one (absent ids are never read
+  // in the walk); each present id's sub-blocks start at its global base plus
+  // the counts of the earlier sub-blocks
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int k = k0 + tid + kSortThreads * u;
-      uint32_t any = 0;
+  for (int u = 0; u < kU; ++u) {
+    const int k = tid + kSortThreads * u;
+    uint32_t c[NW];
+    uint32_t any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      c[w] = k < n_rows ? tab[w * tab_ld + k] : 0u;
+      any |= c[w];
+    }
+    if (any != 0) {
+      uint32_t run = gbase[u];
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        c[u][w] = k < n_rows ? tab[w * tab_ld + k] : 0u;
-        any |= c[u][w];
-      }
-      present[u] = any != 0;
-    }
-    uint32_t base[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int kk = present[u] ? k0 + tid + kSortThreads * u : 0;
-      base[u] = seg_off[kk] + sb[kk] + pre[kk];
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int k = k0 + tid + kSortThreads * u;
-      if (present[u]) {
-        uint32_t run = base[u];
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          tab[w * tab_ld + k] = run;
-          run += c[u][w];
-        }
+        tab[w * tab_ld + k] = run;
+        run += c[w];
       }
     }
   }
@@ -530,6 +527,11 @@ int scatter_waves(int64_t n_rows) {
     if (static_cast<int64_t>(nw) * pad_rows * 4 + kBlockPos * 4 <= 80 * 1024) return nw;
   return 1;
 }
+// The scatter loads every id's global base in one round, ids tid + 1024 u for
+// u < 16 / NW: the LDS rule above leaves at most that many ids for each NW.
+static_assert(kSortThreads * 16 >= kMaxRows && (80 * 1024 - kBlockPos * 4) / (2 * 4) <= kSortThreads * 8 &&
+                  (80 * 1024 - kBlockPos * 4) / (4 * 4) <= kSortThreads * 4,
+              "one round of bases per scatter workgroup");
 
 template <int NW>
 void launch_scatter(int64_t nblk, int n_rows, hipStream_t st, const int32_t* ids, int64_t n_src,
