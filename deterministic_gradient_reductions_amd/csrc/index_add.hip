@@ -207,26 +207,6 @@ __device__ __forceinline__ uint32_t floor_div_rcp(uint32_t n, uint32_t K, uint32
 // where the fold reads it), or -1 for the only chunk of an id (added into out
 // directly).
 
-// Integer scans on DPP row shifts and row broadcasts in registers.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp_add(uint32_t v) {
-  // lanes without a source lane read 0 (the `old` operand)
-  return v + static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
-}
-
-// Inclusive scan over the 64 lanes: shifts by 1, 2, 4, 8 inside each row of
-// 16, then the last lane of row 0 into row 1 and 3 (row_bcast:15) and of row
-// 1 into rows 2 and 3 (row_bcast:31).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v = dpp_add<0x111, 0xF>(v);  // row_shr:1
-  v = dpp_add<0x112, 0xF>(v);  // row_shr:2
-  v = dpp_add<0x114, 0xF>(v);  // row_shr:4
-  v = dpp_add<0x118, 0xF>(v);  // row_shr:8
-  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
-  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
-  return v;
-}
-
 // Inclusive scan over the 16 lanes of row 0 (the other rows are ignored).
 __device__ __forceinline__ uint32_t row_incl_scan(uint32_t v) {
   v = dpp_add<0x111, 0xF>(v);

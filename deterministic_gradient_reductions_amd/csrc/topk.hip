@@ -33,6 +33,8 @@ namespace {
 
 constexpr int kMaxK = 1024;
 constexpr int kSumAhead = 16;  // LDS reads in flight ahead of the softmax sum chain
+constexpr int kRankBits = 16384;             // id window of the counting path
+constexpr int kRankWords = kRankBits / 32;   // its bitmap words per row
 
 // The value of lane ^ m, on the VALU (no LDS round trip): m = 1 and m = 2 by
 // a DPP quad permutation; m = 4 and m = 8 stay inside a row of 16 lanes, so
@@ -159,75 +161,192 @@ __device__ __forceinline__ void topk_load(TopkRow<EPL>& in, const int32_t* __res
   }
 }
 
+// Compiler barrier between the LDS phases of one wave (a wave's LDS accesses
+// execute in program order; this keeps the compiler from moving them).
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+// The row's canonical positions by counting, for a row whose valid ids are
+// distinct and span fewer than kRankBits values (lo .. hi): each valid id sets
+// bit id - lo of the wave's LDS bitmap, a valid slot's position is the number
+// of set bits below its own (the words' exclusive prefix counts from one wave
+// scan, plus a popcount inside the word), and a padding slot's position is nv
+// plus the padding slots before it. Every slot's id and logit are written at
+// that position of is and es. A repeated id shows as a bit that the LDS atomic
+// OR finds already set. Returns false, placing nothing, for a wider span or a
+// repeated id (the row is then sorted); both ways give every slot the same
+// position, so the choice never changes a bit.
+template <int EPL>
+__device__ __forceinline__ bool topk_count(const TopkRow<EPL>& in, bool row, int K, int lane, float* es, int32_t* is,
+                                           uint32_t* bm, uint32_t* pre, int& nv_out) {
+  int lo = 0x7FFFFFFF, hi = -1;
+  int nv = 0;
+#pragma unroll
+  for (int r = 0; r < EPL; ++r) {
+    const bool valid = row && r * 64 + lane < K && in.id[r] >= 0;
+    if (valid) {
+      lo = in.id[r] < lo ? in.id[r] : lo;
+      hi = in.id[r] > hi ? in.id[r] : hi;
+    }
+    nv += __builtin_popcountll(__ballot(valid));
+  }
+  auto mm = [&](int olo, int ohi) {
+    lo = olo < lo ? olo : lo;
+    hi = ohi > hi ? ohi : hi;
+  };
+  mm(static_cast<int>(xor_lane<32>(static_cast<uint32_t>(lo), lane)), static_cast<int>(xor_lane<32>(static_cast<uint32_t>(hi), lane)));
+  mm(static_cast<int>(xor_lane<16>(static_cast<uint32_t>(lo), lane)), static_cast<int>(xor_lane<16>(static_cast<uint32_t>(hi), lane)));
+  mm(static_cast<int>(xor_lane<8>(static_cast<uint32_t>(lo), lane)), static_cast<int>(xor_lane<8>(static_cast<uint32_t>(hi), lane)));
+  mm(static_cast<int>(xor_lane<4>(static_cast<uint32_t>(lo), lane)), static_cast<int>(xor_lane<4>(static_cast<uint32_t>(hi), lane)));
+  mm(static_cast<int>(xor_lane<2>(static_cast<uint32_t>(lo), lane)), static_cast<int>(xor_lane<2>(static_cast<uint32_t>(hi), lane)));
+  mm(static_cast<int>(xor_lane<1>(static_cast<uint32_t>(lo), lane)), static_cast<int>(xor_lane<1>(static_cast<uint32_t>(hi), lane)));
+  if (nv > 0 && hi - lo >= kRankBits) return false;  // (wave-uniform; hi >= lo >= 0 here)
+  uint4* const b4 = reinterpret_cast<uint4*>(bm);
+  static_assert(kRankWords == 64 * 8, "a lane owns eight bitmap words");
+  b4[2 * lane] = make_uint4(0u, 0u, 0u, 0u);
+  b4[2 * lane + 1] = make_uint4(0u, 0u, 0u, 0u);
+  lds_order();
+  bool dup = false;
+#pragma unroll
+  for (int r = 0; r < EPL; ++r) {
+    if (row && r * 64 + lane < K && in.id[r] >= 0) {
+      const uint32_t b = static_cast<uint32_t>(in.id[r] - lo), bit = 1u << (b & 31u);
+      dup = dup || (atomicOr(&bm[b >> 5], bit) & bit) != 0u;
+    }
+  }
+  if (__ballot(dup) != 0ull) return false;
+  lds_order();
+  // lane l owns words 8 l .. 8 l + 7
+  const uint4 wa = b4[2 * lane], wb = b4[2 * lane + 1];
+  const uint32_t c[8] = {static_cast<uint32_t>(__builtin_popcount(wa.x)), static_cast<uint32_t>(__builtin_popcount(wa.y)),
+                         static_cast<uint32_t>(__builtin_popcount(wa.z)), static_cast<uint32_t>(__builtin_popcount(wa.w)),
+                         static_cast<uint32_t>(__builtin_popcount(wb.x)), static_cast<uint32_t>(__builtin_popcount(wb.y)),
+                         static_cast<uint32_t>(__builtin_popcount(wb.z)), static_cast<uint32_t>(__builtin_popcount(wb.w))};
+  const uint32_t tot = ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
+  uint32_t run = wave_incl_scan(tot) - tot;
+  uint32_t pr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pr[j] = run;
+    run += c[j];
+  }
+  uint4* const p4 = reinterpret_cast<uint4*>(pre);
+  p4[2 * lane] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+  p4[2 * lane + 1] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+  lds_order();
+  int pads = 0;  // padding slots in the registers before r (wave-uniform)
+#pragma unroll
+  for (int r = 0; r < EPL; ++r) {
+    const bool in_row = row && r * 64 + lane < K;
+    const bool valid = in_row && in.id[r] >= 0, pad = in_row && in.id[r] < 0;
+    const uint64_t pm = __ballot(pad);
+    int pos = 0;
+    if (valid) {
+      const uint32_t b = static_cast<uint32_t>(in.id[r] - lo), w = b >> 5;
+      pos = static_cast<int>(pre[w] + static_cast<uint32_t>(__builtin_popcount(bm[w] & ((1u << (b & 31u)) - 1u))));
+    } else {
+      pos = nv + pads +
+            static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(pm >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(pm), 0u)));
+    }
+    if (valid || pad) {
+      is[pos] = in.id[r];
+      es[pos] = in.lg[r];
+    }
+    pads += __builtin_popcountll(pm);
+  }
+  lds_order();
+  nv_out = nv;
+  return true;
+}
+
 // One row, by one wave, from its loaded ids and logits; es and is are the
 // wave's LDS rows.
 template <int EPL>
 __device__ __forceinline__ void topk_row(const TopkRow<EPL>& in, int64_t q, bool row, int K, int lane, float* es,
-                                         int32_t* is, int32_t* __restrict__ ids_out,
+                                         int32_t* is, uint32_t* bm, uint32_t* pre, int32_t* __restrict__ ids_out,
                                          float* __restrict__ logits_out, float* __restrict__ probs,
                                          int64_t ld_out) {
   constexpr int N = 64 * EPL;  // padded row length, a power of two
-  // element i = r * 64 + lane: partners at distance d < 64 sit in another
-  // lane, at d >= 64 in another register
-  uint64_t key[EPL];
-#pragma unroll
-  for (int r = 0; r < EPL; ++r) {
-    const int i = r * 64 + lane;
-    if (row && i < K) {
-      const int32_t id = in.id[r];
-      const uint32_t hi = id >= 0 ? static_cast<uint32_t>(id) : 0x80000000u;
-      key[r] = static_cast<uint64_t>(hi) << 32 | static_cast<uint32_t>(i);
-    } else {
-      key[r] = ~0ull;
-    }
-  }
-  // keys of 32 bits (id << 10 | slot) when every id of the row is below
-  // 2^21 - 1 (K <= 1024 slots), else of 64 bits: the same order, half the
-  // cross-lane traffic
-  const bool narrow = wave_ids_narrow<EPL>(key);
-  if (narrow) {
-    uint32_t k32[EPL];
-#pragma unroll
-    for (int r = 0; r < EPL; ++r) {
-      const uint32_t hi = static_cast<uint32_t>(key[r] >> 32), lo = static_cast<uint32_t>(key[r]);
-      k32[r] = key[r] == ~0ull ? ~0u : ((hi == 0x80000000u ? 0x1FFFFFu : hi) << 10 | lo);
-    }
-    bitonic<EPL>(k32, lane);
-#pragma unroll
-    for (int r = 0; r < EPL; ++r) {
-      const uint32_t hi = k32[r] >> 10, lo = k32[r] & 0x3FFu;
-      key[r] = k32[r] == ~0u ? ~0ull
-                             : (static_cast<uint64_t>(hi == 0x1FFFFFu ? 0x80000000u : hi) << 32 | lo);
-    }
-  } else {
-    bitonic<EPL>(key, lane);
-  }
-  // ids and logits by source slot from the wave's LDS rows (parked there in
-  // slot order; padding keeps its own negative id); the valid slots come
-  // first. (The previous row's reads of these rows precede these writes in
-  // the wave's order.)
-#pragma unroll
-  for (int r = 0; r < EPL; ++r) {
-    es[r * 64 + lane] = in.lg[r];
-    is[r * 64 + lane] = in.id[r];
-  }
   int32_t idv[EPL];
   float lg[EPL];
-  int nv_lane = 0;
+  int nv = 0;
+  if (topk_count<EPL>(in, row, K, lane, es, is, bm, pre, nv)) {
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+      const int i = r * 64 + lane;
+      const bool in_row = row && i < K;
+      idv[r] = in_row ? is[i] : 0;
+      lg[r] = in_row ? es[i] : 0.0f;
+    }
+  } else {
+    // element i = r * 64 + lane: partners at distance d < 64 sit in another
+    // lane, at d >= 64 in another register
+    uint64_t key[EPL];
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+      const int i = r * 64 + lane;
+      if (row && i < K) {
+        const int32_t id = in.id[r];
+        const uint32_t hi = id >= 0 ? static_cast<uint32_t>(id) : 0x80000000u;
+        key[r] = static_cast<uint64_t>(hi) << 32 | static_cast<uint32_t>(i);
+      } else {
+        key[r] = ~0ull;
+      }
+    }
+    // keys of 32 bits (id << 10 | slot) when every id of the row is below
+    // 2^21 - 1 (K <= 1024 slots), else of 64 bits: the same order, half the
+    // cross-lane traffic
+    const bool narrow = wave_ids_narrow<EPL>(key);
+    if (narrow) {
+      uint32_t k32[EPL];
+#pragma unroll
+      for (int r = 0; r < EPL; ++r) {
+        const uint32_t hi = static_cast<uint32_t>(key[r] >> 32), lo = static_cast<uint32_t>(key[r]);
+        k32[r] = key[r] == ~0ull ? ~0u : ((hi == 0x80000000u ? 0x1FFFFFu : hi) << 10 | lo);
+      }
+      bitonic<EPL>(k32, lane);
+#pragma unroll
+      for (int r = 0; r < EPL; ++r) {
+        const uint32_t hi = k32[r] >> 10, lo = k32[r] & 0x3FFu;
+        key[r] = k32[r] == ~0u ? ~0ull
+                               : (static_cast<uint64_t>(hi == 0x1FFFFFu ? 0x80000000u : hi) << 32 | lo);
+      }
+    } else {
+      bitonic<EPL>(key, lane);
+    }
+    // ids and logits by source slot from the wave's LDS rows (parked there in
+    // slot order; padding keeps its own negative id); the valid slots come
+    // first.
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+      es[r * 64 + lane] = in.lg[r];
+      is[r * 64 + lane] = in.id[r];
+    }
+    int nv_lane = 0;
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+      const int i = r * 64 + lane;
+      const uint32_t slot = static_cast<uint32_t>(key[r]);
+      const bool in_row = row && i < K;
+      idv[r] = in_row ? is[slot] : 0;
+      lg[r] = in_row ? es[slot] : 0.0f;
+      nv_lane += (in_row && (key[r] >> 32) < 0x80000000ull) ? 1 : 0;
+    }
+    uint32_t nvu = static_cast<uint32_t>(nv_lane);
+    nvu += xor_lane<32>(nvu, lane);
+    nvu += xor_lane<16>(nvu, lane);
+    nvu += xor_lane<8>(nvu, lane);
+    nvu += xor_lane<4>(nvu, lane);
+    nvu += xor_lane<2>(nvu, lane);
+    nvu += xor_lane<1>(nvu, lane);
+    nv = static_cast<int>(nvu);
+  }
+  // exact maximum of the valid logits (positions below nv) over the wave
+  // (butterflies over lane distances 32, 16, .., 1, the same in every lane)
   float mx = -__builtin_inff();
 #pragma unroll
-  for (int r = 0; r < EPL; ++r) {
-    const int i = r * 64 + lane;
-    const uint32_t slot = static_cast<uint32_t>(key[r]);
-    const bool in_row = row && i < K;
-    idv[r] = in_row ? is[slot] : 0;
-    lg[r] = in_row ? es[slot] : 0.0f;
-    const bool valid = in_row && (key[r] >> 32) < 0x80000000ull;
-    nv_lane += valid ? 1 : 0;
-    if (valid) mx = mx > lg[r] ? mx : lg[r];
-  }
-  // exact maximum and valid count over the wave
-  // (butterflies over lane distances 32, 16, .., 1, the same in every lane)
+  for (int r = 0; r < EPL; ++r)
+    if (r * 64 + lane < nv) mx = mx > lg[r] ? mx : lg[r];
   auto max_step = [&](float o) { mx = mx > o ? mx : o; };
   max_step(__uint_as_float(xor_lane<32>(__float_as_uint(mx), lane)));
   max_step(__uint_as_float(xor_lane<16>(__float_as_uint(mx), lane)));
@@ -235,14 +354,6 @@ __device__ __forceinline__ void topk_row(const TopkRow<EPL>& in, int64_t q, bool
   max_step(__uint_as_float(xor_lane<4>(__float_as_uint(mx), lane)));
   max_step(__uint_as_float(xor_lane<2>(__float_as_uint(mx), lane)));
   max_step(__uint_as_float(xor_lane<1>(__float_as_uint(mx), lane)));
-  uint32_t nvu = static_cast<uint32_t>(nv_lane);
-  nvu += xor_lane<32>(nvu, lane);
-  nvu += xor_lane<16>(nvu, lane);
-  nvu += xor_lane<8>(nvu, lane);
-  nvu += xor_lane<4>(nvu, lane);
-  nvu += xor_lane<2>(nvu, lane);
-  nvu += xor_lane<1>(nvu, lane);
-  const int nv = static_cast<int>(nvu);
   // e values in sorted order: each wave parks its row in LDS, then every lane
   // runs the row's left-to-right sum from the same uniform-address LDS reads
   // (four values per read, the reads issued ahead of their adds), so the wave
@@ -300,11 +411,14 @@ __global__ __launch_bounds__(256) void topk_canon_kernel(const int32_t* __restri
   constexpr int N = 64 * EPL;
   __shared__ __attribute__((aligned(16))) float es[4][N];  // each wave's logits by slot, then its e values in sorted order
   __shared__ int32_t is[4][N];                             // each wave's ids by slot
+  __shared__ __attribute__((aligned(16))) uint32_t bm[4][kRankWords];   // each wave's id bitmap (counting path)
+  __shared__ __attribute__((aligned(16))) uint32_t pre[4][kRankWords];  // its words' exclusive prefix counts
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   TopkRow<EPL> in;
   topk_load<EPL>(in, ids, logits, q, q < Q, K, ld, lane);
-  topk_row<EPL>(in, q, q < Q, K, lane, es[wave], is[wave], ids_out, logits_out, probs, ld_out);
+  topk_row<EPL>(in, q, q < Q, K, lane, es[wave], is[wave], bm[wave], pre[wave], ids_out, logits_out, probs,
+                 ld_out);
 }
 
 }  // namespace

@@ -71,6 +71,26 @@ def test_padding_keeps_its_own_negative_id():
     check(ids, inp.logits, "topk negative padding")
 
 
+def test_counting_window_edges():
+    """Rows whose distinct valid ids span exactly 16384 values (the widest span
+    counted from the id bitmap) and 16385 (sorted), at base 0 and at 2^24; a
+    narrow row with one repeated id (sorted); all of them sharing workgroups
+    with ordinary rows."""
+    inp = W.topk_inputs(Q=16, K=512, n_keys=8192, seed=13, distinct=True, pad_frac=0.05)
+    ids = inp.ids.copy()
+    rng = np.random.default_rng(17)
+    for q, base, top in [(0, 0, 16383), (1, 0, 16384), (2, 1 << 24, 16383), (3, 1 << 24, 16384), (4, 5, 300000),
+                         (9, (1 << 31) - 16384, 16383)]:
+        valid = ids[q] >= 0
+        n = int(valid.sum())
+        vals = np.concatenate([[0, top], rng.choice(np.arange(1, top), n - 2, replace=False)])
+        ids[q, valid] = (base + rng.permutation(vals)).astype(np.int32)
+    v = np.flatnonzero(ids[5] >= 0)
+    ids[5, v[-1]] = ids[5, v[0]]  # a repeated id
+    note("topk counting window edges")
+    check(ids, inp.logits, "topk window edges")
+
+
 def test_full_size_and_slot_order_invariance():
     inp = W.topk_inputs(seed=7)  # 4096 x 512
     note("topk full size")
