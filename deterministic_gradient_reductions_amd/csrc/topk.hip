@@ -7,9 +7,12 @@
 // softmax is summed again in that order, and a row without any valid id gets
 // probabilities of zero.
 //
-// One wave per row. Each of the K slots becomes a 64-bit key (id << 32 | slot
-// for a valid id, 2^31 << 32 | slot for padding, all ones for the positions
-// that round K up to a power of two): the keys are distinct, so the sorted
+// One wave per row. A row whose valid ids are distinct and span at most
+// kRankBits values is placed by counting from a bitmap of its id window
+// (topk_count); any other row is sorted. For the sort, each of the K slots
+// becomes a 64-bit key (id << 32 | slot for a valid id, 2^31 << 32 | slot
+// for padding, all ones for the positions that round K up to a power of
+// two): the keys are distinct, so the sorted
 // order is unique and equals the stable order with padding last. When every
 // id of the row is below 2^21 - 1 the same order is carried by a 32-bit key
 // (id << 10 | slot, padding as id 2^21 - 1), which halves the cross-lane
