@@ -357,6 +357,69 @@ def test_topk():
         inside("topk rows", np.where(rows < QQ, rows, 0), QQ)
 
 
+def topk_count_positions(row, K, window=16384):
+    """The counting path of the top-k kernel restated: None when the row is sorted instead
+    (a repeated valid id, or valid ids spanning more than `window` values), else every
+    slot's position, with the bitmap word indices checked against the bitmap."""
+    v = row >= 0
+    nv = int(v.sum())
+    pos = np.empty(K, np.int64)
+    if nv:
+        ids = row[v].astype(np.int64)
+        lo, hi = ids.min(), ids.max()
+        if hi - lo >= window:
+            return None
+        b = ids - lo
+        if np.unique(b).size != nv:
+            return None
+        w = b >> 5
+        inside("topk bitmap words", w, window // 32)
+        bm = np.zeros(window // 32, np.uint32)
+        np.bitwise_or.at(bm, w, (np.uint32(1) << (b & 31).astype(np.uint32)))
+        cnt = np.bitwise_count(bm).astype(np.int64)
+        # lane l owns words 8 l .. 8 l + 7: the lane totals' exclusive wave scan, then a running sum
+        lane_tot = cnt.reshape(64, 8).sum(1)
+        lane_pre = np.cumsum(lane_tot) - lane_tot
+        pre = (lane_pre[:, None] + np.cumsum(cnt.reshape(64, 8), 1) - cnt.reshape(64, 8)).ravel()
+        below = np.bitwise_count(bm[w] & ((np.uint32(1) << (b & 31).astype(np.uint32)) - np.uint32(1)))
+        pos[v] = pre[w] + below
+    pos[~v] = nv + np.cumsum(~v)[~v] - 1
+    inside("topk positions", pos, K)
+    return pos
+
+
+def test_topk_counting_positions():
+    """The counting placement gives every slot of the workload's rows (and of edge rows) a
+    distinct position inside the row, and the ids land in the canonical order."""
+    tk = W.topk_inputs(seed=7)
+    Q, K = tk.ids.shape
+    rng = np.random.default_rng(3)
+    edge = []
+    for lo, span in [(0, 16383), (0, 16384), (1 << 24, 16383), ((1 << 31) - 16384, 16383)]:
+        r = tk.ids[0].copy()
+        vals = np.concatenate([[0, span], rng.choice(np.arange(1, span), int((r >= 0).sum()) - 2, replace=False)])
+        r[r >= 0] = lo + rng.permutation(vals)
+        edge.append(r)
+    dup = tk.ids[1].copy()
+    vi = np.flatnonzero(dup >= 0)
+    dup[vi[-1]] = dup[vi[0]]
+    edge += [dup, np.full(K, -1, np.int32)]
+    counted = 0
+    for row in list(tk.ids) + edge:
+        pos = topk_count_positions(row, K)
+        hi = np.where(row >= 0, row.astype(np.int64), 2 ** 31).astype(np.uint64)
+        canon = row[np.argsort((hi << np.uint64(32)) | np.arange(K, dtype=np.uint64))]
+        if pos is None:
+            continue
+        counted += 1
+        assert np.array_equal(np.sort(pos), np.arange(K))
+        placed = np.empty(K, row.dtype)
+        placed[pos] = row
+        assert np.array_equal(placed, canon)
+    assert counted == Q + 4  # every workload row, the two in-window edge rows per base and the all-padding row
+    assert topk_count_positions(edge[1], K) is None and topk_count_positions(dup, K) is None
+
+
 # ------------------------------------------------------------------ index_add / indexer dK
 def replay_index_add(ids, n_rows, dim, L, Q=None, K=None):
     """Descriptors, gather reads, scratch slots and fold reads of det_index_add (and the
