@@ -34,7 +34,8 @@ def check(ids, logits, what, out_pad=0):
 @pytest.mark.parametrize("Q,K,n_keys,distinct,pad", [(64, 512, 8192, True, 0.05), (33, 1000, 4096, True, 0.1),
                                                      (50, 64, 100, False, 0.3), (7, 1, 5, False, 0.5),
                                                      (20, 129, 300, False, 0.0), (9, 1024, 2000, True, 0.02),
-                                                     (12, 37, 20, False, 0.2)])
+                                                     (12, 37, 20, False, 0.2), (16, 37, 5000, True, 0.2),
+                                                     (16, 100, 300, True, 0.1)])
 def test_parity(Q, K, n_keys, distinct, pad):
     note("topk parity Q=%d K=%d distinct=%s pad=%.2f" % (Q, K, distinct, pad))
     inp = W.topk_inputs(Q=Q, K=K, n_keys=n_keys, seed=K, distinct=distinct, pad_frac=pad)
