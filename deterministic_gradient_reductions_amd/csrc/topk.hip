@@ -155,12 +155,20 @@ __device__ __forceinline__ void topk_load(TopkRow<EPL>& in, const int32_t* __res
                                           int lane) {
   const int32_t* const ir = ids + (row ? q : 0) * ld;
   const float* const lr = logits + (row ? q : 0) * ld;
+  // Every id load before the logit loads, none under a branch (a position past
+  // K reads slot K - 1 of the row and is then replaced): the placement needs
+  // only the ids, so it starts while the logits are still in flight.
+  int32_t iv[EPL];
+  float lv[EPL];
+#pragma unroll
+  for (int r = 0; r < EPL; ++r) iv[r] = ir[r * 64 + lane < K ? r * 64 + lane : K - 1];
+#pragma unroll
+  for (int r = 0; r < EPL; ++r) lv[r] = lr[r * 64 + lane < K ? r * 64 + lane : K - 1];
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
-    const int i = r * 64 + lane;
-    const bool in_row = row && i < K;
-    in.id[r] = in_row ? ir[i] : 0;
-    in.lg[r] = in_row ? lr[i] : 0.0f;
+    const bool in_row = row && r * 64 + lane < K;
+    in.id[r] = in_row ? iv[r] : 0;
+    in.lg[r] = in_row ? lv[r] : 0.0f;
   }
 }
 
